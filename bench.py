@@ -1,0 +1,255 @@
+#!/usr/bin/env python3
+"""Attention throughput on one MI355X.
+
+One step = the whole hot path on one batch: fa_fwd (scores, mask, online
+softmax, O and L) followed by fa_bwd (D, dQ, dK, dV recomputed from L).
+Prints one JSON line with forward+backward TFLOP/s (the value), forward
+TFLOP/s, both as fractions of the bf16 dense MFMA peak, a roofline entry for
+the dominant kernel and the fp64 CPU oracle timed on the host as a baseline.
+
+FLOP convention (algorithmic work over visible (query, key) pairs; masked-out
+tiles are never credited): forward 4*d*pairs, backward 10*d*pairs.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--cpu-baseline off]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import workloads as wl  # noqa: E402
+
+METRIC = "attention TFLOP/s (fwd, fwd+bwd) and % of MI355X bf16 MFMA peak"
+PEAK_TFLOPS = {"bf16": 2516.6, "f32": 157.3}   # dense MFMA bf16; fp32 vector/matrix
+PEAK_HBM_GBS = 8000.0
+DEFAULT_WORKLOAD = "gpt2s_causal_b8h12n1024"
+
+
+# --------------------------------------------------------------- accounting
+
+def visible_pairs(N: int, H: int, causal: bool, seqlens, block_mask, mask_block: int = 128,
+                  B: int = 1) -> int:
+    """Number of visible (query, key) pairs summed over batch and heads."""
+    lens = [N] * B if seqlens is None else [int(min(max(s, 0), N)) for s in seqlens]
+    total = 0
+    for L in lens:
+        if block_mask is None:
+            if causal:
+                total += L * (L + 1) // 2 + (N - L) * L
+            else:
+                total += N * L
+            continue
+        I, J = np.nonzero(np.asarray(block_mask))
+        r0 = I.astype(np.int64) * mask_block
+        r1 = np.minimum(r0 + mask_block, N)
+        c0 = J.astype(np.int64) * mask_block
+        c1 = np.minimum(c0 + mask_block, L)
+        keep = c1 > c0
+        r0, r1, c0, c1 = r0[keep], r1[keep], c0[keep], c1[keep]
+        if not causal:
+            total += int(((r1 - r0) * (c1 - c0)).sum())
+        else:
+            for a, b_, c, e in zip(r0, r1, c0, c1):
+                i = np.arange(a, b_)
+                total += int(np.clip(np.minimum(i + 1, e) - c, 0, None).sum())
+    return total * H
+
+
+def kernel_bytes(B, H, N, d, esize, seqlens):
+    """Compulsory HBM bytes of the forward kernel and of the backward pair."""
+    t = B * H * N * d * esize
+    kv_valid = H * d * esize * (B * N if seqlens is None else int(np.minimum(seqlens, N).sum()))
+    rowstat = B * H * N * 4
+    fwd = 2 * t + 2 * kv_valid + rowstat                      # Q, O + K, V + L
+    bwd = 5 * t + 2 * kv_valid + 3 * rowstat                  # Q,O,dO,dQ..dV + K,V + L,D,D
+    return fwd, bwd
+
+
+# ------------------------------------------------------------------- timing
+
+def run_gpu(w: wl.Workload, inp: dict, steps: int, warmup: int):
+    import torch
+    import exact_io_aware_64_amd as fa
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    to = lambda x: torch.from_numpy(x).to(tdt).to(dev)  # noqa: E731
+    q, k, v, do = (to(inp[n]) for n in ("q", "k", "v", "do"))
+    sl = None if inp["seqlens"] is None else torch.from_numpy(inp["seqlens"]).to(dev)
+    bm = None if inp["block_mask"] is None else torch.from_numpy(inp["block_mask"]).to(dev)
+    o = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+    code = fa.FA_BF16 if w.dtype == "bf16" else fa.FA_F32
+    ws = torch.empty(fa.fa_bwd_workspace_bytes(code, w.B, w.H, w.N, w.d), dtype=torch.uint8,
+                     device=dev)
+    kw = dict(scale=w.scale, causal=w.causal, seqlens_k=sl, block_mask=bm, mask_block=128)
+    stream = torch.cuda.current_stream(dev)
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        fa.fa_fwd(q, k, v, o, lse, **kw)
+        if ev is not None:
+            ev[1].record(stream)
+        fa.fa_bwd(q, k, v, o, do, lse, dq, dk, dv, ws, **kw)
+        if ev is not None:
+            ev[2].record(stream)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    # wall clock over exactly `steps` steps, no events inside
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3 / steps
+    # per-call device durations from HIP events on the launch stream
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    for e in evs:
+        step(e)
+    torch.cuda.synchronize()
+    fwd_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    bwd_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+    props = torch.cuda.get_device_properties(dev)
+    outs = dict(o=o, lse=lse, dq=dq, dk=dk, dv=dv)
+    return wall_ms, fwd_ms, bwd_ms, props, outs
+
+
+def cpu_baseline(w: wl.Workload, inp: dict, outs: dict, flops_fb: float):
+    """The fp64 oracle as it stands, on the host cores, on the same inputs.
+    Full problem when it fits ~10-30 s, else a sample of heads, scaled."""
+    from oracle import attention_ref as ref
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        cores = len(os.sched_getaffinity(0))
+    args = dict(scale=w.scale, causal=w.causal, seqlens=inp["seqlens"],
+                block_mask=inp["block_mask"], mask_block=128)
+    H = w.H
+    # one head first, to size the sample
+    sub = lambda x, hs: x[:, :hs]  # noqa: E731
+    t0 = time.perf_counter()
+    ref.forward(sub(inp["q"], 1), sub(inp["k"], 1), sub(inp["v"], 1), **args)
+    ref.backward(sub(inp["q"], 1), sub(inp["k"], 1), sub(inp["v"], 1), sub(inp["do"], 1), **args)
+    per_head = time.perf_counter() - t0
+    hs = int(max(1, min(H, 15.0 / max(per_head, 1e-6))))
+    t0 = time.perf_counter()
+    O, L = ref.forward(sub(inp["q"], hs), sub(inp["k"], hs), sub(inp["v"], hs), **args)
+    G = ref.backward(sub(inp["q"], hs), sub(inp["k"], hs), sub(inp["v"], hs),
+                     sub(inp["do"], hs), **args)
+    secs = time.perf_counter() - t0
+    frac = hs / H
+    tflops = flops_fb * frac / secs / 1e12
+    # the same sample doubles as a parity spot check of the GPU outputs
+    npf = lambda t: t[:, :hs].float().cpu().numpy().astype(np.float64)  # noqa: E731
+    parity = dict(O_maxabs=float(np.abs(npf(outs["o"]) - O).max()),
+                  L_maxabs=float(np.abs(npf(outs["lse"]) - L).max()))
+    for name, g in zip(("dQ", "dK", "dV"), G):
+        parity[f"{name}_relfro"] = float(np.linalg.norm(npf(outs["d" + name[1].lower()]) - g)
+                                         / np.linalg.norm(g))
+    base = dict(value=tflops, unit="TFLOP/s", cores=int(cores), kind="oracle",
+                sample=f"fp64 NumPy oracle fwd+bwd on {hs} of {H} heads x batch {w.B} "
+                       f"(whole sequences), {secs:.1f} s; value scaled by FLOPs of the sample",
+                seconds=secs)
+    return base, parity
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=wl.WORKLOAD_ORDER)
+    ap.add_argument("--cpu-baseline", default="on", choices=["on", "off"])
+    args = ap.parse_args(argv)
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: the attention path needs no collective and "
+              "this build runs on a single MI355X (heads shard across GPUs with no "
+              "communication). Run with --gpus 1.", file=sys.stderr)
+        return 2
+
+    w = wl.WORKLOADS[args.workload]
+    inp = wl.make_inputs(w)
+    pairs = visible_pairs(w.N, w.H, w.causal, inp["seqlens"], inp["block_mask"], 128, w.B)
+    flops_f = 4.0 * w.d * pairs
+    flops_b = 10.0 * w.d * pairs
+    esize = 2 if w.dtype == "bf16" else 4
+    bytes_f, bytes_b = kernel_bytes(w.B, w.H, w.N, w.d, esize, inp["seqlens"])
+
+    wall_ms, fwd_ms, bwd_ms, props, outs = run_gpu(w, inp, args.steps, args.warmup)
+    peak = PEAK_TFLOPS[w.dtype]
+    tf_fb = (flops_f + flops_b) / (wall_ms * 1e-3) / 1e12
+    tf_f = flops_f / (fwd_ms * 1e-3) / 1e12
+    tf_b = flops_b / (bwd_ms * 1e-3) / 1e12
+
+    # Roofline of the dominant launch (the one with the largest device time).
+    def roof(name, flops, nbytes, ms):
+        t_mfma = flops / (peak * 1e12)
+        t_hbm = nbytes / (PEAK_HBM_GBS * 1e9)
+        if t_mfma >= t_hbm:
+            ach = flops / (ms * 1e-3) / 1e12
+            return dict(kernel=name, bound="mfma", achieved=ach, peak=peak, unit="TFLOP/s",
+                        frac=ach / peak, traffic=None)
+        ach = nbytes / (ms * 1e-3) / 1e9
+        return dict(kernel=name, bound="hbm", achieved=ach, peak=PEAK_HBM_GBS, unit="GB/s",
+                    frac=ach / PEAK_HBM_GBS, traffic=None)
+
+    if fwd_ms >= bwd_ms:
+        roofline = roof("fwd_bf16_kernel", flops_f, bytes_f, fwd_ms)
+    else:
+        roofline = roof("dq_kernel+dkdv_kernel", flops_b, bytes_b, bwd_ms)
+
+    base = None
+    parity = None
+    if args.cpu_baseline == "on":
+        base, parity = cpu_baseline(w, inp, outs, flops_f + flops_b)
+
+    line = {
+        "metric": METRIC,
+        "value": tf_fb,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": wall_ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic: seeded iid normal inputs, bf16-rounded (RNE)"
+        if w.dtype == "bf16" else "synthetic: seeded iid normal fp32 inputs",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d,
+                   "causal": w.causal, "key_padding": inp["seqlens"] is not None,
+                   "block_sparse": inp["block_mask"] is not None, "pairs": pairs},
+        "fwd_tflops": tf_f,
+        "bwd_tflops": tf_b,
+        "fwd_ms": fwd_ms,
+        "bwd_ms": bwd_ms,
+        "fwd_frac_peak": tf_f / peak,
+        "fwdbwd_frac_peak": tf_fb / peak,
+        "peak_tflops": peak,
+        "device": {"name": props.name, "cus": props.multi_processor_count},
+        "roofline": roofline,
+        "cpu_baseline": base,
+        "parity_sample": parity,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

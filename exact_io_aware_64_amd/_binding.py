@@ -1,0 +1,182 @@
+"""ctypes binding of libfa.so (include/fa.h).
+
+Argument marshalling only: PyTorch tensors provide device memory, strides and
+the current HIP stream; every step of the computation runs in the library's
+HIP kernels.  There is no fallback: if libfa.so is missing or fails to load,
+every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libfa.so")
+
+FA_BF16 = 0
+FA_F32 = 1
+FA_OK = 0
+FA_ERR_INVALID_ARG = 1
+FA_ERR_UNSUPPORTED = 2
+FA_ERR_HIP = 3
+
+# Public entry points declared in include/fa.h.
+EXPORTED = ("fa_fwd", "fa_bwd", "fa_bwd_workspace_bytes", "fa_status_string", "fa_last_error")
+
+
+class FaError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{fa_status_string(status)}: {message}")
+        self.status = status
+
+
+class fa_strides(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int64), ("head", ctypes.c_int64), ("seq", ctypes.c_int64)]
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Loads libfa.so once.  Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(
+            f"{path} not found: build it first (python -m exact_io_aware_64_amd.build)")
+    lib = ctypes.CDLL(path)
+    P, S, I, F = ctypes.c_void_p, fa_strides, ctypes.c_int, ctypes.c_float
+    lib.fa_fwd.restype = I
+    lib.fa_fwd.argtypes = [I, P, S, P, S, P, S, P, S, P, I, I, I, I, F, I, P, P, I, P]
+    lib.fa_bwd.restype = I
+    lib.fa_bwd.argtypes = [I, P, S, P, S, P, S, P, S, P, S, P, P, S, P, S, P, S, P,
+                           ctypes.c_size_t, I, I, I, I, F, I, P, P, I, P]
+    lib.fa_bwd_workspace_bytes.restype = ctypes.c_size_t
+    lib.fa_bwd_workspace_bytes.argtypes = [I, I, I, I, I]
+    lib.fa_status_string.restype = ctypes.c_char_p
+    lib.fa_status_string.argtypes = [I]
+    lib.fa_last_error.restype = ctypes.c_char_p
+    lib.fa_last_error.argtypes = []
+    _lib = lib
+    return lib
+
+
+def fa_status_string(status: int) -> str:
+    return load_library().fa_status_string(int(status)).decode()
+
+
+def fa_last_error() -> str:
+    return load_library().fa_last_error().decode()
+
+
+def fa_bwd_workspace_bytes(dtype: int, B: int, H: int, N: int, d: int) -> int:
+    return int(load_library().fa_bwd_workspace_bytes(dtype, B, H, N, d))
+
+
+# ------------------------------------------------------------ marshalling
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return FA_BF16
+    if t.dtype == torch.float32:
+        return FA_F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _strides(t) -> fa_strides:
+    if t.dim() != 4:
+        raise ValueError("expected a rank-4 tensor indexed [B, H, N, d]")
+    if t.stride(3) != 1:
+        raise ValueError("the last dimension must be contiguous")
+    return fa_strides(t.stride(0), t.stride(1), t.stride(2))
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(t, stream):
+    if stream is not None:
+        return stream
+    return _torch().cuda.current_stream(t.device).cuda_stream
+
+
+def _check(st: int):
+    if st != FA_OK:
+        raise FaError(st, fa_last_error())
+
+
+def fa_fwd(q, k, v, o, lse, *, scale: float, causal: bool = False, seqlens_k=None,
+           block_mask=None, mask_block: int = 128, stream=None) -> None:
+    """Calls fa_fwd on tensors indexed [B, H, N, d] (any strides with a
+    contiguous last dimension); o and lse ([B, H, N] fp32, contiguous) are
+    written."""
+    lib = load_library()
+    B, H, N, d = q.shape
+    for name, t in (("k", k), ("v", v), ("o", o)):
+        if tuple(t.shape) != (B, H, N, d) or t.dtype != q.dtype:
+            raise ValueError(f"{name} must match q in shape and dtype")
+    if tuple(lse.shape) != (B, H, N) or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous fp32 [B, H, N] tensor")
+    st = lib.fa_fwd(_dtype_code(q), _ptr(q), _strides(q), _ptr(k), _strides(k), _ptr(v),
+                    _strides(v), _ptr(o), _strides(o), _ptr(lse), B, H, N, d, float(scale),
+                    int(bool(causal)), _ptr(seqlens_k), _ptr(block_mask), int(mask_block),
+                    _stream(q, stream))
+    _check(st)
+
+
+def fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, workspace, *, scale: float,
+           causal: bool = False, seqlens_k=None, block_mask=None, mask_block: int = 128,
+           stream=None) -> None:
+    """Calls fa_bwd; dq, dk, dv are written in full."""
+    lib = load_library()
+    B, H, N, d = q.shape
+    for name, t in (("k", k), ("v", v), ("o", o), ("dout", dout), ("dq", dq), ("dk", dk),
+                    ("dv", dv)):
+        if tuple(t.shape) != (B, H, N, d) or t.dtype != q.dtype:
+            raise ValueError(f"{name} must match q in shape and dtype")
+    nbytes = workspace.numel() * workspace.element_size()
+    st = lib.fa_bwd(_dtype_code(q), _ptr(q), _strides(q), _ptr(k), _strides(k), _ptr(v),
+                    _strides(v), _ptr(o), _strides(o), _ptr(dout), _strides(dout), _ptr(lse),
+                    _ptr(dq), _strides(dq), _ptr(dk), _strides(dk), _ptr(dv), _strides(dv),
+                    _ptr(workspace), nbytes, B, H, N, d, float(scale), int(bool(causal)),
+                    _ptr(seqlens_k), _ptr(block_mask), int(mask_block), _stream(q, stream))
+    _check(st)
+
+
+# --------------------------------------------- allocating convenience calls
+
+def forward(q, k, v, *, scale: float, causal: bool = False, seqlens_k=None, block_mask=None,
+            mask_block: int = 128):
+    """Allocates O (contiguous [B, H, N, d]) and L, then calls fa_fwd."""
+    torch = _torch()
+    B, H, N, d = q.shape
+    o = torch.empty((B, H, N, d), dtype=q.dtype, device=q.device)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    fa_fwd(q, k, v, o, lse, scale=scale, causal=causal, seqlens_k=seqlens_k,
+           block_mask=block_mask, mask_block=mask_block)
+    return o, lse
+
+
+def backward(q, k, v, o, dout, lse, *, scale: float, causal: bool = False, seqlens_k=None,
+             block_mask=None, mask_block: int = 128, workspace=None):
+    """Allocates dQ, dK, dV (and the workspace unless given), then calls fa_bwd."""
+    torch = _torch()
+    B, H, N, d = q.shape
+    dq = torch.empty((B, H, N, d), dtype=q.dtype, device=q.device)
+    dk = torch.empty_like(dq)
+    dv = torch.empty_like(dq)
+    if workspace is None:
+        nb = fa_bwd_workspace_bytes(_dtype_code(q), B, H, N, d)
+        workspace = torch.empty(nb, dtype=torch.uint8, device=q.device)
+    fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, workspace, scale=scale, causal=causal,
+           seqlens_k=seqlens_k, block_mask=block_mask, mask_block=mask_block)
+    return dq, dk, dv

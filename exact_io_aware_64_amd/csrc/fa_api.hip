@@ -1,0 +1,203 @@
+// Host side of the C ABI declared in include/fa.h: argument validation,
+// launch-argument packing and dispatch.  Validation finishes before the
+// first HIP call, so rejected calls never touch the device.
+#include "../../include/fa.h"
+
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "fa_internal.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+fa_status fail(fa_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+fa_status check_tensor(const char* name, const void* p, fa_strides s, int elem_align) {
+  if (p == nullptr) return fail(FA_ERR_INVALID_ARG, "%s is NULL", name);
+  if (!aligned16(p)) return fail(FA_ERR_INVALID_ARG, "%s is not 16-byte aligned", name);
+  if (s.batch < 0 || s.head < 0 || s.seq < 0)
+    return fail(FA_ERR_INVALID_ARG, "%s has a negative stride", name);
+  if (s.batch % elem_align || s.head % elem_align || s.seq % elem_align)
+    return fail(FA_ERR_INVALID_ARG, "%s strides must be multiples of %d elements", name,
+                elem_align);
+  return FA_OK;
+}
+
+fa_status check_common(fa_dtype dtype, int B, int H, int N, int d, float scale,
+                       const uint8_t* block_mask, int mask_block, int* elem_align) {
+  if (dtype != FA_BF16 && dtype != FA_F32)
+    return fail(FA_ERR_INVALID_ARG, "unknown dtype %d", (int)dtype);
+  if (B <= 0 || H <= 0 || N <= 0)
+    return fail(FA_ERR_INVALID_ARG, "B, H and N must be positive (got %d, %d, %d)", B, H, N);
+  if (d != 64) return fail(FA_ERR_UNSUPPORTED, "head dimension %d is not supported (only 64)", d);
+  if (!(scale > 0.f) || !isfinite(scale))
+    return fail(FA_ERR_INVALID_ARG, "scale must be positive and finite");
+  const long long tiles = ((long long)N + fa::kTile - 1) / fa::kTile;
+  if (tiles * (long long)B * H > 0x7fffffffLL)
+    return fail(FA_ERR_UNSUPPORTED, "problem too large for one launch grid");
+  if (block_mask != nullptr) {
+    if (mask_block <= 0 || mask_block % 128 != 0)
+      return fail(FA_ERR_INVALID_ARG, "mask_block must be a positive multiple of 128 (got %d)",
+                  mask_block);
+    if (tiles > fa::kMaxListTiles)
+      return fail(FA_ERR_UNSUPPORTED, "block mask supports N <= %d", fa::kMaxListTiles * 64);
+  }
+  *elem_align = dtype == FA_BF16 ? 8 : 4;
+  return FA_OK;
+}
+
+fa::Strides cvt(fa_strides s) { return fa::Strides{s.batch, s.head, s.seq}; }
+
+fa_status hip_status(hipError_t e) {
+  if (e == hipSuccess) {
+    g_err[0] = '\0';
+    return FA_OK;
+  }
+  return fail(FA_ERR_HIP, "HIP error %d: %s", (int)e, hipGetErrorString(e));
+}
+
+}  // namespace
+
+extern "C" {
+
+fa_status fa_fwd(fa_dtype dtype, const void* q, fa_strides q_strides, const void* k,
+                 fa_strides k_strides, const void* v, fa_strides v_strides, void* o,
+                 fa_strides o_strides, float* lse, int B, int H, int N, int d, float scale,
+                 int causal, const int32_t* seqlens_k, const uint8_t* block_mask,
+                 int mask_block, hipStream_t stream) {
+  int al = 0;
+  fa_status st = check_common(dtype, B, H, N, d, scale, block_mask, mask_block, &al);
+  if (st != FA_OK) return st;
+  if ((st = check_tensor("q", q, q_strides, al)) != FA_OK) return st;
+  if ((st = check_tensor("k", k, k_strides, al)) != FA_OK) return st;
+  if ((st = check_tensor("v", v, v_strides, al)) != FA_OK) return st;
+  if ((st = check_tensor("o", o, o_strides, al)) != FA_OK) return st;
+  if (lse == nullptr) return fail(FA_ERR_INVALID_ARG, "lse is NULL");
+  if (!aligned16(lse)) return fail(FA_ERR_INVALID_ARG, "lse is not 16-byte aligned");
+  if (seqlens_k != nullptr && ((uintptr_t)seqlens_k & 3u))
+    return fail(FA_ERR_INVALID_ARG, "seqlens_k is not 4-byte aligned");
+
+  fa::FwdArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.lse = lse;
+  a.sq = cvt(q_strides);
+  a.sk = cvt(k_strides);
+  a.sv = cvt(v_strides);
+  a.so = cvt(o_strides);
+  a.B = B;
+  a.H = H;
+  a.N = N;
+  a.scale = scale;
+  a.scale_log2 = (float)((double)scale * 1.4426950408889634);
+  a.seqlens = seqlens_k;
+  a.bmask = block_mask;
+  a.mask_block = block_mask ? mask_block : 128;
+  a.n_mask_tiles = (N + a.mask_block - 1) / a.mask_block;
+  const hipError_t e = dtype == FA_BF16 ? fa::launch_fwd_bf16(a, causal != 0, stream)
+                                        : fa::launch_fwd_f32(a, causal != 0, stream);
+  return hip_status(e);
+}
+
+size_t fa_bwd_workspace_bytes(fa_dtype dtype, int B, int H, int N, int d) {
+  (void)dtype;
+  (void)d;
+  if (B <= 0 || H <= 0 || N <= 0) return 0;
+  const size_t bytes = (size_t)B * (size_t)H * (size_t)N * sizeof(float);
+  return (bytes + 255) & ~(size_t)255;
+}
+
+fa_status fa_bwd(fa_dtype dtype, const void* q, fa_strides q_strides, const void* k,
+                 fa_strides k_strides, const void* v, fa_strides v_strides, const void* o,
+                 fa_strides o_strides, const void* dout, fa_strides dout_strides,
+                 const float* lse, void* dq, fa_strides dq_strides, void* dk,
+                 fa_strides dk_strides, void* dv, fa_strides dv_strides, void* workspace,
+                 size_t workspace_bytes, int B, int H, int N, int d, float scale, int causal,
+                 const int32_t* seqlens_k, const uint8_t* block_mask, int mask_block,
+                 hipStream_t stream) {
+  int al = 0;
+  fa_status st = check_common(dtype, B, H, N, d, scale, block_mask, mask_block, &al);
+  if (st != FA_OK) return st;
+  if ((st = check_tensor("q", q, q_strides, al)) != FA_OK) return st;
+  if ((st = check_tensor("k", k, k_strides, al)) != FA_OK) return st;
+  if ((st = check_tensor("v", v, v_strides, al)) != FA_OK) return st;
+  if ((st = check_tensor("o", o, o_strides, al)) != FA_OK) return st;
+  if ((st = check_tensor("dout", dout, dout_strides, al)) != FA_OK) return st;
+  if ((st = check_tensor("dq", dq, dq_strides, al)) != FA_OK) return st;
+  if ((st = check_tensor("dk", dk, dk_strides, al)) != FA_OK) return st;
+  if ((st = check_tensor("dv", dv, dv_strides, al)) != FA_OK) return st;
+  if (lse == nullptr) return fail(FA_ERR_INVALID_ARG, "lse is NULL");
+  if (!aligned16(lse)) return fail(FA_ERR_INVALID_ARG, "lse is not 16-byte aligned");
+  if (workspace == nullptr) return fail(FA_ERR_INVALID_ARG, "workspace is NULL");
+  if (!aligned16(workspace)) return fail(FA_ERR_INVALID_ARG, "workspace is not 16-byte aligned");
+  const size_t need = fa_bwd_workspace_bytes(dtype, B, H, N, d);
+  if (workspace_bytes < need)
+    return fail(FA_ERR_INVALID_ARG, "workspace too small: %zu < %zu bytes", workspace_bytes,
+                need);
+  if (seqlens_k != nullptr && ((uintptr_t)seqlens_k & 3u))
+    return fail(FA_ERR_INVALID_ARG, "seqlens_k is not 4-byte aligned");
+
+  fa::BwdArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.dout = dout;
+  a.lse = lse;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.dsum = (float*)workspace;
+  a.sq = cvt(q_strides);
+  a.sk = cvt(k_strides);
+  a.sv = cvt(v_strides);
+  a.so = cvt(o_strides);
+  a.sdo = cvt(dout_strides);
+  a.sdq = cvt(dq_strides);
+  a.sdk = cvt(dk_strides);
+  a.sdv = cvt(dv_strides);
+  a.B = B;
+  a.H = H;
+  a.N = N;
+  a.scale = scale;
+  a.scale_log2 = (float)((double)scale * 1.4426950408889634);
+  a.seqlens = seqlens_k;
+  a.bmask = block_mask;
+  a.mask_block = block_mask ? mask_block : 128;
+  a.n_mask_tiles = (N + a.mask_block - 1) / a.mask_block;
+  const hipError_t e = dtype == FA_BF16 ? fa::launch_bwd_bf16(a, causal != 0, stream)
+                                        : fa::launch_bwd_f32(a, causal != 0, stream);
+  return hip_status(e);
+}
+
+const char* fa_status_string(fa_status status) {
+  switch (status) {
+    case FA_OK:
+      return "FA_OK";
+    case FA_ERR_INVALID_ARG:
+      return "FA_ERR_INVALID_ARG";
+    case FA_ERR_UNSUPPORTED:
+      return "FA_ERR_UNSUPPORTED";
+    case FA_ERR_HIP:
+      return "FA_ERR_HIP";
+  }
+  return "FA_UNKNOWN_STATUS";
+}
+
+const char* fa_last_error(void) { return g_err; }
+
+}  // extern "C"

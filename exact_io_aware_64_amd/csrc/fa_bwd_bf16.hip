@@ -1,0 +1,425 @@
+// Attention backward for gfx950, bf16 inputs, fp32 accumulation.
+//
+// The pages only say that the backward pass keeps the softmax statistics and
+// recomputes the attention blocks from them instead of reading a stored
+// N x N matrix (researchpapers.dev explainer, "tiling and recomputation";
+// suanlizi.com summary, "recomputation").  With f = sum(dO * O) the
+// gradients are
+//   P = exp(s - L),  dP = dO V^T,  D_i = dot(dO_i, O_i),  dS = P * (dP - D),
+//   dV = P^T dO,     dK = scale dS^T Q,   dQ = scale dS K.
+//
+// Two kernels run back to back on the caller's stream, so no gradient needs
+// atomics or a transpose of dS:
+//  * dq_kernel: query-stationary, like the forward.  Each lane owns one query
+//    with its Q, dO fragments, L and D in registers; K/V tiles stream through
+//    LDS.  S^T = K Q^T and dP^T = V dO^T come out of the MFMA with one query
+//    per lane, and dQ^T = K^T dS^T takes dS^T straight from the accumulator.
+//    It first computes D for its rows and stores it in the workspace.
+//  * dkdv_kernel: key-stationary.  Each lane owns one key with its K, V
+//    fragments in registers; Q/dO tiles (row-major and transposed copies), L
+//    and D stream through LDS.  S = Q K^T and dP = dO V^T come out with one
+//    key per lane, which is exactly the B operand of dV^T = dO^T P and
+//    dK^T = Q^T dS.
+// Masked tiles are skipped exactly as in the forward pass.
+#include "fa_device.h"
+
+namespace fa {
+namespace {
+
+constexpr int kBQ = 128;   // dq_kernel: query rows per workgroup
+constexpr int kBK = 128;   // dkdv_kernel: key rows per workgroup
+
+// ------------------------------------------------------------------ dQ (+D)
+
+template <bool CAUSAL, bool SEQLEN, bool BMASK>
+__global__ __launch_bounds__(256) void dq_kernel(BwdArgs a) {
+  __shared__ __attribute__((aligned(16))) uint16_t s_k[2][kTile * kRowStride];
+  __shared__ __attribute__((aligned(16))) uint16_t s_kt[2][kTile * kTStride];
+  __shared__ __attribute__((aligned(16))) uint16_t s_v[2][kTile * kRowStride];
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int r = lane & 31, hl = lane >> 5;
+  const int BH = a.B * a.H;
+  const int nqt = (a.N + kBQ - 1) / kBQ;
+  const int id = blockIdx.x;
+  const int qt = CAUSAL ? (nqt - 1 - id / BH) : (id / BH);
+  const int bh = id % BH;
+  const int b = bh / a.H, hh = bh % a.H;
+  const int q0 = qt * kBQ;
+  const int qw = q0 + 32 * w;
+  const int qi = qw + r;
+
+  int kv_len = a.N;
+  if constexpr (SEQLEN) kv_len = min(max(a.seqlens[b], 0), a.N);
+  int kend = kv_len;
+  if constexpr (CAUSAL) kend = min(kend, q0 + kBQ);
+  const int ntk = (kend + kTile - 1) / kTile;
+
+  int nlist = ntk;
+  [[maybe_unused]] uint16_t* tlist = nullptr;
+  if constexpr (BMASK) {
+    __shared__ uint16_t s_list[kMaxListTiles];
+    __shared__ int s_scan[4];
+    tlist = s_list;
+    const int row = q0 / a.mask_block;
+    nlist = build_tile_list(s_list, s_scan, a.bmask + (int64_t)row * a.n_mask_tiles, 1,
+                            a.n_mask_tiles, a.mask_block / kTile, 0, ntk);
+  }
+
+  const uint16_t* Q = (const uint16_t*)a.q + b * a.sq.b + hh * a.sq.h;
+  const uint16_t* K = (const uint16_t*)a.k + b * a.sk.b + hh * a.sk.h;
+  const uint16_t* V = (const uint16_t*)a.v + b * a.sv.b + hh * a.sv.h;
+  const uint16_t* O = (const uint16_t*)a.o + b * a.so.b + hh * a.so.h;
+  const uint16_t* dO = (const uint16_t*)a.dout + b * a.sdo.b + hh * a.sdo.h;
+
+  bf16x8 qf[4], dof[4];
+  float Dq = 0.f;
+  {
+    const uint4 z = make_uint4(0, 0, 0, 0);
+    const bool in = qi < a.N;
+    const uint16_t* qp = Q + (int64_t)qi * a.sq.s + 8 * hl;
+    const uint16_t* dp = dO + (int64_t)qi * a.sdo.s + 8 * hl;
+    const uint16_t* opp = O + (int64_t)qi * a.so.s + 8 * hl;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      qf[ks] = as_bf16x8(in ? ldg16(qp + 16 * ks) : z);
+      dof[ks] = as_bf16x8(in ? ldg16(dp + 16 * ks) : z);
+      const bf16x8 of = as_bf16x8(in ? ldg16(opp + 16 * ks) : z);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) Dq += (float)dof[ks][e] * (float)of[e];
+    }
+  }
+  Dq = half_sum(Dq);
+  float L2 = kInf;  // +inf makes every probability of a dead or padding row 0
+  if (qi < a.N) {
+    if (hl == 0) a.dsum[(int64_t)bh * a.N + qi] = Dq;
+    const float L = a.lse[(int64_t)bh * a.N + qi];
+    if (L != -kInf) L2 = L * kLog2e;
+  }
+  const float c = a.scale_log2;
+
+  f32x16 acc[2] = {zero16(), zero16()};
+
+  // Staging: K rows 2*(tid/8), 2*(tid/8)+1 row-major and transposed; V rows
+  // tid/8 and tid/8+32 row-major; 16-byte column tid%8.
+  const int sr = tid >> 3, sc = tid & 7;
+  uint4 kreg[2], vreg[2];
+  auto tile_at = [&](int it) -> int {
+    if constexpr (BMASK) return tlist[it];
+    return it;
+  };
+  auto gload = [&](int t) {
+    const int k0 = t * kTile;
+    const uint4 z = make_uint4(0, 0, 0, 0);
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int kk = k0 + 2 * sr + u;
+      kreg[u] = kk < a.N ? ldg16(K + (int64_t)kk * a.sk.s + 8 * sc) : z;
+      const int kv = k0 + sr + 32 * u;
+      vreg[u] = kv < a.N ? ldg16(V + (int64_t)kv * a.sv.s + 8 * sc) : z;
+    }
+  };
+  auto swrite = [&](int buf) {
+    store_row16(s_k[buf], 2 * sr, sc, kreg[0]);
+    store_row16(s_k[buf], 2 * sr + 1, sc, kreg[1]);
+    store_pair_transposed(s_kt[buf], 2 * sr, sc, kreg[0], kreg[1]);
+    store_row16(s_v[buf], sr, sc, vreg[0]);
+    store_row16(s_v[buf], sr + 32, sc, vreg[1]);
+  };
+
+  if (nlist > 0) {
+    gload(tile_at(0));
+    swrite(0);
+  }
+  __syncthreads();
+
+  for (int it = 0; it < nlist; ++it) {
+    const int buf = it & 1;
+    const int k0 = tile_at(it) * kTile;
+    if (it + 1 < nlist) gload(tile_at(it + 1));
+
+    const bool active = !CAUSAL || (k0 <= qw + 31);
+    if (active) {
+      const uint16_t* ks_ = s_k[buf];
+      const uint16_t* kt_ = s_kt[buf];
+      const uint16_t* vs_ = s_v[buf];
+      f32x16 st[2], dpt[2];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        st[kb] = zero16();
+        dpt[kb] = zero16();
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+          const int off = (32 * kb + r) * kRowStride + 16 * ks + 8 * hl;
+          st[kb] = mfma32(lds_row8(ks_ + off), qf[ks], st[kb]);
+          dpt[kb] = mfma32(lds_row8(vs_ + off), dof[ks], dpt[kb]);
+        }
+      }
+      const bool need_mask = (k0 + kTile > kv_len) || (CAUSAL && k0 + kTile - 1 > qw);
+      if (need_mask) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            const int key = k0 + 32 * kb + 8 * (e >> 2) + 4 * hl + (e & 3);
+            const bool vis = key < kv_len && (!CAUSAL || key <= qi);
+            if (!vis) st[kb][e] = -kInf;
+          }
+      }
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const float p = fast_exp2(__builtin_fmaf(st[kb][e], c, -L2));
+          st[kb][e] = p * (dpt[kb][e] - Dq);
+        }
+      // dQ^T[d][q] += sum_key K[key][d] dS[q][key]
+#pragma unroll
+      for (int stp = 0; stp < 4; ++stp) {
+        const bf16x8 dsb = pack8(st[stp >> 1], 8 * (stp & 1));
+#pragma unroll
+        for (int db = 0; db < 2; ++db)
+          acc[db] = mfma32(lds_split8(kt_ + (32 * db + r) * kTStride + 16 * stp + 4 * hl), dsb,
+                           acc[db]);
+      }
+    }
+    if (it + 1 < nlist) swrite(buf ^ 1);
+    __syncthreads();
+  }
+
+  if (qi < a.N) {
+    uint16_t* out = (uint16_t*)a.dq + b * a.sdq.b + hh * a.sdq.h + (int64_t)qi * a.sdq.s;
+#pragma unroll
+    for (int db = 0; db < 2; ++db)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        bf16x4 v4;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v4[i] = (__bf16)(acc[db][4 * j + i] * a.scale);
+        *reinterpret_cast<bf16x4*>(out + 32 * db + 8 * j + 4 * hl) = v4;
+      }
+  }
+}
+
+// ---------------------------------------------------------------- dK, dV
+
+template <bool CAUSAL, bool SEQLEN, bool BMASK>
+__global__ __launch_bounds__(256) void dkdv_kernel(BwdArgs a) {
+  __shared__ __attribute__((aligned(16))) uint16_t s_q[2][kTile * kRowStride];
+  __shared__ __attribute__((aligned(16))) uint16_t s_qt[2][kTile * kTStride];
+  __shared__ __attribute__((aligned(16))) uint16_t s_do[2][kTile * kRowStride];
+  __shared__ __attribute__((aligned(16))) uint16_t s_dot[2][kTile * kTStride];
+  __shared__ __attribute__((aligned(16))) float s_l2[2][kTile];
+  __shared__ __attribute__((aligned(16))) float s_d[2][kTile];
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int r = lane & 31, hl = lane >> 5;
+  const int BH = a.B * a.H;
+  const int id = blockIdx.x;
+  // Causal: key tile 0 sees every query, so ascending ids are heaviest first.
+  const int kt = id / BH;
+  const int bh = id % BH;
+  const int b = bh / a.H, hh = bh % a.H;
+  const int k0 = kt * kBK;
+  const int kw = k0 + 32 * w;  // first key of this wave
+  const int kj = kw + r;       // this lane's key
+
+  int kv_len = a.N;
+  if constexpr (SEQLEN) kv_len = min(max(a.seqlens[b], 0), a.N);
+
+  uint16_t* dK = (uint16_t*)a.dk + b * a.sdk.b + hh * a.sdk.h;
+  uint16_t* dV = (uint16_t*)a.dv + b * a.sdv.b + hh * a.sdv.h;
+
+  f32x16 dkt[2] = {zero16(), zero16()};
+  f32x16 dvt[2] = {zero16(), zero16()};
+
+  if (k0 < kv_len) {
+    const int nq = (a.N + kTile - 1) / kTile;
+    const int qt_lo = CAUSAL ? k0 / kTile : 0;
+    int nlist = nq - qt_lo;
+    [[maybe_unused]] uint16_t* tlist = nullptr;
+    if constexpr (BMASK) {
+      __shared__ uint16_t s_list[kMaxListTiles];
+      __shared__ int s_scan[4];
+      tlist = s_list;
+      const int col = k0 / a.mask_block;
+      nlist = build_tile_list(s_list, s_scan, a.bmask + col, a.n_mask_tiles, a.n_mask_tiles,
+                              a.mask_block / kTile, qt_lo, nq);
+    }
+
+    const uint16_t* Q = (const uint16_t*)a.q + b * a.sq.b + hh * a.sq.h;
+    const uint16_t* K = (const uint16_t*)a.k + b * a.sk.b + hh * a.sk.h;
+    const uint16_t* V = (const uint16_t*)a.v + b * a.sv.b + hh * a.sv.h;
+    const uint16_t* dO = (const uint16_t*)a.dout + b * a.sdo.b + hh * a.sdo.h;
+    const float* lse = a.lse + (int64_t)bh * a.N;
+    const float* dsum = a.dsum + (int64_t)bh * a.N;
+
+    bf16x8 kf[4], vf[4];
+    {
+      const uint4 z = make_uint4(0, 0, 0, 0);
+      const bool in = kj < a.N;
+      const uint16_t* kp = K + (int64_t)kj * a.sk.s + 8 * hl;
+      const uint16_t* vp = V + (int64_t)kj * a.sv.s + 8 * hl;
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        kf[ks] = as_bf16x8(in ? ldg16(kp + 16 * ks) : z);
+        vf[ks] = as_bf16x8(in ? ldg16(vp + 16 * ks) : z);
+      }
+    }
+    const float c = a.scale_log2;
+
+    // Staging: Q and dO rows 2*(tid/8), 2*(tid/8)+1 at 16-byte column tid%8,
+    // row-major and transposed; threads 0..63 also fetch L and D of one row.
+    const int sr = tid >> 3, sc = tid & 7;
+    uint4 qreg[2], dreg[2];
+    float lreg = 0.f, dreg_s = 0.f;
+    auto tile_at = [&](int it) -> int {
+      if constexpr (BMASK) return tlist[it];
+      return qt_lo + it;
+    };
+    auto gload = [&](int t) {
+      const int qs = t * kTile;
+      const uint4 z = make_uint4(0, 0, 0, 0);
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int qq = qs + 2 * sr + u;
+        qreg[u] = qq < a.N ? ldg16(Q + (int64_t)qq * a.sq.s + 8 * sc) : z;
+        dreg[u] = qq < a.N ? ldg16(dO + (int64_t)qq * a.sdo.s + 8 * sc) : z;
+      }
+      if (tid < kTile) {
+        const int qq = qs + tid;
+        const float L = qq < a.N ? lse[qq] : -kInf;
+        lreg = (L == -kInf) ? kInf : L * kLog2e;
+        dreg_s = qq < a.N ? dsum[qq] : 0.f;
+      }
+    };
+    auto swrite = [&](int buf) {
+      store_row16(s_q[buf], 2 * sr, sc, qreg[0]);
+      store_row16(s_q[buf], 2 * sr + 1, sc, qreg[1]);
+      store_pair_transposed(s_qt[buf], 2 * sr, sc, qreg[0], qreg[1]);
+      store_row16(s_do[buf], 2 * sr, sc, dreg[0]);
+      store_row16(s_do[buf], 2 * sr + 1, sc, dreg[1]);
+      store_pair_transposed(s_dot[buf], 2 * sr, sc, dreg[0], dreg[1]);
+      if (tid < kTile) {
+        s_l2[buf][tid] = lreg;
+        s_d[buf][tid] = dreg_s;
+      }
+    };
+
+    if (nlist > 0) {
+      gload(tile_at(0));
+      swrite(0);
+    }
+    __syncthreads();
+
+    for (int it = 0; it < nlist; ++it) {
+      const int buf = it & 1;
+      const int qs = tile_at(it) * kTile;
+      if (it + 1 < nlist) gload(tile_at(it + 1));
+
+      const bool active = !CAUSAL || (qs + kTile - 1 >= kw);
+      if (active) {
+        const uint16_t* qs_ = s_q[buf];
+        const uint16_t* qt_ = s_qt[buf];
+        const uint16_t* ds_ = s_do[buf];
+        const uint16_t* dt_ = s_dot[buf];
+        f32x16 s[2], dp[2];
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
+          s[qb] = zero16();
+          dp[qb] = zero16();
+#pragma unroll
+          for (int ks = 0; ks < 4; ++ks) {
+            const int off = (32 * qb + r) * kRowStride + 16 * ks + 8 * hl;
+            s[qb] = mfma32(lds_row8(qs_ + off), kf[ks], s[qb]);
+            dp[qb] = mfma32(lds_row8(ds_ + off), vf[ks], dp[qb]);
+          }
+        }
+        const bool need_mask = (kw + 32 > kv_len) || (CAUSAL && kw + 31 > qs);
+        if (need_mask) {
+#pragma unroll
+          for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+              const int q = qs + 32 * qb + 8 * (e >> 2) + 4 * hl + (e & 3);
+              const bool vis = kj < kv_len && (!CAUSAL || kj <= q);
+              if (!vis) s[qb][e] = -kInf;
+            }
+        }
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const f32x4 l4 = *reinterpret_cast<const f32x4*>(&s_l2[buf][32 * qb + 8 * j + 4 * hl]);
+            const f32x4 d4 = *reinterpret_cast<const f32x4*>(&s_d[buf][32 * qb + 8 * j + 4 * hl]);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int e = 4 * j + i;
+              const float p = fast_exp2(__builtin_fmaf(s[qb][e], c, -l4[i]));
+              s[qb][e] = p;
+              dp[qb][e] = p * (dp[qb][e] - d4[i]);
+            }
+          }
+        // dV^T[d][key] += sum_q dO[q][d] P[q][key];  dK^T[d][key] += sum_q Q[q][d] dS[q][key]
+#pragma unroll
+        for (int stp = 0; stp < 4; ++stp) {
+          const bf16x8 pb = pack8(s[stp >> 1], 8 * (stp & 1));
+          const bf16x8 dsb = pack8(dp[stp >> 1], 8 * (stp & 1));
+#pragma unroll
+          for (int db = 0; db < 2; ++db) {
+            const int off = (32 * db + r) * kTStride + 16 * stp + 4 * hl;
+            dvt[db] = mfma32(lds_split8(dt_ + off), pb, dvt[db]);
+            dkt[db] = mfma32(lds_split8(qt_ + off), dsb, dkt[db]);
+          }
+        }
+      }
+      if (it + 1 < nlist) swrite(buf ^ 1);
+      __syncthreads();
+    }
+  }
+
+  if (kj < a.N) {
+    uint16_t* kout = dK + (int64_t)kj * a.sdk.s;
+    uint16_t* vout = dV + (int64_t)kj * a.sdv.s;
+#pragma unroll
+    for (int db = 0; db < 2; ++db)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        bf16x4 k4, v4;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          k4[i] = (__bf16)(dkt[db][4 * j + i] * a.scale);
+          v4[i] = (__bf16)dvt[db][4 * j + i];
+        }
+        *reinterpret_cast<bf16x4*>(kout + 32 * db + 8 * j + 4 * hl) = k4;
+        *reinterpret_cast<bf16x4*>(vout + 32 * db + 8 * j + 4 * hl) = v4;
+      }
+  }
+}
+
+template <bool C, bool S, bool M>
+hipError_t launch(const BwdArgs& a, hipStream_t stream) {
+  BwdArgs copy = a;
+  void* args[] = {&copy};
+  const int BH = a.B * a.H;
+  dim3 block(256);
+  dim3 gq((unsigned)(((a.N + kBQ - 1) / kBQ) * BH));
+  hipError_t e = hipLaunchKernel((const void*)&dq_kernel<C, S, M>, gq, block, args, 0, stream);
+  if (e != hipSuccess) return e;
+  dim3 gk((unsigned)(((a.N + kBK - 1) / kBK) * BH));
+  return hipLaunchKernel((const void*)&dkdv_kernel<C, S, M>, gk, block, args, 0, stream);
+}
+
+}  // namespace
+
+hipError_t launch_bwd_bf16(const BwdArgs& a, bool causal, hipStream_t stream) {
+  const bool s = a.seqlens != nullptr, m = a.bmask != nullptr;
+  if (causal) {
+    if (s) return m ? launch<true, true, true>(a, stream) : launch<true, true, false>(a, stream);
+    return m ? launch<true, false, true>(a, stream) : launch<true, false, false>(a, stream);
+  }
+  if (s) return m ? launch<false, true, true>(a, stream) : launch<false, true, false>(a, stream);
+  return m ? launch<false, false, true>(a, stream) : launch<false, false, false>(a, stream);
+}
+
+}  // namespace fa

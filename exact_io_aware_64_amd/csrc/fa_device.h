@@ -1,0 +1,152 @@
+// Device-side building blocks for the gfx950 attention kernels: MFMA
+// fragment types, wave-half exchange, LDS tile staging and the kept-tile list.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "fa_internal.h"
+
+namespace fa {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr float kInf = __builtin_inff();
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// Row stride (in 16-bit elements) of a row-major 64x64 tile in LDS.  The pad
+// of 8 elements spreads the 16-byte reads of 16 consecutive rows over all
+// banks.
+constexpr int kRowStride = 72;
+// Row stride of a transposed tile.  A multiple of 4 keeps the 8-byte reads of
+// operand halves aligned.
+constexpr int kTStride = 68;
+
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+  // D[32x32] += A[32x16] * B[16x32].  Lane l supplies row (l % 32) of A and
+  // column (l % 32) of B, both at contraction slots 8*(l/32) .. 8*(l/32)+7, and
+  // holds D[8*(e/4) + 4*(l/32) + e%4][l % 32] in element e.
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x16 zero16() {
+  f32x16 z;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) z[i] = 0.f;
+  return z;
+}
+
+// Max / sum of x over lanes l and l ^ 32 (the two halves of a wave hold the
+// two halves of one query's keys).
+__device__ __forceinline__ float half_max(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                            false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float half_sum(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                            false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Elements [off, off+8) of an accumulator, rounded to bf16 (nearest-even).
+__device__ __forceinline__ bf16x8 pack8(const f32x16& v, int off) {
+  bf16x8 r;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) r[i] = (__bf16)v[off + i];
+  return r;
+}
+
+__device__ __forceinline__ uint4 ldg16(const uint16_t* p) {
+  return *reinterpret_cast<const uint4*>(p);
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(uint4 u) { return __builtin_bit_cast(bf16x8, u); }
+
+// 8 bf16 of one LDS row (16-byte aligned).
+__device__ __forceinline__ bf16x8 lds_row8(const uint16_t* p) {
+  return *reinterpret_cast<const bf16x8*>(p);
+}
+
+// Operand from a transposed tile: 4 elements at p and 4 at p + 8.
+__device__ __forceinline__ bf16x8 lds_split8(const uint16_t* p) {
+  bf16x4 lo = *reinterpret_cast<const bf16x4*>(p);
+  bf16x4 hi = *reinterpret_cast<const bf16x4*>(p + 8);
+  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// Store rows r0 and r0+1 (16 bytes each, columns 8c..8c+7) of a tile both
+// row-major (if nat != nullptr) and transposed into t[col * kTStride + row].
+__device__ __forceinline__ void store_pair_transposed(uint16_t* t, int r0, int c, uint4 a,
+                                                      uint4 b) {
+  const uint32_t aw[4] = {a.x, a.y, a.z, a.w};
+  const uint32_t bw[4] = {b.x, b.y, b.z, b.w};
+#pragma unroll
+  for (int x = 0; x < 8; ++x) {
+    const uint32_t lo = aw[x >> 1], hi = bw[x >> 1];
+    const uint32_t word = (x & 1) ? ((lo >> 16) | (hi & 0xffff0000u))
+                                  : ((lo & 0xffffu) | (hi << 16));
+    *reinterpret_cast<uint32_t*>(t + (8 * c + x) * kTStride + r0) = word;
+  }
+}
+
+__device__ __forceinline__ void store_row16(uint16_t* t, int row, int c, uint4 a) {
+  *reinterpret_cast<uint4*>(t + row * kRowStride + 8 * c) = a;
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave.
+__device__ __forceinline__ int wave_incl_scan(int x) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    int y = __shfl_up(x, off, 64);
+    if (lane >= off) x += y;
+  }
+  return x;
+}
+
+// Builds, in LDS, the list of 64-row tiles t in [t_lo, t_hi) whose mask tile
+// (t / per_mask) is kept: mask entry J lives at mask[J * stride].  Called by
+// all 256 threads of the block; returns the list length (same in every
+// thread).  The list is sorted ascending.
+__device__ __forceinline__ int build_tile_list(uint16_t* list, int* scratch4,
+                                               const uint8_t* mask, int64_t stride,
+                                               int n_mask_tiles, int per_mask, int t_lo,
+                                               int t_hi) {
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  int base = 0;
+  const int j_lo = t_lo / per_mask;
+  const int j_hi = (t_hi + per_mask - 1) / per_mask;  // exclusive
+  for (int c0 = j_lo; c0 < j_hi; c0 += 256) {
+    const int J = c0 + tid;
+    int first = 0, cnt = 0;
+    if (J < j_hi && J < n_mask_tiles && mask[(int64_t)J * stride] != 0) {
+      first = max(J * per_mask, t_lo);
+      const int last = min((J + 1) * per_mask, t_hi);
+      cnt = max(0, last - first);
+    }
+    const int incl = wave_incl_scan(cnt);
+    if (lane == 63) scratch4[w] = incl;
+    __syncthreads();
+    int woff = 0, total = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int v = scratch4[i];
+      woff += (i < w) ? v : 0;
+      total += v;
+    }
+    const int pos = base + woff + incl - cnt;
+    for (int x = 0; x < cnt; ++x) list[pos + x] = (uint16_t)(first + x);
+    base += total;
+    __syncthreads();
+  }
+  return base;
+}
+
+}  // namespace fa

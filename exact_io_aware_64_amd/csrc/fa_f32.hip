@@ -1,0 +1,249 @@
+// fp32 attention (forward and backward) on the vector ALUs.
+//
+// Same tiled algorithm as the bf16 kernels -- K/V (or Q/dO) tiles of 64 rows
+// staged in LDS, online softmax with a running maximum and sum in the
+// forward pass, probabilities recomputed from L in the backward pass
+// (researchpapers.dev explainer, "tiling and recomputation") -- but every
+// product is an fp32 FMA, so results stay within ~1e-6 of exact.  One thread
+// owns one query (forward, dQ) or one key (dK/dV); every thread of a
+// workgroup reads the same LDS row at the same time (a broadcast).  This path
+// serves full-precision callers and small problems; the bf16 MFMA kernels are
+// the throughput path.
+#include "fa_device.h"
+
+namespace fa {
+namespace {
+
+constexpr int kD = 64;
+
+__device__ __forceinline__ bool tile_kept(const uint8_t* bmask, int n_mask_tiles,
+                                          int mask_block, int qrow, int kcol) {
+  return bmask == nullptr ||
+         bmask[(int64_t)(qrow / mask_block) * n_mask_tiles + kcol / mask_block] != 0;
+}
+
+__device__ __forceinline__ void load_row(float* dst, const float* src) {
+#pragma unroll
+  for (int e = 0; e < kD; e += 4) {
+    const float4 x = *reinterpret_cast<const float4*>(src + e);
+    dst[e] = x.x;
+    dst[e + 1] = x.y;
+    dst[e + 2] = x.z;
+    dst[e + 3] = x.w;
+  }
+}
+
+__device__ __forceinline__ void store_row(float* dst, const float* src, float mul) {
+#pragma unroll
+  for (int e = 0; e < kD; e += 4)
+    *reinterpret_cast<float4*>(dst + e) =
+        make_float4(src[e] * mul, src[e + 1] * mul, src[e + 2] * mul, src[e + 3] * mul);
+}
+
+__device__ __forceinline__ void stage_row(float* lds_row, const float* g, bool in) {
+#pragma unroll
+  for (int e = 0; e < kD; e += 4)
+    *reinterpret_cast<float4*>(lds_row + e) =
+        in ? *reinterpret_cast<const float4*>(g + e) : make_float4(0.f, 0.f, 0.f, 0.f);
+}
+
+__device__ __forceinline__ float dot_lds(const float* x, const float* lds_row) {
+  float acc = 0.f;
+#pragma unroll
+  for (int e = 0; e < kD; ++e) acc = __builtin_fmaf(x[e], lds_row[e], acc);
+  return acc;
+}
+
+__global__ __launch_bounds__(64) void fwd_f32_kernel(FwdArgs a, int causal) {
+  __shared__ __attribute__((aligned(16))) float s_k[kTile * kD];
+  __shared__ __attribute__((aligned(16))) float s_v[kTile * kD];
+  const int tid = threadIdx.x;
+  const int BH = a.B * a.H;
+  const int qt = blockIdx.x / BH, bh = blockIdx.x % BH;
+  const int b = bh / a.H, hh = bh % a.H;
+  const int q0 = qt * kTile, qi = q0 + tid;
+  int kv_len = a.N;
+  if (a.seqlens) kv_len = min(max(a.seqlens[b], 0), a.N);
+  const int kend = causal ? min(kv_len, q0 + kTile) : kv_len;
+  const float* Q = (const float*)a.q + b * a.sq.b + hh * a.sq.h;
+  const float* K = (const float*)a.k + b * a.sk.b + hh * a.sk.h;
+  const float* V = (const float*)a.v + b * a.sv.b + hh * a.sv.h;
+
+  float q[kD], o[kD];
+  if (qi < a.N) load_row(q, Q + (int64_t)qi * a.sq.s);
+  else
+    for (int e = 0; e < kD; ++e) q[e] = 0.f;
+  for (int e = 0; e < kD; ++e) o[e] = 0.f;
+  float m = -kInf, l = 0.f;
+  const float c = a.scale_log2;
+
+  for (int k0 = 0; k0 < kend; k0 += kTile) {
+    if (!tile_kept(a.bmask, a.n_mask_tiles, a.mask_block, q0, k0)) continue;
+    const int kk = k0 + tid;
+    stage_row(s_k + tid * kD, K + (int64_t)kk * a.sk.s, kk < a.N);
+    stage_row(s_v + tid * kD, V + (int64_t)kk * a.sv.s, kk < a.N);
+    __syncthreads();
+    float s[kTile];
+    float mx = -kInf;
+#pragma unroll
+    for (int j = 0; j < kTile; ++j) {
+      const int key = k0 + j;
+      const bool vis = key < kv_len && (!causal || key <= qi);
+      s[j] = vis ? dot_lds(q, s_k + j * kD) : -kInf;
+      mx = fmaxf(mx, s[j]);
+    }
+    const float m_new = fmaxf(m, mx * c);
+    const float m_use = (m_new == -kInf) ? 0.f : m_new;
+    const float alpha = fast_exp2(m - m_use);
+    l *= alpha;
+#pragma unroll
+    for (int e = 0; e < kD; ++e) o[e] *= alpha;
+#pragma unroll
+    for (int j = 0; j < kTile; ++j) {
+      const float p = fast_exp2(__builtin_fmaf(s[j], c, -m_use));
+      l += p;
+#pragma unroll
+      for (int e = 0; e < kD; ++e) o[e] = __builtin_fmaf(p, s_v[j * kD + e], o[e]);
+    }
+    m = m_new;
+    __syncthreads();
+  }
+  if (qi < a.N) {
+    store_row((float*)a.o + b * a.so.b + hh * a.so.h + (int64_t)qi * a.so.s, o,
+              l > 0.f ? 1.f / l : 0.f);
+    a.lse[(int64_t)bh * a.N + qi] = l > 0.f ? (m + __builtin_amdgcn_logf(l)) * kLn2 : -kInf;
+  }
+}
+
+// dQ for one query per thread; also writes D_i = dot(dO_i, O_i).
+__global__ __launch_bounds__(64) void dq_f32_kernel(BwdArgs a, int causal) {
+  __shared__ __attribute__((aligned(16))) float s_k[kTile * kD];
+  __shared__ __attribute__((aligned(16))) float s_v[kTile * kD];
+  const int tid = threadIdx.x;
+  const int BH = a.B * a.H;
+  const int qt = blockIdx.x / BH, bh = blockIdx.x % BH;
+  const int b = bh / a.H, hh = bh % a.H;
+  const int q0 = qt * kTile, qi = q0 + tid;
+  int kv_len = a.N;
+  if (a.seqlens) kv_len = min(max(a.seqlens[b], 0), a.N);
+  const int kend = causal ? min(kv_len, q0 + kTile) : kv_len;
+  const float* K = (const float*)a.k + b * a.sk.b + hh * a.sk.h;
+  const float* V = (const float*)a.v + b * a.sv.b + hh * a.sv.h;
+
+  float q[kD], g[kD], acc[kD];
+  float D = 0.f, L2 = kInf;
+  if (qi < a.N) {
+    load_row(q, (const float*)a.q + b * a.sq.b + hh * a.sq.h + (int64_t)qi * a.sq.s);
+    load_row(g, (const float*)a.dout + b * a.sdo.b + hh * a.sdo.h + (int64_t)qi * a.sdo.s);
+    load_row(acc, (const float*)a.o + b * a.so.b + hh * a.so.h + (int64_t)qi * a.so.s);
+#pragma unroll
+    for (int e = 0; e < kD; ++e) D = __builtin_fmaf(g[e], acc[e], D);
+    a.dsum[(int64_t)bh * a.N + qi] = D;
+    const float L = a.lse[(int64_t)bh * a.N + qi];
+    if (L != -kInf) L2 = L * kLog2e;
+  } else {
+    for (int e = 0; e < kD; ++e) q[e] = g[e] = 0.f;
+  }
+  for (int e = 0; e < kD; ++e) acc[e] = 0.f;
+  const float c = a.scale_log2;
+
+  for (int k0 = 0; k0 < kend; k0 += kTile) {
+    if (!tile_kept(a.bmask, a.n_mask_tiles, a.mask_block, q0, k0)) continue;
+    const int kk = k0 + tid;
+    stage_row(s_k + tid * kD, K + (int64_t)kk * a.sk.s, kk < a.N);
+    stage_row(s_v + tid * kD, V + (int64_t)kk * a.sv.s, kk < a.N);
+    __syncthreads();
+    for (int j = 0; j < kTile; ++j) {
+      const int key = k0 + j;
+      const bool vis = key < kv_len && (!causal || key <= qi);
+      const float s = dot_lds(q, s_k + j * kD);
+      const float p = vis ? fast_exp2(__builtin_fmaf(s, c, -L2)) : 0.f;
+      const float dp = dot_lds(g, s_v + j * kD);
+      const float ds = p * (dp - D);
+#pragma unroll
+      for (int e = 0; e < kD; ++e) acc[e] = __builtin_fmaf(ds, s_k[j * kD + e], acc[e]);
+    }
+    __syncthreads();
+  }
+  if (qi < a.N)
+    store_row((float*)a.dq + b * a.sdq.b + hh * a.sdq.h + (int64_t)qi * a.sdq.s, acc, a.scale);
+}
+
+// dK, dV for one key per thread.
+__global__ __launch_bounds__(64) void dkdv_f32_kernel(BwdArgs a, int causal) {
+  __shared__ __attribute__((aligned(16))) float s_q[kTile * kD];
+  __shared__ __attribute__((aligned(16))) float s_g[kTile * kD];
+  __shared__ float s_l2[kTile], s_d[kTile];
+  const int tid = threadIdx.x;
+  const int BH = a.B * a.H;
+  const int kt = blockIdx.x / BH, bh = blockIdx.x % BH;
+  const int b = bh / a.H, hh = bh % a.H;
+  const int k0 = kt * kTile, kj = k0 + tid;
+  int kv_len = a.N;
+  if (a.seqlens) kv_len = min(max(a.seqlens[b], 0), a.N);
+  const float* Q = (const float*)a.q + b * a.sq.b + hh * a.sq.h;
+  const float* G = (const float*)a.dout + b * a.sdo.b + hh * a.sdo.h;
+
+  float kr[kD], vr[kD], dk[kD], dv[kD];
+  if (kj < a.N) {
+    load_row(kr, (const float*)a.k + b * a.sk.b + hh * a.sk.h + (int64_t)kj * a.sk.s);
+    load_row(vr, (const float*)a.v + b * a.sv.b + hh * a.sv.h + (int64_t)kj * a.sv.s);
+  } else {
+    for (int e = 0; e < kD; ++e) kr[e] = vr[e] = 0.f;
+  }
+  for (int e = 0; e < kD; ++e) dk[e] = dv[e] = 0.f;
+  const float c = a.scale_log2;
+
+  if (k0 < kv_len) {
+    for (int qs = causal ? k0 : 0; qs < a.N; qs += kTile) {
+      if (!tile_kept(a.bmask, a.n_mask_tiles, a.mask_block, qs, k0)) continue;
+      const int qq = qs + tid;
+      stage_row(s_q + tid * kD, Q + (int64_t)qq * a.sq.s, qq < a.N);
+      stage_row(s_g + tid * kD, G + (int64_t)qq * a.sdo.s, qq < a.N);
+      const float L = qq < a.N ? a.lse[(int64_t)bh * a.N + qq] : -kInf;
+      s_l2[tid] = (L == -kInf) ? kInf : L * kLog2e;
+      s_d[tid] = qq < a.N ? a.dsum[(int64_t)bh * a.N + qq] : 0.f;
+      __syncthreads();
+      for (int i = 0; i < kTile; ++i) {
+        const int q = qs + i;
+        const bool vis = kj < kv_len && (!causal || kj <= q);
+        const float s = dot_lds(kr, s_q + i * kD);
+        const float p = vis ? fast_exp2(__builtin_fmaf(s, c, -s_l2[i])) : 0.f;
+        const float dp = dot_lds(vr, s_g + i * kD);
+        const float ds = p * (dp - s_d[i]);
+#pragma unroll
+        for (int e = 0; e < kD; ++e) {
+          dv[e] = __builtin_fmaf(p, s_g[i * kD + e], dv[e]);
+          dk[e] = __builtin_fmaf(ds, s_q[i * kD + e], dk[e]);
+        }
+      }
+      __syncthreads();
+    }
+  }
+  if (kj < a.N) {
+    store_row((float*)a.dk + b * a.sdk.b + hh * a.sdk.h + (int64_t)kj * a.sdk.s, dk, a.scale);
+    store_row((float*)a.dv + b * a.sdv.b + hh * a.sdv.h + (int64_t)kj * a.sdv.s, dv, 1.f);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_fwd_f32(const FwdArgs& a, bool causal, hipStream_t stream) {
+  FwdArgs copy = a;
+  int cz = causal ? 1 : 0;
+  void* args[] = {&copy, &cz};
+  dim3 grid((unsigned)(((a.N + kTile - 1) / kTile) * a.B * a.H)), block(64);
+  return hipLaunchKernel((const void*)&fwd_f32_kernel, grid, block, args, 0, stream);
+}
+
+hipError_t launch_bwd_f32(const BwdArgs& a, bool causal, hipStream_t stream) {
+  BwdArgs copy = a;
+  int cz = causal ? 1 : 0;
+  void* args[] = {&copy, &cz};
+  dim3 grid((unsigned)(((a.N + kTile - 1) / kTile) * a.B * a.H)), block(64);
+  hipError_t e = hipLaunchKernel((const void*)&dq_f32_kernel, grid, block, args, 0, stream);
+  if (e != hipSuccess) return e;
+  return hipLaunchKernel((const void*)&dkdv_f32_kernel, grid, block, args, 0, stream);
+}
+
+}  // namespace fa

@@ -1,0 +1,224 @@
+// Fused attention forward for gfx950, bf16 inputs, fp32 accumulation.
+//
+// One workgroup (4 waves) owns 128 query rows of one (batch, head); each wave
+// owns 32 of them and keeps its Q fragment in registers for the whole kernel.
+// Key/value tiles of 64 rows stream through LDS (double-buffered: the global
+// loads of tile t+1 are in flight while tile t is computed), so each K/V
+// element is read from HBM/L2 once per workgroup and the N x N score matrix
+// never leaves registers (suanlizi.com summary, "tiling" and "kernel fusion";
+// researchpapers.dev explainer, "tiling and recomputation").
+//
+// The scores are computed transposed, S^T = K Q^T, on the 32x32x16 bf16 MFMA:
+// in the accumulator layout each lane then holds 32 scores of a single query,
+// so the row maximum and row sum need one exchange between the two wave
+// halves instead of a reduction across 32 lanes.  The online softmax keeps a
+// running maximum m (log2 units) and a running sum l per query and rescales
+// the output accumulator when m grows (researchpapers.dev, "tiling and
+// recomputation"; the max subtraction is the safe softmax of the llm-deploy
+// note).  O^T = V^T P^T is accumulated on the same MFMA; the probabilities
+// feed the B operand straight from the accumulator registers, and V is staged
+// transposed in LDS so the A operand reads are contiguous.
+//
+// Tiles that the mask removes entirely are never loaded: causal and key
+// padding shrink the key range, and a block mask is compacted into a list of
+// kept tiles (suanlizi.com, "block-sparse attention").
+#include "fa_device.h"
+
+namespace fa {
+namespace {
+
+constexpr int kBR = 128;  // query rows per workgroup
+
+template <bool CAUSAL, bool SEQLEN, bool BMASK>
+__global__ __launch_bounds__(256) void fwd_bf16_kernel(FwdArgs a) {
+  __shared__ __attribute__((aligned(16))) uint16_t s_k[2][kTile * kRowStride];
+  __shared__ __attribute__((aligned(16))) uint16_t s_vt[2][kTile * kTStride];
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int r = lane & 31, hl = lane >> 5;
+  const int BH = a.B * a.H;
+  const int nqt = (a.N + kBR - 1) / kBR;
+  const int id = blockIdx.x;
+  // Causal: the longest query tiles are dispatched first.  Consecutive ids
+  // walk the heads, so with B*H a multiple of 8 all tiles of one head land
+  // on the same XCD and share its L2.
+  const int qt = CAUSAL ? (nqt - 1 - id / BH) : (id / BH);
+  const int bh = id % BH;
+  const int b = bh / a.H, hh = bh % a.H;
+  const int q0 = qt * kBR;
+  const int qw = q0 + 32 * w;  // first query of this wave
+  const int qi = qw + r;       // this lane's query
+
+  int kv_len = a.N;
+  if constexpr (SEQLEN) kv_len = min(max(a.seqlens[b], 0), a.N);
+  int kend = kv_len;
+  if constexpr (CAUSAL) kend = min(kend, q0 + kBR);
+  const int ntk = (kend + kTile - 1) / kTile;
+
+  int nlist = ntk;
+  [[maybe_unused]] uint16_t* tlist = nullptr;
+  if constexpr (BMASK) {
+    __shared__ uint16_t s_list[kMaxListTiles];
+    __shared__ int s_scan[4];
+    tlist = s_list;
+    const int row = q0 / a.mask_block;
+    nlist = build_tile_list(s_list, s_scan, a.bmask + (int64_t)row * a.n_mask_tiles, 1,
+                            a.n_mask_tiles, a.mask_block / kTile, 0, ntk);
+  }
+
+  const uint16_t* Q = (const uint16_t*)a.q + b * a.sq.b + hh * a.sq.h;
+  const uint16_t* K = (const uint16_t*)a.k + b * a.sk.b + hh * a.sk.h;
+  const uint16_t* V = (const uint16_t*)a.v + b * a.sv.b + hh * a.sv.h;
+
+  bf16x8 qf[4];
+  {
+    const uint4 z = make_uint4(0, 0, 0, 0);
+    const uint16_t* qp = Q + (int64_t)qi * a.sq.s + 8 * hl;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) qf[ks] = as_bf16x8(qi < a.N ? ldg16(qp + 16 * ks) : z);
+  }
+
+  f32x16 o[2] = {zero16(), zero16()};
+  float m = -kInf, l = 0.f;
+  const float c = a.scale_log2;
+
+  // Staging roles: K chunks (row tid/8 and tid/8 + 32, 16-byte column tid%8);
+  // V rows 2*(tid/8) and 2*(tid/8)+1 at the same column, written transposed.
+  const int sr = tid >> 3, sc = tid & 7;
+  uint4 kreg[2], vreg[2];
+  auto tile_at = [&](int it) -> int {
+    if constexpr (BMASK) return tlist[it];
+    return it;
+  };
+  auto gload = [&](int t) {
+    const int k0 = t * kTile;
+    const uint4 z = make_uint4(0, 0, 0, 0);
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int kk = k0 + sr + 32 * u;
+      kreg[u] = kk < a.N ? ldg16(K + (int64_t)kk * a.sk.s + 8 * sc) : z;
+      const int kv = k0 + 2 * sr + u;
+      vreg[u] = kv < a.N ? ldg16(V + (int64_t)kv * a.sv.s + 8 * sc) : z;
+    }
+  };
+  auto swrite = [&](int buf) {
+    store_row16(s_k[buf], sr, sc, kreg[0]);
+    store_row16(s_k[buf], sr + 32, sc, kreg[1]);
+    store_pair_transposed(s_vt[buf], 2 * sr, sc, vreg[0], vreg[1]);
+  };
+
+  if (nlist > 0) {
+    gload(tile_at(0));
+    swrite(0);
+  }
+  __syncthreads();
+
+  for (int it = 0; it < nlist; ++it) {
+    const int buf = it & 1;
+    const int k0 = tile_at(it) * kTile;
+    if (it + 1 < nlist) gload(tile_at(it + 1));
+
+    const bool active = !CAUSAL || (k0 <= qw + 31);
+    if (active) {
+      const uint16_t* ks_ = s_k[buf];
+      const uint16_t* vt_ = s_vt[buf];
+      f32x16 s[2];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        s[kb] = zero16();
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+          s[kb] = mfma32(lds_row8(ks_ + (32 * kb + r) * kRowStride + 16 * ks + 8 * hl), qf[ks],
+                         s[kb]);
+      }
+      const bool need_mask = (k0 + kTile > kv_len) || (CAUSAL && k0 + kTile - 1 > qw);
+      if (need_mask) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            const int key = k0 + 32 * kb + 8 * (e >> 2) + 4 * hl + (e & 3);
+            const bool vis = key < kv_len && (!CAUSAL || key <= qi);
+            if (!vis) s[kb][e] = -kInf;
+          }
+      }
+      float mx = -kInf;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[kb][e]);
+      mx = half_max(mx);
+      const float m_new = fmaxf(m, mx * c);
+      const float m_use = (m_new == -kInf) ? 0.f : m_new;
+      const float alpha = fast_exp2(m - m_use);
+      float rs = 0.f;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const float p = fast_exp2(__builtin_fmaf(s[kb][e], c, -m_use));
+          s[kb][e] = p;
+          rs += p;
+        }
+      l = l * alpha + rs;
+      m = m_new;
+#pragma unroll
+      for (int db = 0; db < 2; ++db)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) o[db][e] *= alpha;
+      // O^T[d][q] += sum_key V[key][d] P[q][key]; contraction slot e of step
+      // st maps to key 16*st + 4*hl + e (e < 4) or 16*st + 8 + 4*hl + e - 4.
+#pragma unroll
+      for (int st = 0; st < 4; ++st) {
+        const bf16x8 pb = pack8(s[st >> 1], 8 * (st & 1));
+#pragma unroll
+        for (int db = 0; db < 2; ++db)
+          o[db] = mfma32(lds_split8(vt_ + (32 * db + r) * kTStride + 16 * st + 4 * hl), pb,
+                         o[db]);
+      }
+    }
+    if (it + 1 < nlist) swrite(buf ^ 1);
+    __syncthreads();
+  }
+
+  const float lt = half_sum(l);
+  if (qi < a.N) {
+    const float inv = lt > 0.f ? 1.f / lt : 0.f;
+    uint16_t* op = (uint16_t*)a.o + b * a.so.b + hh * a.so.h + (int64_t)qi * a.so.s;
+#pragma unroll
+    for (int db = 0; db < 2; ++db)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        bf16x4 v4;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v4[i] = (__bf16)(o[db][4 * j + i] * inv);
+        *reinterpret_cast<bf16x4*>(op + 32 * db + 8 * j + 4 * hl) = v4;
+      }
+    if (hl == 0)
+      a.lse[(int64_t)bh * a.N + qi] =
+          lt > 0.f ? (m + __builtin_amdgcn_logf(lt)) * kLn2 : -kInf;
+  }
+}
+
+template <bool C, bool S, bool M>
+hipError_t launch(const FwdArgs& a, hipStream_t stream) {
+  const int nqt = (a.N + kBR - 1) / kBR;
+  dim3 grid((unsigned)(nqt * a.B * a.H)), block(256);
+  FwdArgs copy = a;
+  void* args[] = {&copy};
+  return hipLaunchKernel((const void*)&fwd_bf16_kernel<C, S, M>, grid, block, args, 0, stream);
+}
+
+}  // namespace
+
+hipError_t launch_fwd_bf16(const FwdArgs& a, bool causal, hipStream_t stream) {
+  const bool s = a.seqlens != nullptr, m = a.bmask != nullptr;
+  if (causal) {
+    if (s) return m ? launch<true, true, true>(a, stream) : launch<true, true, false>(a, stream);
+    return m ? launch<true, false, true>(a, stream) : launch<true, false, false>(a, stream);
+  }
+  if (s) return m ? launch<false, true, true>(a, stream) : launch<false, true, false>(a, stream);
+  return m ? launch<false, false, true>(a, stream) : launch<false, false, false>(a, stream);
+}
+
+}  // namespace fa

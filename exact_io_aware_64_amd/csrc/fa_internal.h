@@ -1,0 +1,61 @@
+// Internal launch arguments shared by the host API (fa_api.hip) and the
+// kernels.  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+// Key or query rows per LDS tile and per mask expansion unit.
+constexpr int kTile = 64;
+// Largest number of 64-row tiles a block-mask list may hold (N <= 262144).
+constexpr int kMaxListTiles = 4096;
+
+struct Strides {
+  int64_t b, h, s;
+};
+
+struct FwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  Strides sq, sk, sv, so;
+  int B, H, N;
+  float scale;       // softmax scale
+  float scale_log2;  // scale * log2(e): scores enter exp2 directly
+  const int32_t* seqlens;
+  const uint8_t* bmask;
+  int mask_block;
+  int n_mask_tiles;
+};
+
+struct BwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const void* dout;
+  const float* lse;
+  void* dq;
+  void* dk;
+  void* dv;
+  float* dsum;  // workspace: D_i = dot(dO_i, O_i), fp32 [B*H*N]
+  Strides sq, sk, sv, so, sdo, sdq, sdk, sdv;
+  int B, H, N;
+  float scale;
+  float scale_log2;
+  const int32_t* seqlens;
+  const uint8_t* bmask;
+  int mask_block;
+  int n_mask_tiles;
+};
+
+hipError_t launch_fwd_bf16(const FwdArgs& a, bool causal, hipStream_t stream);
+hipError_t launch_bwd_bf16(const BwdArgs& a, bool causal, hipStream_t stream);
+hipError_t launch_fwd_f32(const FwdArgs& a, bool causal, hipStream_t stream);
+hipError_t launch_bwd_f32(const BwdArgs& a, bool causal, hipStream_t stream);
+
+}  // namespace fa

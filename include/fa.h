@@ -1,0 +1,153 @@
+/*
+ * fa.h -- C ABI of the exact, IO-aware, tiled attention library (libfa.so).
+ *
+ * The operation is exact softmax attention computed tile by tile without
+ * ever storing the N x N score or probability matrix in device memory:
+ *   suanlizi.com summary of FlashAttention, "tiling" and "kernel fusion"
+ *     (Q, K, V are processed block by block inside one fused kernel);
+ *   researchpapers.dev explainer "FlashAttention 详解", "tiling and
+ *     recomputation" (online softmax with a running maximum and sum; the
+ *     backward pass recomputes attention blocks from saved statistics);
+ *   suanlizi.com, "block-sparse attention" (only kept blocks are computed).
+ *
+ * Definitions (per batch b, head h, query i, key j):
+ *   s_ij = scale * dot(q_i, k_j)
+ *   visible(i, j) = (!causal || j <= i) && (j < len_b) && block_mask[i/mb][j/mb]
+ *   L_i  = ln sum_{visible j} exp(s_ij)      (natural-log logsumexp, fp32)
+ *   O_i  = sum_{visible j} exp(s_ij - L_i) v_j
+ * A row with no visible key gets O_i = 0 and L_i = -inf and contributes no
+ * gradient.  The backward pass returns the gradients of sum(dO * O).
+ *
+ * Tensor layout.  Q, K, V, O, dO, dQ, dK, dV are rank-4 tensors indexed
+ * [b][h][n][e] (e < d).  Each has its own fa_strides giving the element
+ * strides of b, h and n; the e dimension must be contiguous (stride 1).  So
+ * both [B,H,N,d] and [B,N,H,d] storage are accepted.  L (lse) is always a
+ * contiguous fp32 [B,H,N] array.
+ *
+ * Ownership and synchronisation.  The caller owns every buffer (device
+ * memory).  The library never allocates or frees memory, keeps no state
+ * between calls apart from a per-thread error message, and is safe to call
+ * from several host threads.  Work is enqueued on `stream` (NULL = the
+ * default stream) and the call returns without synchronising; a device fault
+ * surfaces at the caller's next synchronisation.  Outputs must not alias
+ * inputs.  All argument checks run on the host before any HIP call, so a
+ * rejected call touches no device state.
+ */
+#ifndef FA_H_
+#define FA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element type of Q, K, V, O, dO, dQ, dK, dV.  L and internal statistics are
+ * always fp32. */
+typedef enum fa_dtype {
+  FA_BF16 = 0,
+  FA_F32 = 1
+} fa_dtype;
+
+typedef enum fa_status {
+  FA_OK = 0,
+  FA_ERR_INVALID_ARG = 1, /* null pointer, bad size, stride or alignment, scale <= 0,
+                             workspace too small, bad mask_block */
+  FA_ERR_UNSUPPORTED = 2, /* valid request this build does not implement (d != 64,
+                             too many mask tiles) */
+  FA_ERR_HIP = 3          /* a HIP launch reported an error */
+} fa_status;
+
+/* Element strides of the batch, head and sequence dimensions. */
+typedef struct fa_strides {
+  int64_t batch;
+  int64_t head;
+  int64_t seq;
+} fa_strides;
+
+/*
+ * fa_fwd -- forward pass: writes O and L.
+ *
+ *   dtype        FA_BF16 or FA_F32: element type of q, k, v and o.
+ *   q, k, v      device pointers, [B][H][N][d] through their strides.
+ *   o            device pointer, same element type, written in full.
+ *   lse          device fp32 [B*H*N], contiguous, written in full (L above).
+ *   B, H, N      >= 1.   d: must be 64.
+ *   scale        score scale (> 0, finite), typically 1/sqrt(d).
+ *   causal       nonzero: key j is visible to query i only if j <= i.
+ *   seqlens_k    NULL, or device int32[B]: keys j >= seqlens_k[b] are masked
+ *                (values are clamped to [0, N]).  Query rows are not masked.
+ *   block_mask   NULL, or device uint8[T*T], T = ceil(N / mask_block), row-major
+ *                [query tile][key tile], shared by all (b, h); nonzero = kept.
+ *                Skipped tiles are never loaded or computed.
+ *   mask_block   tile edge of block_mask, a positive multiple of 128 (ignored
+ *                when block_mask is NULL).
+ *   stream       HIP stream.
+ * Alignment: every pointer 16-byte aligned; for bf16 every stride a multiple
+ * of 8, for fp32 a multiple of 4.
+ */
+fa_status fa_fwd(fa_dtype dtype,
+                 const void* q, fa_strides q_strides,
+                 const void* k, fa_strides k_strides,
+                 const void* v, fa_strides v_strides,
+                 void* o, fa_strides o_strides,
+                 float* lse,
+                 int B, int H, int N, int d,
+                 float scale, int causal,
+                 const int32_t* seqlens_k,
+                 const uint8_t* block_mask, int mask_block,
+                 hipStream_t stream);
+
+/*
+ * fa_bwd_workspace_bytes -- device workspace that fa_bwd needs: one fp32 per
+ * (b, h, query) for D_i = dot(dO_i, O_i), rounded up to 256 bytes.
+ * Returns 0 for non-positive sizes.
+ */
+size_t fa_bwd_workspace_bytes(fa_dtype dtype, int B, int H, int N, int d);
+
+/*
+ * fa_bwd -- backward pass: writes dQ, dK and dV in full (zeros for keys that
+ * no query sees, e.g. keys past seqlens_k).  The scores and probabilities are
+ * recomputed tile by tile from q, k and the forward's lse; nothing of size
+ * N x N is read or written.
+ *
+ *   q, k, v, o, lse  the forward pass's inputs and outputs (o and lse as
+ *                    written by fa_fwd with the same mask arguments).
+ *   dout             upstream gradient dO, [B][H][N][d] through its strides.
+ *   dq, dk, dv       outputs, element type dtype, through their strides.
+ *   workspace        device buffer of at least fa_bwd_workspace_bytes(...) bytes,
+ *                    16-byte aligned; contents on entry are ignored.
+ *   remaining arguments as for fa_fwd and must match the forward call.
+ */
+fa_status fa_bwd(fa_dtype dtype,
+                 const void* q, fa_strides q_strides,
+                 const void* k, fa_strides k_strides,
+                 const void* v, fa_strides v_strides,
+                 const void* o, fa_strides o_strides,
+                 const void* dout, fa_strides dout_strides,
+                 const float* lse,
+                 void* dq, fa_strides dq_strides,
+                 void* dk, fa_strides dk_strides,
+                 void* dv, fa_strides dv_strides,
+                 void* workspace, size_t workspace_bytes,
+                 int B, int H, int N, int d,
+                 float scale, int causal,
+                 const int32_t* seqlens_k,
+                 const uint8_t* block_mask, int mask_block,
+                 hipStream_t stream);
+
+/* Static, human-readable name of a status code. */
+const char* fa_status_string(fa_status status);
+
+/* Message describing the most recent failure on the calling thread (empty
+ * string if none).  Valid until the next call on the same thread. */
+const char* fa_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_H_ */

@@ -1,0 +1,120 @@
+"""C ABI checks that need no GPU: the library loads, exports every entry point
+declared in include/fa.h, and rejects bad arguments on the host before any
+HIP call (so these calls never launch anything)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import exact_io_aware_64_amd as fa
+from exact_io_aware_64_amd import _binding as bnd
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(bnd.LIB_PATH),
+                                reason="libfa.so not built (run __graft_entry__.build())")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[A-Za-z_][\w\s\*]*?\b(fa_\w+)\s*\(",
+                                 text, flags=re.M)))
+
+
+def test_header_declares_the_expected_entry_points():
+    assert declared_functions() == sorted(fa.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(bnd.LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_status_strings():
+    assert fa.fa_status_string(0) == "FA_OK"
+    assert fa.fa_status_string(1) == "FA_ERR_INVALID_ARG"
+    assert fa.fa_status_string(2) == "FA_ERR_UNSUPPORTED"
+    assert fa.fa_status_string(3) == "FA_ERR_HIP"
+    assert fa.fa_status_string(99) == "FA_UNKNOWN_STATUS"
+
+
+def test_workspace_bytes():
+    assert fa.fa_bwd_workspace_bytes(0, 8, 12, 1024, 64) == 8 * 12 * 1024 * 4
+    assert fa.fa_bwd_workspace_bytes(0, 1, 1, 3, 64) == 256
+    assert fa.fa_bwd_workspace_bytes(0, 0, 1, 3, 64) == 0
+
+
+# Fake, suitably aligned device addresses: every call below must be rejected
+# by host-side validation, so they are never dereferenced.
+A = 0x10000
+S = bnd.fa_strides(8 * 1024 * 64, 1024 * 64, 64)
+
+
+def _fwd(**kw):
+    lib = fa.load_library()
+    args = dict(dtype=0, q=A, sq=S, k=A, sk=S, v=A, sv=S, o=A, so=S, lse=A, B=1, H=1, N=1024,
+                d=64, scale=0.125, causal=1, seqlens=None, bmask=None, mb=128, stream=None)
+    args.update(kw)
+    return lib.fa_fwd(*args.values())
+
+
+def _bwd(**kw):
+    lib = fa.load_library()
+    args = dict(dtype=0, q=A, sq=S, k=A, sk=S, v=A, sv=S, o=A, so=S, do=A, sdo=S, lse=A,
+                dq=A, sdq=S, dk=A, sdk=S, dv=A, sdv=S, ws=A, wsb=4096, B=1, H=1, N=1024,
+                d=64, scale=0.125, causal=0, seqlens=None, bmask=None, mb=128, stream=None)
+    args.update(kw)
+    return lib.fa_bwd(*args.values())
+
+
+@pytest.mark.parametrize("kw,status,msg", [
+    (dict(q=None), 1, "q is NULL"),
+    (dict(lse=None), 1, "lse is NULL"),
+    (dict(v=A + 8), 1, "v is not 16-byte aligned"),
+    (dict(B=0), 1, "must be positive"),
+    (dict(N=-5), 1, "must be positive"),
+    (dict(d=128), 2, "head dimension"),
+    (dict(scale=0.0), 1, "scale"),
+    (dict(scale=float("nan")), 1, "scale"),
+    (dict(dtype=7), 1, "dtype"),
+    (dict(sk=bnd.fa_strides(64, 64, 60)), 1, "multiples of 8"),
+    (dict(so=bnd.fa_strides(-64, 64, 64)), 1, "negative"),
+    (dict(bmask=A, mb=64), 1, "mask_block"),
+    (dict(bmask=A, mb=100), 1, "mask_block"),
+    (dict(bmask=A, N=300000), 2, "block mask"),
+    (dict(seqlens=A + 2), 1, "seqlens_k"),
+])
+def test_fwd_rejects_bad_arguments(kw, status, msg):
+    assert _fwd(**kw) == status
+    assert msg in fa.fa_last_error()
+
+
+@pytest.mark.parametrize("kw,status,msg", [
+    (dict(ws=None), 1, "workspace is NULL"),
+    (dict(wsb=100), 1, "workspace too small"),
+    (dict(dq=None), 1, "dq is NULL"),
+    (dict(do=A + 4), 1, "dout is not 16-byte aligned"),
+    (dict(dtype=1, sdv=bnd.fa_strides(64, 64, 66)), 1, "multiples of 4"),
+    (dict(d=32), 2, "head dimension"),
+])
+def test_bwd_rejects_bad_arguments(kw, status, msg):
+    assert _bwd(**kw) == status
+    assert msg in fa.fa_last_error()
+
+
+def test_missing_library_raises(tmp_path):
+    with pytest.raises(RuntimeError, match="not found"):
+        _load_fresh(str(tmp_path / "nope.so"))
+
+
+def _load_fresh(path):
+    saved = bnd._lib
+    bnd._lib = None
+    try:
+        return bnd.load_library(path)
+    finally:
+        bnd._lib = saved

@@ -1,0 +1,254 @@
+"""GPU parity: the HIP path (through the C ABI binding) against the fp64
+oracle on the same seeded inputs.
+
+Tolerances: O max-abs <= 1e-2, L max-abs <= 1e-3 and gradient relative
+Frobenius error <= 1e-2 for bf16; 1e-5 for all of them in fp32.
+"""
+import functools
+import sys
+
+import numpy as np
+import pytest
+
+import workloads as wl
+from oracle import attention_ref as ref
+from tests.gpu_util import (TOL, device_inputs, gpu_backward, gpu_forward, maxabs, opt_dev,
+                            oracle_args, relfro, to_dev, to_np)
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def check_full(case, layout="bhsd", backward=True, tag=""):
+    """Whole-tensor comparison with the oracle (small and medium sizes)."""
+    _say(f"[parity] {tag} layout={layout}")
+    tol = TOL[case["dtype"]]
+    q, k, v, do, sl, bm = device_inputs(case, layout)
+    o, lse = gpu_forward(case, q, k, v, sl, bm)
+    O, L = ref.forward(case["q"], case["k"], case["v"], **oracle_args(case))
+    eo = maxabs(to_np(o), O)
+    el = maxabs(to_np(lse), L)
+    assert np.array_equal(np.isinf(to_np(lse)), np.isinf(L)), "dead rows differ"
+    assert eo <= tol["O"], f"O max-abs {eo}"
+    assert el <= tol["L"], f"L max-abs {el}"
+    errs = dict(O=eo, L=el)
+    if backward:
+        dq, dk, dv = gpu_backward(case, q, k, v, o, do, lse, sl, bm)
+        gq, gk, gv = ref.backward(case["q"], case["k"], case["v"], case["do"],
+                                  **oracle_args(case))
+        for name, g, gs in (("dQ", dq, gq), ("dK", dk, gk), ("dV", dv, gv)):
+            e = relfro(to_np(g), gs)
+            errs[name] = e
+            assert e <= tol["G"], f"{name} rel-Frobenius {e}"
+            assert np.all(np.isfinite(to_np(g)))
+    _say(f"[parity] {tag} ok {errs}")
+    return errs
+
+
+# ----------------------------------------------------------- the workloads
+
+def test_single_head_f32_n128():
+    w = wl.WORKLOADS["single_head_f32_n128"]
+    case = wl.make_inputs(w)
+    case["mask_block"] = 128
+    check_full(case, tag=w.name, backward=True)
+
+
+@pytest.mark.parametrize("name", ["gpt2s_causal_b8h12n1024", "bertl_padded_b16h16n512"])
+def test_full_size_workload(name):
+    w = wl.WORKLOADS[name]
+    case = wl.make_inputs(w)
+    case["mask_block"] = 128
+    check_full(case, tag=name)
+
+
+@functools.lru_cache(maxsize=1)
+def _sampled_inputs(name):
+    w = wl.WORKLOADS[name]
+    case = wl.make_inputs(w)
+    case["mask_block"] = 128
+    return case
+
+
+@pytest.mark.parametrize("name", ["long_causal_b1h16n16384", "blocksparse_b1h8n65536"])
+def test_sampled_workload(name):
+    """Full-size run checked on sampled query rows (O, L, dQ exact per row),
+    a second backward with dO zeroed outside the sample (dK, dV exact for that
+    restricted problem), and full-tensor gradient identities."""
+    import torch
+    _say(f"[parity] {name} sampled")
+    case = _sampled_inputs(name)
+    tol = TOL["bf16"]
+    rows = case["rows"]
+    B, H, N, d = case["q"].shape
+    q, k, v, do, sl, bm = device_inputs(case)
+    o, lse = gpu_forward(case, q, k, v, sl, bm)
+    dq, dk, dv = gpu_backward(case, q, k, v, o, do, lse, sl, bm)
+    torch.cuda.synchronize()
+    O, L = ref.forward(case["q"], case["k"], case["v"], rows=rows, **oracle_args(case))
+    gq, gk, gv = ref.backward(case["q"], case["k"], case["v"], case["do"], rows=rows,
+                              **oracle_args(case))
+    o_np, l_np, dq_np = to_np(o), to_np(lse), to_np(dq)
+    idx = (np.arange(B)[:, None, None], np.arange(H)[None, :, None], rows)
+    eo = maxabs(o_np[idx], O)
+    el = maxabs(l_np[idx], L)
+    eq = relfro(dq_np[idx], gq)
+    assert eo <= tol["O"], f"O {eo}"
+    assert el <= tol["L"], f"L {el}"
+    assert eq <= tol["G"], f"dQ {eq}"
+    # full-tensor identities on the real run: sum_j dK_j = 0 and
+    # sum_j dV_j = sum_i dO_i for every (b, h) (no row is fully masked here)
+    dk_np, dv_np = to_np(dk), to_np(dv)
+    do_sum = case["do"].astype(np.float64).sum(axis=2)
+    for b in range(B):
+        for h in range(H):
+            assert np.linalg.norm(dk_np[b, h].sum(0)) <= 1e-2 * np.linalg.norm(dk_np[b, h])
+            assert np.linalg.norm(dv_np[b, h].sum(0) - do_sum[b, h]) <= \
+                1e-2 * np.linalg.norm(do_sum[b, h]) + 1e-2 * np.sqrt(N)
+    # restricted problem: dO zero outside the sampled rows
+    do_r = np.zeros_like(case["do"])
+    for b in range(B):
+        for h in range(H):
+            do_r[b, h, rows[b, h]] = case["do"][b, h, rows[b, h]]
+    dor = to_dev(do_r, "bf16")
+    _, dk_r, dv_r = gpu_backward(case, q, k, v, o, dor, lse, sl, bm)
+    ek = relfro(to_np(dk_r), gk)
+    ev = relfro(to_np(dv_r), gv)
+    assert ek <= tol["G"], f"dK {ek}"
+    assert ev <= tol["G"], f"dV {ev}"
+    _say(f"[parity] {name} ok O={eo:.3g} L={el:.3g} dQ={eq:.3g} dK={ek:.3g} dV={ev:.3g}")
+
+
+# ------------------------------------------------------------ edge shapes
+
+EDGE_N = [1, 2, 15, 16, 17, 63, 64, 65, 127, 128, 129, 300, 1000]
+
+
+@pytest.mark.parametrize("N", EDGE_N)
+@pytest.mark.parametrize("causal", [False, True])
+def test_edge_lengths_dense(N, causal):
+    case = wl.random_case(2, 2, N, 64, seed=N * 7 + causal, causal=causal)
+    check_full(case, tag=f"N={N} causal={causal}")
+
+
+@pytest.mark.parametrize("N", [17, 129, 300, 1000])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("masks", ["seqlens", "block", "both"])
+def test_edge_masks(N, causal, masks):
+    seqlens = "random" if masks in ("seqlens", "both") else None
+    keep = 0.5 if masks in ("block", "both") else None
+    case = wl.random_case(3, 2, N, 64, seed=N + 13 * causal, causal=causal, seqlens=seqlens,
+                          block_keep_p=keep)
+    check_full(case, tag=f"N={N} causal={causal} {masks}")
+
+
+@pytest.mark.parametrize("layout", ["bhsd", "bshd"])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_layouts(layout, dtype):
+    case = wl.random_case(2, 3, 200, 64, dtype=dtype, seed=5, causal=True,
+                          seqlens=[150, 200])
+    check_full(case, layout=layout, tag=f"{dtype} {layout}")
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_f32_masks(causal):
+    case = wl.random_case(2, 2, 300, 64, dtype="f32", seed=3, causal=causal, seqlens="random",
+                          block_keep_p=0.5)
+    check_full(case, tag=f"f32 masks causal={causal}")
+
+
+def test_key_lengths_zero_and_full():
+    """len 0 (every row fully masked: O = 0, L = -inf, zero gradients), len 1
+    and len N in one batch."""
+    case = wl.random_case(3, 2, 200, 64, seed=9, seqlens=[0, 1, 200])
+    check_full(case, tag="seqlens 0/1/N")
+
+
+def test_empty_block_mask_rows():
+    rng = np.random.default_rng(4)
+    case = wl.random_case(1, 2, 512, 64, seed=4)
+    bm = (rng.random((4, 4)) < 0.5).astype(np.uint8)
+    bm[1, :] = 0      # query tile 1 sees nothing
+    bm[:, 3] = 0      # key tile 3 is seen by nobody (zero dK, dV)
+    case["block_mask"] = bm
+    check_full(case, tag="empty mask row/column")
+
+
+def test_block_mask_all_ones_equals_dense():
+    case = wl.random_case(1, 2, 384, 64, seed=8, causal=True)
+    q, k, v, do, _, _ = device_inputs(case)
+    o1, l1 = gpu_forward(case, q, k, v, None, None)
+    ones = opt_dev(np.ones((3, 3), np.uint8))
+    o2, l2 = gpu_forward(case, q, k, v, None, ones)
+    assert np.array_equal(to_np(o1), to_np(o2)) and np.array_equal(to_np(l1), to_np(l2))
+
+
+@pytest.mark.parametrize("kind", ["plus", "minus", "mixed"])
+def test_huge_scores_stay_finite(kind):
+    """Scores of +-20000 for every pair (the overflow / underflow examples of
+    the safe-softmax discussion): results stay finite and match the oracle.
+    L is checked to a few fp32 ulps at its magnitude."""
+    N, d = 256, 64
+    q = np.full((1, 1, N, d), 50.0, np.float32)
+    k = np.full((1, 1, N, d), 50.0 if kind != "minus" else -50.0, np.float32)
+    if kind == "mixed":
+        k[0, 0, 1::2] = -50.0
+    rng = np.random.default_rng(0)
+    v = wl.round_to_bf16(rng.standard_normal((1, 1, N, d)).astype(np.float32))
+    do = wl.round_to_bf16(rng.standard_normal((1, 1, N, d)).astype(np.float32))
+    case = dict(q=q, k=k, v=v, do=do, scale=0.125, causal=False, dtype="bf16",
+                seqlens=None, block_mask=None)
+    qd, kd, vd, dod, _, _ = device_inputs(case)
+    o, lse = gpu_forward(case, qd, kd, vd, None, None)
+    O, L = ref.forward(q, k, v, 0.125)
+    assert np.all(np.isfinite(to_np(o))) and np.all(np.isfinite(to_np(lse)))
+    assert maxabs(to_np(o), O) <= 1e-2
+    assert maxabs(to_np(lse), L) <= 8 * np.spacing(np.float32(20000.0)) + 1e-3
+    dq, dk, dv = gpu_backward(case, qd, kd, vd, o, dod, lse, None, None)
+    gq, gk, gv = ref.backward(q, k, v, do, 0.125)
+    for g, gs in ((dq, gq), (dk, gk), (dv, gv)):
+        assert np.all(np.isfinite(to_np(g)))
+        assert relfro(to_np(g), gs) <= 2e-2 or np.linalg.norm(to_np(g) - gs) <= 1e-1
+
+
+def test_repeatable_bitwise():
+    """No atomics anywhere: two runs give identical bits."""
+    case = wl.random_case(2, 4, 700, 64, seed=21, causal=True, seqlens="random")
+    q, k, v, do, sl, bm = device_inputs(case)
+    r1 = gpu_forward(case, q, k, v, sl, bm)
+    r2 = gpu_forward(case, q, k, v, sl, bm)
+    g1 = gpu_backward(case, q, k, v, r1[0], do, r1[1], sl, bm)
+    g2 = gpu_backward(case, q, k, v, r1[0], do, r1[1], sl, bm)
+    for a, b in zip(r1 + g1, r2 + g2):
+        assert np.array_equal(to_np(a), to_np(b))
+
+
+def test_memory_linear_in_N():
+    """Peak device memory of fwd + bwd is the inputs, outputs, L and the
+    per-row workspace: linear in N, nothing N x N (at N = 65536 one bf16
+    score matrix for 8 heads would be 68.7 GB)."""
+    import torch
+    import exact_io_aware_64_amd as fa
+    H, d = 8, 64
+    peaks = {}
+    for N in (4096, 16384, 65536):
+        case = wl.random_case(1, H, 256, d, seed=1)   # values irrelevant here
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+        torch.cuda.reset_peak_memory_stats()
+        base = torch.cuda.memory_allocated()
+        q = torch.randn(1, H, N, d, device="cuda", dtype=torch.bfloat16)
+        k, v, do = torch.randn_like(q), torch.randn_like(q), torch.randn_like(q)
+        bm = torch.eye(N // 128, dtype=torch.uint8, device="cuda")
+        o, lse = fa.forward(q, k, v, scale=0.125, block_mask=bm)
+        dq, dk, dv = fa.backward(q, k, v, o, do, lse, scale=0.125, block_mask=bm)
+        torch.cuda.synchronize()
+        peaks[N] = torch.cuda.max_memory_allocated() - base
+        expect = 8 * H * N * d * 2 + 2 * H * N * 4 + (N // 128) ** 2
+        assert peaks[N] <= 1.1 * expect + (4 << 20), (N, peaks[N], expect)
+        del q, k, v, do, o, lse, dq, dk, dv, bm, case
+    _say(f"[memory] peaks {peaks}")
