@@ -46,7 +46,8 @@ def maxabs(a, b) -> float:
     if a.size == 0:
         return 0.0
     both_inf = np.isinf(a) & np.isinf(b) & (np.sign(a) == np.sign(b))
-    d = np.where(both_inf, 0.0, np.abs(a - b))
+    with np.errstate(invalid="ignore"):
+        d = np.where(both_inf, 0.0, np.abs(a - b))
     return float(np.nanmax(np.where(np.isnan(d), np.inf, d)))
 
 

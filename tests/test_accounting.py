@@ -1,0 +1,50 @@
+"""The bench's FLOP accounting: closed-form pair counts against a brute-force
+count over the oracle's materialised mask, and the single-GPU guard."""
+import numpy as np
+import pytest
+
+import bench
+import workloads as wl
+from oracle import attention_ref as ref
+
+
+@pytest.mark.parametrize("N,causal,seqlens,p", [
+    (300, True, [100, 300, 0], 0.4),
+    (256, False, None, 0.3),
+    (200, True, None, None),
+    (130, False, [5, 130], None),
+    (384, True, [384, 200], 0.5),
+    (1, False, None, None),
+])
+def test_pairs_match_brute_force(N, causal, seqlens, p):
+    rng = np.random.default_rng(N)
+    bm = wl.draw_block_mask(rng, N, p) if p else None
+    B = 1 if seqlens is None else len(seqlens)
+    sl = None if seqlens is None else np.array(seqlens, np.int32)
+    got = bench.visible_pairs(N, 3, causal, sl, bm, 128, B)
+    want = 3 * ref.visible_pair_count(N, causal, sl, bm, 128, B)
+    assert got == want
+
+
+def test_workload_pair_counts():
+    w = wl.WORKLOADS["gpt2s_causal_b8h12n1024"]
+    assert bench.visible_pairs(w.N, w.H, True, None, None, 128, w.B) == 50_380_800
+    w = wl.WORKLOADS["long_causal_b1h16n16384"]
+    assert bench.visible_pairs(w.N, w.H, True, None, None, 128, w.B) == 2_147_614_720
+    w = wl.WORKLOADS["blocksparse_b1h8n65536"]
+    bm = wl.draw_block_mask(np.random.default_rng(0), w.N, 1 / 16)
+    assert bench.visible_pairs(w.N, w.H, False, None, bm, 128, 1) == 8 * int(bm.sum()) * 128 * 128
+
+
+def test_kernel_bytes():
+    f, b = bench.kernel_bytes(8, 12, 1024, 64, 2, None)
+    t = 8 * 12 * 1024 * 64 * 2
+    assert f == 4 * t + 8 * 12 * 1024 * 4
+    assert b == 7 * t + 3 * 8 * 12 * 1024 * 4
+    f2, _ = bench.kernel_bytes(2, 1, 100, 64, 2, np.array([50, 100]))
+    assert f2 == 2 * (2 * 100 * 64 * 2) + 2 * (150 * 64 * 2) + 2 * 100 * 4
+
+
+def test_more_than_one_gpu_is_refused(capsys):
+    assert bench.main(["--gpus", "2"]) == 2
+    assert "one GPU" in capsys.readouterr().err

@@ -187,11 +187,27 @@ def test_block_mask_all_ones_equals_dense():
     assert np.array_equal(to_np(o1), to_np(o2)) and np.array_equal(to_np(l1), to_np(l2))
 
 
+def _product_magnitudes(q, k, v, do, scale):
+    """Element-wise magnitudes |A||B| of the three gradient products, used to
+    bound rounding error when the exact gradient itself vanishes."""
+    q, k, v, do = (np.asarray(x, np.float64)[0, 0] for x in (q, k, v, do))
+    s = scale * q @ k.T
+    p = np.exp(s - s.max(axis=1, keepdims=True))
+    p /= p.sum(axis=1, keepdims=True)
+    dp = do @ v.T
+    ds = p * (dp - (p * dp).sum(axis=1, keepdims=True))
+    return (scale * np.abs(ds) @ np.abs(k), scale * np.abs(ds).T @ np.abs(q),
+            np.abs(p).T @ np.abs(do))
+
+
 @pytest.mark.parametrize("kind", ["plus", "minus", "mixed"])
 def test_huge_scores_stay_finite(kind):
     """Scores of +-20000 for every pair (the overflow / underflow examples of
     the safe-softmax discussion): results stay finite and match the oracle.
-    L is checked to a few fp32 ulps at its magnitude."""
+    L is checked to a few fp32 ulps at its magnitude.  With all keys equal the
+    exact dQ is 0 while fp32 scores near 20000 carry ~1e-3 absolute error, so
+    gradients are bounded relative to the magnitude of their products,
+    ||g - g*|| <= 1e-2 || |A| |B| ||."""
     N, d = 256, 64
     q = np.full((1, 1, N, d), 50.0, np.float32)
     k = np.full((1, 1, N, d), 50.0 if kind != "minus" else -50.0, np.float32)
@@ -210,9 +226,12 @@ def test_huge_scores_stay_finite(kind):
     assert maxabs(to_np(lse), L) <= 8 * np.spacing(np.float32(20000.0)) + 1e-3
     dq, dk, dv = gpu_backward(case, qd, kd, vd, o, dod, lse, None, None)
     gq, gk, gv = ref.backward(q, k, v, do, 0.125)
-    for g, gs in ((dq, gq), (dk, gk), (dv, gv)):
-        assert np.all(np.isfinite(to_np(g)))
-        assert relfro(to_np(g), gs) <= 2e-2 or np.linalg.norm(to_np(g) - gs) <= 1e-1
+    mags = _product_magnitudes(q, k, v, do, 0.125)
+    for name, g, gs, mag in zip(("dQ", "dK", "dV"), (dq, dk, dv), (gq, gk, gv), mags):
+        gn = to_np(g)
+        assert np.all(np.isfinite(gn)), name
+        err = np.linalg.norm(gn[0, 0] - gs[0, 0])
+        assert err <= 1e-2 * np.linalg.norm(mag), (name, err, np.linalg.norm(mag))
 
 
 def test_repeatable_bitwise():
