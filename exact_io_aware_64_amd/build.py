@@ -26,6 +26,7 @@ SOURCES = ["fa_api.hip", "fa_fwd_bf16.hip", "fa_bwd_bf16.hip", "fa_f32.hip"]
 # would otherwise pair independent fp32 operations into them.
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 CFLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall",
+          "-mllvm", "-amdgpu-mfma-vgpr-form",
           "-Wno-unused-command-line-argument"] + DEVICE_FLAGS
 
 

@@ -24,7 +24,7 @@ fa_status fail(fa_status st, const char* fmt, ...) {
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
-fa_status check_tensor(const char* name, const void* p, fa_strides s, int elem_align) {
+fa_status check_tensor(const char* name, const void* p, fa_strides s, int elem_align, int N) {
   if (p == nullptr) return fail(FA_ERR_INVALID_ARG, "%s is NULL", name);
   if (!aligned16(p)) return fail(FA_ERR_INVALID_ARG, "%s is not 16-byte aligned", name);
   if (s.batch < 0 || s.head < 0 || s.seq < 0)
@@ -32,6 +32,11 @@ fa_status check_tensor(const char* name, const void* p, fa_strides s, int elem_a
   if (s.batch % elem_align || s.head % elem_align || s.seq % elem_align)
     return fail(FA_ERR_INVALID_ARG, "%s strides must be multiples of %d elements", name,
                 elem_align);
+  // The kernels address one (batch, head) slice with 32-bit byte offsets,
+  // including up to 128 rows past its end.
+  const int esize = elem_align == 8 ? 2 : 4;
+  if (((long long)N + 128) * (long long)s.seq * esize >= (1LL << 31))
+    return fail(FA_ERR_UNSUPPORTED, "%s: one (batch, head) slice spans 2 GiB or more", name);
   return FA_OK;
 }
 
@@ -80,10 +85,10 @@ fa_status fa_fwd(fa_dtype dtype, const void* q, fa_strides q_strides, const void
   int al = 0;
   fa_status st = check_common(dtype, B, H, N, d, scale, block_mask, mask_block, &al);
   if (st != FA_OK) return st;
-  if ((st = check_tensor("q", q, q_strides, al)) != FA_OK) return st;
-  if ((st = check_tensor("k", k, k_strides, al)) != FA_OK) return st;
-  if ((st = check_tensor("v", v, v_strides, al)) != FA_OK) return st;
-  if ((st = check_tensor("o", o, o_strides, al)) != FA_OK) return st;
+  if ((st = check_tensor("q", q, q_strides, al, N)) != FA_OK) return st;
+  if ((st = check_tensor("k", k, k_strides, al, N)) != FA_OK) return st;
+  if ((st = check_tensor("v", v, v_strides, al, N)) != FA_OK) return st;
+  if ((st = check_tensor("o", o, o_strides, al, N)) != FA_OK) return st;
   if (lse == nullptr) return fail(FA_ERR_INVALID_ARG, "lse is NULL");
   if (!aligned16(lse)) return fail(FA_ERR_INVALID_ARG, "lse is not 16-byte aligned");
   if (seqlens_k != nullptr && ((uintptr_t)seqlens_k & 3u))
@@ -132,14 +137,14 @@ fa_status fa_bwd(fa_dtype dtype, const void* q, fa_strides q_strides, const void
   int al = 0;
   fa_status st = check_common(dtype, B, H, N, d, scale, block_mask, mask_block, &al);
   if (st != FA_OK) return st;
-  if ((st = check_tensor("q", q, q_strides, al)) != FA_OK) return st;
-  if ((st = check_tensor("k", k, k_strides, al)) != FA_OK) return st;
-  if ((st = check_tensor("v", v, v_strides, al)) != FA_OK) return st;
-  if ((st = check_tensor("o", o, o_strides, al)) != FA_OK) return st;
-  if ((st = check_tensor("dout", dout, dout_strides, al)) != FA_OK) return st;
-  if ((st = check_tensor("dq", dq, dq_strides, al)) != FA_OK) return st;
-  if ((st = check_tensor("dk", dk, dk_strides, al)) != FA_OK) return st;
-  if ((st = check_tensor("dv", dv, dv_strides, al)) != FA_OK) return st;
+  if ((st = check_tensor("q", q, q_strides, al, N)) != FA_OK) return st;
+  if ((st = check_tensor("k", k, k_strides, al, N)) != FA_OK) return st;
+  if ((st = check_tensor("v", v, v_strides, al, N)) != FA_OK) return st;
+  if ((st = check_tensor("o", o, o_strides, al, N)) != FA_OK) return st;
+  if ((st = check_tensor("dout", dout, dout_strides, al, N)) != FA_OK) return st;
+  if ((st = check_tensor("dq", dq, dq_strides, al, N)) != FA_OK) return st;
+  if ((st = check_tensor("dk", dk, dk_strides, al, N)) != FA_OK) return st;
+  if ((st = check_tensor("dv", dv, dv_strides, al, N)) != FA_OK) return st;
   if (lse == nullptr) return fail(FA_ERR_INVALID_ARG, "lse is NULL");
   if (!aligned16(lse)) return fail(FA_ERR_INVALID_ARG, "lse is not 16-byte aligned");
   if (workspace == nullptr) return fail(FA_ERR_INVALID_ARG, "workspace is NULL");

@@ -66,25 +66,31 @@ __global__ __launch_bounds__(256) void dq_kernel(BwdArgs a) {
                             a.n_mask_tiles, a.mask_block / kTile, 0, ntk);
   }
 
-  const uint16_t* Q = (const uint16_t*)a.q + b * a.sq.b + hh * a.sq.h;
-  const uint16_t* K = (const uint16_t*)a.k + b * a.sk.b + hh * a.sk.h;
-  const uint16_t* V = (const uint16_t*)a.v + b * a.sv.b + hh * a.sv.h;
-  const uint16_t* O = (const uint16_t*)a.o + b * a.so.b + hh * a.so.h;
-  const uint16_t* dO = (const uint16_t*)a.dout + b * a.sdo.b + hh * a.sdo.h;
+  const __amdgpu_buffer_rsrc_t rq =
+      make_rsrc((const uint16_t*)a.q + b * a.sq.b + hh * a.sq.h, slice_bytes(a.N, a.sq.s, 2));
+  const __amdgpu_buffer_rsrc_t rk =
+      make_rsrc((const uint16_t*)a.k + b * a.sk.b + hh * a.sk.h, slice_bytes(a.N, a.sk.s, 2));
+  const __amdgpu_buffer_rsrc_t rv =
+      make_rsrc((const uint16_t*)a.v + b * a.sv.b + hh * a.sv.h, slice_bytes(a.N, a.sv.s, 2));
+  const __amdgpu_buffer_rsrc_t ro =
+      make_rsrc((const uint16_t*)a.o + b * a.so.b + hh * a.so.h, slice_bytes(a.N, a.so.s, 2));
+  const __amdgpu_buffer_rsrc_t rdo = make_rsrc(
+      (const uint16_t*)a.dout + b * a.sdo.b + hh * a.sdo.h, slice_bytes(a.N, a.sdo.s, 2));
+  const int ssk = (int)a.sk.s * 2, ssv = (int)a.sv.s * 2;
 
+  // Q and dO fragments (B operands, lane (r, hl) holds row qi, columns
+  // 16 ks + 8 hl .. +7) and D_i = dot(dO_i, O_i) over the two wave halves.
   bf16x8 qf[4], dof[4];
   float Dq = 0.f;
   {
-    const uint4 z = make_uint4(0, 0, 0, 0);
-    const bool in = qi < a.N;
-    const uint16_t* qp = Q + (int64_t)qi * a.sq.s + 8 * hl;
-    const uint16_t* dp = dO + (int64_t)qi * a.sdo.s + 8 * hl;
-    const uint16_t* opp = O + (int64_t)qi * a.so.s + 8 * hl;
+    const int oq = qi * (int)a.sq.s * 2 + 16 * hl;
+    const int odo = qi * (int)a.sdo.s * 2 + 16 * hl;
+    const int oo = qi * (int)a.so.s * 2 + 16 * hl;
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
-      qf[ks] = as_bf16x8(in ? ldg16(qp + 16 * ks) : z);
-      dof[ks] = as_bf16x8(in ? ldg16(dp + 16 * ks) : z);
-      const bf16x8 of = as_bf16x8(in ? ldg16(opp + 16 * ks) : z);
+      qf[ks] = as_bf16x8(ldb16(rq, oq + 32 * ks));
+      dof[ks] = as_bf16x8(ldb16(rdo, odo + 32 * ks));
+      const bf16x8 of = as_bf16x8(ldb16(ro, oo + 32 * ks));
 #pragma unroll
       for (int e = 0; e < 8; ++e) Dq += (float)dof[ks][e] * (float)of[e];
     }
@@ -103,6 +109,8 @@ __global__ __launch_bounds__(256) void dq_kernel(BwdArgs a) {
   // Staging: K rows 2*(tid/8), 2*(tid/8)+1 row-major and transposed; V rows
   // tid/8 and tid/8+32 row-major; 16-byte column tid%8.
   const int sr = tid >> 3, sc = tid & 7;
+  const int k_off0 = 2 * sr * ssk + 16 * sc, k_off1 = (2 * sr + 1) * ssk + 16 * sc;
+  const int v_off0 = sr * ssv + 16 * sc, v_off1 = (sr + 32) * ssv + 16 * sc;
   uint4 kreg[2], vreg[2];
   auto tile_at = [&](int it) -> int {
     if constexpr (BMASK) return tlist[it];
@@ -110,14 +118,10 @@ __global__ __launch_bounds__(256) void dq_kernel(BwdArgs a) {
   };
   auto gload = [&](int t) {
     const int k0 = t * kTile;
-    const uint4 z = make_uint4(0, 0, 0, 0);
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int kk = k0 + 2 * sr + u;
-      kreg[u] = kk < a.N ? ldg16(K + (int64_t)kk * a.sk.s + 8 * sc) : z;
-      const int kv = k0 + sr + 32 * u;
-      vreg[u] = kv < a.N ? ldg16(V + (int64_t)kv * a.sv.s + 8 * sc) : z;
-    }
+    kreg[0] = ldb16(rk, k_off0 + k0 * ssk);
+    kreg[1] = ldb16(rk, k_off1 + k0 * ssk);
+    vreg[0] = ldb16(rv, v_off0 + k0 * ssv);
+    vreg[1] = ldb16(rv, v_off1 + k0 * ssv);
   };
   auto swrite = [&](int buf) {
     store_row16(s_k[buf], 2 * sr, sc, kreg[0]);
@@ -143,28 +147,24 @@ __global__ __launch_bounds__(256) void dq_kernel(BwdArgs a) {
       const uint16_t* ks_ = s_k[buf];
       const uint16_t* kt_ = s_kt[buf];
       const uint16_t* vs_ = s_v[buf];
-      f32x16 st[2], dpt[2];
+      f32x16 st[2] = {zero16(), zero16()}, dpt[2] = {zero16(), zero16()};
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        st[kb] = zero16();
-        dpt[kb] = zero16();
+      for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
+        for (int kb = 0; kb < 2; ++kb) {
           const int off = (32 * kb + r) * kRowStride + 16 * ks + 8 * hl;
           st[kb] = mfma32(lds_row8(ks_ + off), qf[ks], st[kb]);
           dpt[kb] = mfma32(lds_row8(vs_ + off), dof[ks], dpt[kb]);
         }
-      }
       const bool need_mask = (k0 + kTile > kv_len) || (CAUSAL && k0 + kTile - 1 > qw);
       if (need_mask) {
+        const int last = CAUSAL ? min(kv_len - 1, qi) : kv_len - 1;
+        const int lim = last - k0 - 4 * hl;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-          for (int e = 0; e < 16; ++e) {
-            const int key = k0 + 32 * kb + 8 * (e >> 2) + 4 * hl + (e & 3);
-            const bool vis = key < kv_len && (!CAUSAL || key <= qi);
-            if (!vis) st[kb][e] = -kInf;
-          }
+          for (int e = 0; e < 16; ++e)
+            if (32 * kb + 8 * (e >> 2) + (e & 3) > lim) st[kb][e] = -kInf;
       }
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
@@ -247,30 +247,40 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdArgs a) {
                               a.mask_block / kTile, qt_lo, nq);
     }
 
-    const uint16_t* Q = (const uint16_t*)a.q + b * a.sq.b + hh * a.sq.h;
-    const uint16_t* K = (const uint16_t*)a.k + b * a.sk.b + hh * a.sk.h;
-    const uint16_t* V = (const uint16_t*)a.v + b * a.sv.b + hh * a.sv.h;
-    const uint16_t* dO = (const uint16_t*)a.dout + b * a.sdo.b + hh * a.sdo.h;
+    const __amdgpu_buffer_rsrc_t rq =
+        make_rsrc((const uint16_t*)a.q + b * a.sq.b + hh * a.sq.h, slice_bytes(a.N, a.sq.s, 2));
+    const __amdgpu_buffer_rsrc_t rk =
+        make_rsrc((const uint16_t*)a.k + b * a.sk.b + hh * a.sk.h, slice_bytes(a.N, a.sk.s, 2));
+    const __amdgpu_buffer_rsrc_t rv =
+        make_rsrc((const uint16_t*)a.v + b * a.sv.b + hh * a.sv.h, slice_bytes(a.N, a.sv.s, 2));
+    const __amdgpu_buffer_rsrc_t rdo = make_rsrc(
+        (const uint16_t*)a.dout + b * a.sdo.b + hh * a.sdo.h, slice_bytes(a.N, a.sdo.s, 2));
     const float* lse = a.lse + (int64_t)bh * a.N;
     const float* dsum = a.dsum + (int64_t)bh * a.N;
+    const int ssq = (int)a.sq.s * 2, ssdo = (int)a.sdo.s * 2;
 
+    // K and V fragments (B operands): lane (r, hl) holds row kj, columns
+    // 16 ks + 8 hl .. +7.
     bf16x8 kf[4], vf[4];
     {
-      const uint4 z = make_uint4(0, 0, 0, 0);
-      const bool in = kj < a.N;
-      const uint16_t* kp = K + (int64_t)kj * a.sk.s + 8 * hl;
-      const uint16_t* vp = V + (int64_t)kj * a.sv.s + 8 * hl;
+      const int ok = kj * (int)a.sk.s * 2 + 16 * hl;
+      const int ov = kj * (int)a.sv.s * 2 + 16 * hl;
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
-        kf[ks] = as_bf16x8(in ? ldg16(kp + 16 * ks) : z);
-        vf[ks] = as_bf16x8(in ? ldg16(vp + 16 * ks) : z);
+        kf[ks] = as_bf16x8(ldb16(rk, ok + 32 * ks));
+        vf[ks] = as_bf16x8(ldb16(rv, ov + 32 * ks));
       }
     }
     const float c = a.scale_log2;
+    // Causal: element e of block qb holds query qs + 4*hl + off(qb, e) and is
+    // visible iff off >= qs_lim - qs; keys past the sequence see nothing.
+    const int key_lim = (kj < kv_len) ? (CAUSAL ? kj - 4 * hl : -(1 << 30)) : (1 << 30);
 
     // Staging: Q and dO rows 2*(tid/8), 2*(tid/8)+1 at 16-byte column tid%8,
     // row-major and transposed; threads 0..63 also fetch L and D of one row.
     const int sr = tid >> 3, sc = tid & 7;
+    const int q_off0 = 2 * sr * ssq + 16 * sc, q_off1 = (2 * sr + 1) * ssq + 16 * sc;
+    const int d_off0 = 2 * sr * ssdo + 16 * sc, d_off1 = (2 * sr + 1) * ssdo + 16 * sc;
     uint4 qreg[2], dreg[2];
     float lreg = 0.f, dreg_s = 0.f;
     auto tile_at = [&](int it) -> int {
@@ -279,13 +289,10 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdArgs a) {
     };
     auto gload = [&](int t) {
       const int qs = t * kTile;
-      const uint4 z = make_uint4(0, 0, 0, 0);
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const int qq = qs + 2 * sr + u;
-        qreg[u] = qq < a.N ? ldg16(Q + (int64_t)qq * a.sq.s + 8 * sc) : z;
-        dreg[u] = qq < a.N ? ldg16(dO + (int64_t)qq * a.sdo.s + 8 * sc) : z;
-      }
+      qreg[0] = ldb16(rq, q_off0 + qs * ssq);
+      qreg[1] = ldb16(rq, q_off1 + qs * ssq);
+      dreg[0] = ldb16(rdo, d_off0 + qs * ssdo);
+      dreg[1] = ldb16(rdo, d_off1 + qs * ssdo);
       if (tid < kTile) {
         const int qq = qs + tid;
         const float L = qq < a.N ? lse[qq] : -kInf;
@@ -323,28 +330,23 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdArgs a) {
         const uint16_t* qt_ = s_qt[buf];
         const uint16_t* ds_ = s_do[buf];
         const uint16_t* dt_ = s_dot[buf];
-        f32x16 s[2], dp[2];
+        f32x16 s[2] = {zero16(), zero16()}, dp[2] = {zero16(), zero16()};
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb) {
-          s[qb] = zero16();
-          dp[qb] = zero16();
+        for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
-          for (int ks = 0; ks < 4; ++ks) {
+          for (int qb = 0; qb < 2; ++qb) {
             const int off = (32 * qb + r) * kRowStride + 16 * ks + 8 * hl;
             s[qb] = mfma32(lds_row8(qs_ + off), kf[ks], s[qb]);
             dp[qb] = mfma32(lds_row8(ds_ + off), vf[ks], dp[qb]);
           }
-        }
         const bool need_mask = (kw + 32 > kv_len) || (CAUSAL && kw + 31 > qs);
         if (need_mask) {
+          const int lim = key_lim - qs;
 #pragma unroll
           for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
-            for (int e = 0; e < 16; ++e) {
-              const int q = qs + 32 * qb + 8 * (e >> 2) + 4 * hl + (e & 3);
-              const bool vis = kj < kv_len && (!CAUSAL || kj <= q);
-              if (!vis) s[qb][e] = -kInf;
-            }
+            for (int e = 0; e < 16; ++e)
+              if (32 * qb + 8 * (e >> 2) + (e & 3) < lim) s[qb][e] = -kInf;
         }
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb)

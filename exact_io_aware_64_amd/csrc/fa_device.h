@@ -63,8 +63,22 @@ __device__ __forceinline__ bf16x8 pack8(const f32x16& v, int off) {
   return r;
 }
 
-__device__ __forceinline__ uint4 ldg16(const uint16_t* p) {
-  return *reinterpret_cast<const uint4*>(p);
+// Buffer resource over one (batch, head) slice of a tensor.  Loads through
+// it take 32-bit byte offsets, and any 16-byte load that starts at or past
+// `bytes` returns zeros, so rows past the end need no branch.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  // dword3 0x00020000: the raw-buffer format word for gfx9-family GPUs.
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           0x00020000);
+}
+
+__device__ __forceinline__ uint4 ldb16(__amdgpu_buffer_rsrc_t r, int byte_off) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0));
+}
+
+// Bytes spanned by rows 0..n-1 of 64 elements with row stride `ss` (elements).
+__device__ __forceinline__ uint32_t slice_bytes(int n, int64_t ss, int esize) {
+  return (uint32_t)(((int64_t)(n - 1) * ss + 64) * esize);
 }
 
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 u) { return __builtin_bit_cast(bf16x8, u); }
@@ -81,8 +95,8 @@ __device__ __forceinline__ bf16x8 lds_split8(const uint16_t* p) {
   return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
-// Store rows r0 and r0+1 (16 bytes each, columns 8c..8c+7) of a tile both
-// row-major (if nat != nullptr) and transposed into t[col * kTStride + row].
+// Store rows r0 and r0+1 (16 bytes each, columns 8c..8c+7) of a tile
+// transposed, into t[col * kTStride + row].
 __device__ __forceinline__ void store_pair_transposed(uint16_t* t, int r0, int c, uint4 a,
                                                       uint4 b) {
   const uint32_t aw[4] = {a.x, a.y, a.z, a.w};

@@ -28,6 +28,12 @@ namespace fa {
 namespace {
 
 constexpr int kBR = 128;  // query rows per workgroup
+// The running maximum is only moved (and O, l rescaled) when a tile's
+// maximum exceeds it by more than this many log2 units; until then the
+// probabilities are taken against the stale maximum and stay below
+// 2^kSlack.  O = acc / l and L = m + log2(l) are unchanged by the choice of
+// reference, so the result is the same up to rounding.
+constexpr float kSlack = 8.f;
 
 template <bool CAUSAL, bool SEQLEN, bool BMASK>
 __global__ __launch_bounds__(256) void fwd_bf16_kernel(FwdArgs a) {
@@ -66,16 +72,21 @@ __global__ __launch_bounds__(256) void fwd_bf16_kernel(FwdArgs a) {
                             a.n_mask_tiles, a.mask_block / kTile, 0, ntk);
   }
 
-  const uint16_t* Q = (const uint16_t*)a.q + b * a.sq.b + hh * a.sq.h;
-  const uint16_t* K = (const uint16_t*)a.k + b * a.sk.b + hh * a.sk.h;
-  const uint16_t* V = (const uint16_t*)a.v + b * a.sv.b + hh * a.sv.h;
+  const __amdgpu_buffer_rsrc_t rq =
+      make_rsrc((const uint16_t*)a.q + b * a.sq.b + hh * a.sq.h, slice_bytes(a.N, a.sq.s, 2));
+  const __amdgpu_buffer_rsrc_t rk =
+      make_rsrc((const uint16_t*)a.k + b * a.sk.b + hh * a.sk.h, slice_bytes(a.N, a.sk.s, 2));
+  const __amdgpu_buffer_rsrc_t rv =
+      make_rsrc((const uint16_t*)a.v + b * a.sv.b + hh * a.sv.h, slice_bytes(a.N, a.sv.s, 2));
+  const int ssk = (int)a.sk.s * 2, ssv = (int)a.sv.s * 2;
 
+  // Q fragment: B operand of S^T = K Q^T, lane (r, hl) holds
+  // Q[qi][16 ks + 8 hl .. +7].  Rows past N read as zeros.
   bf16x8 qf[4];
   {
-    const uint4 z = make_uint4(0, 0, 0, 0);
-    const uint16_t* qp = Q + (int64_t)qi * a.sq.s + 8 * hl;
+    const int off = qi * (int)a.sq.s * 2 + 16 * hl;
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) qf[ks] = as_bf16x8(qi < a.N ? ldg16(qp + 16 * ks) : z);
+    for (int ks = 0; ks < 4; ++ks) qf[ks] = as_bf16x8(ldb16(rq, off + 32 * ks));
   }
 
   f32x16 o[2] = {zero16(), zero16()};
@@ -85,6 +96,8 @@ __global__ __launch_bounds__(256) void fwd_bf16_kernel(FwdArgs a) {
   // Staging roles: K chunks (row tid/8 and tid/8 + 32, 16-byte column tid%8);
   // V rows 2*(tid/8) and 2*(tid/8)+1 at the same column, written transposed.
   const int sr = tid >> 3, sc = tid & 7;
+  const int k_off0 = sr * ssk + 16 * sc, k_off1 = (sr + 32) * ssk + 16 * sc;
+  const int v_off0 = 2 * sr * ssv + 16 * sc, v_off1 = (2 * sr + 1) * ssv + 16 * sc;
   uint4 kreg[2], vreg[2];
   auto tile_at = [&](int it) -> int {
     if constexpr (BMASK) return tlist[it];
@@ -92,14 +105,10 @@ __global__ __launch_bounds__(256) void fwd_bf16_kernel(FwdArgs a) {
   };
   auto gload = [&](int t) {
     const int k0 = t * kTile;
-    const uint4 z = make_uint4(0, 0, 0, 0);
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int kk = k0 + sr + 32 * u;
-      kreg[u] = kk < a.N ? ldg16(K + (int64_t)kk * a.sk.s + 8 * sc) : z;
-      const int kv = k0 + 2 * sr + u;
-      vreg[u] = kv < a.N ? ldg16(V + (int64_t)kv * a.sv.s + 8 * sc) : z;
-    }
+    kreg[0] = ldb16(rk, k_off0 + k0 * ssk);
+    kreg[1] = ldb16(rk, k_off1 + k0 * ssk);
+    vreg[0] = ldb16(rv, v_off0 + k0 * ssv);
+    vreg[1] = ldb16(rv, v_off1 + k0 * ssv);
   };
   auto swrite = [&](int buf) {
     store_row16(s_k[buf], sr, sc, kreg[0]);
@@ -122,35 +131,50 @@ __global__ __launch_bounds__(256) void fwd_bf16_kernel(FwdArgs a) {
     if (active) {
       const uint16_t* ks_ = s_k[buf];
       const uint16_t* vt_ = s_vt[buf];
-      f32x16 s[2];
+      // S^T for keys k0 .. k0+63 as two interleaved 32-key accumulator chains.
+      bf16x8 ka[2][4];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        s[kb] = zero16();
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks)
-          s[kb] = mfma32(lds_row8(ks_ + (32 * kb + r) * kRowStride + 16 * ks + 8 * hl), qf[ks],
-                         s[kb]);
+          ka[kb][ks] = lds_row8(ks_ + (32 * kb + r) * kRowStride + 16 * ks + 8 * hl);
+      f32x16 s[2] = {zero16(), zero16()};
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        s[0] = mfma32(ka[0][ks], qf[ks], s[0]);
+        s[1] = mfma32(ka[1][ks], qf[ks], s[1]);
       }
       const bool need_mask = (k0 + kTile > kv_len) || (CAUSAL && k0 + kTile - 1 > qw);
       if (need_mask) {
+        // element e of block kb holds key k0 + 4*hl + off(kb, e); it is
+        // visible iff off <= lim
+        const int last = CAUSAL ? min(kv_len - 1, qi) : kv_len - 1;
+        const int lim = last - k0 - 4 * hl;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-          for (int e = 0; e < 16; ++e) {
-            const int key = k0 + 32 * kb + 8 * (e >> 2) + 4 * hl + (e & 3);
-            const bool vis = key < kv_len && (!CAUSAL || key <= qi);
-            if (!vis) s[kb][e] = -kInf;
-          }
+          for (int e = 0; e < 16; ++e)
+            if (32 * kb + 8 * (e >> 2) + (e & 3) > lim) s[kb][e] = -kInf;
       }
       float mx = -kInf;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[kb][e]);
-      mx = half_max(mx);
-      const float m_new = fmaxf(m, mx * c);
-      const float m_use = (m_new == -kInf) ? 0.f : m_new;
-      const float alpha = fast_exp2(m - m_use);
+      const float mt = half_max(mx) * c;  // tile maximum, log2 units
+      const bool grow = mt > m + kSlack;
+      if (__any(grow)) {
+        // alpha is 0 when m was -inf (nothing accumulated yet) and exactly 1
+        // in lanes that keep their reference.
+        const float alpha = grow ? fast_exp2(m - mt) : 1.f;
+        l *= alpha;
+#pragma unroll
+        for (int db = 0; db < 2; ++db)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) o[db][e] *= alpha;
+        m = grow ? mt : m;
+      }
+      const float m_use = (m == -kInf) ? 0.f : m;
       float rs = 0.f;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
@@ -160,21 +184,20 @@ __global__ __launch_bounds__(256) void fwd_bf16_kernel(FwdArgs a) {
           s[kb][e] = p;
           rs += p;
         }
-      l = l * alpha + rs;
-      m = m_new;
-#pragma unroll
-      for (int db = 0; db < 2; ++db)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) o[db][e] *= alpha;
+      l += rs;
       // O^T[d][q] += sum_key V[key][d] P[q][key]; contraction slot e of step
       // st maps to key 16*st + 4*hl + e (e < 4) or 16*st + 8 + 4*hl + e - 4.
+      bf16x8 va[4][2];
+#pragma unroll
+      for (int st = 0; st < 4; ++st)
+#pragma unroll
+        for (int db = 0; db < 2; ++db)
+          va[st][db] = lds_split8(vt_ + (32 * db + r) * kTStride + 16 * st + 4 * hl);
 #pragma unroll
       for (int st = 0; st < 4; ++st) {
         const bf16x8 pb = pack8(s[st >> 1], 8 * (st & 1));
-#pragma unroll
-        for (int db = 0; db < 2; ++db)
-          o[db] = mfma32(lds_split8(vt_ + (32 * db + r) * kTStride + 16 * st + 4 * hl), pb,
-                         o[db]);
+        o[0] = mfma32(va[st][0], pb, o[0]);
+        o[1] = mfma32(va[st][1], pb, o[1]);
       }
     }
     if (it + 1 < nlist) swrite(buf ^ 1);

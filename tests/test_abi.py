@@ -87,6 +87,7 @@ def _bwd(**kw):
     (dict(bmask=A, mb=100), 1, "mask_block"),
     (dict(bmask=A, N=300000), 2, "block mask"),
     (dict(seqlens=A + 2), 1, "seqlens_k"),
+    (dict(sq=bnd.fa_strides(0, 0, 1 << 20), N=1024), 2, "2 GiB"),
 ])
 def test_fwd_rejects_bad_arguments(kw, status, msg):
     assert _fwd(**kw) == status
