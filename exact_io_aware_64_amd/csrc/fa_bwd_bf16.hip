@@ -34,7 +34,6 @@ constexpr int kBK = 128;   // dkdv_kernel: key rows per workgroup
 template <bool CAUSAL, bool SEQLEN, bool BMASK>
 __global__ __launch_bounds__(256) void dq_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t s_k[2][kTile * kRowStride];
-  __shared__ __attribute__((aligned(16))) uint16_t s_kt[2][kTile * kTStride];
   __shared__ __attribute__((aligned(16))) uint16_t s_v[2][kTile * kRowStride];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -106,11 +105,12 @@ __global__ __launch_bounds__(256) void dq_kernel(BwdArgs a) {
 
   f32x16 acc[2] = {zero16(), zero16()};
 
-  // Staging: K rows 2*(tid/8), 2*(tid/8)+1 row-major and transposed; V rows
-  // tid/8 and tid/8+32 row-major; 16-byte column tid%8.
+  // Staging: rows tid/8 and tid/8 + 32 of the K and V tiles, 16-byte column
+  // tid%8, row-major.  K^T operands come from transpose reads of the K tile.
   const int sr = tid >> 3, sc = tid & 7;
-  const int k_off0 = 2 * sr * ssk + 16 * sc, k_off1 = (2 * sr + 1) * ssk + 16 * sc;
+  const int k_off0 = sr * ssk + 16 * sc, k_off1 = (sr + 32) * ssk + 16 * sc;
   const int v_off0 = sr * ssv + 16 * sc, v_off1 = (sr + 32) * ssv + 16 * sc;
+  const int trl = tr_lane_offset(lane);
   uint4 kreg[2], vreg[2];
   auto tile_at = [&](int it) -> int {
     if constexpr (BMASK) return tlist[it];
@@ -124,9 +124,8 @@ __global__ __launch_bounds__(256) void dq_kernel(BwdArgs a) {
     vreg[1] = ldb16(rv, v_off1 + k0 * ssv);
   };
   auto swrite = [&](int buf) {
-    store_row16(s_k[buf], 2 * sr, sc, kreg[0]);
-    store_row16(s_k[buf], 2 * sr + 1, sc, kreg[1]);
-    store_pair_transposed(s_kt[buf], 2 * sr, sc, kreg[0], kreg[1]);
+    store_row16(s_k[buf], sr, sc, kreg[0]);
+    store_row16(s_k[buf], sr + 32, sc, kreg[1]);
     store_row16(s_v[buf], sr, sc, vreg[0]);
     store_row16(s_v[buf], sr + 32, sc, vreg[1]);
   };
@@ -145,7 +144,6 @@ __global__ __launch_bounds__(256) void dq_kernel(BwdArgs a) {
     const bool active = !CAUSAL || (k0 <= qw + 31);
     if (active) {
       const uint16_t* ks_ = s_k[buf];
-      const uint16_t* kt_ = s_kt[buf];
       const uint16_t* vs_ = s_v[buf];
       f32x16 st[2] = {zero16(), zero16()}, dpt[2] = {zero16(), zero16()};
 #pragma unroll
@@ -179,8 +177,7 @@ __global__ __launch_bounds__(256) void dq_kernel(BwdArgs a) {
         const bf16x8 dsb = pack8(st[stp >> 1], 8 * (stp & 1));
 #pragma unroll
         for (int db = 0; db < 2; ++db)
-          acc[db] = mfma32(lds_split8(kt_ + (32 * db + r) * kTStride + 16 * stp + 4 * hl), dsb,
-                           acc[db]);
+          acc[db] = mfma32(tr_operand(ks_ + trl + 16 * stp * kRowStride + 32 * db), dsb, acc[db]);
       }
     }
     if (it + 1 < nlist) swrite(buf ^ 1);
@@ -206,11 +203,9 @@ __global__ __launch_bounds__(256) void dq_kernel(BwdArgs a) {
 template <bool CAUSAL, bool SEQLEN, bool BMASK>
 __global__ __launch_bounds__(256) void dkdv_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t s_q[2][kTile * kRowStride];
-  __shared__ __attribute__((aligned(16))) uint16_t s_qt[2][kTile * kTStride];
   __shared__ __attribute__((aligned(16))) uint16_t s_do[2][kTile * kRowStride];
-  __shared__ __attribute__((aligned(16))) uint16_t s_dot[2][kTile * kTStride];
   __shared__ __attribute__((aligned(16))) float s_l2[2][kTile];
-  __shared__ __attribute__((aligned(16))) float s_d[2][kTile];
+  __shared__ __attribute__((aligned(16))) float s_nd[2][kTile];  // -D
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int r = lane & 31, hl = lane >> 5;
@@ -276,11 +271,13 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdArgs a) {
     // visible iff off >= qs_lim - qs; keys past the sequence see nothing.
     const int key_lim = (kj < kv_len) ? (CAUSAL ? kj - 4 * hl : -(1 << 30)) : (1 << 30);
 
-    // Staging: Q and dO rows 2*(tid/8), 2*(tid/8)+1 at 16-byte column tid%8,
-    // row-major and transposed; threads 0..63 also fetch L and D of one row.
+    // Staging: rows tid/8 and tid/8 + 32 of the Q and dO tiles, 16-byte column
+    // tid%8, row-major (Q^T and dO^T operands come from transpose reads);
+    // threads 0..63 also fetch L (as log2 units) and -D of one row.
     const int sr = tid >> 3, sc = tid & 7;
-    const int q_off0 = 2 * sr * ssq + 16 * sc, q_off1 = (2 * sr + 1) * ssq + 16 * sc;
-    const int d_off0 = 2 * sr * ssdo + 16 * sc, d_off1 = (2 * sr + 1) * ssdo + 16 * sc;
+    const int q_off0 = sr * ssq + 16 * sc, q_off1 = (sr + 32) * ssq + 16 * sc;
+    const int d_off0 = sr * ssdo + 16 * sc, d_off1 = (sr + 32) * ssdo + 16 * sc;
+    const int trl = tr_lane_offset(lane);
     uint4 qreg[2], dreg[2];
     float lreg = 0.f, dreg_s = 0.f;
     auto tile_at = [&](int it) -> int {
@@ -297,19 +294,17 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdArgs a) {
         const int qq = qs + tid;
         const float L = qq < a.N ? lse[qq] : -kInf;
         lreg = (L == -kInf) ? kInf : L * kLog2e;
-        dreg_s = qq < a.N ? dsum[qq] : 0.f;
+        dreg_s = qq < a.N ? -dsum[qq] : 0.f;
       }
     };
     auto swrite = [&](int buf) {
-      store_row16(s_q[buf], 2 * sr, sc, qreg[0]);
-      store_row16(s_q[buf], 2 * sr + 1, sc, qreg[1]);
-      store_pair_transposed(s_qt[buf], 2 * sr, sc, qreg[0], qreg[1]);
-      store_row16(s_do[buf], 2 * sr, sc, dreg[0]);
-      store_row16(s_do[buf], 2 * sr + 1, sc, dreg[1]);
-      store_pair_transposed(s_dot[buf], 2 * sr, sc, dreg[0], dreg[1]);
+      store_row16(s_q[buf], sr, sc, qreg[0]);
+      store_row16(s_q[buf], sr + 32, sc, qreg[1]);
+      store_row16(s_do[buf], sr, sc, dreg[0]);
+      store_row16(s_do[buf], sr + 32, sc, dreg[1]);
       if (tid < kTile) {
         s_l2[buf][tid] = lreg;
-        s_d[buf][tid] = dreg_s;
+        s_nd[buf][tid] = dreg_s;
       }
     };
 
@@ -327,10 +322,18 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdArgs a) {
       const bool active = !CAUSAL || (qs + kTile - 1 >= kw);
       if (active) {
         const uint16_t* qs_ = s_q[buf];
-        const uint16_t* qt_ = s_qt[buf];
         const uint16_t* ds_ = s_do[buf];
-        const uint16_t* dt_ = s_dot[buf];
-        f32x16 s[2] = {zero16(), zero16()}, dp[2] = {zero16(), zero16()};
+        // dP accumulators start at -D (row of each element), so the MFMA
+        // leaves dP - D in them directly.
+        f32x16 s[2] = {zero16(), zero16()}, dp[2];
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const f32x4 d4 = *reinterpret_cast<const f32x4*>(&s_nd[buf][32 * qb + 8 * j + 4 * hl]);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) dp[qb][4 * j + i] = d4[i];
+          }
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
@@ -353,13 +356,12 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdArgs a) {
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
             const f32x4 l4 = *reinterpret_cast<const f32x4*>(&s_l2[buf][32 * qb + 8 * j + 4 * hl]);
-            const f32x4 d4 = *reinterpret_cast<const f32x4*>(&s_d[buf][32 * qb + 8 * j + 4 * hl]);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
               const int e = 4 * j + i;
               const float p = fast_exp2(__builtin_fmaf(s[qb][e], c, -l4[i]));
               s[qb][e] = p;
-              dp[qb][e] = p * (dp[qb][e] - d4[i]);
+              dp[qb][e] *= p;
             }
           }
         // dV^T[d][key] += sum_q dO[q][d] P[q][key];  dK^T[d][key] += sum_q Q[q][d] dS[q][key]
@@ -369,9 +371,9 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdArgs a) {
           const bf16x8 dsb = pack8(dp[stp >> 1], 8 * (stp & 1));
 #pragma unroll
           for (int db = 0; db < 2; ++db) {
-            const int off = (32 * db + r) * kTStride + 16 * stp + 4 * hl;
-            dvt[db] = mfma32(lds_split8(dt_ + off), pb, dvt[db]);
-            dkt[db] = mfma32(lds_split8(qt_ + off), dsb, dkt[db]);
+            const int off = trl + 16 * stp * kRowStride + 32 * db;
+            dvt[db] = mfma32(tr_operand(ds_ + off), pb, dvt[db]);
+            dkt[db] = mfma32(tr_operand(qs_ + off), dsb, dkt[db]);
           }
         }
       }

@@ -22,9 +22,6 @@ constexpr float kLn2 = 0.6931471805599453f;
 // of 8 elements spreads the 16-byte reads of 16 consecutive rows over all
 // banks.
 constexpr int kRowStride = 72;
-// Row stride of a transposed tile.  A multiple of 4 keeps the 8-byte reads of
-// operand halves aligned.
-constexpr int kTStride = 68;
 
 __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
   // D[32x32] += A[32x16] * B[16x32].  Lane l supplies row (l % 32) of A and
@@ -88,26 +85,29 @@ __device__ __forceinline__ bf16x8 lds_row8(const uint16_t* p) {
   return *reinterpret_cast<const bf16x8*>(p);
 }
 
-// Operand from a transposed tile: 4 elements at p and 4 at p + 8.
-__device__ __forceinline__ bf16x8 lds_split8(const uint16_t* p) {
-  bf16x4 lo = *reinterpret_cast<const bf16x4*>(p);
-  bf16x4 hi = *reinterpret_cast<const bf16x4*>(p + 8);
-  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+
+// Per-lane offset (in elements) for tr_operand over a row-major tile with row
+// stride kRowStride.
+__device__ __forceinline__ int tr_lane_offset(int lane) {
+  const int j = lane & 15, g = lane >> 4;
+  return (4 * (g >> 1) + (j >> 2)) * kRowStride + 16 * (g & 1) + 4 * (j & 3);
 }
 
-// Store rows r0 and r0+1 (16 bytes each, columns 8c..8c+7) of a tile
-// transposed, into t[col * kTStride + row].
-__device__ __forceinline__ void store_pair_transposed(uint16_t* t, int r0, int c, uint4 a,
-                                                      uint4 b) {
-  const uint32_t aw[4] = {a.x, a.y, a.z, a.w};
-  const uint32_t bw[4] = {b.x, b.y, b.z, b.w};
-#pragma unroll
-  for (int x = 0; x < 8; ++x) {
-    const uint32_t lo = aw[x >> 1], hi = bw[x >> 1];
-    const uint32_t word = (x & 1) ? ((lo >> 16) | (hi & 0xffff0000u))
-                                  : ((lo & 0xffffu) | (hi << 16));
-    *reinterpret_cast<uint32_t*>(t + (8 * c + x) * kTStride + r0) = word;
-  }
+// A operand of a 32x32x16 MFMA whose contraction runs over the ROWS of a
+// row-major LDS tile X: lane (r, hl) receives X[rbase + 4 hl + t][cbase + r]
+// in slots t = 0..3 and X[rbase + 8 + 4 hl + t][cbase + r] in slots 4..7.
+// Built from two ds_read_b64_tr_b16: within each 16-lane group, lane i
+// receives element 16 t + i (t = 0..3) of the 64 elements the group reads,
+// so source lane j reads X[row0 + j / 4][col0 + 4 (j % 4) .. +3].
+// `p` = tile + tr_lane_offset(lane) + rbase * kRowStride + cbase.
+__device__ __forceinline__ bf16x8 tr_operand(const uint16_t* p) {
+  typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+  const lds_i16x4* lo = (const lds_i16x4*)(p);
+  const lds_i16x4* hi = (const lds_i16x4*)(p + 8 * kRowStride);
+  const i16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16(const_cast<lds_i16x4*>(lo));
+  const i16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16(const_cast<lds_i16x4*>(hi));
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
 __device__ __forceinline__ void store_row16(uint16_t* t, int row, int c, uint4 a) {

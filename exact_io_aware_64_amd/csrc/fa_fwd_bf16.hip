@@ -16,8 +16,8 @@
 // the output accumulator when m grows (researchpapers.dev, "tiling and
 // recomputation"; the max subtraction is the safe softmax of the llm-deploy
 // note).  O^T = V^T P^T is accumulated on the same MFMA; the probabilities
-// feed the B operand straight from the accumulator registers, and V is staged
-// transposed in LDS so the A operand reads are contiguous.
+// feed the B operand straight from the accumulator registers, and the V^T
+// operand is read from the row-major V tile with LDS transpose reads.
 //
 // Tiles that the mask removes entirely are never loaded: causal and key
 // padding shrink the key range, and a block mask is compacted into a list of
@@ -38,7 +38,7 @@ constexpr float kSlack = 8.f;
 template <bool CAUSAL, bool SEQLEN, bool BMASK>
 __global__ __launch_bounds__(256) void fwd_bf16_kernel(FwdArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t s_k[2][kTile * kRowStride];
-  __shared__ __attribute__((aligned(16))) uint16_t s_vt[2][kTile * kTStride];
+  __shared__ __attribute__((aligned(16))) uint16_t s_v[2][kTile * kRowStride];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int r = lane & 31, hl = lane >> 5;
@@ -93,11 +93,12 @@ __global__ __launch_bounds__(256) void fwd_bf16_kernel(FwdArgs a) {
   float m = -kInf, l = 0.f;
   const float c = a.scale_log2;
 
-  // Staging roles: K chunks (row tid/8 and tid/8 + 32, 16-byte column tid%8);
-  // V rows 2*(tid/8) and 2*(tid/8)+1 at the same column, written transposed.
+  // Staging roles: rows tid/8 and tid/8 + 32 of the K and V tiles, 16-byte
+  // column tid%8, stored row-major.
   const int sr = tid >> 3, sc = tid & 7;
   const int k_off0 = sr * ssk + 16 * sc, k_off1 = (sr + 32) * ssk + 16 * sc;
-  const int v_off0 = 2 * sr * ssv + 16 * sc, v_off1 = (2 * sr + 1) * ssv + 16 * sc;
+  const int v_off0 = sr * ssv + 16 * sc, v_off1 = (sr + 32) * ssv + 16 * sc;
+  const int trl = tr_lane_offset(lane);
   uint4 kreg[2], vreg[2];
   auto tile_at = [&](int it) -> int {
     if constexpr (BMASK) return tlist[it];
@@ -113,7 +114,8 @@ __global__ __launch_bounds__(256) void fwd_bf16_kernel(FwdArgs a) {
   auto swrite = [&](int buf) {
     store_row16(s_k[buf], sr, sc, kreg[0]);
     store_row16(s_k[buf], sr + 32, sc, kreg[1]);
-    store_pair_transposed(s_vt[buf], 2 * sr, sc, vreg[0], vreg[1]);
+    store_row16(s_v[buf], sr, sc, vreg[0]);
+    store_row16(s_v[buf], sr + 32, sc, vreg[1]);
   };
 
   if (nlist > 0) {
@@ -130,7 +132,7 @@ __global__ __launch_bounds__(256) void fwd_bf16_kernel(FwdArgs a) {
     const bool active = !CAUSAL || (k0 <= qw + 31);
     if (active) {
       const uint16_t* ks_ = s_k[buf];
-      const uint16_t* vt_ = s_vt[buf];
+      const uint16_t* vs_ = s_v[buf];
       // S^T for keys k0 .. k0+63 as two interleaved 32-key accumulator chains.
       bf16x8 ka[2][4];
 #pragma unroll
@@ -192,7 +194,7 @@ __global__ __launch_bounds__(256) void fwd_bf16_kernel(FwdArgs a) {
       for (int st = 0; st < 4; ++st)
 #pragma unroll
         for (int db = 0; db < 2; ++db)
-          va[st][db] = lds_split8(vt_ + (32 * db + r) * kTStride + 16 * st + 4 * hl);
+          va[st][db] = tr_operand(vs_ + trl + 16 * st * kRowStride + 32 * db);
 #pragma unroll
       for (int st = 0; st < 4; ++st) {
         const bf16x8 pb = pack8(s[st >> 1], 8 * (st & 1));
