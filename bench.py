@@ -65,18 +65,39 @@ def visible_pairs(N: int, H: int, causal: bool, seqlens, block_mask, mask_block:
 
 
 def kernel_bytes(B, H, N, d, esize, seqlens):
-    """Compulsory HBM bytes of the forward kernel and of the backward pair."""
+    """Compulsory HBM bytes per launch of each kernel: every tensor the kernel
+    must read or write once (keys and values only up to each sequence's key
+    length), plus the fp32 row statistics L and D."""
     t = B * H * N * d * esize
     kv_valid = H * d * esize * (B * N if seqlens is None else int(np.minimum(seqlens, N).sum()))
     rowstat = B * H * N * 4
-    fwd = 2 * t + 2 * kv_valid + rowstat                      # Q, O + K, V + L
-    bwd = 5 * t + 2 * kv_valid + 3 * rowstat                  # Q,O,dO,dQ..dV + K,V + L,D,D
-    return fwd, bwd
+    return {
+        "fwd_bf16_kernel": 2 * t + 2 * kv_valid + rowstat,         # Q, O; K, V; L
+        "dq_kernel": 4 * t + 2 * kv_valid + 2 * rowstat,           # Q, O, dO, dQ; K, V; L, D
+        "dkdv_kernel": 4 * t + 2 * kv_valid + 2 * rowstat,         # Q, dO, dK, dV; K, V; L, D
+    }
+
+
+def kernel_flops(d, pairs):
+    """Algorithmic FLOPs per launch.  The method's backward pass is five
+    products over visible pairs (S recomputed, dV, dP, dQ, dK; 2*d each): the
+    dK/dV kernel performs four of them, the dQ kernel the fifth (its own
+    recomputation of S and dP duplicates work and is not credited)."""
+    return {"fwd_bf16_kernel": 4.0 * d * pairs, "dq_kernel": 2.0 * d * pairs,
+            "dkdv_kernel": 8.0 * d * pairs}
 
 
 # ------------------------------------------------------------------- timing
 
+KERNELS = ("fwd_bf16_kernel", "dq_kernel", "dkdv_kernel")
+
+
 def run_gpu(w: wl.Workload, inp: dict, steps: int, warmup: int):
+    """Times `steps` steps after `warmup` untimed ones.  One step is fa_fwd,
+    then the two phases of the backward pass (fa_bwd_dq, fa_bwd_dkdv), each a
+    single kernel launch on the current stream; HIP events recorded on that
+    stream between the launches give each kernel's device time, and the wall
+    clock around the whole timed region gives the step time."""
     import torch
     import exact_io_aware_64_amd as fa
 
@@ -102,29 +123,27 @@ def run_gpu(w: wl.Workload, inp: dict, steps: int, warmup: int):
         fa.fa_fwd(q, k, v, o, lse, **kw)
         if ev is not None:
             ev[1].record(stream)
-        fa.fa_bwd(q, k, v, o, do, lse, dq, dk, dv, ws, **kw)
+        fa.fa_bwd_dq(q, k, v, o, do, lse, dq, ws, **kw)
         if ev is not None:
             ev[2].record(stream)
+        fa.fa_bwd_dkdv(q, k, v, do, lse, dk, dv, ws, **kw)
+        if ev is not None:
+            ev[3].record(stream)
 
     for _ in range(warmup):
         step()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
     torch.cuda.synchronize()
-    # wall clock over exactly `steps` steps, no events inside
     t0 = time.perf_counter()
-    for _ in range(steps):
-        step()
-    torch.cuda.synchronize()
-    wall_ms = (time.perf_counter() - t0) * 1e3 / steps
-    # per-call device durations from HIP events on the launch stream
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
     for e in evs:
         step(e)
     torch.cuda.synchronize()
-    fwd_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
-    bwd_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+    wall_ms = (time.perf_counter() - t0) * 1e3 / steps
+    kernel_ms = {name: float(np.mean([e[i].elapsed_time(e[i + 1]) for e in evs]))
+                 for i, name in enumerate(KERNELS)}
     props = torch.cuda.get_device_properties(dev)
     outs = dict(o=o, lse=lse, dq=dq, dk=dk, dv=dv)
-    return wall_ms, fwd_ms, bwd_ms, props, outs
+    return wall_ms, kernel_ms, props, outs
 
 
 def cpu_baseline(w: wl.Workload, inp: dict, outs: dict, flops_fb: float,
@@ -229,30 +248,34 @@ def main(argv=None):
     flops_f = 4.0 * w.d * pairs
     flops_b = 10.0 * w.d * pairs
     esize = 2 if w.dtype == "bf16" else 4
-    bytes_f, bytes_b = kernel_bytes(w.B, w.H, w.N, w.d, esize, inp["seqlens"])
 
-    wall_ms, fwd_ms, bwd_ms, props, outs = run_gpu(w, inp, args.steps, args.warmup)
+    wall_ms, kernel_ms, props, outs = run_gpu(w, inp, args.steps, args.warmup)
+    fwd_ms = kernel_ms["fwd_bf16_kernel"]
+    bwd_ms = kernel_ms["dq_kernel"] + kernel_ms["dkdv_kernel"]
     peak = PEAK_TFLOPS[w.dtype]
     tf_fb = (flops_f + flops_b) / (wall_ms * 1e-3) / 1e12
     tf_f = flops_f / (fwd_ms * 1e-3) / 1e12
     tf_b = flops_b / (bwd_ms * 1e-3) / 1e12
 
-    # Roofline of the dominant launch (the one with the largest device time).
-    def roof(name, flops, nbytes, ms):
-        t_mfma = flops / (peak * 1e12)
-        t_hbm = nbytes / (PEAK_HBM_GBS * 1e9)
-        if t_mfma >= t_hbm:
-            ach = flops / (ms * 1e-3) / 1e12
-            return dict(kernel=name, bound="mfma", achieved=ach, peak=peak, unit="TFLOP/s",
-                        frac=ach / peak, traffic=None)
-        ach = nbytes / (ms * 1e-3) / 1e9
-        return dict(kernel=name, bound="hbm", achieved=ach, peak=PEAK_HBM_GBS, unit="GB/s",
-                    frac=ach / PEAK_HBM_GBS, traffic=None)
-
-    if fwd_ms >= bwd_ms:
-        roofline = roof("fwd_bf16_kernel", flops_f, bytes_f, fwd_ms)
+    # Roofline of the dominant kernel (largest device time per step): its
+    # algorithmic FLOPs and compulsory bytes per launch against its own
+    # event-timed duration.
+    kflops = kernel_flops(w.d, pairs)
+    kbytes = kernel_bytes(w.B, w.H, w.N, w.d, esize, inp["seqlens"])
+    dom = max(KERNELS, key=lambda n: kernel_ms[n])
+    ms = kernel_ms[dom]
+    t_mfma = kflops[dom] / (peak * 1e12)
+    t_hbm = kbytes[dom] / (PEAK_HBM_GBS * 1e9)
+    if t_mfma >= t_hbm:
+        ach = kflops[dom] / (ms * 1e-3) / 1e12
+        roofline = dict(kernel=dom, bound="mfma", achieved=ach, peak=peak, unit="TFLOP/s",
+                        frac=ach / peak)
     else:
-        roofline = roof("dq_kernel+dkdv_kernel", flops_b, bytes_b, bwd_ms)
+        ach = kbytes[dom] / (ms * 1e-3) / 1e9
+        roofline = dict(kernel=dom, bound="hbm", achieved=ach, peak=PEAK_HBM_GBS, unit="GB/s",
+                        frac=ach / PEAK_HBM_GBS)
+    roofline.update(traffic=None, flops_per_launch=kflops[dom],
+                    compulsory_bytes_per_launch=kbytes[dom], launch_ms=ms)
 
     base = None
     parity = None
@@ -280,6 +303,7 @@ def main(argv=None):
         "bwd_tflops": tf_b,
         "fwd_ms": fwd_ms,
         "bwd_ms": bwd_ms,
+        "kernel_ms": kernel_ms,
         "fwd_frac_peak": tf_f / peak,
         "fwdbwd_frac_peak": tf_fb / peak,
         "peak_tflops": peak,

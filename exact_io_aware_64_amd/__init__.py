@@ -11,6 +11,8 @@ from ._binding import (  # noqa: F401
     FaError,
     backward,
     fa_bwd,
+    fa_bwd_dkdv,
+    fa_bwd_dq,
     fa_bwd_workspace_bytes,
     fa_fwd,
     fa_last_error,

@@ -22,7 +22,8 @@ FA_ERR_UNSUPPORTED = 2
 FA_ERR_HIP = 3
 
 # Public entry points declared in include/fa.h.
-EXPORTED = ("fa_fwd", "fa_bwd", "fa_bwd_workspace_bytes", "fa_status_string", "fa_last_error")
+EXPORTED = ("fa_fwd", "fa_bwd", "fa_bwd_dq", "fa_bwd_dkdv", "fa_bwd_workspace_bytes",
+            "fa_status_string", "fa_last_error")
 
 
 class FaError(RuntimeError):
@@ -53,6 +54,12 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.fa_bwd.restype = I
     lib.fa_bwd.argtypes = [I, P, S, P, S, P, S, P, S, P, S, P, P, S, P, S, P, S, P,
                            ctypes.c_size_t, I, I, I, I, F, I, P, P, I, P]
+    lib.fa_bwd_dq.restype = I
+    lib.fa_bwd_dq.argtypes = [I, P, S, P, S, P, S, P, S, P, S, P, P, S, P, ctypes.c_size_t,
+                              I, I, I, I, F, I, P, P, I, P]
+    lib.fa_bwd_dkdv.restype = I
+    lib.fa_bwd_dkdv.argtypes = [I, P, S, P, S, P, S, P, S, P, P, S, P, S, P, ctypes.c_size_t,
+                                I, I, I, I, F, I, P, P, I, P]
     lib.fa_bwd_workspace_bytes.restype = ctypes.c_size_t
     lib.fa_bwd_workspace_bytes.argtypes = [I, I, I, I, I]
     lib.fa_status_string.restype = ctypes.c_char_p
@@ -133,22 +140,55 @@ def fa_fwd(q, k, v, o, lse, *, scale: float, causal: bool = False, seqlens_k=Non
     _check(st)
 
 
+def _check_like(q, named):
+    B, H, N, d = q.shape
+    for name, t in named:
+        if tuple(t.shape) != (B, H, N, d) or t.dtype != q.dtype:
+            raise ValueError(f"{name} must match q in shape and dtype")
+    return B, H, N, d
+
+
 def fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, workspace, *, scale: float,
            causal: bool = False, seqlens_k=None, block_mask=None, mask_block: int = 128,
            stream=None) -> None:
     """Calls fa_bwd; dq, dk, dv are written in full."""
     lib = load_library()
-    B, H, N, d = q.shape
-    for name, t in (("k", k), ("v", v), ("o", o), ("dout", dout), ("dq", dq), ("dk", dk),
-                    ("dv", dv)):
-        if tuple(t.shape) != (B, H, N, d) or t.dtype != q.dtype:
-            raise ValueError(f"{name} must match q in shape and dtype")
+    B, H, N, d = _check_like(q, (("k", k), ("v", v), ("o", o), ("dout", dout), ("dq", dq),
+                                 ("dk", dk), ("dv", dv)))
     nbytes = workspace.numel() * workspace.element_size()
     st = lib.fa_bwd(_dtype_code(q), _ptr(q), _strides(q), _ptr(k), _strides(k), _ptr(v),
                     _strides(v), _ptr(o), _strides(o), _ptr(dout), _strides(dout), _ptr(lse),
                     _ptr(dq), _strides(dq), _ptr(dk), _strides(dk), _ptr(dv), _strides(dv),
                     _ptr(workspace), nbytes, B, H, N, d, float(scale), int(bool(causal)),
                     _ptr(seqlens_k), _ptr(block_mask), int(mask_block), _stream(q, stream))
+    _check(st)
+
+
+def fa_bwd_dq(q, k, v, o, dout, lse, dq, workspace, *, scale: float, causal: bool = False,
+              seqlens_k=None, block_mask=None, mask_block: int = 128, stream=None) -> None:
+    """Calls fa_bwd_dq: writes D into the workspace and dq in full."""
+    lib = load_library()
+    B, H, N, d = _check_like(q, (("k", k), ("v", v), ("o", o), ("dout", dout), ("dq", dq)))
+    nbytes = workspace.numel() * workspace.element_size()
+    st = lib.fa_bwd_dq(_dtype_code(q), _ptr(q), _strides(q), _ptr(k), _strides(k), _ptr(v),
+                       _strides(v), _ptr(o), _strides(o), _ptr(dout), _strides(dout),
+                       _ptr(lse), _ptr(dq), _strides(dq), _ptr(workspace), nbytes, B, H, N, d,
+                       float(scale), int(bool(causal)), _ptr(seqlens_k), _ptr(block_mask),
+                       int(mask_block), _stream(q, stream))
+    _check(st)
+
+
+def fa_bwd_dkdv(q, k, v, dout, lse, dk, dv, workspace, *, scale: float, causal: bool = False,
+                seqlens_k=None, block_mask=None, mask_block: int = 128, stream=None) -> None:
+    """Calls fa_bwd_dkdv: reads D from the workspace, writes dk and dv in full."""
+    lib = load_library()
+    B, H, N, d = _check_like(q, (("k", k), ("v", v), ("dout", dout), ("dk", dk), ("dv", dv)))
+    nbytes = workspace.numel() * workspace.element_size()
+    st = lib.fa_bwd_dkdv(_dtype_code(q), _ptr(q), _strides(q), _ptr(k), _strides(k), _ptr(v),
+                         _strides(v), _ptr(dout), _strides(dout), _ptr(lse), _ptr(dk),
+                         _strides(dk), _ptr(dv), _strides(dv), _ptr(workspace), nbytes, B, H,
+                         N, d, float(scale), int(bool(causal)), _ptr(seqlens_k),
+                         _ptr(block_mask), int(mask_block), _stream(q, stream))
     _check(st)
 
 

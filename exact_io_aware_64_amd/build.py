@@ -39,15 +39,22 @@ def hipcc() -> str:
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc(), *CFLAGS, "-I", os.path.join(ROOT, "include"), "-c",
-           os.path.join(CSRC, src), "-o", obj]
+    cmd = [hipcc(), *CFLAGS, "-Rpass-analysis=kernel-resource-usage",
+           "-I", os.path.join(ROOT, "include"), "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     noise = "is not a recognized feature for this target"
-    err = "\n".join(l for l in r.stderr.splitlines() if noise not in l)
+    lines = [l for l in r.stderr.splitlines() if noise not in l]
+    usage = [l for l in lines if "kernel-resource-usage" in l]
+    err = "\n".join(l for l in lines if "kernel-resource-usage" not in l)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{err}")
     if err.strip():
         sys.stderr.write(err + "\n")
+    # A kernel that spills or calls an out-of-line function uses scratch
+    # memory, which costs far more than any register it saves: refuse it.
+    for l in usage:
+        if "ScratchSize" in l and not l.rstrip().endswith(": 0 [-Rpass-analysis=kernel-resource-usage]"):
+            raise RuntimeError(f"{src}: a kernel uses scratch memory:\n{l}")
     return obj
 
 

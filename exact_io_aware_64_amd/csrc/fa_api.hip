@@ -126,25 +126,33 @@ size_t fa_bwd_workspace_bytes(fa_dtype dtype, int B, int H, int N, int d) {
   return (bytes + 255) & ~(size_t)255;
 }
 
-fa_status fa_bwd(fa_dtype dtype, const void* q, fa_strides q_strides, const void* k,
-                 fa_strides k_strides, const void* v, fa_strides v_strides, const void* o,
-                 fa_strides o_strides, const void* dout, fa_strides dout_strides,
-                 const float* lse, void* dq, fa_strides dq_strides, void* dk,
-                 fa_strides dk_strides, void* dv, fa_strides dv_strides, void* workspace,
-                 size_t workspace_bytes, int B, int H, int N, int d, float scale, int causal,
-                 const int32_t* seqlens_k, const uint8_t* block_mask, int mask_block,
-                 hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+fa_status bwd_impl(int phases, fa_dtype dtype, const void* q, fa_strides q_strides,
+                   const void* k, fa_strides k_strides, const void* v, fa_strides v_strides,
+                   const void* o, fa_strides o_strides, const void* dout,
+                   fa_strides dout_strides, const float* lse, void* dq, fa_strides dq_strides,
+                   void* dk, fa_strides dk_strides, void* dv, fa_strides dv_strides,
+                   void* workspace, size_t workspace_bytes, int B, int H, int N, int d,
+                   float scale, int causal, const int32_t* seqlens_k,
+                   const uint8_t* block_mask, int mask_block, hipStream_t stream) {
   int al = 0;
   fa_status st = check_common(dtype, B, H, N, d, scale, block_mask, mask_block, &al);
   if (st != FA_OK) return st;
   if ((st = check_tensor("q", q, q_strides, al, N)) != FA_OK) return st;
   if ((st = check_tensor("k", k, k_strides, al, N)) != FA_OK) return st;
   if ((st = check_tensor("v", v, v_strides, al, N)) != FA_OK) return st;
-  if ((st = check_tensor("o", o, o_strides, al, N)) != FA_OK) return st;
+  if (phases & fa::kPhaseDQ) {
+    if ((st = check_tensor("o", o, o_strides, al, N)) != FA_OK) return st;
+    if ((st = check_tensor("dq", dq, dq_strides, al, N)) != FA_OK) return st;
+  }
   if ((st = check_tensor("dout", dout, dout_strides, al, N)) != FA_OK) return st;
-  if ((st = check_tensor("dq", dq, dq_strides, al, N)) != FA_OK) return st;
-  if ((st = check_tensor("dk", dk, dk_strides, al, N)) != FA_OK) return st;
-  if ((st = check_tensor("dv", dv, dv_strides, al, N)) != FA_OK) return st;
+  if (phases & fa::kPhaseDKDV) {
+    if ((st = check_tensor("dk", dk, dk_strides, al, N)) != FA_OK) return st;
+    if ((st = check_tensor("dv", dv, dv_strides, al, N)) != FA_OK) return st;
+  }
   if (lse == nullptr) return fail(FA_ERR_INVALID_ARG, "lse is NULL");
   if (!aligned16(lse)) return fail(FA_ERR_INVALID_ARG, "lse is not 16-byte aligned");
   if (workspace == nullptr) return fail(FA_ERR_INVALID_ARG, "workspace is NULL");
@@ -184,9 +192,55 @@ fa_status fa_bwd(fa_dtype dtype, const void* q, fa_strides q_strides, const void
   a.bmask = block_mask;
   a.mask_block = block_mask ? mask_block : 128;
   a.n_mask_tiles = (N + a.mask_block - 1) / a.mask_block;
-  const hipError_t e = dtype == FA_BF16 ? fa::launch_bwd_bf16(a, causal != 0, stream)
-                                        : fa::launch_bwd_f32(a, causal != 0, stream);
+  const hipError_t e = dtype == FA_BF16 ? fa::launch_bwd_bf16(a, causal != 0, phases, stream)
+                                        : fa::launch_bwd_f32(a, causal != 0, phases, stream);
   return hip_status(e);
+}
+
+}  // namespace
+
+extern "C" {
+
+fa_status fa_bwd(fa_dtype dtype, const void* q, fa_strides q_strides, const void* k,
+                 fa_strides k_strides, const void* v, fa_strides v_strides, const void* o,
+                 fa_strides o_strides, const void* dout, fa_strides dout_strides,
+                 const float* lse, void* dq, fa_strides dq_strides, void* dk,
+                 fa_strides dk_strides, void* dv, fa_strides dv_strides, void* workspace,
+                 size_t workspace_bytes, int B, int H, int N, int d, float scale, int causal,
+                 const int32_t* seqlens_k, const uint8_t* block_mask, int mask_block,
+                 hipStream_t stream) {
+  return bwd_impl(fa::kPhaseDQ | fa::kPhaseDKDV, dtype, q, q_strides, k, k_strides, v,
+                  v_strides, o, o_strides, dout, dout_strides, lse, dq, dq_strides, dk,
+                  dk_strides, dv, dv_strides, workspace, workspace_bytes, B, H, N, d, scale,
+                  causal, seqlens_k, block_mask, mask_block, stream);
+}
+
+fa_status fa_bwd_dq(fa_dtype dtype, const void* q, fa_strides q_strides, const void* k,
+                    fa_strides k_strides, const void* v, fa_strides v_strides, const void* o,
+                    fa_strides o_strides, const void* dout, fa_strides dout_strides,
+                    const float* lse, void* dq, fa_strides dq_strides, void* workspace,
+                    size_t workspace_bytes, int B, int H, int N, int d, float scale,
+                    int causal, const int32_t* seqlens_k, const uint8_t* block_mask,
+                    int mask_block, hipStream_t stream) {
+  const fa_strides none{0, 0, 0};
+  return bwd_impl(fa::kPhaseDQ, dtype, q, q_strides, k, k_strides, v, v_strides, o,
+                  o_strides, dout, dout_strides, lse, dq, dq_strides, nullptr, none, nullptr,
+                  none, workspace, workspace_bytes, B, H, N, d, scale, causal, seqlens_k,
+                  block_mask, mask_block, stream);
+}
+
+fa_status fa_bwd_dkdv(fa_dtype dtype, const void* q, fa_strides q_strides, const void* k,
+                      fa_strides k_strides, const void* v, fa_strides v_strides,
+                      const void* dout, fa_strides dout_strides, const float* lse, void* dk,
+                      fa_strides dk_strides, void* dv, fa_strides dv_strides, void* workspace,
+                      size_t workspace_bytes, int B, int H, int N, int d, float scale,
+                      int causal, const int32_t* seqlens_k, const uint8_t* block_mask,
+                      int mask_block, hipStream_t stream) {
+  const fa_strides none{0, 0, 0};
+  return bwd_impl(fa::kPhaseDKDV, dtype, q, q_strides, k, k_strides, v, v_strides, nullptr,
+                  none, dout, dout_strides, lse, nullptr, none, dk, dk_strides, dv, dv_strides,
+                  workspace, workspace_bytes, B, H, N, d, scale, causal, seqlens_k, block_mask,
+                  mask_block, stream);
 }
 
 const char* fa_status_string(fa_status status) {

@@ -21,6 +21,8 @@
 //    key per lane, which is exactly the B operand of dV^T = dO^T P and
 //    dK^T = Q^T dS.
 // Masked tiles are skipped exactly as in the forward pass.
+#include <type_traits>
+
 #include "fa_device.h"
 
 namespace fa {
@@ -112,18 +114,18 @@ __global__ __launch_bounds__(256) void dq_kernel(BwdArgs a) {
   const int v_off0 = sr * ssv + 16 * sc, v_off1 = (sr + 32) * ssv + 16 * sc;
   const int trl = tr_lane_offset(lane);
   uint4 kreg[2], vreg[2];
-  auto tile_at = [&](int it) -> int {
+  auto tile_at = [&](int it) FA_INLINE -> int {
     if constexpr (BMASK) return tlist[it];
     return it;
   };
-  auto gload = [&](int t) {
+  auto gload = [&](int t) FA_INLINE {
     const int k0 = t * kTile;
     kreg[0] = ldb16(rk, k_off0 + k0 * ssk);
     kreg[1] = ldb16(rk, k_off1 + k0 * ssk);
     vreg[0] = ldb16(rv, v_off0 + k0 * ssv);
     vreg[1] = ldb16(rv, v_off1 + k0 * ssv);
   };
-  auto swrite = [&](int buf) {
+  auto swrite = [&](int buf) FA_INLINE {
     store_row16(s_k[buf], sr, sc, kreg[0]);
     store_row16(s_k[buf], sr + 32, sc, kreg[1]);
     store_row16(s_v[buf], sr, sc, vreg[0]);
@@ -134,6 +136,9 @@ __global__ __launch_bounds__(256) void dq_kernel(BwdArgs a) {
     gload(tile_at(0));
     swrite(0);
   }
+  // Every load issued so far (Q fragment, first tile) is complete here;
+  // saying so keeps the loop's wait counts from covering them.
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
   for (int it = 0; it < nlist; ++it) {
@@ -279,32 +284,132 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdArgs a) {
     const int d_off0 = sr * ssdo + 16 * sc, d_off1 = (sr + 32) * ssdo + 16 * sc;
     const int trl = tr_lane_offset(lane);
     uint4 qreg[2], dreg[2];
-    float lreg = 0.f, dreg_s = 0.f;
-    auto tile_at = [&](int it) -> int {
+    // Raw L and D of row qs + tid (threads 0..63), converted only when they
+    // are written to LDS so that no wait on the loads sits at the start of a
+    // tile.  Rows past N read as 0 through the buffer resources.
+    float lraw = 0.f, draw = 0.f;
+    int lrow = 0;
+    const __amdgpu_buffer_rsrc_t rl = make_rsrc(lse, (uint32_t)a.N * 4);
+    const __amdgpu_buffer_rsrc_t rd = make_rsrc(dsum, (uint32_t)a.N * 4);
+    auto tile_at = [&](int it) FA_INLINE -> int {
       if constexpr (BMASK) return tlist[it];
       return qt_lo + it;
     };
-    auto gload = [&](int t) {
+    auto gload = [&](int t) FA_INLINE {
       const int qs = t * kTile;
       qreg[0] = ldb16(rq, q_off0 + qs * ssq);
       qreg[1] = ldb16(rq, q_off1 + qs * ssq);
       dreg[0] = ldb16(rdo, d_off0 + qs * ssdo);
       dreg[1] = ldb16(rdo, d_off1 + qs * ssdo);
       if (tid < kTile) {
-        const int qq = qs + tid;
-        const float L = qq < a.N ? lse[qq] : -kInf;
-        lreg = (L == -kInf) ? kInf : L * kLog2e;
-        dreg_s = qq < a.N ? -dsum[qq] : 0.f;
+        lrow = qs + tid;
+        lraw = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rl, 4 * lrow, 0, 0));
+        draw = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rd, 4 * lrow, 0, 0));
       }
     };
-    auto swrite = [&](int buf) {
+    auto swrite = [&](int buf) FA_INLINE {
       store_row16(s_q[buf], sr, sc, qreg[0]);
       store_row16(s_q[buf], sr + 32, sc, qreg[1]);
       store_row16(s_do[buf], sr, sc, dreg[0]);
       store_row16(s_do[buf], sr + 32, sc, dreg[1]);
       if (tid < kTile) {
-        s_l2[buf][tid] = lreg;
-        s_nd[buf][tid] = dreg_s;
+        // +inf in log2 units makes every probability of a dead or missing row 0
+        const bool live = lrow < a.N && lraw != -kInf;
+        s_l2[buf][tid] = live ? lraw * kLog2e : kInf;
+        s_nd[buf][tid] = lrow < a.N ? -draw : 0.f;
+      }
+    };
+
+    // One 64-query tile as 32 issue slots, each holding one MFMA, a share
+    // of the vector work and the LDS reads of the operand needed kLead
+    // slots later; scheduling fences keep the slots in this order so that
+    // the exponentials and dS products of one 32-query half run on the
+    // vector ALU while the matrix core works on the other half:
+    //   slots  0.. 7  S, dP of queries 0..31                (MFMA)
+    //   slots  8..15  S, dP of queries 32..63               (MFMA) | P, dS of 0..31
+    //   slots 16..23  dV, dK contributions of queries 0..31 (MFMA) | P, dS of 32..63
+    //   slots 24..31  dV, dK contributions of 32..63        (MFMA)
+    auto tile = [&](auto mask_c, int buf, int qs) FA_INLINE {
+      constexpr bool MASK = decltype(mask_c)::value;
+      constexpr int kLead = 4;
+      const uint16_t* qs_ = s_q[buf];
+      const uint16_t* ds_ = s_do[buf];
+      f32x16 sc_[2] = {zero16(), zero16()}, dp[2];
+      uint32_t pkp[4][4], pkd[4][4];  // bf16 pairs of P and dS per step
+      f32x4 l4[2][4];
+      bf16x8 opa[32];
+      // A operand of slot t.
+      auto load_a = [&](int t) FA_INLINE {
+        if (t < 16) {
+          const int qb = t >> 3, ks = (t & 7) >> 1;
+          const int off = (32 * qb + r) * kRowStride + 16 * ks + 8 * hl;
+          opa[t] = lds_row8(((t & 1) ? ds_ : qs_) + off);
+        } else {
+          const int stp = (t - 16) >> 2, u = (t - 16) & 3;
+          const int off = trl + 16 * stp * kRowStride + 32 * (u >> 1);
+          opa[t] = tr_operand(((u & 1) ? qs_ : ds_) + off);
+        }
+      };
+      auto load_l = [&](int qb, int j) FA_INLINE {
+        l4[qb][j] = *reinterpret_cast<const f32x4*>(&s_l2[buf][32 * qb + 8 * j + 4 * hl]);
+      };
+      // dP accumulators start at -D (row of each element), so the MFMA
+      // leaves dP - D in them directly.
+      auto init_dp = [&](int qb) FA_INLINE {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const f32x4 d4 = *reinterpret_cast<const f32x4*>(&s_nd[buf][32 * qb + 8 * j + 4 * hl]);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) dp[qb][4 * j + i] = d4[i];
+        }
+      };
+      // Elements 2 ch and 2 ch + 1 of half qb: P = 2^(S c - L log2 e),
+      // dS = P (dP - D), each pair rounded to bf16.
+      auto probs = [&](int qb, int ch) FA_INLINE {
+        float pv[2], dv2[2];
+#pragma unroll
+        for (int x = 0; x < 2; ++x) {
+          const int e = 2 * ch + x;
+          float sv = sc_[qb][e];
+          if constexpr (MASK) {
+            if (32 * qb + 8 * (e >> 2) + (e & 3) < key_lim - qs) sv = -kInf;
+          }
+          pv[x] = fast_exp2(__builtin_fmaf(sv, c, -l4[qb][e >> 2][e & 3]));
+          dv2[x] = dp[qb][e] * pv[x];
+        }
+        pkp[2 * qb + (ch >> 2)][ch & 3] = pack2(pv[0], pv[1]);
+        pkd[2 * qb + (ch >> 2)][ch & 3] = pack2(dv2[0], dv2[1]);
+      };
+
+      init_dp(0);
+#pragma unroll
+      for (int t = 0; t < kLead; ++t) load_a(t);
+      load_l(0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int t = 0; t < 32; ++t) {
+        if (t + kLead < 32) load_a(t + kLead);
+        if (t == 2) init_dp(1);
+        if (t >= 4 && t < 7) load_l(0, t - 3);
+        if (t >= 12 && t < 16) load_l(1, t - 12);
+        if (t < 16) {
+          const int qb = t >> 3, ks = (t & 7) >> 1;
+          if (t & 1)
+            dp[qb] = mfma32(opa[t], vf[ks], dp[qb]);
+          else
+            sc_[qb] = mfma32(opa[t], kf[ks], sc_[qb]);
+        } else {
+          const int stp = (t - 16) >> 2, u = (t - 16) & 3, db = u >> 1;
+          const bf16x8 bop = as_bf16x8(make_uint4(
+              (u & 1) ? pkd[stp][0] : pkp[stp][0], (u & 1) ? pkd[stp][1] : pkp[stp][1],
+              (u & 1) ? pkd[stp][2] : pkp[stp][2], (u & 1) ? pkd[stp][3] : pkp[stp][3]));
+          if (u & 1)
+            dkt[db] = mfma32(opa[t], bop, dkt[db]);
+          else
+            dvt[db] = mfma32(opa[t], bop, dvt[db]);
+        }
+        if (t >= 8 && t < 24) probs((t - 8) >> 3, (t - 8) & 7);
+        __builtin_amdgcn_sched_barrier(0);
       }
     };
 
@@ -312,6 +417,9 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdArgs a) {
       gload(tile_at(0));
       swrite(0);
     }
+    // Every load issued so far (K, V fragments, first tile) is complete here;
+    // saying so keeps the loop's wait counts from covering them.
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
 
     for (int it = 0; it < nlist; ++it) {
@@ -321,61 +429,11 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdArgs a) {
 
       const bool active = !CAUSAL || (qs + kTile - 1 >= kw);
       if (active) {
-        const uint16_t* qs_ = s_q[buf];
-        const uint16_t* ds_ = s_do[buf];
-        // dP accumulators start at -D (row of each element), so the MFMA
-        // leaves dP - D in them directly.
-        f32x16 s[2] = {zero16(), zero16()}, dp[2];
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const f32x4 d4 = *reinterpret_cast<const f32x4*>(&s_nd[buf][32 * qb + 8 * j + 4 * hl]);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) dp[qb][4 * j + i] = d4[i];
-          }
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks)
-#pragma unroll
-          for (int qb = 0; qb < 2; ++qb) {
-            const int off = (32 * qb + r) * kRowStride + 16 * ks + 8 * hl;
-            s[qb] = mfma32(lds_row8(qs_ + off), kf[ks], s[qb]);
-            dp[qb] = mfma32(lds_row8(ds_ + off), vf[ks], dp[qb]);
-          }
         const bool need_mask = (kw + 32 > kv_len) || (CAUSAL && kw + 31 > qs);
-        if (need_mask) {
-          const int lim = key_lim - qs;
-#pragma unroll
-          for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-            for (int e = 0; e < 16; ++e)
-              if (32 * qb + 8 * (e >> 2) + (e & 3) < lim) s[qb][e] = -kInf;
-        }
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const f32x4 l4 = *reinterpret_cast<const f32x4*>(&s_l2[buf][32 * qb + 8 * j + 4 * hl]);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const int e = 4 * j + i;
-              const float p = fast_exp2(__builtin_fmaf(s[qb][e], c, -l4[i]));
-              s[qb][e] = p;
-              dp[qb][e] *= p;
-            }
-          }
-        // dV^T[d][key] += sum_q dO[q][d] P[q][key];  dK^T[d][key] += sum_q Q[q][d] dS[q][key]
-#pragma unroll
-        for (int stp = 0; stp < 4; ++stp) {
-          const bf16x8 pb = pack8(s[stp >> 1], 8 * (stp & 1));
-          const bf16x8 dsb = pack8(dp[stp >> 1], 8 * (stp & 1));
-#pragma unroll
-          for (int db = 0; db < 2; ++db) {
-            const int off = trl + 16 * stp * kRowStride + 32 * db;
-            dvt[db] = mfma32(tr_operand(ds_ + off), pb, dvt[db]);
-            dkt[db] = mfma32(tr_operand(qs_ + off), dsb, dkt[db]);
-          }
-        }
+        if (need_mask)
+          tile(std::true_type{}, buf, qs);
+        else
+          tile(std::false_type{}, buf, qs);
       }
       if (it + 1 < nlist) swrite(buf ^ 1);
       __syncthreads();
@@ -402,28 +460,35 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdArgs a) {
 }
 
 template <bool C, bool S, bool M>
-hipError_t launch(const BwdArgs& a, hipStream_t stream) {
+hipError_t launch(const BwdArgs& a, int phases, hipStream_t stream) {
   BwdArgs copy = a;
   void* args[] = {&copy};
   const int BH = a.B * a.H;
   dim3 block(256);
-  dim3 gq((unsigned)(((a.N + kBQ - 1) / kBQ) * BH));
-  hipError_t e = hipLaunchKernel((const void*)&dq_kernel<C, S, M>, gq, block, args, 0, stream);
-  if (e != hipSuccess) return e;
-  dim3 gk((unsigned)(((a.N + kBK - 1) / kBK) * BH));
-  return hipLaunchKernel((const void*)&dkdv_kernel<C, S, M>, gk, block, args, 0, stream);
+  if (phases & kPhaseDQ) {
+    dim3 gq((unsigned)(((a.N + kBQ - 1) / kBQ) * BH));
+    hipError_t e =
+        hipLaunchKernel((const void*)&dq_kernel<C, S, M>, gq, block, args, 0, stream);
+    if (e != hipSuccess) return e;
+  }
+  if (phases & kPhaseDKDV) {
+    dim3 gk((unsigned)(((a.N + kBK - 1) / kBK) * BH));
+    return hipLaunchKernel((const void*)&dkdv_kernel<C, S, M>, gk, block, args, 0, stream);
+  }
+  return hipSuccess;
 }
 
 }  // namespace
 
-hipError_t launch_bwd_bf16(const BwdArgs& a, bool causal, hipStream_t stream) {
+hipError_t launch_bwd_bf16(const BwdArgs& a, bool causal, int phases, hipStream_t stream) {
   const bool s = a.seqlens != nullptr, m = a.bmask != nullptr;
+  const int p = phases;
   if (causal) {
-    if (s) return m ? launch<true, true, true>(a, stream) : launch<true, true, false>(a, stream);
-    return m ? launch<true, false, true>(a, stream) : launch<true, false, false>(a, stream);
+    if (s) return m ? launch<true, true, true>(a, p, stream) : launch<true, true, false>(a, p, stream);
+    return m ? launch<true, false, true>(a, p, stream) : launch<true, false, false>(a, p, stream);
   }
-  if (s) return m ? launch<false, true, true>(a, stream) : launch<false, true, false>(a, stream);
-  return m ? launch<false, false, true>(a, stream) : launch<false, false, false>(a, stream);
+  if (s) return m ? launch<false, true, true>(a, p, stream) : launch<false, true, false>(a, p, stream);
+  return m ? launch<false, false, true>(a, p, stream) : launch<false, false, false>(a, p, stream);
 }
 
 }  // namespace fa

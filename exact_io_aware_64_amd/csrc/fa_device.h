@@ -60,6 +60,13 @@ __device__ __forceinline__ bf16x8 pack8(const f32x16& v, int off) {
   return r;
 }
 
+// Two floats rounded to bf16 (nearest-even) and packed low, high.
+__device__ __forceinline__ uint32_t pack2(float lo, float hi) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){lo, hi}, bf16x2));
+}
+
 // Buffer resource over one (batch, head) slice of a tensor.  Loads through
 // it take 32-bit byte offsets, and any 16-byte load that starts at or past
 // `bytes` returns zeros, so rows past the end need no branch.
@@ -113,6 +120,88 @@ __device__ __forceinline__ bf16x8 tr_operand(const uint16_t* p) {
 __device__ __forceinline__ void store_row16(uint16_t* t, int row, int c, uint4 a) {
   *reinterpret_cast<uint4*>(t + row * kRowStride + 8 * c) = a;
 }
+
+// ---------------------------------------------------------------------------
+// Swizzled 64 x 64 bf16 tiles in LDS.
+//
+// Row r of a tile occupies 128 contiguous bytes (eight 16-byte chunks), and
+// logical chunk c of row r is stored at physical chunk c ^ swz(r).  With this
+// XOR pattern both reads the kernels make are free of bank conflicts on
+// gfx950's LDS: 16-byte row reads (16 lanes reading one chunk column of 16
+// consecutive rows) and ds_read_b64_tr_b16 transpose reads (32 lanes reading
+// 4 chunks of 4 consecutive rows).  swz depends only on (r / 2) % 8, so a
+// tile offset by a multiple of 16 rows keeps the same pattern.
+constexpr int kTileElems = 64 * 64;
+
+__device__ __forceinline__ int swz(int row) {
+  const int p = (row >> 1) & 7;
+  return (p >> 1) | ((p & 1) << 2);
+}
+
+// Element offset of (row, col) inside a swizzled tile.
+__device__ __forceinline__ int toff(int row, int col) {
+  return row * 64 + (((col >> 3) ^ swz(row)) << 3) + (col & 7);
+}
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// Copies rows row0 .. row0+63 of one (batch, head) slice (byte row stride
+// `stride_b`, buffer resource `rs`) straight from memory into the swizzled
+// tile, without passing through registers: buffer_load_dwordx4 ... lds puts
+// lane l's 16 bytes at the wave's LDS base + 16 l, so lane l fetches the
+// logical chunk that belongs at physical chunk l % 8 of row l / 8.  Each of
+// the 4 waves of a workgroup copies 16 rows; rows past the end of the slice
+// read as zeros.  Completion is tracked by the wave's vmcnt.
+__device__ __forceinline__ void stage_tile(__amdgpu_buffer_rsrc_t rs, int row0, int stride_b,
+                                           uint16_t* tile, int w, int lane) {
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int row = 16 * w + 8 * u + (lane >> 3);
+    const int voff = (row0 + row) * stride_b + (((lane & 7) ^ swz(row)) << 4);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)(tile + (16 * w + 8 * u) * 64), 16,
+                                             voff, 0, 0, 0);
+  }
+}
+
+// 8 consecutive bf16 of a tile row (a 16-byte aligned chunk).
+__device__ __forceinline__ bf16x8 tile_row8(const uint16_t* tile, int off) {
+  return *reinterpret_cast<const bf16x8*>(tile + off);
+}
+
+// Row-read offset for the MFMA operand whose contraction runs along a tile
+// row: lane (r, hl) reads row r (+ 32 kb, i.e. + 2048 kb elements) at columns
+// 16 ks + 8 hl .. +7.
+__device__ __forceinline__ int row_off(int r, int hl, int ks) { return toff(r, 16 * ks + 8 * hl); }
+
+// Transpose-read offsets for tr_read: the A operand of a 32x32x16 MFMA whose
+// contraction runs over tile ROWS 16 st .. 16 st + 15 (+ 1024 st elements)
+// and whose output rows are tile columns 32 db .. 32 db + 31.  Lane (r, hl)
+// receives X[16 st + 4 hl + t][32 db + r] in slots t = 0..3 and
+// X[16 st + 8 + 4 hl + t][32 db + r] in slots 4..7.  Within each 16-lane
+// group of a ds_read_b64_tr_b16, lane i receives element 16 t + i (t = 0..3)
+// of the 64 elements the group reads, and source lane j reads 4 elements of
+// row j / 4; `hi` selects the rows 8 .. 15 of the step.
+__device__ __forceinline__ int tr_off(int lane, int hi, int db) {
+  const int j = lane & 15, g = lane >> 4;
+  return toff(8 * hi + 4 * (g >> 1) + (j >> 2), 32 * db + 16 * (g & 1) + 4 * (j & 3));
+}
+
+__device__ __forceinline__ bf16x8 tr_read(const uint16_t* tile, int off_lo, int off_hi) {
+  typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+  const i16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(tile + off_lo));
+  const i16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(tile + off_hi));
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+__device__ __forceinline__ bf16x8 words_to_bf16x8(uint32_t a, uint32_t b, uint32_t c,
+                                                  uint32_t d) {
+  return __builtin_bit_cast(bf16x8, make_uint4(a, b, c, d));
+}
+
+#define FA_FENCE() __builtin_amdgcn_sched_barrier(0)
+// Lambdas in the kernels hold per-tile code; a call left out of line would
+// spill the captured state to scratch memory.
+#define FA_INLINE __attribute__((always_inline))
 
 // Inclusive prefix sum over the 64 lanes of a wave.
 __device__ __forceinline__ int wave_incl_scan(int x) {

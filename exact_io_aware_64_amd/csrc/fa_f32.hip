@@ -236,14 +236,18 @@ hipError_t launch_fwd_f32(const FwdArgs& a, bool causal, hipStream_t stream) {
   return hipLaunchKernel((const void*)&fwd_f32_kernel, grid, block, args, 0, stream);
 }
 
-hipError_t launch_bwd_f32(const BwdArgs& a, bool causal, hipStream_t stream) {
+hipError_t launch_bwd_f32(const BwdArgs& a, bool causal, int phases, hipStream_t stream) {
   BwdArgs copy = a;
   int cz = causal ? 1 : 0;
   void* args[] = {&copy, &cz};
   dim3 grid((unsigned)(((a.N + kTile - 1) / kTile) * a.B * a.H)), block(64);
-  hipError_t e = hipLaunchKernel((const void*)&dq_f32_kernel, grid, block, args, 0, stream);
-  if (e != hipSuccess) return e;
-  return hipLaunchKernel((const void*)&dkdv_f32_kernel, grid, block, args, 0, stream);
+  if (phases & kPhaseDQ) {
+    hipError_t e = hipLaunchKernel((const void*)&dq_f32_kernel, grid, block, args, 0, stream);
+    if (e != hipSuccess) return e;
+  }
+  if (phases & kPhaseDKDV)
+    return hipLaunchKernel((const void*)&dkdv_f32_kernel, grid, block, args, 0, stream);
+  return hipSuccess;
 }
 
 }  // namespace fa

@@ -2,43 +2,53 @@
 //
 // One workgroup (4 waves) owns 128 query rows of one (batch, head); each wave
 // owns 32 of them and keeps its Q fragment in registers for the whole kernel.
-// Key/value tiles of 64 rows stream through LDS (double-buffered: the global
-// loads of tile t+1 are in flight while tile t is computed), so each K/V
-// element is read from HBM/L2 once per workgroup and the N x N score matrix
-// never leaves registers (suanlizi.com summary, "tiling" and "kernel fusion";
-// researchpapers.dev explainer, "tiling and recomputation").
+// Key/value tiles of 64 rows stream through LDS, double-buffered and copied
+// straight from memory into LDS (the copy of tile t+1 is in flight while
+// tile t is computed), so each K/V element is read from HBM/L2 once per
+// workgroup and the N x N score matrix never leaves registers (suanlizi.com
+// summary, "tiling" and "kernel fusion"; researchpapers.dev explainer,
+// "tiling and recomputation").
 //
 // The scores are computed transposed, S^T = K Q^T, on the 32x32x16 bf16 MFMA:
-// in the accumulator layout each lane then holds 32 scores of a single query,
-// so the row maximum and row sum need one exchange between the two wave
-// halves instead of a reduction across 32 lanes.  The online softmax keeps a
-// running maximum m (log2 units) and a running sum l per query and rescales
-// the output accumulator when m grows (researchpapers.dev, "tiling and
-// recomputation"; the max subtraction is the safe softmax of the llm-deploy
-// note).  O^T = V^T P^T is accumulated on the same MFMA; the probabilities
-// feed the B operand straight from the accumulator registers, and the V^T
-// operand is read from the row-major V tile with LDS transpose reads.
+// in the accumulator layout each lane then holds 32 scores of a single query
+// (the two wave halves hold its two interleaved key halves).  O^T = V^T P^T is
+// accumulated on the same MFMA; the probabilities feed the B operand straight
+// from the accumulator registers and the V^T operand comes from the V tile
+// through LDS transpose reads.
+//
+// Online softmax (researchpapers.dev, "tiling and recomputation"; the maximum
+// subtraction is the safe softmax of the llm-deploy note).  Each query keeps
+// a reference maximum m (log2 units) and a running sum l, and the output is
+// O = acc / l, L = (m + log2 l) ln 2 -- a ratio that does not depend on which
+// reference was used, so m only has to bound the scores, not equal their
+// maximum.  Probabilities of each 32-key half tile are computed against the
+// current m; if some lane's partial sum exceeds 2^12 (or is not finite, as on
+// the first tile where m = -inf) every probability of that half may be too
+// large, and only then is the half's true maximum taken, m raised, acc and l
+// rescaled and the half recomputed.  In steady state no row maximum is
+// computed at all.
 //
 // Tiles that the mask removes entirely are never loaded: causal and key
 // padding shrink the key range, and a block mask is compacted into a list of
 // kept tiles (suanlizi.com, "block-sparse attention").
+#include <type_traits>
+
 #include "fa_device.h"
 
 namespace fa {
 namespace {
 
-constexpr int kBR = 128;  // query rows per workgroup
-// The running maximum is only moved (and O, l rescaled) when a tile's
-// maximum exceeds it by more than this many log2 units; until then the
-// probabilities are taken against the stale maximum and stay below
-// 2^kSlack.  O = acc / l and L = m + log2(l) are unchanged by the choice of
-// reference, so the result is the same up to rounding.
-constexpr float kSlack = 8.f;
+constexpr int kBR = 128;               // query rows per workgroup
+constexpr float kSumLimit = 4096.f;    // largest partial sum the fast path accepts
 
 template <bool CAUSAL, bool SEQLEN, bool BMASK>
 __global__ __launch_bounds__(256) void fwd_bf16_kernel(FwdArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t s_k[2][kTile * kRowStride];
-  __shared__ __attribute__((aligned(16))) uint16_t s_v[2][kTile * kRowStride];
+  // Two buffers, each a K tile and a V tile; separate arrays so that the
+  // copies into one buffer and the reads of the other never alias.
+  __shared__ __attribute__((aligned(16))) uint16_t s_k0[kTileElems];
+  __shared__ __attribute__((aligned(16))) uint16_t s_v0[kTileElems];
+  __shared__ __attribute__((aligned(16))) uint16_t s_k1[kTileElems];
+  __shared__ __attribute__((aligned(16))) uint16_t s_v1[kTileElems];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int r = lane & 31, hl = lane >> 5;
@@ -93,116 +103,164 @@ __global__ __launch_bounds__(256) void fwd_bf16_kernel(FwdArgs a) {
   float m = -kInf, l = 0.f;
   const float c = a.scale_log2;
 
-  // Staging roles: rows tid/8 and tid/8 + 32 of the K and V tiles, 16-byte
-  // column tid%8, stored row-major.
-  const int sr = tid >> 3, sc = tid & 7;
-  const int k_off0 = sr * ssk + 16 * sc, k_off1 = (sr + 32) * ssk + 16 * sc;
-  const int v_off0 = sr * ssv + 16 * sc, v_off1 = (sr + 32) * ssv + 16 * sc;
-  const int trl = tr_lane_offset(lane);
-  uint4 kreg[2], vreg[2];
-  auto tile_at = [&](int it) -> int {
+  // Per-lane LDS offsets: K rows (A operand of S^T, contraction over d) and
+  // V^T transpose reads (A operand of O^T, contraction over keys).
+  int roff[4];
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) roff[ks] = row_off(r, hl, ks);
+  int troff[2][2];
+#pragma unroll
+  for (int hi = 0; hi < 2; ++hi)
+#pragma unroll
+    for (int db = 0; db < 2; ++db) troff[hi][db] = tr_off(lane, hi, db);
+
+  auto tile_at = [&](int it) FA_INLINE -> int {
     if constexpr (BMASK) return tlist[it];
     return it;
   };
-  auto gload = [&](int t) {
-    const int k0 = t * kTile;
-    kreg[0] = ldb16(rk, k_off0 + k0 * ssk);
-    kreg[1] = ldb16(rk, k_off1 + k0 * ssk);
-    vreg[0] = ldb16(rv, v_off0 + k0 * ssv);
-    vreg[1] = ldb16(rv, v_off1 + k0 * ssv);
-  };
-  auto swrite = [&](int buf) {
-    store_row16(s_k[buf], sr, sc, kreg[0]);
-    store_row16(s_k[buf], sr + 32, sc, kreg[1]);
-    store_row16(s_v[buf], sr, sc, vreg[0]);
-    store_row16(s_v[buf], sr + 32, sc, vreg[1]);
+  auto stage = [&](int t, uint16_t* kt, uint16_t* vt) FA_INLINE {
+    stage_tile(rk, t * kTile, ssk, kt, w, lane);
+    stage_tile(rv, t * kTile, ssv, vt, w, lane);
   };
 
-  if (nlist > 0) {
-    gload(tile_at(0));
-    swrite(0);
-  }
-  __syncthreads();
+  // Raises m to cover the scores of half kb, rescales acc and l, and
+  // recomputes the half's probabilities (the rare path of the online softmax).
+  auto rescale_to = [&](const f32x16& sv) FA_INLINE {
+    float mx = -kInf;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sv[e]);
+    const float mt = half_max(mx) * c;
+    const float m_new = fmaxf(m, mt);
+    const float alpha = (m_new == m) ? 1.f : fast_exp2(m - m_new);
+    l *= alpha;
+#pragma unroll
+    for (int db = 0; db < 2; ++db)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) o[db][e] *= alpha;
+    m = m_new;
+  };
 
-  for (int it = 0; it < nlist; ++it) {
-    const int buf = it & 1;
+  // One 64-key tile as 16 MFMA issue slots separated by scheduling fences:
+  //   slots  0.. 3  S^T of keys  0..31                 (MFMA)
+  //   slots  4.. 7  S^T of keys 32..63                 (MFMA) | P of keys 0..31
+  //   slots  8..11  O^T += V^T P^T, keys 0..31         (MFMA) | P of keys 32..63
+  //   slots 12..15  O^T += V^T P^T, keys 32..63        (MFMA)
+  // with the LDS reads of each operand issued a few slots ahead.
+  auto body = [&](auto mask_c, const uint16_t* kt, const uint16_t* vt, int k0) FA_INLINE {
+    constexpr bool MASK = decltype(mask_c)::value;
+    f32x16 s[2] = {zero16(), zero16()};
+    bf16x8 ka[2][4], va[4][2];
+    uint32_t pk[4][4];   // bf16 pairs of P for PV steps 0..3
+    float ps[2] = {0.f, 0.f};
+    // element e of half kb holds key k0 + 32 kb + 8 (e / 4) + 4 hl + e % 4;
+    // visible iff 32 kb + 8 (e / 4) + e % 4 <= lim
+    [[maybe_unused]] int lim = 0;
+    if constexpr (MASK) lim = (CAUSAL ? min(kv_len - 1, qi) : kv_len - 1) - k0 - 4 * hl;
+
+    auto probs = [&](int kb, int e0) FA_INLINE {  // elements e0 .. e0+3 of half kb
+      float p[4];
+#pragma unroll
+      for (int x = 0; x < 4; ++x) {
+        const int e = e0 + x;
+        float sv = s[kb][e];
+        if constexpr (MASK) {
+          if (32 * kb + 8 * (e >> 2) + (e & 3) > lim) sv = -kInf;
+        }
+        p[x] = fast_exp2(__builtin_fmaf(sv, c, -m));
+        ps[kb] += p[x];
+      }
+      const int st = 2 * kb + (e0 >> 3), wd = (e0 & 7) >> 1;
+      pk[st][wd] = pack2(p[0], p[1]);
+      pk[st][wd + 1] = pack2(p[2], p[3]);
+    };
+    // the rare path: true maximum of half kb, rescale, recompute its P
+    auto fix_half = [&](int kb) FA_INLINE {
+      if constexpr (MASK) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+          if (32 * kb + 8 * (e >> 2) + (e & 3) > lim) s[kb][e] = -kInf;
+      }
+      rescale_to(s[kb]);
+      const float m_use = (m == -kInf) ? 0.f : m;
+      ps[kb] = 0.f;
+#pragma unroll
+      for (int e = 0; e < 16; e += 2) {
+        const float p0 = fast_exp2(__builtin_fmaf(s[kb][e], c, -m_use));
+        const float p1 = fast_exp2(__builtin_fmaf(s[kb][e + 1], c, -m_use));
+        ps[kb] += p0 + p1;
+        pk[2 * kb + (e >> 3)][(e & 7) >> 1] = pack2(p0, p1);
+      }
+    };
+
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) ka[0][ks] = tile_row8(kt, roff[ks]);
+    FA_FENCE();
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {  // slots 0..3
+      s[0] = mfma32(ka[0][ks], qf[ks], s[0]);
+      ka[1][ks] = tile_row8(kt, 2048 + roff[ks]);
+      FA_FENCE();
+    }
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {  // slots 4..7
+      s[1] = mfma32(ka[1][ks], qf[ks], s[1]);
+      const int st = ks >> 1, db = ks & 1;
+      va[st][db] = tr_read(vt + 1024 * st, troff[0][db], troff[1][db]);
+      probs(0, 4 * ks);
+      FA_FENCE();
+    }
+    if (__any(!(ps[0] <= kSumLimit))) fix_half(0);
+    l += ps[0];
+    FA_FENCE();
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {  // slots 8..11
+      const int st = i >> 1, db = i & 1;
+      o[db] = mfma32(va[st][db], words_to_bf16x8(pk[st][0], pk[st][1], pk[st][2], pk[st][3]),
+                     o[db]);
+      va[2 + st][db] = tr_read(vt + 1024 * (2 + st), troff[0][db], troff[1][db]);
+      probs(1, 4 * i);
+      FA_FENCE();
+    }
+    if (__any(!(ps[1] <= kSumLimit))) fix_half(1);
+    l += ps[1];
+    FA_FENCE();
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {  // slots 12..15
+      const int st = 2 + (i >> 1), db = i & 1;
+      o[db] = mfma32(va[st][db], words_to_bf16x8(pk[st][0], pk[st][1], pk[st][2], pk[st][3]),
+                     o[db]);
+      FA_FENCE();
+    }
+  };
+
+  auto compute = [&](int it, const uint16_t* kt, const uint16_t* vt) FA_INLINE {
     const int k0 = tile_at(it) * kTile;
-    if (it + 1 < nlist) gload(tile_at(it + 1));
-
     const bool active = !CAUSAL || (k0 <= qw + 31);
     if (active) {
-      const uint16_t* ks_ = s_k[buf];
-      const uint16_t* vs_ = s_v[buf];
-      // S^T for keys k0 .. k0+63 as two interleaved 32-key accumulator chains.
-      bf16x8 ka[2][4];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks)
-          ka[kb][ks] = lds_row8(ks_ + (32 * kb + r) * kRowStride + 16 * ks + 8 * hl);
-      f32x16 s[2] = {zero16(), zero16()};
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        s[0] = mfma32(ka[0][ks], qf[ks], s[0]);
-        s[1] = mfma32(ka[1][ks], qf[ks], s[1]);
-      }
       const bool need_mask = (k0 + kTile > kv_len) || (CAUSAL && k0 + kTile - 1 > qw);
-      if (need_mask) {
-        // element e of block kb holds key k0 + 4*hl + off(kb, e); it is
-        // visible iff off <= lim
-        const int last = CAUSAL ? min(kv_len - 1, qi) : kv_len - 1;
-        const int lim = last - k0 - 4 * hl;
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int e = 0; e < 16; ++e)
-            if (32 * kb + 8 * (e >> 2) + (e & 3) > lim) s[kb][e] = -kInf;
-      }
-      float mx = -kInf;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[kb][e]);
-      const float mt = half_max(mx) * c;  // tile maximum, log2 units
-      const bool grow = mt > m + kSlack;
-      if (__any(grow)) {
-        // alpha is 0 when m was -inf (nothing accumulated yet) and exactly 1
-        // in lanes that keep their reference.
-        const float alpha = grow ? fast_exp2(m - mt) : 1.f;
-        l *= alpha;
-#pragma unroll
-        for (int db = 0; db < 2; ++db)
-#pragma unroll
-          for (int e = 0; e < 16; ++e) o[db][e] *= alpha;
-        m = grow ? mt : m;
-      }
-      const float m_use = (m == -kInf) ? 0.f : m;
-      float rs = 0.f;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const float p = fast_exp2(__builtin_fmaf(s[kb][e], c, -m_use));
-          s[kb][e] = p;
-          rs += p;
-        }
-      l += rs;
-      // O^T[d][q] += sum_key V[key][d] P[q][key]; contraction slot e of step
-      // st maps to key 16*st + 4*hl + e (e < 4) or 16*st + 8 + 4*hl + e - 4.
-      bf16x8 va[4][2];
-#pragma unroll
-      for (int st = 0; st < 4; ++st)
-#pragma unroll
-        for (int db = 0; db < 2; ++db)
-          va[st][db] = tr_operand(vs_ + trl + 16 * st * kRowStride + 32 * db);
-#pragma unroll
-      for (int st = 0; st < 4; ++st) {
-        const bf16x8 pb = pack8(s[st >> 1], 8 * (st & 1));
-        o[0] = mfma32(va[st][0], pb, o[0]);
-        o[1] = mfma32(va[st][1], pb, o[1]);
-      }
+      if (need_mask)
+        body(std::true_type{}, kt, vt, k0);
+      else
+        body(std::false_type{}, kt, vt, k0);
     }
-    if (it + 1 < nlist) swrite(buf ^ 1);
+  };
+
+  if (nlist > 0) stage(tile_at(0), s_k0, s_v0);
+  // Every load issued so far (Q fragment, first tile) is complete here;
+  // saying so also keeps the loop's wait counts from covering them.
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+
+  // Two tiles per trip so that each buffer is a fixed array.
+  for (int it = 0; it < nlist; it += 2) {
+    if (it + 1 < nlist) stage(tile_at(it + 1), s_k1, s_v1);
+    compute(it, s_k0, s_v0);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (it + 1 >= nlist) break;
+    if (it + 2 < nlist) stage(tile_at(it + 2), s_k0, s_v0);
+    compute(it + 1, s_k1, s_v1);
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   }
 

@@ -53,9 +53,14 @@ struct BwdArgs {
   int n_mask_tiles;
 };
 
+// Backward phases: kPhaseDQ writes D (workspace) and dQ; kPhaseDKDV reads D
+// and writes dK, dV.  The full backward pass is both, in this order.
+constexpr int kPhaseDQ = 1;
+constexpr int kPhaseDKDV = 2;
+
 hipError_t launch_fwd_bf16(const FwdArgs& a, bool causal, hipStream_t stream);
-hipError_t launch_bwd_bf16(const BwdArgs& a, bool causal, hipStream_t stream);
+hipError_t launch_bwd_bf16(const BwdArgs& a, bool causal, int phases, hipStream_t stream);
 hipError_t launch_fwd_f32(const FwdArgs& a, bool causal, hipStream_t stream);
-hipError_t launch_bwd_f32(const BwdArgs& a, bool causal, hipStream_t stream);
+hipError_t launch_bwd_f32(const BwdArgs& a, bool causal, int phases, hipStream_t stream);
 
 }  // namespace fa

@@ -139,6 +139,51 @@ fa_status fa_bwd(fa_dtype dtype,
                  const uint8_t* block_mask, int mask_block,
                  hipStream_t stream);
 
+/*
+ * fa_bwd_dq, fa_bwd_dkdv -- the two phases of fa_bwd, exported separately so
+ * that a caller can schedule or time them on their own.  fa_bwd is exactly
+ * fa_bwd_dq followed by fa_bwd_dkdv on the same stream, with the same
+ * arguments and workspace.
+ *
+ *   fa_bwd_dq    writes D_i = dot(dO_i, O_i) for every row into `workspace`
+ *                and writes dQ in full.  Reads q, k, v, o, dout, lse.
+ *   fa_bwd_dkdv  writes dK and dV in full.  Reads q, k, v, dout, lse and the
+ *                D that a preceding fa_bwd_dq with the same problem left in
+ *                `workspace` (stream order is enough; the workspace must not
+ *                be reused in between).
+ * Arguments mean what they mean for fa_bwd; validation and errors are the
+ * same.
+ */
+fa_status fa_bwd_dq(fa_dtype dtype,
+                    const void* q, fa_strides q_strides,
+                    const void* k, fa_strides k_strides,
+                    const void* v, fa_strides v_strides,
+                    const void* o, fa_strides o_strides,
+                    const void* dout, fa_strides dout_strides,
+                    const float* lse,
+                    void* dq, fa_strides dq_strides,
+                    void* workspace, size_t workspace_bytes,
+                    int B, int H, int N, int d,
+                    float scale, int causal,
+                    const int32_t* seqlens_k,
+                    const uint8_t* block_mask, int mask_block,
+                    hipStream_t stream);
+
+fa_status fa_bwd_dkdv(fa_dtype dtype,
+                      const void* q, fa_strides q_strides,
+                      const void* k, fa_strides k_strides,
+                      const void* v, fa_strides v_strides,
+                      const void* dout, fa_strides dout_strides,
+                      const float* lse,
+                      void* dk, fa_strides dk_strides,
+                      void* dv, fa_strides dv_strides,
+                      void* workspace, size_t workspace_bytes,
+                      int B, int H, int N, int d,
+                      float scale, int causal,
+                      const int32_t* seqlens_k,
+                      const uint8_t* block_mask, int mask_block,
+                      hipStream_t stream);
+
 /* Static, human-readable name of a status code. */
 const char* fa_status_string(fa_status status);
 

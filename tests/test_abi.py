@@ -107,6 +107,48 @@ def test_bwd_rejects_bad_arguments(kw, status, msg):
     assert msg in fa.fa_last_error()
 
 
+def _bwd_dq(**kw):
+    lib = fa.load_library()
+    args = dict(dtype=0, q=A, sq=S, k=A, sk=S, v=A, sv=S, o=A, so=S, do=A, sdo=S, lse=A,
+                dq=A, sdq=S, ws=A, wsb=4096, B=1, H=1, N=1024, d=64, scale=0.125, causal=0,
+                seqlens=None, bmask=None, mb=128, stream=None)
+    args.update(kw)
+    return lib.fa_bwd_dq(*args.values())
+
+
+def _bwd_dkdv(**kw):
+    lib = fa.load_library()
+    args = dict(dtype=0, q=A, sq=S, k=A, sk=S, v=A, sv=S, do=A, sdo=S, lse=A, dk=A, sdk=S,
+                dv=A, sdv=S, ws=A, wsb=4096, B=1, H=1, N=1024, d=64, scale=0.125, causal=0,
+                seqlens=None, bmask=None, mb=128, stream=None)
+    args.update(kw)
+    return lib.fa_bwd_dkdv(*args.values())
+
+
+@pytest.mark.parametrize("kw,status,msg", [
+    (dict(dq=None), 1, "dq is NULL"),
+    (dict(o=A + 4), 1, "o is not 16-byte aligned"),
+    (dict(wsb=100), 1, "workspace too small"),
+    (dict(lse=None), 1, "lse is NULL"),
+    (dict(N=0), 1, "must be positive"),
+])
+def test_bwd_dq_rejects_bad_arguments(kw, status, msg):
+    assert _bwd_dq(**kw) == status
+    assert msg in fa.fa_last_error()
+
+
+@pytest.mark.parametrize("kw,status,msg", [
+    (dict(dk=None), 1, "dk is NULL"),
+    (dict(dv=A + 2), 1, "dv is not 16-byte aligned"),
+    (dict(ws=None), 1, "workspace is NULL"),
+    (dict(do=None), 1, "dout is NULL"),
+    (dict(d=128), 2, "head dimension"),
+])
+def test_bwd_dkdv_rejects_bad_arguments(kw, status, msg):
+    assert _bwd_dkdv(**kw) == status
+    assert msg in fa.fa_last_error()
+
+
 def test_missing_library_raises(tmp_path):
     with pytest.raises(RuntimeError, match="not found"):
         _load_fresh(str(tmp_path / "nope.so"))

@@ -37,12 +37,20 @@ def test_workload_pair_counts():
 
 
 def test_kernel_bytes():
-    f, b = bench.kernel_bytes(8, 12, 1024, 64, 2, None)
+    kb = bench.kernel_bytes(8, 12, 1024, 64, 2, None)
     t = 8 * 12 * 1024 * 64 * 2
-    assert f == 4 * t + 8 * 12 * 1024 * 4
-    assert b == 7 * t + 3 * 8 * 12 * 1024 * 4
-    f2, _ = bench.kernel_bytes(2, 1, 100, 64, 2, np.array([50, 100]))
-    assert f2 == 2 * (2 * 100 * 64 * 2) + 2 * (150 * 64 * 2) + 2 * 100 * 4
+    row = 8 * 12 * 1024 * 4
+    assert kb["fwd_bf16_kernel"] == 4 * t + row
+    assert kb["dq_kernel"] == 6 * t + 2 * row
+    assert kb["dkdv_kernel"] == 6 * t + 2 * row
+    kb2 = bench.kernel_bytes(2, 1, 100, 64, 2, np.array([50, 100]))
+    assert kb2["fwd_bf16_kernel"] == 2 * (2 * 100 * 64 * 2) + 2 * (150 * 64 * 2) + 2 * 100 * 4
+
+
+def test_kernel_flops_sum_to_the_method():
+    kf = bench.kernel_flops(64, 1000)
+    assert kf["fwd_bf16_kernel"] == 4 * 64 * 1000
+    assert kf["dq_kernel"] + kf["dkdv_kernel"] == 10 * 64 * 1000
 
 
 def test_more_than_one_gpu_is_refused(capsys):

@@ -246,6 +246,28 @@ def test_repeatable_bitwise():
         assert np.array_equal(to_np(a), to_np(b))
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_split_phases_equal_fused_call(dtype):
+    """fa_bwd_dq followed by fa_bwd_dkdv gives exactly what fa_bwd gives."""
+    import torch
+    import exact_io_aware_64_amd as fa
+    case = wl.random_case(2, 3, 333, 64, dtype=dtype, seed=31, causal=True, seqlens="random",
+                          block_keep_p=0.6)
+    q, k, v, do, sl, bm = device_inputs(case)
+    o, lse = gpu_forward(case, q, k, v, sl, bm)
+    g1 = gpu_backward(case, q, k, v, o, do, lse, sl, bm)
+    kw = dict(scale=case["scale"], causal=case["causal"], seqlens_k=sl, block_mask=bm,
+              mask_block=128)
+    code = fa.FA_BF16 if dtype == "bf16" else fa.FA_F32
+    ws = torch.empty(fa.fa_bwd_workspace_bytes(code, *q.shape), dtype=torch.uint8,
+                     device=q.device)
+    dq, dk, dv = (torch.full_like(q, float("nan")) for _ in range(3))
+    fa.fa_bwd_dq(q, k, v, o, do, lse, dq, ws, **kw)
+    fa.fa_bwd_dkdv(q, k, v, do, lse, dk, dv, ws, **kw)
+    for a, b in zip(g1, (dq, dk, dv)):
+        assert np.array_equal(to_np(a), to_np(b))
+
+
 def test_memory_linear_in_N():
     """Peak device memory of fwd + bwd is the inputs, outputs, L and the
     per-row workspace: linear in N, nothing N x N (at N = 65536 one bf16
