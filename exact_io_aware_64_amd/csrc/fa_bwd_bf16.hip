@@ -35,10 +35,15 @@ constexpr int kBK = 128;   // dkdv_kernel: key rows per workgroup
 
 template <bool CAUSAL, bool SEQLEN, bool BMASK>
 __global__ __launch_bounds__(256) void dq_kernel(BwdArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t s_k[2][kTile * kRowStride];
-  __shared__ __attribute__((aligned(16))) uint16_t s_v[2][kTile * kRowStride];
+  // Two buffers, each a K tile and a V tile (separate arrays so that the
+  // copies into one and the reads of the other never alias).
+  __shared__ __attribute__((aligned(16))) uint16_t s_k0[kTileElems];
+  __shared__ __attribute__((aligned(16))) uint16_t s_v0[kTileElems];
+  __shared__ __attribute__((aligned(16))) uint16_t s_k1[kTileElems];
+  __shared__ __attribute__((aligned(16))) uint16_t s_v1[kTileElems];
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = tid >> 6;
   const int r = lane & 31, hl = lane >> 5;
   const int BH = a.B * a.H;
   const int nqt = (a.N + kBQ - 1) / kBQ;
@@ -107,85 +112,121 @@ __global__ __launch_bounds__(256) void dq_kernel(BwdArgs a) {
 
   f32x16 acc[2] = {zero16(), zero16()};
 
-  // Staging: rows tid/8 and tid/8 + 32 of the K and V tiles, 16-byte column
-  // tid%8, row-major.  K^T operands come from transpose reads of the K tile.
-  const int sr = tid >> 3, sc = tid & 7;
-  const int k_off0 = sr * ssk + 16 * sc, k_off1 = (sr + 32) * ssk + 16 * sc;
-  const int v_off0 = sr * ssv + 16 * sc, v_off1 = (sr + 32) * ssv + 16 * sc;
-  const int trl = tr_lane_offset(lane);
-  uint4 kreg[2], vreg[2];
+  // Per-lane LDS offsets: K and V rows (A operands of S^T and dP^T) and K^T
+  // transpose reads (A operand of dQ^T).
+  int roff[4];
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) roff[ks] = row_off(r, hl, ks);
+  int troff[2][2];
+#pragma unroll
+  for (int hi = 0; hi < 2; ++hi)
+#pragma unroll
+    for (int db = 0; db < 2; ++db) troff[hi][db] = tr_off(lane, hi, db);
+
   auto tile_at = [&](int it) FA_INLINE -> int {
     if constexpr (BMASK) return tlist[it];
     return it;
   };
-  auto gload = [&](int t) FA_INLINE {
-    const int k0 = t * kTile;
-    kreg[0] = ldb16(rk, k_off0 + k0 * ssk);
-    kreg[1] = ldb16(rk, k_off1 + k0 * ssk);
-    vreg[0] = ldb16(rv, v_off0 + k0 * ssv);
-    vreg[1] = ldb16(rv, v_off1 + k0 * ssv);
-  };
-  auto swrite = [&](int buf) FA_INLINE {
-    store_row16(s_k[buf], sr, sc, kreg[0]);
-    store_row16(s_k[buf], sr + 32, sc, kreg[1]);
-    store_row16(s_v[buf], sr, sc, vreg[0]);
-    store_row16(s_v[buf], sr + 32, sc, vreg[1]);
+  auto stage = [&](int t, uint16_t* kt, uint16_t* vt) FA_INLINE {
+    stage_tile(rk, t * kTile, ssk, kt, w, lane);
+    stage_tile(rv, t * kTile, ssv, vt, w, lane);
   };
 
-  if (nlist > 0) {
-    gload(tile_at(0));
-    swrite(0);
-  }
-  // Every load issued so far (Q fragment, first tile) is complete here;
-  // saying so keeps the loop's wait counts from covering them.
+  // One 64-key tile as 24 MFMA issue slots separated by scheduling fences:
+  //   slots  0.. 7  S^T, dP^T of keys  0..31                 (MFMA)
+  //   slots  8..15  S^T, dP^T of keys 32..63                 (MFMA) | P, dS of keys 0..31
+  //   slots 16..23  dQ^T += K^T dS^T (steps 0..3)            (MFMA) | P, dS of keys 32..63
+  // with each LDS operand read four slots ahead.  dS of keys 32..47 is done
+  // by slot 19 and of 48..63 by slot 21, ahead of the steps that use them.
+  auto body = [&](auto mask_c, const uint16_t* kt, const uint16_t* vt, int k0) FA_INLINE {
+    constexpr bool MASK = decltype(mask_c)::value;
+    constexpr int kLead = 4;
+    f32x16 st[2] = {zero16(), zero16()}, dpt[2] = {zero16(), zero16()};
+    uint32_t pkd[4][4];  // bf16 pairs of dS per step
+    bf16x8 opa[24];
+    [[maybe_unused]] int lim = 0;
+    if constexpr (MASK) lim = (CAUSAL ? min(kv_len - 1, qi) : kv_len - 1) - k0 - 4 * hl;
+    // A operand of slot t
+    auto load_a = [&](int t) FA_INLINE {
+      if (t < 16) {
+        const int kb = t >> 3, ks = (t & 7) >> 1;
+        opa[t] = tile_row8((t & 1) ? vt : kt, 2048 * kb + roff[ks]);
+      } else {
+        const int stp = (t - 16) >> 1, db = t & 1;
+        opa[t] = tr_read(kt + 1024 * stp, troff[0][db], troff[1][db]);
+      }
+    };
+    // elements 2 ch, 2 ch + 1 of half kb: P = 2^(S c - L log2 e), dS = P (dP - D)
+    auto probs = [&](int kb, int ch) FA_INLINE {
+      float ds[2];
+#pragma unroll
+      for (int x = 0; x < 2; ++x) {
+        const int e = 2 * ch + x;
+        float sv = st[kb][e];
+        if constexpr (MASK) {
+          if (32 * kb + 8 * (e >> 2) + (e & 3) > lim) sv = -kInf;
+        }
+        const float p = fast_exp2(__builtin_fmaf(sv, c, -L2));
+        ds[x] = p * (dpt[kb][e] - Dq);
+      }
+      pkd[2 * kb + (ch >> 2)][ch & 3] = pack2(ds[0], ds[1]);
+    };
+
+#pragma unroll
+    for (int t = 0; t < kLead; ++t) load_a(t);
+    FA_FENCE();
+#pragma unroll
+    for (int t = 0; t < 24; ++t) {
+      if (t + kLead < 24) load_a(t + kLead);
+      if (t < 16) {
+        const int kb = t >> 3, ks = (t & 7) >> 1;
+        if (t & 1)
+          dpt[kb] = mfma32(opa[t], dof[ks], dpt[kb]);
+        else
+          st[kb] = mfma32(opa[t], qf[ks], st[kb]);
+      } else {
+        const int stp = (t - 16) >> 1, db = t & 1;
+        acc[db] = mfma32(opa[t], words_to_bf16x8(pkd[stp][0], pkd[stp][1], pkd[stp][2],
+                                                 pkd[stp][3]), acc[db]);
+      }
+      if (t >= 8 && t < 16) probs(0, t - 8);
+      if (t >= 16 && t < 20) {  // chunks 0..5 of half 1 over four slots
+        probs(1, (3 * (t - 16)) >> 1);
+        if ((t - 16) & 1) probs(1, ((3 * (t - 16)) >> 1) + 1);
+      }
+      if (t == 20 || t == 21) probs(1, t - 14);
+      FA_FENCE();
+    }
+  };
+
+  auto compute = [&](int it, const uint16_t* kt, const uint16_t* vt) FA_INLINE {
+    const int k0 = tile_at(it) * kTile;
+    const bool active = !CAUSAL || (k0 <= qw + 31);
+    if (active) {
+      const bool need_mask = (k0 + kTile > kv_len) || (CAUSAL && k0 + kTile - 1 > qw);
+      if (need_mask)
+        body(std::true_type{}, kt, vt, k0);
+      else
+        body(std::false_type{}, kt, vt, k0);
+    }
+  };
+
+  if (nlist > 0) stage(tile_at(0), s_k0, s_v0);
+  // Every load issued so far (fragments, first tile) is complete here;
+  // saying so also keeps the loop's wait counts from covering them.
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
-  for (int it = 0; it < nlist; ++it) {
-    const int buf = it & 1;
-    const int k0 = tile_at(it) * kTile;
-    if (it + 1 < nlist) gload(tile_at(it + 1));
-
-    const bool active = !CAUSAL || (k0 <= qw + 31);
-    if (active) {
-      const uint16_t* ks_ = s_k[buf];
-      const uint16_t* vs_ = s_v[buf];
-      f32x16 st[2] = {zero16(), zero16()}, dpt[2] = {zero16(), zero16()};
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks)
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          const int off = (32 * kb + r) * kRowStride + 16 * ks + 8 * hl;
-          st[kb] = mfma32(lds_row8(ks_ + off), qf[ks], st[kb]);
-          dpt[kb] = mfma32(lds_row8(vs_ + off), dof[ks], dpt[kb]);
-        }
-      const bool need_mask = (k0 + kTile > kv_len) || (CAUSAL && k0 + kTile - 1 > qw);
-      if (need_mask) {
-        const int last = CAUSAL ? min(kv_len - 1, qi) : kv_len - 1;
-        const int lim = last - k0 - 4 * hl;
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int e = 0; e < 16; ++e)
-            if (32 * kb + 8 * (e >> 2) + (e & 3) > lim) st[kb][e] = -kInf;
-      }
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const float p = fast_exp2(__builtin_fmaf(st[kb][e], c, -L2));
-          st[kb][e] = p * (dpt[kb][e] - Dq);
-        }
-      // dQ^T[d][q] += sum_key K[key][d] dS[q][key]
-#pragma unroll
-      for (int stp = 0; stp < 4; ++stp) {
-        const bf16x8 dsb = pack8(st[stp >> 1], 8 * (stp & 1));
-#pragma unroll
-        for (int db = 0; db < 2; ++db)
-          acc[db] = mfma32(tr_operand(ks_ + trl + 16 * stp * kRowStride + 32 * db), dsb, acc[db]);
-      }
-    }
-    if (it + 1 < nlist) swrite(buf ^ 1);
+  // Two tiles per trip so that each buffer is a fixed array.
+  for (int it = 0; it < nlist; it += 2) {
+    if (it + 1 < nlist) stage(tile_at(it + 1), s_k1, s_v1);
+    compute(it, s_k0, s_v0);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (it + 1 >= nlist) break;
+    if (it + 2 < nlist) stage(tile_at(it + 2), s_k0, s_v0);
+    compute(it + 1, s_k1, s_v1);
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   }
 
@@ -207,12 +248,18 @@ __global__ __launch_bounds__(256) void dq_kernel(BwdArgs a) {
 
 template <bool CAUSAL, bool SEQLEN, bool BMASK>
 __global__ __launch_bounds__(256) void dkdv_kernel(BwdArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t s_q[2][kTile * kRowStride];
-  __shared__ __attribute__((aligned(16))) uint16_t s_do[2][kTile * kRowStride];
-  __shared__ __attribute__((aligned(16))) float s_l2[2][kTile];
+  // Two buffers, each a Q tile and a dO tile (separate arrays so that the
+  // copies into one and the reads of the other never alias), plus -L / scale
+  // and -D of the tile's 64 rows.
+  __shared__ __attribute__((aligned(16))) uint16_t s_q0[kTileElems];
+  __shared__ __attribute__((aligned(16))) uint16_t s_do0[kTileElems];
+  __shared__ __attribute__((aligned(16))) uint16_t s_q1[kTileElems];
+  __shared__ __attribute__((aligned(16))) uint16_t s_do1[kTileElems];
+  __shared__ __attribute__((aligned(16))) float s_nl[2][kTile];  // -L / scale
   __shared__ __attribute__((aligned(16))) float s_nd[2][kTile];  // -D
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = tid >> 6;
   const int r = lane & 31, hl = lane >> 5;
   const int BH = a.B * a.H;
   const int id = blockIdx.x;
@@ -272,18 +319,22 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdArgs a) {
       }
     }
     const float c = a.scale_log2;
+    const float inv_scale = 1.f / a.scale;
     // Causal: element e of block qb holds query qs + 4*hl + off(qb, e) and is
     // visible iff off >= qs_lim - qs; keys past the sequence see nothing.
     const int key_lim = (kj < kv_len) ? (CAUSAL ? kj - 4 * hl : -(1 << 30)) : (1 << 30);
 
-    // Staging: rows tid/8 and tid/8 + 32 of the Q and dO tiles, 16-byte column
-    // tid%8, row-major (Q^T and dO^T operands come from transpose reads);
-    // threads 0..63 also fetch L (as log2 units) and -D of one row.
-    const int sr = tid >> 3, sc = tid & 7;
-    const int q_off0 = sr * ssq + 16 * sc, q_off1 = (sr + 32) * ssq + 16 * sc;
-    const int d_off0 = sr * ssdo + 16 * sc, d_off1 = (sr + 32) * ssdo + 16 * sc;
-    const int trl = tr_lane_offset(lane);
-    uint4 qreg[2], dreg[2];
+    // Per-lane LDS offsets: Q and dO rows (A operands of S and dP) and Q^T,
+    // dO^T transpose reads (A operands of dK^T and dV^T).
+    int roff[4];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) roff[ks] = row_off(r, hl, ks);
+    int troff[2][2];
+#pragma unroll
+    for (int hi = 0; hi < 2; ++hi)
+#pragma unroll
+      for (int db = 0; db < 2; ++db) troff[hi][db] = tr_off(lane, hi, db);
+
     // Raw L and D of row qs + tid (threads 0..63), converted only when they
     // are written to LDS so that no wait on the loads sits at the start of a
     // tile.  Rows past N read as 0 through the buffer resources.
@@ -295,12 +346,11 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdArgs a) {
       if constexpr (BMASK) return tlist[it];
       return qt_lo + it;
     };
-    auto gload = [&](int t) FA_INLINE {
+    // Q and dO tiles go straight to LDS; L and D through registers.
+    auto gload = [&](int t, uint16_t* qt_, uint16_t* dt_) FA_INLINE {
       const int qs = t * kTile;
-      qreg[0] = ldb16(rq, q_off0 + qs * ssq);
-      qreg[1] = ldb16(rq, q_off1 + qs * ssq);
-      dreg[0] = ldb16(rdo, d_off0 + qs * ssdo);
-      dreg[1] = ldb16(rdo, d_off1 + qs * ssdo);
+      stage_tile(rq, qs, ssq, qt_, w, lane);
+      stage_tile(rdo, qs, ssdo, dt_, w, lane);
       if (tid < kTile) {
         lrow = qs + tid;
         lraw = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rl, 4 * lrow, 0, 0));
@@ -308,14 +358,10 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdArgs a) {
       }
     };
     auto swrite = [&](int buf) FA_INLINE {
-      store_row16(s_q[buf], sr, sc, qreg[0]);
-      store_row16(s_q[buf], sr + 32, sc, qreg[1]);
-      store_row16(s_do[buf], sr, sc, dreg[0]);
-      store_row16(s_do[buf], sr + 32, sc, dreg[1]);
       if (tid < kTile) {
-        // +inf in log2 units makes every probability of a dead or missing row 0
+        // -inf makes every probability of a dead or missing row 0
         const bool live = lrow < a.N && lraw != -kInf;
-        s_l2[buf][tid] = live ? lraw * kLog2e : kInf;
+        s_nl[buf][tid] = live ? -lraw * inv_scale : -kInf;
         s_nd[buf][tid] = lrow < a.N ? -draw : 0.f;
       }
     };
@@ -329,69 +375,65 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdArgs a) {
     //   slots  8..15  S, dP of queries 32..63               (MFMA) | P, dS of 0..31
     //   slots 16..23  dV, dK contributions of queries 0..31 (MFMA) | P, dS of 32..63
     //   slots 24..31  dV, dK contributions of 32..63        (MFMA)
-    auto tile = [&](auto mask_c, int buf, int qs) FA_INLINE {
+    auto tile = [&](auto mask_c, int buf, const uint16_t* qs_, const uint16_t* ds_, int qs)
+        FA_INLINE {
       constexpr bool MASK = decltype(mask_c)::value;
       constexpr int kLead = 4;
-      const uint16_t* qs_ = s_q[buf];
-      const uint16_t* ds_ = s_do[buf];
-      f32x16 sc_[2] = {zero16(), zero16()}, dp[2];
+      f32x16 sc_[2], dp[2];
       uint32_t pkp[4][4], pkd[4][4];  // bf16 pairs of P and dS per step
-      f32x4 l4[2][4];
       bf16x8 opa[32];
       // A operand of slot t.
       auto load_a = [&](int t) FA_INLINE {
         if (t < 16) {
           const int qb = t >> 3, ks = (t & 7) >> 1;
-          const int off = (32 * qb + r) * kRowStride + 16 * ks + 8 * hl;
-          opa[t] = lds_row8(((t & 1) ? ds_ : qs_) + off);
+          opa[t] = tile_row8((t & 1) ? ds_ : qs_, 2048 * qb + roff[ks]);
         } else {
-          const int stp = (t - 16) >> 2, u = (t - 16) & 3;
-          const int off = trl + 16 * stp * kRowStride + 32 * (u >> 1);
-          opa[t] = tr_operand(((u & 1) ? qs_ : ds_) + off);
+          const int stp = (t - 16) >> 2, u = (t - 16) & 3, db = u >> 1;
+          opa[t] = tr_read(((u & 1) ? qs_ : ds_) + 1024 * stp, troff[0][db], troff[1][db]);
         }
       };
-      auto load_l = [&](int qb, int j) FA_INLINE {
-        l4[qb][j] = *reinterpret_cast<const f32x4*>(&s_l2[buf][32 * qb + 8 * j + 4 * hl]);
-      };
-      // dP accumulators start at -D (row of each element), so the MFMA
-      // leaves dP - D in them directly.
-      auto init_dp = [&](int qb) FA_INLINE {
+      // The accumulators start at the row constants of their elements: S at
+      // -L / scale and dP at -D, so the MFMAs leave S - L / scale (whose
+      // product with scale log2 e is the log2 probability) and dP - D.
+      auto init_acc = [&](int qb) FA_INLINE {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const f32x4 d4 = *reinterpret_cast<const f32x4*>(&s_nd[buf][32 * qb + 8 * j + 4 * hl]);
+          const int row = 32 * qb + 8 * j + 4 * hl;
+          const f32x4 l4 = *reinterpret_cast<const f32x4*>(&s_nl[buf][row]);
+          const f32x4 d4 = *reinterpret_cast<const f32x4*>(&s_nd[buf][row]);
 #pragma unroll
-          for (int i = 0; i < 4; ++i) dp[qb][4 * j + i] = d4[i];
+          for (int i = 0; i < 4; ++i) {
+            sc_[qb][4 * j + i] = l4[i];
+            dp[qb][4 * j + i] = d4[i];
+          }
         }
       };
-      // Elements 2 ch and 2 ch + 1 of half qb: P = 2^(S c - L log2 e),
+      // Elements 2 ch and 2 ch + 1 of half qb: P = 2^(c (S - L / scale)),
       // dS = P (dP - D), each pair rounded to bf16.
       auto probs = [&](int qb, int ch) FA_INLINE {
         float pv[2], dv2[2];
 #pragma unroll
         for (int x = 0; x < 2; ++x) {
           const int e = 2 * ch + x;
-          float sv = sc_[qb][e];
+          float sv = sc_[qb][e] * c;
           if constexpr (MASK) {
             if (32 * qb + 8 * (e >> 2) + (e & 3) < key_lim - qs) sv = -kInf;
           }
-          pv[x] = fast_exp2(__builtin_fmaf(sv, c, -l4[qb][e >> 2][e & 3]));
+          pv[x] = fast_exp2(sv);
           dv2[x] = dp[qb][e] * pv[x];
         }
         pkp[2 * qb + (ch >> 2)][ch & 3] = pack2(pv[0], pv[1]);
         pkd[2 * qb + (ch >> 2)][ch & 3] = pack2(dv2[0], dv2[1]);
       };
 
-      init_dp(0);
+      init_acc(0);
 #pragma unroll
       for (int t = 0; t < kLead; ++t) load_a(t);
-      load_l(0, 0);
-      __builtin_amdgcn_sched_barrier(0);
+      FA_FENCE();
 #pragma unroll
       for (int t = 0; t < 32; ++t) {
         if (t + kLead < 32) load_a(t + kLead);
-        if (t == 2) init_dp(1);
-        if (t >= 4 && t < 7) load_l(0, t - 3);
-        if (t >= 12 && t < 16) load_l(1, t - 12);
+        if (t == 2) init_acc(1);
         if (t < 16) {
           const int qb = t >> 3, ks = (t & 7) >> 1;
           if (t & 1)
@@ -400,42 +442,54 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdArgs a) {
             sc_[qb] = mfma32(opa[t], kf[ks], sc_[qb]);
         } else {
           const int stp = (t - 16) >> 2, u = (t - 16) & 3, db = u >> 1;
-          const bf16x8 bop = as_bf16x8(make_uint4(
-              (u & 1) ? pkd[stp][0] : pkp[stp][0], (u & 1) ? pkd[stp][1] : pkp[stp][1],
-              (u & 1) ? pkd[stp][2] : pkp[stp][2], (u & 1) ? pkd[stp][3] : pkp[stp][3]));
+          const bf16x8 bop = (u & 1) ? words_to_bf16x8(pkd[stp][0], pkd[stp][1], pkd[stp][2],
+                                                       pkd[stp][3])
+                                     : words_to_bf16x8(pkp[stp][0], pkp[stp][1], pkp[stp][2],
+                                                       pkp[stp][3]);
           if (u & 1)
             dkt[db] = mfma32(opa[t], bop, dkt[db]);
           else
             dvt[db] = mfma32(opa[t], bop, dvt[db]);
         }
         if (t >= 8 && t < 24) probs((t - 8) >> 3, (t - 8) & 7);
-        __builtin_amdgcn_sched_barrier(0);
+        FA_FENCE();
       }
     };
 
-    if (nlist > 0) {
-      gload(tile_at(0));
-      swrite(0);
-    }
-    // Every load issued so far (K, V fragments, first tile) is complete here;
-    // saying so keeps the loop's wait counts from covering them.
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-
-    for (int it = 0; it < nlist; ++it) {
-      const int buf = it & 1;
+    auto compute = [&](int it, int buf, const uint16_t* qs_, const uint16_t* ds_) FA_INLINE {
       const int qs = tile_at(it) * kTile;
-      if (it + 1 < nlist) gload(tile_at(it + 1));
-
       const bool active = !CAUSAL || (qs + kTile - 1 >= kw);
       if (active) {
         const bool need_mask = (kw + 32 > kv_len) || (CAUSAL && kw + 31 > qs);
         if (need_mask)
-          tile(std::true_type{}, buf, qs);
+          tile(std::true_type{}, buf, qs_, ds_, qs);
         else
-          tile(std::false_type{}, buf, qs);
+          tile(std::false_type{}, buf, qs_, ds_, qs);
       }
-      if (it + 1 < nlist) swrite(buf ^ 1);
+    };
+
+    if (nlist > 0) {
+      gload(tile_at(0), s_q0, s_do0);
+      __builtin_amdgcn_s_waitcnt(0);
+      swrite(0);
+    }
+    // Every load issued so far (K, V fragments, first tile) is complete here;
+    // saying so also keeps the loop's wait counts from covering them.
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+
+    // Two tiles per trip so that each buffer is a fixed array.
+    for (int it = 0; it < nlist; it += 2) {
+      if (it + 1 < nlist) gload(tile_at(it + 1), s_q1, s_do1);
+      compute(it, 0, s_q0, s_do0);
+      __builtin_amdgcn_s_waitcnt(0);
+      if (it + 1 < nlist) swrite(1);
+      __syncthreads();
+      if (it + 1 >= nlist) break;
+      if (it + 2 < nlist) gload(tile_at(it + 2), s_q0, s_do0);
+      compute(it + 1, 1, s_q1, s_do1);
+      __builtin_amdgcn_s_waitcnt(0);
+      if (it + 2 < nlist) swrite(0);
       __syncthreads();
     }
   }
