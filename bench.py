@@ -11,10 +11,18 @@ FLOP convention (algorithmic work over visible (query, key) pairs; masked-out
 tiles are never credited): forward 4*d*pairs, backward 10*d*pairs.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--cpu-baseline off]
+
+HBM traffic of the dominant kernel comes from rocprofv3 counter runs kept in
+profiles/hbm_traffic_<workload>.json (written by --pmc-summary from a
+FETCH_SIZE run and a WRITE_SIZE run of this script, scaled by the same
+counters read on a plain copy of known size, --mode copy); it is reported
+only while the kernel's sources still hash to the value recorded there.
 """
 from __future__ import annotations
 
 import argparse
+import csv
+import hashlib
 import json
 import os
 import sys
@@ -117,16 +125,21 @@ def run_gpu(w: wl.Workload, inp: dict, steps: int, warmup: int):
     kw = dict(scale=w.scale, causal=w.causal, seqlens_k=sl, block_mask=bm, mask_block=128)
     stream = torch.cuda.current_stream(dev)
 
+    # argument marshalling done once, so the host keeps ahead of the GPU
+    fwd = fa.prepare_fwd(q, k, v, o, lse, **kw)
+    bdq = fa.prepare_bwd_dq(q, k, v, o, do, lse, dq, ws, **kw)
+    bdkdv = fa.prepare_bwd_dkdv(q, k, v, do, lse, dk, dv, ws, **kw)
+
     def step(ev=None):
         if ev is not None:
             ev[0].record(stream)
-        fa.fa_fwd(q, k, v, o, lse, **kw)
+        fwd()
         if ev is not None:
             ev[1].record(stream)
-        fa.fa_bwd_dq(q, k, v, o, do, lse, dq, ws, **kw)
+        bdq()
         if ev is not None:
             ev[2].record(stream)
-        fa.fa_bwd_dkdv(q, k, v, do, lse, dk, dv, ws, **kw)
+        bdkdv()
         if ev is not None:
             ev[3].record(stream)
 
@@ -222,6 +235,121 @@ def copy_calibration(mib: int, steps: int, warmup: int) -> int:
     return 0
 
 
+# ------------------------------------------------------------ HBM traffic
+
+KERNEL_SOURCES = {
+    "fwd_bf16_kernel": ("fa_fwd_bf16.hip",),
+    "dq_kernel": ("fa_bwd_bf16.hip",),
+    "dkdv_kernel": ("fa_bwd_bf16.hip",),
+}
+COMMON_SOURCES = ("fa_device.h", "fa_internal.h")
+
+
+def kernel_source_hash(kernel: str) -> str:
+    """sha256 over the sources a kernel is compiled from and the build flags."""
+    pkg = os.path.join(ROOT, "exact_io_aware_64_amd")
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[kernel] + COMMON_SOURCES:
+        with open(os.path.join(pkg, "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    with open(os.path.join(pkg, "build.py"), "rb") as fh:
+        h.update(fh.read())
+    return h.hexdigest()
+
+
+def _short_kernel_name(name: str) -> str:
+    name = name.replace("void ", "").replace("fa::(anonymous namespace)::", "")
+    return name.split("(")[0].split("<")[0].strip()
+
+
+def read_counter_csv(path: str, counter: str):
+    """Mean value per dispatch of `counter` for each kernel of a rocprofv3
+    counter_collection.csv, keyed by the kernel's short name."""
+    per = {}
+    with open(path) as fh:
+        for row in csv.DictReader(fh):
+            if row["Counter_Name"] != counter:
+                continue
+            k = _short_kernel_name(row["Kernel_Name"])
+            per.setdefault(k, {}).setdefault(row["Dispatch_Id"], 0.0)
+            per[k][row["Dispatch_Id"]] += float(row["Counter_Value"])
+    return {k: (float(np.mean(list(v.values()))), len(v)) for k, v in per.items()}
+
+
+def pmc_summary(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, workload, copy_bytes,
+                command):
+    """Builds the traffic record: per-kernel FETCH_SIZE / WRITE_SIZE (KiB per
+    dispatch) scaled by what the same counters read for a copy kernel that
+    moves copy_bytes in and copy_bytes out."""
+    f = read_counter_csv(fetch_csv, "FETCH_SIZE")
+    wr = read_counter_csv(write_csv, "WRITE_SIZE")
+    cf = read_counter_csv(copy_fetch_csv, "FETCH_SIZE")
+    cw = read_counter_csv(copy_write_csv, "WRITE_SIZE")
+    # the copy is the dispatch with the largest counter value
+    cf_kib = max(v for v, _ in cf.values())
+    cw_kib = max(v for v, _ in cw.values())
+    f_fetch = copy_bytes / (cf_kib * 1024.0)
+    f_write = copy_bytes / (cw_kib * 1024.0)
+    kernels = {}
+    for k in KERNEL_SOURCES:
+        if k not in f or k not in wr:
+            continue
+        fk, nf = f[k]
+        wk, nw = wr[k]
+        kernels[k] = dict(fetch_kib=fk, write_kib=wk, dispatches=[nf, nw],
+                          fetch_bytes=fk * 1024.0 * f_fetch, write_bytes=wk * 1024.0 * f_write,
+                          bytes_per_launch=fk * 1024.0 * f_fetch + wk * 1024.0 * f_write,
+                          source_sha256=kernel_source_hash(k))
+    return dict(workload=workload, command=command,
+                copy_calibration=dict(bytes=copy_bytes, fetch_kib=cf_kib, write_kib=cw_kib,
+                                      fetch_factor=f_fetch, write_factor=f_write),
+                kernels=kernels)
+
+
+def traffic_for(kernel: str, workload: str):
+    """Measured HBM bytes per launch of `kernel` on `workload`, or None when
+    no record exists or the kernel changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", f"hbm_traffic_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        rec = json.load(fh)
+    ent = rec.get("kernels", {}).get(kernel)
+    if not ent or ent.get("source_sha256") != kernel_source_hash(kernel):
+        return None
+    return float(ent["bytes_per_launch"])
+
+
+def trace_summary(stats_csv: str, bench_log: str, workload: str, command: str) -> str:
+    """Markdown summary of a rocprofv3 --kernel-trace --stats run of this
+    script: per-kernel launch statistics and the JSON line the run printed."""
+    rows = []
+    with open(stats_csv) as fh:
+        for row in csv.DictReader(fh):
+            rows.append((_short_kernel_name(row["Name"]), int(row["Calls"]),
+                         float(row["AverageNs"]) / 1e3, float(row["MinNs"]) / 1e3,
+                         float(row["MaxNs"]) / 1e3, float(row["Percentage"])))
+    line = None
+    with open(bench_log) as fh:
+        for l in fh:
+            if l.startswith("{"):
+                line = json.loads(l)
+    out = [f"# Kernel trace: {workload}", "", "Command (repository root, MI355X, `TMPDIR=/tmp`):",
+           "", "```", command, "```", "",
+           "| kernel | calls | avg us | min us | max us | % time |", "|---|---|---|---|---|---|"]
+    for k, n, av, mn, mx, pc in rows:
+        out.append(f"| {k} | {n} | {av:.2f} | {mn:.2f} | {mx:.2f} | {pc:.2f} |")
+    if line:
+        km = {k: round(v * 1e3, 2) for k, v in line["kernel_ms"].items()}
+        out += ["", "Bench line of the same run (HIP events on the launch stream, us per launch):",
+                "", f"- kernels: {km}",
+                f"- fwd {line['fwd_tflops']:.1f} TFLOP/s, bwd {line['bwd_tflops']:.1f} TFLOP/s, "
+                f"fwd+bwd {line['value']:.1f} TFLOP/s ({100 * line['fwdbwd_frac_peak']:.1f} % of "
+                f"{line['peak_tflops']})",
+                f"- roofline: {json.dumps(line['roofline'])}"]
+    return "\n".join(out) + "\n"
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -232,7 +360,30 @@ def main(argv=None):
     ap.add_argument("--mode", default="attention", choices=["attention", "copy"],
                     help="copy: time a plain 1 GiB device copy (counter calibration)")
     ap.add_argument("--copy-mib", type=int, default=1024)
+    ap.add_argument("--pmc-summary", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV",
+                                                     "COPY_FETCH_CSV", "COPY_WRITE_CSV"),
+                    help="summarise rocprofv3 FETCH_SIZE / WRITE_SIZE runs of this script "
+                         "(attention and --mode copy) into profiles/hbm_traffic_<workload>.json")
+    ap.add_argument("--pmc-command", default="",
+                    help="the rocprofv3 commands that produced the --pmc-summary inputs")
+    ap.add_argument("--trace-summary", nargs=2, metavar=("KERNEL_STATS_CSV", "BENCH_LOG"),
+                    help="write profiles/kernel_trace_<workload>.md from a rocprofv3 "
+                         "--kernel-trace --stats run of this script")
     args = ap.parse_args(argv)
+    if args.trace_summary:
+        md = trace_summary(*args.trace_summary, workload=args.workload, command=args.pmc_command)
+        with open(os.path.join(ROOT, "profiles", f"kernel_trace_{args.workload}.md"), "w") as fh:
+            fh.write(md)
+        print(md)
+        return 0
+    if args.pmc_summary:
+        rec = pmc_summary(*args.pmc_summary, workload=args.workload,
+                          copy_bytes=args.copy_mib << 20, command=args.pmc_command)
+        out = os.path.join(ROOT, "profiles", f"hbm_traffic_{args.workload}.json")
+        with open(out, "w") as fh:
+            json.dump(rec, fh, indent=1)
+        print(json.dumps(rec["kernels"]), flush=True)
+        return 0
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures one GPU only: the attention path needs no collective and "
@@ -274,7 +425,7 @@ def main(argv=None):
         ach = kbytes[dom] / (ms * 1e-3) / 1e9
         roofline = dict(kernel=dom, bound="hbm", achieved=ach, peak=PEAK_HBM_GBS, unit="GB/s",
                         frac=ach / PEAK_HBM_GBS)
-    roofline.update(traffic=None, flops_per_launch=kflops[dom],
+    roofline.update(traffic=traffic_for(dom, w.name), flops_per_launch=kflops[dom],
                     compulsory_bytes_per_launch=kbytes[dom], launch_ms=ms)
 
     base = None

@@ -19,4 +19,7 @@ from ._binding import (  # noqa: F401
     fa_status_string,
     forward,
     load_library,
+    prepare_bwd_dkdv,
+    prepare_bwd_dq,
+    prepare_fwd,
 )

@@ -192,6 +192,66 @@ def fa_bwd_dkdv(q, k, v, dout, lse, dk, dv, workspace, *, scale: float, causal: 
     _check(st)
 
 
+# ---------------------------------------------------------- prepared calls
+
+class Prepared:
+    """One C-ABI call with every argument converted once: calling it costs a
+    single ctypes call, so a tight loop of launches is not held back by the
+    host.  Tensors must stay alive (and keep their storage) while it is used."""
+
+    def __init__(self, fn, args, keep):
+        self._fn = fn
+        self._args = args
+        self._keep = keep  # the tensors whose pointers are baked into args
+
+    def __call__(self) -> None:
+        _check(self._fn(*self._args))
+
+
+def prepare_fwd(q, k, v, o, lse, *, scale: float, causal: bool = False, seqlens_k=None,
+                block_mask=None, mask_block: int = 128, stream=None) -> Prepared:
+    """fa_fwd with fixed arguments (see fa_fwd)."""
+    lib = load_library()
+    B, H, N, d = _check_like(q, (("k", k), ("v", v), ("o", o)))
+    if tuple(lse.shape) != (B, H, N) or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous fp32 [B, H, N] tensor")
+    args = (_dtype_code(q), _ptr(q), _strides(q), _ptr(k), _strides(k), _ptr(v), _strides(v),
+            _ptr(o), _strides(o), _ptr(lse), B, H, N, d, float(scale), int(bool(causal)),
+            _ptr(seqlens_k), _ptr(block_mask), int(mask_block), _stream(q, stream))
+    return Prepared(lib.fa_fwd, args, (q, k, v, o, lse, seqlens_k, block_mask))
+
+
+def prepare_bwd_dq(q, k, v, o, dout, lse, dq, workspace, *, scale: float, causal: bool = False,
+                   seqlens_k=None, block_mask=None, mask_block: int = 128,
+                   stream=None) -> Prepared:
+    """fa_bwd_dq with fixed arguments (see fa_bwd_dq)."""
+    lib = load_library()
+    B, H, N, d = _check_like(q, (("k", k), ("v", v), ("o", o), ("dout", dout), ("dq", dq)))
+    nbytes = workspace.numel() * workspace.element_size()
+    args = (_dtype_code(q), _ptr(q), _strides(q), _ptr(k), _strides(k), _ptr(v), _strides(v),
+            _ptr(o), _strides(o), _ptr(dout), _strides(dout), _ptr(lse), _ptr(dq), _strides(dq),
+            _ptr(workspace), nbytes, B, H, N, d, float(scale), int(bool(causal)),
+            _ptr(seqlens_k), _ptr(block_mask), int(mask_block), _stream(q, stream))
+    return Prepared(lib.fa_bwd_dq, args,
+                    (q, k, v, o, dout, lse, dq, workspace, seqlens_k, block_mask))
+
+
+def prepare_bwd_dkdv(q, k, v, dout, lse, dk, dv, workspace, *, scale: float,
+                     causal: bool = False, seqlens_k=None, block_mask=None,
+                     mask_block: int = 128, stream=None) -> Prepared:
+    """fa_bwd_dkdv with fixed arguments (see fa_bwd_dkdv)."""
+    lib = load_library()
+    B, H, N, d = _check_like(q, (("k", k), ("v", v), ("dout", dout), ("dk", dk), ("dv", dv)))
+    nbytes = workspace.numel() * workspace.element_size()
+    args = (_dtype_code(q), _ptr(q), _strides(q), _ptr(k), _strides(k), _ptr(v), _strides(v),
+            _ptr(dout), _strides(dout), _ptr(lse), _ptr(dk), _strides(dk), _ptr(dv),
+            _strides(dv), _ptr(workspace), nbytes, B, H, N, d, float(scale),
+            int(bool(causal)), _ptr(seqlens_k), _ptr(block_mask), int(mask_block),
+            _stream(q, stream))
+    return Prepared(lib.fa_bwd_dkdv, args,
+                    (q, k, v, dout, lse, dk, dv, workspace, seqlens_k, block_mask))
+
+
 # --------------------------------------------- allocating convenience calls
 
 def forward(q, k, v, *, scale: float, causal: bool = False, seqlens_k=None, block_mask=None,

@@ -268,6 +268,27 @@ def test_split_phases_equal_fused_call(dtype):
         assert np.array_equal(to_np(a), to_np(b))
 
 
+def test_prepared_calls_equal_direct_calls():
+    """The binding's prepared calls (arguments converted once) launch exactly
+    what the direct calls launch."""
+    import torch
+    import exact_io_aware_64_amd as fa
+    case = wl.random_case(2, 2, 257, 64, seed=41, causal=True, seqlens="random")
+    q, k, v, do, sl, bm = device_inputs(case)
+    o1, l1 = gpu_forward(case, q, k, v, sl, bm)
+    g1 = gpu_backward(case, q, k, v, o1, do, l1, sl, bm)
+    kw = dict(scale=case["scale"], causal=True, seqlens_k=sl, block_mask=bm)
+    o2, l2 = torch.empty_like(q), torch.empty_like(l1)
+    dq, dk, dv = (torch.empty_like(q) for _ in range(3))
+    ws = torch.empty(fa.fa_bwd_workspace_bytes(fa.FA_BF16, *q.shape), dtype=torch.uint8,
+                     device=q.device)
+    fa.prepare_fwd(q, k, v, o2, l2, **kw)()
+    fa.prepare_bwd_dq(q, k, v, o2, do, l2, dq, ws, **kw)()
+    fa.prepare_bwd_dkdv(q, k, v, do, l2, dk, dv, ws, **kw)()
+    for a, b in zip((o1, l1) + tuple(g1), (o2, l2, dq, dk, dv)):
+        assert np.array_equal(to_np(a), to_np(b))
+
+
 def test_memory_linear_in_N():
     """Peak device memory of fwd + bwd is the inputs, outputs, L and the
     per-row workspace: linear in N, nothing N x N (at N = 65536 one bf16
