@@ -2,7 +2,8 @@
 """Attention throughput on one MI355X.
 
 One step = the whole hot path on one batch: fa_fwd (scores, mask, online
-softmax, O and L) followed by fa_bwd (D, dQ, dK, dV recomputed from L).
+softmax, O and L) followed by fa_bwd (D, dQ, dK, dV recomputed from L), one
+kernel launch each.
 Prints one JSON line with forward+backward TFLOP/s (the value), forward
 TFLOP/s, both as fractions of the bf16 dense MFMA peak, a roofline entry for
 the dominant kernel and the fp64 CPU oracle timed on the host as a baseline.
@@ -75,37 +76,35 @@ def visible_pairs(N: int, H: int, causal: bool, seqlens, block_mask, mask_block:
 def kernel_bytes(B, H, N, d, esize, seqlens):
     """Compulsory HBM bytes per launch of each kernel: every tensor the kernel
     must read or write once (keys and values only up to each sequence's key
-    length), plus the fp32 row statistics L and D."""
+    length), plus the fp32 row statistic L."""
     t = B * H * N * d * esize
     kv_valid = H * d * esize * (B * N if seqlens is None else int(np.minimum(seqlens, N).sum()))
     rowstat = B * H * N * 4
     return {
-        "fwd_bf16_kernel": 2 * t + 2 * kv_valid + rowstat,         # Q, O; K, V; L
-        "dq_kernel": 4 * t + 2 * kv_valid + 2 * rowstat,           # Q, O, dO, dQ; K, V; L, D
-        "dkdv_kernel": 4 * t + 2 * kv_valid + 2 * rowstat,         # Q, dO, dK, dV; K, V; L, D
+        "fwd_bf16_kernel": 2 * t + 2 * kv_valid + rowstat,     # Q, O; K, V; L
+        "bwd_kernel": 6 * t + 2 * kv_valid + rowstat,          # Q, O, dO, dQ, dK, dV; K, V; L
     }
 
 
 def kernel_flops(d, pairs):
-    """Algorithmic FLOPs per launch.  The method's backward pass is five
-    products over visible pairs (S recomputed, dV, dP, dQ, dK; 2*d each): the
-    dK/dV kernel performs four of them, the dQ kernel the fifth (its own
-    recomputation of S and dP duplicates work and is not credited)."""
-    return {"fwd_bf16_kernel": 4.0 * d * pairs, "dq_kernel": 2.0 * d * pairs,
-            "dkdv_kernel": 8.0 * d * pairs}
+    """Algorithmic FLOPs per launch: the forward pass is two products over the
+    visible pairs (S, O; 2*d each), the backward pass five (S recomputed, dV,
+    dP, dQ, dK).  The backward kernel's second recomputation of S and dP (in
+    its dQ workgroups) duplicates work and is not credited."""
+    return {"fwd_bf16_kernel": 4.0 * d * pairs, "bwd_kernel": 10.0 * d * pairs}
 
 
 # ------------------------------------------------------------------- timing
 
-KERNELS = ("fwd_bf16_kernel", "dq_kernel", "dkdv_kernel")
+KERNELS = ("fwd_bf16_kernel", "bwd_kernel")
 
 
 def run_gpu(w: wl.Workload, inp: dict, steps: int, warmup: int):
-    """Times `steps` steps after `warmup` untimed ones.  One step is fa_fwd,
-    then the two phases of the backward pass (fa_bwd_dq, fa_bwd_dkdv), each a
-    single kernel launch on the current stream; HIP events recorded on that
-    stream between the launches give each kernel's device time, and the wall
-    clock around the whole timed region gives the step time."""
+    """Times `steps` steps after `warmup` untimed ones.  One step is fa_fwd
+    then fa_bwd, each a single kernel launch on the current stream; HIP
+    events recorded on that stream around the launches give each kernel's
+    device time, and the wall clock around the whole timed region gives the
+    step time."""
     import torch
     import exact_io_aware_64_amd as fa
 
@@ -119,16 +118,11 @@ def run_gpu(w: wl.Workload, inp: dict, steps: int, warmup: int):
     o = torch.empty_like(q)
     lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
-    code = fa.FA_BF16 if w.dtype == "bf16" else fa.FA_F32
-    ws = torch.empty(fa.fa_bwd_workspace_bytes(code, w.B, w.H, w.N, w.d), dtype=torch.uint8,
-                     device=dev)
     kw = dict(scale=w.scale, causal=w.causal, seqlens_k=sl, block_mask=bm, mask_block=128)
     stream = torch.cuda.current_stream(dev)
-
     # argument marshalling done once, so the host keeps ahead of the GPU
     fwd = fa.prepare_fwd(q, k, v, o, lse, **kw)
-    bdq = fa.prepare_bwd_dq(q, k, v, o, do, lse, dq, ws, **kw)
-    bdkdv = fa.prepare_bwd_dkdv(q, k, v, do, lse, dk, dv, ws, **kw)
+    bwd = fa.prepare_bwd(q, k, v, o, do, lse, dq, dk, dv, **kw)
 
     def step(ev=None):
         if ev is not None:
@@ -136,16 +130,13 @@ def run_gpu(w: wl.Workload, inp: dict, steps: int, warmup: int):
         fwd()
         if ev is not None:
             ev[1].record(stream)
-        bdq()
+        bwd()
         if ev is not None:
             ev[2].record(stream)
-        bdkdv()
-        if ev is not None:
-            ev[3].record(stream)
 
     for _ in range(warmup):
         step()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for e in evs:
@@ -239,8 +230,7 @@ def copy_calibration(mib: int, steps: int, warmup: int) -> int:
 
 KERNEL_SOURCES = {
     "fwd_bf16_kernel": ("fa_fwd_bf16.hip",),
-    "dq_kernel": ("fa_bwd_bf16.hip",),
-    "dkdv_kernel": ("fa_bwd_bf16.hip",),
+    "bwd_kernel": ("fa_bwd_bf16.hip",),
 }
 COMMON_SOURCES = ("fa_device.h", "fa_internal.h")
 
@@ -402,7 +392,7 @@ def main(argv=None):
 
     wall_ms, kernel_ms, props, outs = run_gpu(w, inp, args.steps, args.warmup)
     fwd_ms = kernel_ms["fwd_bf16_kernel"]
-    bwd_ms = kernel_ms["dq_kernel"] + kernel_ms["dkdv_kernel"]
+    bwd_ms = kernel_ms["bwd_kernel"]
     peak = PEAK_TFLOPS[w.dtype]
     tf_fb = (flops_f + flops_b) / (wall_ms * 1e-3) / 1e12
     tf_f = flops_f / (fwd_ms * 1e-3) / 1e12

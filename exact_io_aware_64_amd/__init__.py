@@ -19,7 +19,6 @@ from ._binding import (  # noqa: F401
     fa_status_string,
     forward,
     load_library,
-    prepare_bwd_dkdv,
-    prepare_bwd_dq,
+    prepare_bwd,
     prepare_fwd,
 )

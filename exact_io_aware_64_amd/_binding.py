@@ -58,8 +58,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.fa_bwd_dq.argtypes = [I, P, S, P, S, P, S, P, S, P, S, P, P, S, P, ctypes.c_size_t,
                               I, I, I, I, F, I, P, P, I, P]
     lib.fa_bwd_dkdv.restype = I
-    lib.fa_bwd_dkdv.argtypes = [I, P, S, P, S, P, S, P, S, P, P, S, P, S, P, ctypes.c_size_t,
-                                I, I, I, I, F, I, P, P, I, P]
+    lib.fa_bwd_dkdv.argtypes = [I, P, S, P, S, P, S, P, S, P, S, P, P, S, P, S, P,
+                                ctypes.c_size_t, I, I, I, I, F, I, P, P, I, P]
     lib.fa_bwd_workspace_bytes.restype = ctypes.c_size_t
     lib.fa_bwd_workspace_bytes.argtypes = [I, I, I, I, I]
     lib.fa_status_string.restype = ctypes.c_char_p
@@ -116,6 +116,10 @@ def _stream(t, stream):
     return _torch().cuda.current_stream(t.device).cuda_stream
 
 
+def _nbytes(t) -> int:
+    return 0 if t is None else t.numel() * t.element_size()
+
+
 def _check(st: int):
     if st != FA_OK:
         raise FaError(st, fa_last_error())
@@ -148,14 +152,14 @@ def _check_like(q, named):
     return B, H, N, d
 
 
-def fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, workspace, *, scale: float,
+def fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, workspace=None, *, scale: float,
            causal: bool = False, seqlens_k=None, block_mask=None, mask_block: int = 128,
            stream=None) -> None:
     """Calls fa_bwd; dq, dk, dv are written in full."""
     lib = load_library()
     B, H, N, d = _check_like(q, (("k", k), ("v", v), ("o", o), ("dout", dout), ("dq", dq),
                                  ("dk", dk), ("dv", dv)))
-    nbytes = workspace.numel() * workspace.element_size()
+    nbytes = _nbytes(workspace)
     st = lib.fa_bwd(_dtype_code(q), _ptr(q), _strides(q), _ptr(k), _strides(k), _ptr(v),
                     _strides(v), _ptr(o), _strides(o), _ptr(dout), _strides(dout), _ptr(lse),
                     _ptr(dq), _strides(dq), _ptr(dk), _strides(dk), _ptr(dv), _strides(dv),
@@ -164,12 +168,13 @@ def fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, workspace, *, scale: float,
     _check(st)
 
 
-def fa_bwd_dq(q, k, v, o, dout, lse, dq, workspace, *, scale: float, causal: bool = False,
-              seqlens_k=None, block_mask=None, mask_block: int = 128, stream=None) -> None:
-    """Calls fa_bwd_dq: writes D into the workspace and dq in full."""
+def fa_bwd_dq(q, k, v, o, dout, lse, dq, workspace=None, *, scale: float,
+              causal: bool = False, seqlens_k=None, block_mask=None, mask_block: int = 128,
+              stream=None) -> None:
+    """Calls fa_bwd_dq: writes dq in full."""
     lib = load_library()
     B, H, N, d = _check_like(q, (("k", k), ("v", v), ("o", o), ("dout", dout), ("dq", dq)))
-    nbytes = workspace.numel() * workspace.element_size()
+    nbytes = _nbytes(workspace)
     st = lib.fa_bwd_dq(_dtype_code(q), _ptr(q), _strides(q), _ptr(k), _strides(k), _ptr(v),
                        _strides(v), _ptr(o), _strides(o), _ptr(dout), _strides(dout),
                        _ptr(lse), _ptr(dq), _strides(dq), _ptr(workspace), nbytes, B, H, N, d,
@@ -178,14 +183,17 @@ def fa_bwd_dq(q, k, v, o, dout, lse, dq, workspace, *, scale: float, causal: boo
     _check(st)
 
 
-def fa_bwd_dkdv(q, k, v, dout, lse, dk, dv, workspace, *, scale: float, causal: bool = False,
-                seqlens_k=None, block_mask=None, mask_block: int = 128, stream=None) -> None:
-    """Calls fa_bwd_dkdv: reads D from the workspace, writes dk and dv in full."""
+def fa_bwd_dkdv(q, k, v, o, dout, lse, dk, dv, workspace=None, *, scale: float,
+                causal: bool = False, seqlens_k=None, block_mask=None, mask_block: int = 128,
+                stream=None) -> None:
+    """Calls fa_bwd_dkdv: writes dk and dv in full."""
     lib = load_library()
-    B, H, N, d = _check_like(q, (("k", k), ("v", v), ("dout", dout), ("dk", dk), ("dv", dv)))
-    nbytes = workspace.numel() * workspace.element_size()
+    B, H, N, d = _check_like(q, (("k", k), ("v", v), ("o", o), ("dout", dout), ("dk", dk),
+                                 ("dv", dv)))
+    nbytes = _nbytes(workspace)
     st = lib.fa_bwd_dkdv(_dtype_code(q), _ptr(q), _strides(q), _ptr(k), _strides(k), _ptr(v),
-                         _strides(v), _ptr(dout), _strides(dout), _ptr(lse), _ptr(dk),
+                         _strides(v), _ptr(o), _strides(o), _ptr(dout), _strides(dout),
+                         _ptr(lse), _ptr(dk),
                          _strides(dk), _ptr(dv), _strides(dv), _ptr(workspace), nbytes, B, H,
                          N, d, float(scale), int(bool(causal)), _ptr(seqlens_k),
                          _ptr(block_mask), int(mask_block), _stream(q, stream))
@@ -221,35 +229,20 @@ def prepare_fwd(q, k, v, o, lse, *, scale: float, causal: bool = False, seqlens_
     return Prepared(lib.fa_fwd, args, (q, k, v, o, lse, seqlens_k, block_mask))
 
 
-def prepare_bwd_dq(q, k, v, o, dout, lse, dq, workspace, *, scale: float, causal: bool = False,
-                   seqlens_k=None, block_mask=None, mask_block: int = 128,
-                   stream=None) -> Prepared:
-    """fa_bwd_dq with fixed arguments (see fa_bwd_dq)."""
+def prepare_bwd(q, k, v, o, dout, lse, dq, dk, dv, workspace=None, *, scale: float,
+                causal: bool = False, seqlens_k=None, block_mask=None, mask_block: int = 128,
+                stream=None) -> Prepared:
+    """fa_bwd with fixed arguments (see fa_bwd)."""
     lib = load_library()
-    B, H, N, d = _check_like(q, (("k", k), ("v", v), ("o", o), ("dout", dout), ("dq", dq)))
-    nbytes = workspace.numel() * workspace.element_size()
+    B, H, N, d = _check_like(q, (("k", k), ("v", v), ("o", o), ("dout", dout), ("dq", dq),
+                                 ("dk", dk), ("dv", dv)))
     args = (_dtype_code(q), _ptr(q), _strides(q), _ptr(k), _strides(k), _ptr(v), _strides(v),
             _ptr(o), _strides(o), _ptr(dout), _strides(dout), _ptr(lse), _ptr(dq), _strides(dq),
-            _ptr(workspace), nbytes, B, H, N, d, float(scale), int(bool(causal)),
-            _ptr(seqlens_k), _ptr(block_mask), int(mask_block), _stream(q, stream))
-    return Prepared(lib.fa_bwd_dq, args,
-                    (q, k, v, o, dout, lse, dq, workspace, seqlens_k, block_mask))
-
-
-def prepare_bwd_dkdv(q, k, v, dout, lse, dk, dv, workspace, *, scale: float,
-                     causal: bool = False, seqlens_k=None, block_mask=None,
-                     mask_block: int = 128, stream=None) -> Prepared:
-    """fa_bwd_dkdv with fixed arguments (see fa_bwd_dkdv)."""
-    lib = load_library()
-    B, H, N, d = _check_like(q, (("k", k), ("v", v), ("dout", dout), ("dk", dk), ("dv", dv)))
-    nbytes = workspace.numel() * workspace.element_size()
-    args = (_dtype_code(q), _ptr(q), _strides(q), _ptr(k), _strides(k), _ptr(v), _strides(v),
-            _ptr(dout), _strides(dout), _ptr(lse), _ptr(dk), _strides(dk), _ptr(dv),
-            _strides(dv), _ptr(workspace), nbytes, B, H, N, d, float(scale),
-            int(bool(causal)), _ptr(seqlens_k), _ptr(block_mask), int(mask_block),
-            _stream(q, stream))
-    return Prepared(lib.fa_bwd_dkdv, args,
-                    (q, k, v, dout, lse, dk, dv, workspace, seqlens_k, block_mask))
+            _ptr(dk), _strides(dk), _ptr(dv), _strides(dv), _ptr(workspace), _nbytes(workspace),
+            B, H, N, d, float(scale), int(bool(causal)), _ptr(seqlens_k), _ptr(block_mask),
+            int(mask_block), _stream(q, stream))
+    return Prepared(lib.fa_bwd, args,
+                    (q, k, v, o, dout, lse, dq, dk, dv, workspace, seqlens_k, block_mask))
 
 
 # --------------------------------------------- allocating convenience calls
@@ -276,7 +269,7 @@ def backward(q, k, v, o, dout, lse, *, scale: float, causal: bool = False, seqle
     dv = torch.empty_like(dq)
     if workspace is None:
         nb = fa_bwd_workspace_bytes(_dtype_code(q), B, H, N, d)
-        workspace = torch.empty(nb, dtype=torch.uint8, device=q.device)
+        workspace = torch.empty(nb, dtype=torch.uint8, device=q.device) if nb else None
     fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, workspace, scale=scale, causal=causal,
            seqlens_k=seqlens_k, block_mask=block_mask, mask_block=mask_block)
     return dq, dk, dv

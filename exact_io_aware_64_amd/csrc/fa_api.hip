@@ -119,11 +119,13 @@ fa_status fa_fwd(fa_dtype dtype, const void* q, fa_strides q_strides, const void
 }
 
 size_t fa_bwd_workspace_bytes(fa_dtype dtype, int B, int H, int N, int d) {
+  // Every kernel of the backward pass keeps its row statistics on chip.
   (void)dtype;
+  (void)B;
+  (void)H;
+  (void)N;
   (void)d;
-  if (B <= 0 || H <= 0 || N <= 0) return 0;
-  const size_t bytes = (size_t)B * (size_t)H * (size_t)N * sizeof(float);
-  return (bytes + 255) & ~(size_t)255;
+  return 0;
 }
 
 }  // extern "C"
@@ -144,8 +146,8 @@ fa_status bwd_impl(int phases, fa_dtype dtype, const void* q, fa_strides q_strid
   if ((st = check_tensor("q", q, q_strides, al, N)) != FA_OK) return st;
   if ((st = check_tensor("k", k, k_strides, al, N)) != FA_OK) return st;
   if ((st = check_tensor("v", v, v_strides, al, N)) != FA_OK) return st;
+  if ((st = check_tensor("o", o, o_strides, al, N)) != FA_OK) return st;
   if (phases & fa::kPhaseDQ) {
-    if ((st = check_tensor("o", o, o_strides, al, N)) != FA_OK) return st;
     if ((st = check_tensor("dq", dq, dq_strides, al, N)) != FA_OK) return st;
   }
   if ((st = check_tensor("dout", dout, dout_strides, al, N)) != FA_OK) return st;
@@ -155,12 +157,15 @@ fa_status bwd_impl(int phases, fa_dtype dtype, const void* q, fa_strides q_strid
   }
   if (lse == nullptr) return fail(FA_ERR_INVALID_ARG, "lse is NULL");
   if (!aligned16(lse)) return fail(FA_ERR_INVALID_ARG, "lse is not 16-byte aligned");
-  if (workspace == nullptr) return fail(FA_ERR_INVALID_ARG, "workspace is NULL");
-  if (!aligned16(workspace)) return fail(FA_ERR_INVALID_ARG, "workspace is not 16-byte aligned");
   const size_t need = fa_bwd_workspace_bytes(dtype, B, H, N, d);
-  if (workspace_bytes < need)
-    return fail(FA_ERR_INVALID_ARG, "workspace too small: %zu < %zu bytes", workspace_bytes,
-                need);
+  if (need > 0) {
+    if (workspace == nullptr) return fail(FA_ERR_INVALID_ARG, "workspace is NULL");
+    if (!aligned16(workspace))
+      return fail(FA_ERR_INVALID_ARG, "workspace is not 16-byte aligned");
+    if (workspace_bytes < need)
+      return fail(FA_ERR_INVALID_ARG, "workspace too small: %zu < %zu bytes", workspace_bytes,
+                  need);
+  }
   if (seqlens_k != nullptr && ((uintptr_t)seqlens_k & 3u))
     return fail(FA_ERR_INVALID_ARG, "seqlens_k is not 4-byte aligned");
 
@@ -174,7 +179,6 @@ fa_status bwd_impl(int phases, fa_dtype dtype, const void* q, fa_strides q_strid
   a.dq = dq;
   a.dk = dk;
   a.dv = dv;
-  a.dsum = (float*)workspace;
   a.sq = cvt(q_strides);
   a.sk = cvt(k_strides);
   a.sv = cvt(v_strides);
@@ -231,16 +235,17 @@ fa_status fa_bwd_dq(fa_dtype dtype, const void* q, fa_strides q_strides, const v
 
 fa_status fa_bwd_dkdv(fa_dtype dtype, const void* q, fa_strides q_strides, const void* k,
                       fa_strides k_strides, const void* v, fa_strides v_strides,
-                      const void* dout, fa_strides dout_strides, const float* lse, void* dk,
+                      const void* o, fa_strides o_strides, const void* dout,
+                      fa_strides dout_strides, const float* lse, void* dk,
                       fa_strides dk_strides, void* dv, fa_strides dv_strides, void* workspace,
                       size_t workspace_bytes, int B, int H, int N, int d, float scale,
                       int causal, const int32_t* seqlens_k, const uint8_t* block_mask,
                       int mask_block, hipStream_t stream) {
   const fa_strides none{0, 0, 0};
-  return bwd_impl(fa::kPhaseDKDV, dtype, q, q_strides, k, k_strides, v, v_strides, nullptr,
-                  none, dout, dout_strides, lse, nullptr, none, dk, dk_strides, dv, dv_strides,
-                  workspace, workspace_bytes, B, H, N, d, scale, causal, seqlens_k, block_mask,
-                  mask_block, stream);
+  return bwd_impl(fa::kPhaseDKDV, dtype, q, q_strides, k, k_strides, v, v_strides, o,
+                  o_strides, dout, dout_strides, lse, nullptr, none, dk, dk_strides, dv,
+                  dv_strides, workspace, workspace_bytes, B, H, N, d, scale, causal, seqlens_k,
+                  block_mask, mask_block, stream);
 }
 
 const char* fa_status_string(fa_status status) {

@@ -8,19 +8,21 @@
 //   P = exp(s - L),  dP = dO V^T,  D_i = dot(dO_i, O_i),  dS = P * (dP - D),
 //   dV = P^T dO,     dK = scale dS^T Q,   dQ = scale dS K.
 //
-// Two kernels run back to back on the caller's stream, so no gradient needs
-// atomics or a transpose of dS:
-//  * dq_kernel: query-stationary, like the forward.  Each lane owns one query
-//    with its Q, dO fragments, L and D in registers; K/V tiles stream through
-//    LDS.  S^T = K Q^T and dP^T = V dO^T come out of the MFMA with one query
-//    per lane, and dQ^T = K^T dS^T takes dS^T straight from the accumulator.
-//    It first computes D for its rows and stores it in the workspace.
-//  * dkdv_kernel: key-stationary.  Each lane owns one key with its K, V
-//    fragments in registers; Q/dO tiles (row-major and transposed copies), L
-//    and D stream through LDS.  S = Q K^T and dP = dO V^T come out with one
-//    key per lane, which is exactly the B operand of dV^T = dO^T P and
-//    dK^T = Q^T dS.
-// Masked tiles are skipped exactly as in the forward pass.
+// One kernel, launched once, whose workgroups take one of two roles; no
+// gradient needs atomics or a transpose of dS, and the roles share nothing:
+//  * dQ role: query-stationary, like the forward.  Each lane owns one query
+//    with its Q, dO fragments, L and D in registers (D computed from its own
+//    dO and O rows); K/V tiles stream through LDS.  S^T = K Q^T and
+//    dP^T = V dO^T come out of the MFMA with one query per lane, and
+//    dQ^T = K^T dS^T takes dS^T straight from the accumulator.
+//  * dK/dV role: key-stationary.  Each lane owns one key with its K, V
+//    fragments in registers; Q, dO and O tiles and L stream through LDS, and
+//    each wave computes D for the rows it copied.  S = Q K^T and dP = dO V^T
+//    come out with one key per lane, which is exactly the B operand of
+//    dV^T = dO^T P and dK^T = Q^T dS.
+// One launch carries both roles, heaviest work first, so that the GPU stays
+// busy to the end without a second kernel's launch gap and tail.  Masked tiles are skipped exactly as
+// in the forward pass.
 #include <type_traits>
 
 #include "fa_device.h"
@@ -28,28 +30,24 @@
 namespace fa {
 namespace {
 
-constexpr int kBQ = 128;   // dq_kernel: query rows per workgroup
-constexpr int kBK = 128;   // dkdv_kernel: key rows per workgroup
+constexpr int kBQ = 128;   // dQ role: query rows per workgroup
+constexpr int kBK = 128;   // dK/dV role: key rows per workgroup
 
 // ------------------------------------------------------------------ dQ (+D)
 
+// dQ for the 128 queries of work item `item` (query tile, batch, head).
+// s_k0/s_v0 and s_k1/s_v1 are the two K/V tile buffers.
 template <bool CAUSAL, bool SEQLEN, bool BMASK>
-__global__ __launch_bounds__(256) void dq_kernel(BwdArgs a) {
-  // Two buffers, each a K tile and a V tile (separate arrays so that the
-  // copies into one and the reads of the other never alias).
-  __shared__ __attribute__((aligned(16))) uint16_t s_k0[kTileElems];
-  __shared__ __attribute__((aligned(16))) uint16_t s_v0[kTileElems];
-  __shared__ __attribute__((aligned(16))) uint16_t s_k1[kTileElems];
-  __shared__ __attribute__((aligned(16))) uint16_t s_v1[kTileElems];
-
+__device__ __forceinline__ void dq_role(const BwdArgs& a, int item, uint16_t* s_k0,
+                                        uint16_t* s_v0, uint16_t* s_k1, uint16_t* s_v1,
+                                        uint16_t* s_list, int* s_scan) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = tid >> 6;
   const int r = lane & 31, hl = lane >> 5;
   const int BH = a.B * a.H;
   const int nqt = (a.N + kBQ - 1) / kBQ;
-  const int id = blockIdx.x;
-  const int qt = CAUSAL ? (nqt - 1 - id / BH) : (id / BH);
-  const int bh = id % BH;
+  const int qt = CAUSAL ? (nqt - 1 - item / BH) : (item / BH);
+  const int bh = item % BH;
   const int b = bh / a.H, hh = bh % a.H;
   const int q0 = qt * kBQ;
   const int qw = q0 + 32 * w;
@@ -64,8 +62,6 @@ __global__ __launch_bounds__(256) void dq_kernel(BwdArgs a) {
   int nlist = ntk;
   [[maybe_unused]] uint16_t* tlist = nullptr;
   if constexpr (BMASK) {
-    __shared__ uint16_t s_list[kMaxListTiles];
-    __shared__ int s_scan[4];
     tlist = s_list;
     const int row = q0 / a.mask_block;
     nlist = build_tile_list(s_list, s_scan, a.bmask + (int64_t)row * a.n_mask_tiles, 1,
@@ -104,7 +100,6 @@ __global__ __launch_bounds__(256) void dq_kernel(BwdArgs a) {
   Dq = half_sum(Dq);
   float L2 = kInf;  // +inf makes every probability of a dead or padding row 0
   if (qi < a.N) {
-    if (hl == 0) a.dsum[(int64_t)bh * a.N + qi] = Dq;
     const float L = a.lse[(int64_t)bh * a.N + qi];
     if (L != -kInf) L2 = L * kLog2e;
   }
@@ -246,26 +241,22 @@ __global__ __launch_bounds__(256) void dq_kernel(BwdArgs a) {
 
 // ---------------------------------------------------------------- dK, dV
 
+// dK, dV for the 128 keys of work item `item` (key tile, batch, head).
+// s_q0/s_do0/s_o0 and s_q1/s_do1/s_o1 are the two Q/dO/O tile buffers;
+// s_nl and s_nd hold -L / scale and -D of each buffer's 64 rows.
 template <bool CAUSAL, bool SEQLEN, bool BMASK>
-__global__ __launch_bounds__(256) void dkdv_kernel(BwdArgs a) {
-  // Two buffers, each a Q tile and a dO tile (separate arrays so that the
-  // copies into one and the reads of the other never alias), plus -L / scale
-  // and -D of the tile's 64 rows.
-  __shared__ __attribute__((aligned(16))) uint16_t s_q0[kTileElems];
-  __shared__ __attribute__((aligned(16))) uint16_t s_do0[kTileElems];
-  __shared__ __attribute__((aligned(16))) uint16_t s_q1[kTileElems];
-  __shared__ __attribute__((aligned(16))) uint16_t s_do1[kTileElems];
-  __shared__ __attribute__((aligned(16))) float s_nl[2][kTile];  // -L / scale
-  __shared__ __attribute__((aligned(16))) float s_nd[2][kTile];  // -D
-
+__device__ __forceinline__ void dkdv_role(const BwdArgs& a, int item, uint16_t* s_q0,
+                                          uint16_t* s_do0, uint16_t* s_o0, uint16_t* s_q1,
+                                          uint16_t* s_do1, uint16_t* s_o1,
+                                          float (*s_nl)[kTile], float (*s_nd)[kTile],
+                                          uint16_t* s_list, int* s_scan) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = tid >> 6;
   const int r = lane & 31, hl = lane >> 5;
   const int BH = a.B * a.H;
-  const int id = blockIdx.x;
-  // Causal: key tile 0 sees every query, so ascending ids are heaviest first.
-  const int kt = id / BH;
-  const int bh = id % BH;
+  // Causal: key tile 0 sees every query, so ascending items are heaviest first.
+  const int kt = item / BH;
+  const int bh = item % BH;
   const int b = bh / a.H, hh = bh % a.H;
   const int k0 = kt * kBK;
   const int kw = k0 + 32 * w;  // first key of this wave
@@ -286,8 +277,6 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdArgs a) {
     int nlist = nq - qt_lo;
     [[maybe_unused]] uint16_t* tlist = nullptr;
     if constexpr (BMASK) {
-      __shared__ uint16_t s_list[kMaxListTiles];
-      __shared__ int s_scan[4];
       tlist = s_list;
       const int col = k0 / a.mask_block;
       nlist = build_tile_list(s_list, s_scan, a.bmask + col, a.n_mask_tiles, a.n_mask_tiles,
@@ -302,9 +291,10 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdArgs a) {
         make_rsrc((const uint16_t*)a.v + b * a.sv.b + hh * a.sv.h, slice_bytes(a.N, a.sv.s, 2));
     const __amdgpu_buffer_rsrc_t rdo = make_rsrc(
         (const uint16_t*)a.dout + b * a.sdo.b + hh * a.sdo.h, slice_bytes(a.N, a.sdo.s, 2));
+    const __amdgpu_buffer_rsrc_t ro = make_rsrc(
+        (const uint16_t*)a.o + b * a.so.b + hh * a.so.h, slice_bytes(a.N, a.so.s, 2));
     const float* lse = a.lse + (int64_t)bh * a.N;
-    const float* dsum = a.dsum + (int64_t)bh * a.N;
-    const int ssq = (int)a.sq.s * 2, ssdo = (int)a.sdo.s * 2;
+    const int ssq = (int)a.sq.s * 2, ssdo = (int)a.sdo.s * 2, sso = (int)a.so.s * 2;
 
     // K and V fragments (B operands): lane (r, hl) holds row kj, columns
     // 16 ks + 8 hl .. +7.
@@ -335,35 +325,48 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdArgs a) {
 #pragma unroll
       for (int db = 0; db < 2; ++db) troff[hi][db] = tr_off(lane, hi, db);
 
-    // Raw L and D of row qs + tid (threads 0..63), converted only when they
-    // are written to LDS so that no wait on the loads sits at the start of a
-    // tile.  Rows past N read as 0 through the buffer resources.
-    float lraw = 0.f, draw = 0.f;
+    // Raw L of row qs + tid (threads 0..63), converted only when it is
+    // written to LDS so that no wait on the load sits at the start of a tile.
+    // Rows past N read as 0 through the buffer resources.
+    float lraw = 0.f;
     int lrow = 0;
     const __amdgpu_buffer_rsrc_t rl = make_rsrc(lse, (uint32_t)a.N * 4);
-    const __amdgpu_buffer_rsrc_t rd = make_rsrc(dsum, (uint32_t)a.N * 4);
     auto tile_at = [&](int it) FA_INLINE -> int {
       if constexpr (BMASK) return tlist[it];
       return qt_lo + it;
     };
-    // Q and dO tiles go straight to LDS; L and D through registers.
-    auto gload = [&](int t, uint16_t* qt_, uint16_t* dt_) FA_INLINE {
+    // Q, dO and O tiles go straight to LDS; L through registers.
+    auto gload = [&](int t, uint16_t* qt_, uint16_t* dt_, uint16_t* ot_) FA_INLINE {
       const int qs = t * kTile;
       stage_tile(rq, qs, ssq, qt_, w, lane);
       stage_tile(rdo, qs, ssdo, dt_, w, lane);
+      stage_tile(ro, qs, sso, ot_, w, lane);
       if (tid < kTile) {
         lrow = qs + tid;
         lraw = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rl, 4 * lrow, 0, 0));
-        draw = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rd, 4 * lrow, 0, 0));
       }
     };
-    auto swrite = [&](int buf) FA_INLINE {
+    // After the wave's own copies are complete: -L / scale of the tile's
+    // rows (threads 0..63) and -D of the 16 rows this wave copied, D_i =
+    // dot(dO_i, O_i) over four lanes per row.  The barrier that follows
+    // publishes both to every wave.
+    auto swrite = [&](int buf, const uint16_t* dt_, const uint16_t* ot_) FA_INLINE {
       if (tid < kTile) {
         // -inf makes every probability of a dead or missing row 0
         const bool live = lrow < a.N && lraw != -kInf;
         s_nl[buf][tid] = live ? -lraw * inv_scale : -kInf;
-        s_nd[buf][tid] = lrow < a.N ? -draw : 0.f;
       }
+      // lanes 0..31: rows 8 w .. 8 w + 7, lanes 32..63: rows 8 w + 32 .. + 39
+      const int rl = stage_row(w, lane >> 2 << 3 & 63, lane >> 5), qq = lane & 3;
+      float acc = 0.f;
+#pragma unroll
+      for (int cc = 0; cc < 2; ++cc) {
+        const int off = toff(rl, 16 * qq + 8 * cc);
+        acc = dot8_bf16(tile_row8(dt_, off), tile_row8(ot_, off), acc);
+      }
+      acc += quad_xor1(acc);
+      acc += quad_xor2(acc);
+      if (qq == 0) s_nd[buf][rl] = -acc;  // rows past N read as zeros: D = 0
     };
 
     // One 64-query tile as 32 issue slots, each holding one MFMA, a share
@@ -378,7 +381,7 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdArgs a) {
     auto tile = [&](auto mask_c, int buf, const uint16_t* qs_, const uint16_t* ds_, int qs)
         FA_INLINE {
       constexpr bool MASK = decltype(mask_c)::value;
-      constexpr int kLead = 4;
+      constexpr int kLead = 2;
       f32x16 sc_[2], dp[2];
       uint32_t pkp[4][4], pkd[4][4];  // bf16 pairs of P and dS per step
       bf16x8 opa[32];
@@ -469,9 +472,9 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdArgs a) {
     };
 
     if (nlist > 0) {
-      gload(tile_at(0), s_q0, s_do0);
+      gload(tile_at(0), s_q0, s_do0, s_o0);
       __builtin_amdgcn_s_waitcnt(0);
-      swrite(0);
+      swrite(0, s_do0, s_o0);
     }
     // Every load issued so far (K, V fragments, first tile) is complete here;
     // saying so also keeps the loop's wait counts from covering them.
@@ -480,16 +483,16 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdArgs a) {
 
     // Two tiles per trip so that each buffer is a fixed array.
     for (int it = 0; it < nlist; it += 2) {
-      if (it + 1 < nlist) gload(tile_at(it + 1), s_q1, s_do1);
+      if (it + 1 < nlist) gload(tile_at(it + 1), s_q1, s_do1, s_o1);
       compute(it, 0, s_q0, s_do0);
       __builtin_amdgcn_s_waitcnt(0);
-      if (it + 1 < nlist) swrite(1);
+      if (it + 1 < nlist) swrite(1, s_do1, s_o1);
       __syncthreads();
       if (it + 1 >= nlist) break;
-      if (it + 2 < nlist) gload(tile_at(it + 2), s_q0, s_do0);
+      if (it + 2 < nlist) gload(tile_at(it + 2), s_q0, s_do0, s_o0);
       compute(it + 1, 1, s_q1, s_do1);
       __builtin_amdgcn_s_waitcnt(0);
-      if (it + 2 < nlist) swrite(0);
+      if (it + 2 < nlist) swrite(0, s_do0, s_o0);
       __syncthreads();
     }
   }
@@ -513,23 +516,73 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdArgs a) {
   }
 }
 
+// The fused backward kernel.  Work items: query tiles for the dQ role and
+// key tiles for the dK/dV role (each times B*H), each role in its own
+// heavy-first order.
+template <bool CAUSAL, bool SEQLEN, bool BMASK>
+__global__ __launch_bounds__(256) void bwd_kernel(BwdArgs a, int phases) {
+  // Six tile arrays: the dQ role uses two per buffer (K, V), the dK/dV role
+  // three (Q, dO, O).  Separate arrays, so that the copies into one buffer
+  // and the reads of the other never alias.
+  __shared__ __attribute__((aligned(16))) uint16_t s_a0[kTileElems];
+  __shared__ __attribute__((aligned(16))) uint16_t s_b0[kTileElems];
+  __shared__ __attribute__((aligned(16))) uint16_t s_c0[kTileElems];
+  __shared__ __attribute__((aligned(16))) uint16_t s_a1[kTileElems];
+  __shared__ __attribute__((aligned(16))) uint16_t s_b1[kTileElems];
+  __shared__ __attribute__((aligned(16))) uint16_t s_c1[kTileElems];
+  __shared__ __attribute__((aligned(16))) float s_nl[2][kTile];  // -L / scale
+  __shared__ __attribute__((aligned(16))) float s_nd[2][kTile];  // -D
+  __shared__ uint16_t s_list[BMASK ? kMaxListTiles : 1];
+  __shared__ int s_scan[4];
+
+  // Workgroup ids go to the 8 XCDs round robin.  With B*H a multiple of 8,
+  // ids are mapped so that every work item of one (batch, head) -- both
+  // roles -- runs on the same XCD and shares its L2: XCD x serves the heads
+  // x, x + 8, ..., walking them fastest; it takes all its dK/dV tiles
+  // (heaviest first) before its dQ tiles, so that mostly one role runs at a
+  // time (mixing them grows the working set each L2 has to hold) while the
+  // switch from one to the other and the tail still overlap.  Items are
+  // numbered tile * B*H + (batch, head), as the roles expect.
+  const int id = blockIdx.x;
+  const int BH = a.B * a.H;
+  bool dkdv;
+  int item;
+  if (phases == (kPhaseDQ | kPhaseDKDV)) {
+    if ((BH & 7) == 0) {
+      const int hpx = BH >> 3, x = id & 7, j = id >> 3;
+      const int m = j / hpx, nt = (a.N + kBQ - 1) / kBQ;
+      dkdv = m < nt;
+      item = (dkdv ? m : m - nt) * BH + x + 8 * (j % hpx);
+    } else {
+      dkdv = (id & 1) == 0;
+      item = id >> 1;
+    }
+  } else {
+    dkdv = phases == kPhaseDKDV;
+    item = id;
+  }
+  if (dkdv)
+    dkdv_role<CAUSAL, SEQLEN, BMASK>(a, item, s_a0, s_b0, s_c0, s_a1, s_b1, s_c1, s_nl, s_nd,
+                                     s_list, s_scan);
+  else
+    dq_role<CAUSAL, SEQLEN, BMASK>(a, item, s_a0, s_b0, s_a1, s_b1, s_list, s_scan);
+}
+
 template <bool C, bool S, bool M>
 hipError_t launch(const BwdArgs& a, int phases, hipStream_t stream) {
+  static_assert(kBQ == kBK, "the interleaved grid pairs one query tile with one key tile");
   BwdArgs copy = a;
-  void* args[] = {&copy};
-  const int BH = a.B * a.H;
-  dim3 block(256);
-  if (phases & kPhaseDQ) {
-    dim3 gq((unsigned)(((a.N + kBQ - 1) / kBQ) * BH));
-    hipError_t e =
-        hipLaunchKernel((const void*)&dq_kernel<C, S, M>, gq, block, args, 0, stream);
-    if (e != hipSuccess) return e;
-  }
-  if (phases & kPhaseDKDV) {
-    dim3 gk((unsigned)(((a.N + kBK - 1) / kBK) * BH));
-    return hipLaunchKernel((const void*)&dkdv_kernel<C, S, M>, gk, block, args, 0, stream);
-  }
-  return hipSuccess;
+  int ph = phases;
+  void* args[] = {&copy, &ph};
+  const int per_role = ((a.N + kBQ - 1) / kBQ) * a.B * a.H;
+  int n = 0;
+  if (phases == (kPhaseDQ | kPhaseDKDV))
+    n = 2 * per_role;
+  else if (phases == kPhaseDQ || phases == kPhaseDKDV)
+    n = per_role;
+  if (n == 0) return hipSuccess;
+  return hipLaunchKernel((const void*)&bwd_kernel<C, S, M>, dim3((unsigned)n), dim3(256), args,
+                         0, stream);
 }
 
 }  // namespace

@@ -67,6 +67,28 @@ __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){lo, hi}, bf16x2));
 }
 
+// acc + sum of the 8 products x[i] * y[i] (bf16 products are exact in fp32).
+__device__ __forceinline__ float dot8_bf16(bf16x8 x, bf16x8 y, float acc) {
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(x, x, 0, 1),
+                                        __builtin_shufflevector(y, y, 0, 1), acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(x, x, 2, 3),
+                                        __builtin_shufflevector(y, y, 2, 3), acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(x, x, 4, 5),
+                                        __builtin_shufflevector(y, y, 4, 5), acc, false);
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(x, x, 6, 7),
+                                         __builtin_shufflevector(y, y, 6, 7), acc, false);
+}
+
+// x of the lane whose index differs in bit 0 (quad_xor1) or bit 1 (quad_xor2)
+// within each group of four lanes (DPP quad permutations [1,0,3,2] and
+// [2,3,0,1]).
+__device__ __forceinline__ float quad_xor1(float x) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xF, 0xF, true));
+}
+__device__ __forceinline__ float quad_xor2(float x) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x4E, 0xF, 0xF, true));
+}
+
 // Buffer resource over one (batch, head) slice of a tensor.  Loads through
 // it take 32-bit byte offsets, and any 16-byte load that starts at or past
 // `bytes` returns zeros, so rows past the end need no branch.
@@ -149,18 +171,25 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 // `stride_b`, buffer resource `rs`) straight from memory into the swizzled
 // tile, without passing through registers: buffer_load_dwordx4 ... lds puts
 // lane l's 16 bytes at the wave's LDS base + 16 l, so lane l fetches the
-// logical chunk that belongs at physical chunk l % 8 of row l / 8.  Each of
-// the 4 waves of a workgroup copies 16 rows; rows past the end of the slice
-// read as zeros.  Completion is tracked by the wave's vmcnt.
+// logical chunk that belongs at physical chunk l % 8 of row l / 8.  Wave w
+// copies rows 8 w .. 8 w + 7 and 8 w + 32 .. 8 w + 39 (stage_rows); the
+// swizzle repeats every 32 rows, so both instructions share one per-lane
+// offset and the second adds 32 rows to the uniform offset.  Rows past the
+// end of the slice read as zeros.  Completion is tracked by the wave's
+// vmcnt.
+__device__ __forceinline__ int stage_row(int w, int lane, int u) {
+  return 8 * w + 32 * u + (lane >> 3);
+}
+
 __device__ __forceinline__ void stage_tile(__amdgpu_buffer_rsrc_t rs, int row0, int stride_b,
                                            uint16_t* tile, int w, int lane) {
+  const int row = stage_row(w, lane, 0);
+  const int voff = row * stride_b + (((lane & 7) ^ swz(row)) << 4);
 #pragma unroll
-  for (int u = 0; u < 2; ++u) {
-    const int row = 16 * w + 8 * u + (lane >> 3);
-    const int voff = (row0 + row) * stride_b + (((lane & 7) ^ swz(row)) << 4);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)(tile + (16 * w + 8 * u) * 64), 16,
-                                             voff, 0, 0, 0);
-  }
+  for (int u = 0; u < 2; ++u)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        rs, (lds_void_t*)(tile + (8 * w + 32 * u) * 64), 16, voff,
+        __builtin_amdgcn_readfirstlane((row0 + 32 * u) * stride_b), 0, 0);
 }
 
 // 8 consecutive bf16 of a tile row (a 16-byte aligned chunk).

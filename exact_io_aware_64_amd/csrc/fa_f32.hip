@@ -115,7 +115,7 @@ __global__ __launch_bounds__(64) void fwd_f32_kernel(FwdArgs a, int causal) {
   }
 }
 
-// dQ for one query per thread; also writes D_i = dot(dO_i, O_i).
+// dQ for one query per thread.
 __global__ __launch_bounds__(64) void dq_f32_kernel(BwdArgs a, int causal) {
   __shared__ __attribute__((aligned(16))) float s_k[kTile * kD];
   __shared__ __attribute__((aligned(16))) float s_v[kTile * kD];
@@ -138,7 +138,6 @@ __global__ __launch_bounds__(64) void dq_f32_kernel(BwdArgs a, int causal) {
     load_row(acc, (const float*)a.o + b * a.so.b + hh * a.so.h + (int64_t)qi * a.so.s);
 #pragma unroll
     for (int e = 0; e < kD; ++e) D = __builtin_fmaf(g[e], acc[e], D);
-    a.dsum[(int64_t)bh * a.N + qi] = D;
     const float L = a.lse[(int64_t)bh * a.N + qi];
     if (L != -kInf) L2 = L * kLog2e;
   } else {
@@ -169,7 +168,8 @@ __global__ __launch_bounds__(64) void dq_f32_kernel(BwdArgs a, int causal) {
     store_row((float*)a.dq + b * a.sdq.b + hh * a.sdq.h + (int64_t)qi * a.sdq.s, acc, a.scale);
 }
 
-// dK, dV for one key per thread.
+// dK, dV for one key per thread.  Each staged query row also gets its
+// D_i = dot(dO_i, O_i), computed by the thread that stages it.
 __global__ __launch_bounds__(64) void dkdv_f32_kernel(BwdArgs a, int causal) {
   __shared__ __attribute__((aligned(16))) float s_q[kTile * kD];
   __shared__ __attribute__((aligned(16))) float s_g[kTile * kD];
@@ -183,6 +183,7 @@ __global__ __launch_bounds__(64) void dkdv_f32_kernel(BwdArgs a, int causal) {
   if (a.seqlens) kv_len = min(max(a.seqlens[b], 0), a.N);
   const float* Q = (const float*)a.q + b * a.sq.b + hh * a.sq.h;
   const float* G = (const float*)a.dout + b * a.sdo.b + hh * a.sdo.h;
+  const float* O = (const float*)a.o + b * a.so.b + hh * a.so.h;
 
   float kr[kD], vr[kD], dk[kD], dv[kD];
   if (kj < a.N) {
@@ -202,7 +203,13 @@ __global__ __launch_bounds__(64) void dkdv_f32_kernel(BwdArgs a, int causal) {
       stage_row(s_g + tid * kD, G + (int64_t)qq * a.sdo.s, qq < a.N);
       const float L = qq < a.N ? a.lse[(int64_t)bh * a.N + qq] : -kInf;
       s_l2[tid] = (L == -kInf) ? kInf : L * kLog2e;
-      s_d[tid] = qq < a.N ? a.dsum[(int64_t)bh * a.N + qq] : 0.f;
+      float dd = 0.f;
+      if (qq < a.N) {
+        const float* orow = O + (int64_t)qq * a.so.s;
+        const float* grow = G + (int64_t)qq * a.sdo.s;
+        for (int e = 0; e < kD; ++e) dd = __builtin_fmaf(grow[e], orow[e], dd);
+      }
+      s_d[tid] = dd;
       __syncthreads();
       for (int i = 0; i < kTile; ++i) {
         const int q = qs + i;

@@ -42,7 +42,6 @@ struct BwdArgs {
   void* dq;
   void* dk;
   void* dv;
-  float* dsum;  // workspace: D_i = dot(dO_i, O_i), fp32 [B*H*N]
   Strides sq, sk, sv, so, sdo, sdq, sdk, sdv;
   int B, H, N;
   float scale;
@@ -53,8 +52,8 @@ struct BwdArgs {
   int n_mask_tiles;
 };
 
-// Backward phases: kPhaseDQ writes D (workspace) and dQ; kPhaseDKDV reads D
-// and writes dK, dV.  The full backward pass is both, in this order.
+// Backward roles: kPhaseDQ writes dQ, kPhaseDKDV writes dK and dV.  They are
+// independent; the full backward pass runs both in one launch.
 constexpr int kPhaseDQ = 1;
 constexpr int kPhaseDKDV = 2;
 

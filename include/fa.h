@@ -102,9 +102,10 @@ fa_status fa_fwd(fa_dtype dtype,
                  hipStream_t stream);
 
 /*
- * fa_bwd_workspace_bytes -- device workspace that fa_bwd needs: one fp32 per
- * (b, h, query) for D_i = dot(dO_i, O_i), rounded up to 256 bytes.
- * Returns 0 for non-positive sizes.
+ * fa_bwd_workspace_bytes -- device workspace that fa_bwd, fa_bwd_dq and
+ * fa_bwd_dkdv need.  Every kernel of this build keeps its per-row statistics
+ * (L, D = dot(dO_i, O_i)) on chip, so the result is 0 for every problem; the
+ * workspace arguments are kept so that a future kernel may use them.
  */
 size_t fa_bwd_workspace_bytes(fa_dtype dtype, int B, int H, int N, int d);
 
@@ -112,14 +113,15 @@ size_t fa_bwd_workspace_bytes(fa_dtype dtype, int B, int H, int N, int d);
  * fa_bwd -- backward pass: writes dQ, dK and dV in full (zeros for keys that
  * no query sees, e.g. keys past seqlens_k).  The scores and probabilities are
  * recomputed tile by tile from q, k and the forward's lse; nothing of size
- * N x N is read or written.
+ * N x N is read or written.  One kernel launch.
  *
  *   q, k, v, o, lse  the forward pass's inputs and outputs (o and lse as
  *                    written by fa_fwd with the same mask arguments).
  *   dout             upstream gradient dO, [B][H][N][d] through its strides.
  *   dq, dk, dv       outputs, element type dtype, through their strides.
- *   workspace        device buffer of at least fa_bwd_workspace_bytes(...) bytes,
- *                    16-byte aligned; contents on entry are ignored.
+ *   workspace        device buffer of at least fa_bwd_workspace_bytes(...) bytes
+ *                    (16-byte aligned); may be NULL when that size is 0, as it is
+ *                    in this build.
  *   remaining arguments as for fa_fwd and must match the forward call.
  */
 fa_status fa_bwd(fa_dtype dtype,
@@ -140,19 +142,12 @@ fa_status fa_bwd(fa_dtype dtype,
                  hipStream_t stream);
 
 /*
- * fa_bwd_dq, fa_bwd_dkdv -- the two phases of fa_bwd, exported separately so
- * that a caller can schedule or time them on their own.  fa_bwd is exactly
- * fa_bwd_dq followed by fa_bwd_dkdv on the same stream, with the same
- * arguments and workspace.
- *
- *   fa_bwd_dq    writes D_i = dot(dO_i, O_i) for every row into `workspace`
- *                and writes dQ in full.  Reads q, k, v, o, dout, lse.
- *   fa_bwd_dkdv  writes dK and dV in full.  Reads q, k, v, dout, lse and the
- *                D that a preceding fa_bwd_dq with the same problem left in
- *                `workspace` (stream order is enough; the workspace must not
- *                be reused in between).
- * Arguments mean what they mean for fa_bwd; validation and errors are the
- * same.
+ * fa_bwd_dq, fa_bwd_dkdv -- the two halves of fa_bwd, each one kernel launch
+ * of its own: fa_bwd_dq writes dQ, fa_bwd_dkdv writes dK and dV.  They are
+ * independent of each other (either may run alone, in any order or on
+ * different streams) and together give exactly what fa_bwd gives.  Both
+ * read q, k, v, o, dout and lse; arguments mean what they mean for fa_bwd,
+ * and validation and errors are the same.
  */
 fa_status fa_bwd_dq(fa_dtype dtype,
                     const void* q, fa_strides q_strides,
@@ -173,6 +168,7 @@ fa_status fa_bwd_dkdv(fa_dtype dtype,
                       const void* q, fa_strides q_strides,
                       const void* k, fa_strides k_strides,
                       const void* v, fa_strides v_strides,
+                      const void* o, fa_strides o_strides,
                       const void* dout, fa_strides dout_strides,
                       const float* lse,
                       void* dk, fa_strides dk_strides,

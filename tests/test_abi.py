@@ -43,8 +43,9 @@ def test_status_strings():
 
 
 def test_workspace_bytes():
-    assert fa.fa_bwd_workspace_bytes(0, 8, 12, 1024, 64) == 8 * 12 * 1024 * 4
-    assert fa.fa_bwd_workspace_bytes(0, 1, 1, 3, 64) == 256
+    # every backward kernel keeps its row statistics on chip
+    assert fa.fa_bwd_workspace_bytes(0, 8, 12, 1024, 64) == 0
+    assert fa.fa_bwd_workspace_bytes(1, 1, 1, 3, 64) == 0
     assert fa.fa_bwd_workspace_bytes(0, 0, 1, 3, 64) == 0
 
 
@@ -95,9 +96,8 @@ def test_fwd_rejects_bad_arguments(kw, status, msg):
 
 
 @pytest.mark.parametrize("kw,status,msg", [
-    (dict(ws=None), 1, "workspace is NULL"),
-    (dict(wsb=100), 1, "workspace too small"),
     (dict(dq=None), 1, "dq is NULL"),
+    (dict(o=None), 1, "o is NULL"),
     (dict(do=A + 4), 1, "dout is not 16-byte aligned"),
     (dict(dtype=1, sdv=bnd.fa_strides(64, 64, 66)), 1, "multiples of 4"),
     (dict(d=32), 2, "head dimension"),
@@ -118,7 +118,8 @@ def _bwd_dq(**kw):
 
 def _bwd_dkdv(**kw):
     lib = fa.load_library()
-    args = dict(dtype=0, q=A, sq=S, k=A, sk=S, v=A, sv=S, do=A, sdo=S, lse=A, dk=A, sdk=S,
+    args = dict(dtype=0, q=A, sq=S, k=A, sk=S, v=A, sv=S, o=A, so=S, do=A, sdo=S, lse=A, dk=A,
+                sdk=S,
                 dv=A, sdv=S, ws=A, wsb=4096, B=1, H=1, N=1024, d=64, scale=0.125, causal=0,
                 seqlens=None, bmask=None, mb=128, stream=None)
     args.update(kw)
@@ -128,7 +129,6 @@ def _bwd_dkdv(**kw):
 @pytest.mark.parametrize("kw,status,msg", [
     (dict(dq=None), 1, "dq is NULL"),
     (dict(o=A + 4), 1, "o is not 16-byte aligned"),
-    (dict(wsb=100), 1, "workspace too small"),
     (dict(lse=None), 1, "lse is NULL"),
     (dict(N=0), 1, "must be positive"),
 ])
@@ -140,7 +140,7 @@ def test_bwd_dq_rejects_bad_arguments(kw, status, msg):
 @pytest.mark.parametrize("kw,status,msg", [
     (dict(dk=None), 1, "dk is NULL"),
     (dict(dv=A + 2), 1, "dv is not 16-byte aligned"),
-    (dict(ws=None), 1, "workspace is NULL"),
+    (dict(o=None), 1, "o is NULL"),
     (dict(do=None), 1, "dout is NULL"),
     (dict(d=128), 2, "head dimension"),
 ])

@@ -41,16 +41,15 @@ def test_kernel_bytes():
     t = 8 * 12 * 1024 * 64 * 2
     row = 8 * 12 * 1024 * 4
     assert kb["fwd_bf16_kernel"] == 4 * t + row
-    assert kb["dq_kernel"] == 6 * t + 2 * row
-    assert kb["dkdv_kernel"] == 6 * t + 2 * row
+    assert kb["bwd_kernel"] == 8 * t + row
     kb2 = bench.kernel_bytes(2, 1, 100, 64, 2, np.array([50, 100]))
     assert kb2["fwd_bf16_kernel"] == 2 * (2 * 100 * 64 * 2) + 2 * (150 * 64 * 2) + 2 * 100 * 4
 
 
-def test_kernel_flops_sum_to_the_method():
+def test_kernel_flops_are_the_method():
     kf = bench.kernel_flops(64, 1000)
     assert kf["fwd_bf16_kernel"] == 4 * 64 * 1000
-    assert kf["dq_kernel"] + kf["dkdv_kernel"] == 10 * 64 * 1000
+    assert kf["bwd_kernel"] == 10 * 64 * 1000
 
 
 def test_more_than_one_gpu_is_refused(capsys):

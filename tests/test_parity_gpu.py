@@ -247,8 +247,9 @@ def test_repeatable_bitwise():
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
-def test_split_phases_equal_fused_call(dtype):
-    """fa_bwd_dq followed by fa_bwd_dkdv gives exactly what fa_bwd gives."""
+def test_split_halves_equal_full_call(dtype):
+    """fa_bwd_dkdv and fa_bwd_dq are independent (dK/dV first here, with no
+    dQ call before it) and together give exactly what fa_bwd gives."""
     import torch
     import exact_io_aware_64_amd as fa
     case = wl.random_case(2, 3, 333, 64, dtype=dtype, seed=31, causal=True, seqlens="random",
@@ -258,12 +259,9 @@ def test_split_phases_equal_fused_call(dtype):
     g1 = gpu_backward(case, q, k, v, o, do, lse, sl, bm)
     kw = dict(scale=case["scale"], causal=case["causal"], seqlens_k=sl, block_mask=bm,
               mask_block=128)
-    code = fa.FA_BF16 if dtype == "bf16" else fa.FA_F32
-    ws = torch.empty(fa.fa_bwd_workspace_bytes(code, *q.shape), dtype=torch.uint8,
-                     device=q.device)
     dq, dk, dv = (torch.full_like(q, float("nan")) for _ in range(3))
-    fa.fa_bwd_dq(q, k, v, o, do, lse, dq, ws, **kw)
-    fa.fa_bwd_dkdv(q, k, v, do, lse, dk, dv, ws, **kw)
+    fa.fa_bwd_dkdv(q, k, v, o, do, lse, dk, dv, **kw)
+    fa.fa_bwd_dq(q, k, v, o, do, lse, dq, **kw)
     for a, b in zip(g1, (dq, dk, dv)):
         assert np.array_equal(to_np(a), to_np(b))
 
@@ -280,11 +278,8 @@ def test_prepared_calls_equal_direct_calls():
     kw = dict(scale=case["scale"], causal=True, seqlens_k=sl, block_mask=bm)
     o2, l2 = torch.empty_like(q), torch.empty_like(l1)
     dq, dk, dv = (torch.empty_like(q) for _ in range(3))
-    ws = torch.empty(fa.fa_bwd_workspace_bytes(fa.FA_BF16, *q.shape), dtype=torch.uint8,
-                     device=q.device)
     fa.prepare_fwd(q, k, v, o2, l2, **kw)()
-    fa.prepare_bwd_dq(q, k, v, o2, do, l2, dq, ws, **kw)()
-    fa.prepare_bwd_dkdv(q, k, v, do, l2, dk, dv, ws, **kw)()
+    fa.prepare_bwd(q, k, v, o2, do, l2, dq, dk, dv, **kw)()
     for a, b in zip((o1, l1) + tuple(g1), (o2, l2, dq, dk, dv)):
         assert np.array_equal(to_np(a), to_np(b))
 
