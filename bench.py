@@ -99,12 +99,16 @@ def kernel_flops(d, pairs):
 KERNELS = ("fwd_bf16_kernel", "bwd_kernel")
 
 
-def run_gpu(w: wl.Workload, inp: dict, steps: int, warmup: int):
+def run_gpu(w: wl.Workload, inp: dict, steps: int, warmup: int, prewarm_s: float = 1.0):
     """Times `steps` steps after `warmup` untimed ones.  One step is fa_fwd
     then fa_bwd, each a single kernel launch on the current stream; HIP
     events recorded on that stream around the launches give each kernel's
     device time, and the wall clock around the whole timed region gives the
-    step time."""
+    step time.
+
+    Before the warmup steps the step runs untimed for `prewarm_s` seconds of
+    wall time: an idle MI355X takes a few milliseconds of sustained load to
+    raise its clocks, and a short warmup would otherwise time the ramp."""
     import torch
     import exact_io_aware_64_amd as fa
 
@@ -134,6 +138,12 @@ def run_gpu(w: wl.Workload, inp: dict, steps: int, warmup: int):
         if ev is not None:
             ev[2].record(stream)
 
+    torch.cuda.synchronize()
+    t_end = time.perf_counter() + prewarm_s
+    while time.perf_counter() < t_end:
+        for _ in range(8):
+            step()
+        torch.cuda.synchronize()
     for _ in range(warmup):
         step()
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
@@ -343,8 +353,10 @@ def trace_summary(stats_csv: str, bench_log: str, workload: str, command: str) -
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--prewarm-s", type=float, default=1.0,
+                    help="seconds of untimed steps before the warmup steps (clock ramp)")
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=wl.WORKLOAD_ORDER)
     ap.add_argument("--cpu-baseline", default="on", choices=["on", "off"])
     ap.add_argument("--mode", default="attention", choices=["attention", "copy"],
@@ -390,7 +402,7 @@ def main(argv=None):
     flops_b = 10.0 * w.d * pairs
     esize = 2 if w.dtype == "bf16" else 4
 
-    wall_ms, kernel_ms, props, outs = run_gpu(w, inp, args.steps, args.warmup)
+    wall_ms, kernel_ms, props, outs = run_gpu(w, inp, args.steps, args.warmup, args.prewarm_s)
     fwd_ms = kernel_ms["fwd_bf16_kernel"]
     bwd_ms = kernel_ms["bwd_kernel"]
     peak = PEAK_TFLOPS[w.dtype]
@@ -430,6 +442,7 @@ def main(argv=None):
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "prewarm_s": args.prewarm_s,
         "ms_per_step": wall_ms,
         "higher_is_better": True,
         "scaling": "weak",
