@@ -22,8 +22,8 @@ FA_ERR_UNSUPPORTED = 2
 FA_ERR_HIP = 3
 
 # Public entry points declared in include/fa.h.
-EXPORTED = ("fa_fwd", "fa_bwd", "fa_bwd_dq", "fa_bwd_dkdv", "fa_bwd_workspace_bytes",
-            "fa_status_string", "fa_last_error")
+EXPORTED = ("fa_fwd", "fa_bwd", "fa_bwd_dq", "fa_bwd_dkdv", "fa_fwd_dropout",
+            "fa_bwd_dropout", "fa_bwd_workspace_bytes", "fa_status_string", "fa_last_error")
 
 
 class FaError(RuntimeError):
@@ -60,6 +60,13 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.fa_bwd_dkdv.restype = I
     lib.fa_bwd_dkdv.argtypes = [I, P, S, P, S, P, S, P, S, P, S, P, P, S, P, S, P,
                                 ctypes.c_size_t, I, I, I, I, F, I, P, P, I, P]
+    U64, U32 = ctypes.c_uint64, ctypes.c_uint32
+    lib.fa_fwd_dropout.restype = I
+    lib.fa_fwd_dropout.argtypes = [I, P, S, P, S, P, S, P, S, P, I, I, I, I, F, I, P, P, I,
+                                   F, U64, U32, P]
+    lib.fa_bwd_dropout.restype = I
+    lib.fa_bwd_dropout.argtypes = [I, P, S, P, S, P, S, P, S, P, S, P, P, S, P, S, P, S, P,
+                                   ctypes.c_size_t, I, I, I, I, F, I, P, P, I, F, U64, U32, P]
     lib.fa_bwd_workspace_bytes.restype = ctypes.c_size_t
     lib.fa_bwd_workspace_bytes.argtypes = [I, I, I, I, I]
     lib.fa_status_string.restype = ctypes.c_char_p
@@ -125,23 +132,36 @@ def _check(st: int):
         raise FaError(st, fa_last_error())
 
 
+def _fwd_args(q, k, v, o, lse, scale, causal, seqlens_k, block_mask, mask_block):
+    B, H, N, d = _check_like(q, (("k", k), ("v", v), ("o", o)))
+    if tuple(lse.shape) != (B, H, N) or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous fp32 [B, H, N] tensor")
+    return (_dtype_code(q), _ptr(q), _strides(q), _ptr(k), _strides(k), _ptr(v), _strides(v),
+            _ptr(o), _strides(o), _ptr(lse), B, H, N, d, float(scale), int(bool(causal)),
+            _ptr(seqlens_k), _ptr(block_mask), int(mask_block))
+
+
+def _drop_args(dropout_p, seed, offset):
+    return (float(dropout_p), int(seed) & (2**64 - 1), int(offset) & (2**32 - 1))
+
+
 def fa_fwd(q, k, v, o, lse, *, scale: float, causal: bool = False, seqlens_k=None,
            block_mask=None, mask_block: int = 128, stream=None) -> None:
     """Calls fa_fwd on tensors indexed [B, H, N, d] (any strides with a
     contiguous last dimension); o and lse ([B, H, N] fp32, contiguous) are
     written."""
     lib = load_library()
-    B, H, N, d = q.shape
-    for name, t in (("k", k), ("v", v), ("o", o)):
-        if tuple(t.shape) != (B, H, N, d) or t.dtype != q.dtype:
-            raise ValueError(f"{name} must match q in shape and dtype")
-    if tuple(lse.shape) != (B, H, N) or not lse.is_contiguous():
-        raise ValueError("lse must be a contiguous fp32 [B, H, N] tensor")
-    st = lib.fa_fwd(_dtype_code(q), _ptr(q), _strides(q), _ptr(k), _strides(k), _ptr(v),
-                    _strides(v), _ptr(o), _strides(o), _ptr(lse), B, H, N, d, float(scale),
-                    int(bool(causal)), _ptr(seqlens_k), _ptr(block_mask), int(mask_block),
-                    _stream(q, stream))
-    _check(st)
+    args = _fwd_args(q, k, v, o, lse, scale, causal, seqlens_k, block_mask, mask_block)
+    _check(lib.fa_fwd(*args, _stream(q, stream)))
+
+
+def fa_fwd_dropout(q, k, v, o, lse, *, scale: float, dropout_p: float, seed: int,
+                   offset: int = 0, causal: bool = False, seqlens_k=None, block_mask=None,
+                   mask_block: int = 128, stream=None) -> None:
+    """Calls fa_fwd_dropout (fa_fwd with dropout on the probabilities)."""
+    lib = load_library()
+    args = _fwd_args(q, k, v, o, lse, scale, causal, seqlens_k, block_mask, mask_block)
+    _check(lib.fa_fwd_dropout(*args, *_drop_args(dropout_p, seed, offset), _stream(q, stream)))
 
 
 def _check_like(q, named):
@@ -152,20 +172,36 @@ def _check_like(q, named):
     return B, H, N, d
 
 
+def _bwd_args(q, k, v, o, dout, lse, dq, dk, dv, workspace, scale, causal, seqlens_k,
+              block_mask, mask_block):
+    B, H, N, d = _check_like(q, (("k", k), ("v", v), ("o", o), ("dout", dout), ("dq", dq),
+                                 ("dk", dk), ("dv", dv)))
+    return (_dtype_code(q), _ptr(q), _strides(q), _ptr(k), _strides(k), _ptr(v), _strides(v),
+            _ptr(o), _strides(o), _ptr(dout), _strides(dout), _ptr(lse), _ptr(dq), _strides(dq),
+            _ptr(dk), _strides(dk), _ptr(dv), _strides(dv), _ptr(workspace), _nbytes(workspace),
+            B, H, N, d, float(scale), int(bool(causal)), _ptr(seqlens_k), _ptr(block_mask),
+            int(mask_block))
+
+
 def fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, workspace=None, *, scale: float,
            causal: bool = False, seqlens_k=None, block_mask=None, mask_block: int = 128,
            stream=None) -> None:
     """Calls fa_bwd; dq, dk, dv are written in full."""
     lib = load_library()
-    B, H, N, d = _check_like(q, (("k", k), ("v", v), ("o", o), ("dout", dout), ("dq", dq),
-                                 ("dk", dk), ("dv", dv)))
-    nbytes = _nbytes(workspace)
-    st = lib.fa_bwd(_dtype_code(q), _ptr(q), _strides(q), _ptr(k), _strides(k), _ptr(v),
-                    _strides(v), _ptr(o), _strides(o), _ptr(dout), _strides(dout), _ptr(lse),
-                    _ptr(dq), _strides(dq), _ptr(dk), _strides(dk), _ptr(dv), _strides(dv),
-                    _ptr(workspace), nbytes, B, H, N, d, float(scale), int(bool(causal)),
-                    _ptr(seqlens_k), _ptr(block_mask), int(mask_block), _stream(q, stream))
-    _check(st)
+    args = _bwd_args(q, k, v, o, dout, lse, dq, dk, dv, workspace, scale, causal, seqlens_k,
+                     block_mask, mask_block)
+    _check(lib.fa_bwd(*args, _stream(q, stream)))
+
+
+def fa_bwd_dropout(q, k, v, o, dout, lse, dq, dk, dv, workspace=None, *, scale: float,
+                   dropout_p: float, seed: int, offset: int = 0, causal: bool = False,
+                   seqlens_k=None, block_mask=None, mask_block: int = 128,
+                   stream=None) -> None:
+    """Calls fa_bwd_dropout; needs the forward call's dropout_p, seed and offset."""
+    lib = load_library()
+    args = _bwd_args(q, k, v, o, dout, lse, dq, dk, dv, workspace, scale, causal, seqlens_k,
+                     block_mask, mask_block)
+    _check(lib.fa_bwd_dropout(*args, *_drop_args(dropout_p, seed, offset), _stream(q, stream)))
 
 
 def fa_bwd_dq(q, k, v, o, dout, lse, dq, workspace=None, *, scale: float,
@@ -217,51 +253,57 @@ class Prepared:
 
 
 def prepare_fwd(q, k, v, o, lse, *, scale: float, causal: bool = False, seqlens_k=None,
-                block_mask=None, mask_block: int = 128, stream=None) -> Prepared:
-    """fa_fwd with fixed arguments (see fa_fwd)."""
+                block_mask=None, mask_block: int = 128, dropout_p: float = 0.0, seed: int = 0,
+                offset: int = 0, stream=None) -> Prepared:
+    """fa_fwd (or fa_fwd_dropout when dropout_p > 0) with fixed arguments."""
     lib = load_library()
-    B, H, N, d = _check_like(q, (("k", k), ("v", v), ("o", o)))
-    if tuple(lse.shape) != (B, H, N) or not lse.is_contiguous():
-        raise ValueError("lse must be a contiguous fp32 [B, H, N] tensor")
-    args = (_dtype_code(q), _ptr(q), _strides(q), _ptr(k), _strides(k), _ptr(v), _strides(v),
-            _ptr(o), _strides(o), _ptr(lse), B, H, N, d, float(scale), int(bool(causal)),
-            _ptr(seqlens_k), _ptr(block_mask), int(mask_block), _stream(q, stream))
-    return Prepared(lib.fa_fwd, args, (q, k, v, o, lse, seqlens_k, block_mask))
+    args = _fwd_args(q, k, v, o, lse, scale, causal, seqlens_k, block_mask, mask_block)
+    keep = (q, k, v, o, lse, seqlens_k, block_mask)
+    if dropout_p > 0:
+        return Prepared(lib.fa_fwd_dropout,
+                        args + _drop_args(dropout_p, seed, offset) + (_stream(q, stream),), keep)
+    return Prepared(lib.fa_fwd, args + (_stream(q, stream),), keep)
 
 
 def prepare_bwd(q, k, v, o, dout, lse, dq, dk, dv, workspace=None, *, scale: float,
                 causal: bool = False, seqlens_k=None, block_mask=None, mask_block: int = 128,
+                dropout_p: float = 0.0, seed: int = 0, offset: int = 0,
                 stream=None) -> Prepared:
-    """fa_bwd with fixed arguments (see fa_bwd)."""
+    """fa_bwd (or fa_bwd_dropout when dropout_p > 0) with fixed arguments."""
     lib = load_library()
-    B, H, N, d = _check_like(q, (("k", k), ("v", v), ("o", o), ("dout", dout), ("dq", dq),
-                                 ("dk", dk), ("dv", dv)))
-    args = (_dtype_code(q), _ptr(q), _strides(q), _ptr(k), _strides(k), _ptr(v), _strides(v),
-            _ptr(o), _strides(o), _ptr(dout), _strides(dout), _ptr(lse), _ptr(dq), _strides(dq),
-            _ptr(dk), _strides(dk), _ptr(dv), _strides(dv), _ptr(workspace), _nbytes(workspace),
-            B, H, N, d, float(scale), int(bool(causal)), _ptr(seqlens_k), _ptr(block_mask),
-            int(mask_block), _stream(q, stream))
-    return Prepared(lib.fa_bwd, args,
-                    (q, k, v, o, dout, lse, dq, dk, dv, workspace, seqlens_k, block_mask))
+    args = _bwd_args(q, k, v, o, dout, lse, dq, dk, dv, workspace, scale, causal, seqlens_k,
+                     block_mask, mask_block)
+    keep = (q, k, v, o, dout, lse, dq, dk, dv, workspace, seqlens_k, block_mask)
+    if dropout_p > 0:
+        return Prepared(lib.fa_bwd_dropout,
+                        args + _drop_args(dropout_p, seed, offset) + (_stream(q, stream),), keep)
+    return Prepared(lib.fa_bwd, args + (_stream(q, stream),), keep)
 
 
 # --------------------------------------------- allocating convenience calls
 
 def forward(q, k, v, *, scale: float, causal: bool = False, seqlens_k=None, block_mask=None,
-            mask_block: int = 128):
-    """Allocates O (contiguous [B, H, N, d]) and L, then calls fa_fwd."""
+            mask_block: int = 128, dropout_p: float = 0.0, seed: int = 0, offset: int = 0):
+    """Allocates O (contiguous [B, H, N, d]) and L, then calls fa_fwd (or
+    fa_fwd_dropout when dropout_p > 0)."""
     torch = _torch()
     B, H, N, d = q.shape
     o = torch.empty((B, H, N, d), dtype=q.dtype, device=q.device)
     lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
-    fa_fwd(q, k, v, o, lse, scale=scale, causal=causal, seqlens_k=seqlens_k,
-           block_mask=block_mask, mask_block=mask_block)
+    kw = dict(scale=scale, causal=causal, seqlens_k=seqlens_k, block_mask=block_mask,
+              mask_block=mask_block)
+    if dropout_p > 0:
+        fa_fwd_dropout(q, k, v, o, lse, dropout_p=dropout_p, seed=seed, offset=offset, **kw)
+    else:
+        fa_fwd(q, k, v, o, lse, **kw)
     return o, lse
 
 
 def backward(q, k, v, o, dout, lse, *, scale: float, causal: bool = False, seqlens_k=None,
-             block_mask=None, mask_block: int = 128, workspace=None):
-    """Allocates dQ, dK, dV (and the workspace unless given), then calls fa_bwd."""
+             block_mask=None, mask_block: int = 128, workspace=None, dropout_p: float = 0.0,
+             seed: int = 0, offset: int = 0):
+    """Allocates dQ, dK, dV (and the workspace unless given), then calls fa_bwd
+    (or fa_bwd_dropout when dropout_p > 0)."""
     torch = _torch()
     B, H, N, d = q.shape
     dq = torch.empty((B, H, N, d), dtype=q.dtype, device=q.device)
@@ -270,6 +312,11 @@ def backward(q, k, v, o, dout, lse, *, scale: float, causal: bool = False, seqle
     if workspace is None:
         nb = fa_bwd_workspace_bytes(_dtype_code(q), B, H, N, d)
         workspace = torch.empty(nb, dtype=torch.uint8, device=q.device) if nb else None
-    fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, workspace, scale=scale, causal=causal,
-           seqlens_k=seqlens_k, block_mask=block_mask, mask_block=mask_block)
+    kw = dict(scale=scale, causal=causal, seqlens_k=seqlens_k, block_mask=block_mask,
+              mask_block=mask_block)
+    if dropout_p > 0:
+        fa_bwd_dropout(q, k, v, o, dout, lse, dq, dk, dv, workspace, dropout_p=dropout_p,
+                       seed=seed, offset=offset, **kw)
+    else:
+        fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, workspace, **kw)
     return dq, dk, dv

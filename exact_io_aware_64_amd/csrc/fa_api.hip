@@ -65,6 +65,22 @@ fa_status check_common(fa_dtype dtype, int B, int H, int N, int d, float scale,
 
 fa::Strides cvt(fa_strides s) { return fa::Strides{s.batch, s.head, s.seq}; }
 
+// Keep threshold t = floor(256 (1 - p) + 1/2), computed in double; p = 0
+// gives t = 256 (keep every pair).
+fa_status make_dropout(float p, uint64_t seed, uint32_t offset, fa::Dropout* d) {
+  if (!(p >= 0.f && p < 1.f))
+    return fail(FA_ERR_INVALID_ARG, "dropout_p must lie in [0, 1) (got %g)", (double)p);
+  const int t = (int)floor(256.0 * (1.0 - (double)p) + 0.5);
+  if (t < 1)
+    return fail(FA_ERR_INVALID_ARG, "dropout_p %g rounds to dropping every pair", (double)p);
+  d->t = (uint32_t)t;
+  d->scale = (float)(256.0 / t);
+  d->seed_lo = (uint32_t)seed;
+  d->seed_hi = (uint32_t)(seed >> 32);
+  d->offset = offset;
+  return FA_OK;
+}
+
 fa_status hip_status(hipError_t e) {
   if (e == hipSuccess) {
     g_err[0] = '\0';
@@ -73,15 +89,12 @@ fa_status hip_status(hipError_t e) {
   return fail(FA_ERR_HIP, "HIP error %d: %s", (int)e, hipGetErrorString(e));
 }
 
-}  // namespace
-
-extern "C" {
-
-fa_status fa_fwd(fa_dtype dtype, const void* q, fa_strides q_strides, const void* k,
-                 fa_strides k_strides, const void* v, fa_strides v_strides, void* o,
-                 fa_strides o_strides, float* lse, int B, int H, int N, int d, float scale,
-                 int causal, const int32_t* seqlens_k, const uint8_t* block_mask,
-                 int mask_block, hipStream_t stream) {
+fa_status fwd_impl(fa_dtype dtype, const void* q, fa_strides q_strides, const void* k,
+                   fa_strides k_strides, const void* v, fa_strides v_strides, void* o,
+                   fa_strides o_strides, float* lse, int B, int H, int N, int d, float scale,
+                   int causal, const int32_t* seqlens_k, const uint8_t* block_mask,
+                   int mask_block, float dropout_p, uint64_t seed, uint32_t offset,
+                   hipStream_t stream) {
   int al = 0;
   fa_status st = check_common(dtype, B, H, N, d, scale, block_mask, mask_block, &al);
   if (st != FA_OK) return st;
@@ -93,6 +106,8 @@ fa_status fa_fwd(fa_dtype dtype, const void* q, fa_strides q_strides, const void
   if (!aligned16(lse)) return fail(FA_ERR_INVALID_ARG, "lse is not 16-byte aligned");
   if (seqlens_k != nullptr && ((uintptr_t)seqlens_k & 3u))
     return fail(FA_ERR_INVALID_ARG, "seqlens_k is not 4-byte aligned");
+  fa::Dropout drop{};
+  if ((st = make_dropout(dropout_p, seed, offset, &drop)) != FA_OK) return st;
 
   fa::FwdArgs a{};
   a.q = q;
@@ -113,9 +128,34 @@ fa_status fa_fwd(fa_dtype dtype, const void* q, fa_strides q_strides, const void
   a.bmask = block_mask;
   a.mask_block = block_mask ? mask_block : 128;
   a.n_mask_tiles = (N + a.mask_block - 1) / a.mask_block;
+  a.drop = drop;
   const hipError_t e = dtype == FA_BF16 ? fa::launch_fwd_bf16(a, causal != 0, stream)
                                         : fa::launch_fwd_f32(a, causal != 0, stream);
   return hip_status(e);
+}
+
+}  // namespace
+
+extern "C" {
+
+fa_status fa_fwd(fa_dtype dtype, const void* q, fa_strides q_strides, const void* k,
+                 fa_strides k_strides, const void* v, fa_strides v_strides, void* o,
+                 fa_strides o_strides, float* lse, int B, int H, int N, int d, float scale,
+                 int causal, const int32_t* seqlens_k, const uint8_t* block_mask,
+                 int mask_block, hipStream_t stream) {
+  return fwd_impl(dtype, q, q_strides, k, k_strides, v, v_strides, o, o_strides, lse, B, H, N,
+                  d, scale, causal, seqlens_k, block_mask, mask_block, 0.f, 0, 0, stream);
+}
+
+fa_status fa_fwd_dropout(fa_dtype dtype, const void* q, fa_strides q_strides, const void* k,
+                         fa_strides k_strides, const void* v, fa_strides v_strides, void* o,
+                         fa_strides o_strides, float* lse, int B, int H, int N, int d,
+                         float scale, int causal, const int32_t* seqlens_k,
+                         const uint8_t* block_mask, int mask_block, float dropout_p,
+                         uint64_t seed, uint32_t offset, hipStream_t stream) {
+  return fwd_impl(dtype, q, q_strides, k, k_strides, v, v_strides, o, o_strides, lse, B, H, N,
+                  d, scale, causal, seqlens_k, block_mask, mask_block, dropout_p, seed, offset,
+                  stream);
 }
 
 size_t fa_bwd_workspace_bytes(fa_dtype dtype, int B, int H, int N, int d) {
@@ -139,7 +179,8 @@ fa_status bwd_impl(int phases, fa_dtype dtype, const void* q, fa_strides q_strid
                    void* dk, fa_strides dk_strides, void* dv, fa_strides dv_strides,
                    void* workspace, size_t workspace_bytes, int B, int H, int N, int d,
                    float scale, int causal, const int32_t* seqlens_k,
-                   const uint8_t* block_mask, int mask_block, hipStream_t stream) {
+                   const uint8_t* block_mask, int mask_block, float dropout_p, uint64_t seed,
+                   uint32_t offset, hipStream_t stream) {
   int al = 0;
   fa_status st = check_common(dtype, B, H, N, d, scale, block_mask, mask_block, &al);
   if (st != FA_OK) return st;
@@ -168,6 +209,8 @@ fa_status bwd_impl(int phases, fa_dtype dtype, const void* q, fa_strides q_strid
   }
   if (seqlens_k != nullptr && ((uintptr_t)seqlens_k & 3u))
     return fail(FA_ERR_INVALID_ARG, "seqlens_k is not 4-byte aligned");
+  fa::Dropout drop{};
+  if ((st = make_dropout(dropout_p, seed, offset, &drop)) != FA_OK) return st;
 
   fa::BwdArgs a{};
   a.q = q;
@@ -196,6 +239,7 @@ fa_status bwd_impl(int phases, fa_dtype dtype, const void* q, fa_strides q_strid
   a.bmask = block_mask;
   a.mask_block = block_mask ? mask_block : 128;
   a.n_mask_tiles = (N + a.mask_block - 1) / a.mask_block;
+  a.drop = drop;
   const hipError_t e = dtype == FA_BF16 ? fa::launch_bwd_bf16(a, causal != 0, phases, stream)
                                         : fa::launch_bwd_f32(a, causal != 0, phases, stream);
   return hip_status(e);
@@ -216,7 +260,22 @@ fa_status fa_bwd(fa_dtype dtype, const void* q, fa_strides q_strides, const void
   return bwd_impl(fa::kPhaseDQ | fa::kPhaseDKDV, dtype, q, q_strides, k, k_strides, v,
                   v_strides, o, o_strides, dout, dout_strides, lse, dq, dq_strides, dk,
                   dk_strides, dv, dv_strides, workspace, workspace_bytes, B, H, N, d, scale,
-                  causal, seqlens_k, block_mask, mask_block, stream);
+                  causal, seqlens_k, block_mask, mask_block, 0.f, 0, 0, stream);
+}
+
+fa_status fa_bwd_dropout(fa_dtype dtype, const void* q, fa_strides q_strides, const void* k,
+                         fa_strides k_strides, const void* v, fa_strides v_strides,
+                         const void* o, fa_strides o_strides, const void* dout,
+                         fa_strides dout_strides, const float* lse, void* dq,
+                         fa_strides dq_strides, void* dk, fa_strides dk_strides, void* dv,
+                         fa_strides dv_strides, void* workspace, size_t workspace_bytes, int B,
+                         int H, int N, int d, float scale, int causal,
+                         const int32_t* seqlens_k, const uint8_t* block_mask, int mask_block,
+                         float dropout_p, uint64_t seed, uint32_t offset, hipStream_t stream) {
+  return bwd_impl(fa::kPhaseDQ | fa::kPhaseDKDV, dtype, q, q_strides, k, k_strides, v,
+                  v_strides, o, o_strides, dout, dout_strides, lse, dq, dq_strides, dk,
+                  dk_strides, dv, dv_strides, workspace, workspace_bytes, B, H, N, d, scale,
+                  causal, seqlens_k, block_mask, mask_block, dropout_p, seed, offset, stream);
 }
 
 fa_status fa_bwd_dq(fa_dtype dtype, const void* q, fa_strides q_strides, const void* k,
@@ -230,7 +289,7 @@ fa_status fa_bwd_dq(fa_dtype dtype, const void* q, fa_strides q_strides, const v
   return bwd_impl(fa::kPhaseDQ, dtype, q, q_strides, k, k_strides, v, v_strides, o,
                   o_strides, dout, dout_strides, lse, dq, dq_strides, nullptr, none, nullptr,
                   none, workspace, workspace_bytes, B, H, N, d, scale, causal, seqlens_k,
-                  block_mask, mask_block, stream);
+                  block_mask, mask_block, 0.f, 0, 0, stream);
 }
 
 fa_status fa_bwd_dkdv(fa_dtype dtype, const void* q, fa_strides q_strides, const void* k,
@@ -245,7 +304,7 @@ fa_status fa_bwd_dkdv(fa_dtype dtype, const void* q, fa_strides q_strides, const
   return bwd_impl(fa::kPhaseDKDV, dtype, q, q_strides, k, k_strides, v, v_strides, o,
                   o_strides, dout, dout_strides, lse, nullptr, none, dk, dk_strides, dv,
                   dv_strides, workspace, workspace_bytes, B, H, N, d, scale, causal, seqlens_k,
-                  block_mask, mask_block, stream);
+                  block_mask, mask_block, 0.f, 0, 0, stream);
 }
 
 const char* fa_status_string(fa_status status) {

@@ -23,6 +23,14 @@
 // One launch carries both roles, heaviest work first, so that the GPU stays
 // busy to the end without a second kernel's launch gap and tail.  Masked tiles are skipped exactly as
 // in the forward pass.
+//
+// Dropout (DROP), with keep indicator Z and keep scale s:
+//   dV = (s Z P)^T dO,  dP = s Z (dO V^T),  dS = P (dP - D),  D_i = dot(dO_i, O_i).
+// Each role regenerates the forward pass's keep bytes, one Philox call per
+// lane and 32 x 32 block, in its MFMA-only slots; the dK/dV role holds the
+// pairs key-major and transposes the bytes of its call first.  There dP no
+// longer starts at -D (a dropped pair still needs -P D), so -D is read from
+// LDS next to the pair instead.
 #include <type_traits>
 
 #include "fa_device.h"
@@ -37,7 +45,7 @@ constexpr int kBK = 128;   // dK/dV role: key rows per workgroup
 
 // dQ for the 128 queries of work item `item` (query tile, batch, head).
 // s_k0/s_v0 and s_k1/s_v1 are the two K/V tile buffers.
-template <bool CAUSAL, bool SEQLEN, bool BMASK>
+template <bool CAUSAL, bool SEQLEN, bool BMASK, bool DROP>
 __device__ __forceinline__ void dq_role(const BwdArgs& a, int item, uint16_t* s_k0,
                                         uint16_t* s_v0, uint16_t* s_k1, uint16_t* s_v1,
                                         uint16_t* s_list, int* s_scan) {
@@ -139,6 +147,7 @@ __device__ __forceinline__ void dq_role(const BwdArgs& a, int item, uint16_t* s_
     f32x16 st[2] = {zero16(), zero16()}, dpt[2] = {zero16(), zero16()};
     uint32_t pkd[4][4];  // bf16 pairs of dS per step
     bf16x8 opa[24];
+    [[maybe_unused]] DropBlock zb[2];  // keep bytes of the two halves
     [[maybe_unused]] int lim = 0;
     if constexpr (MASK) lim = (CAUSAL ? min(kv_len - 1, qi) : kv_len - 1) - k0 - 4 * hl;
     // A operand of slot t
@@ -162,7 +171,12 @@ __device__ __forceinline__ void dq_role(const BwdArgs& a, int item, uint16_t* s_
           if (32 * kb + 8 * (e >> 2) + (e & 3) > lim) sv = -kInf;
         }
         const float p = fast_exp2(__builtin_fmaf(sv, c, -L2));
-        ds[x] = p * (dpt[kb][e] - Dq);
+        if constexpr (DROP) {
+          const float dpe = drop_keep(zb[kb], e, a.drop.t) ? a.drop.scale * dpt[kb][e] : 0.f;
+          ds[x] = p * (dpe - Dq);
+        } else {
+          ds[x] = p * (dpt[kb][e] - Dq);
+        }
       }
       pkd[2 * kb + (ch >> 2)][ch & 3] = pack2(ds[0], ds[1]);
     };
@@ -190,6 +204,17 @@ __device__ __forceinline__ void dq_role(const BwdArgs& a, int item, uint16_t* s_
         if ((t - 16) & 1) probs(1, ((3 * (t - 16)) >> 1) + 1);
       }
       if (t == 20 || t == 21) probs(1, t - 14);
+      if constexpr (DROP) {  // half t / 4, in the MFMA-only slots 0..7
+        if (t < 8) {
+          DropBlock& z = zb[t >> 2];
+          if ((t & 3) == 0)
+            drop_start(z, (uint32_t)((k0 >> 2) + 8 * (t >> 2) + 2 * (lane & 3) + hl),
+                       (uint32_t)(qi >> 2), (uint32_t)bh, a.drop.offset);
+          const int r0 = (10 * (t & 3)) >> 2, r1 = (10 * ((t & 3) + 1)) >> 2;
+          philox_rounds(z.v, a.drop.seed_lo, a.drop.seed_hi, r0, r1);
+          if ((t & 3) == 3) drop_finish<false>(z, lane);
+        }
+      }
       FA_FENCE();
     }
   };
@@ -244,7 +269,7 @@ __device__ __forceinline__ void dq_role(const BwdArgs& a, int item, uint16_t* s_
 // dK, dV for the 128 keys of work item `item` (key tile, batch, head).
 // s_q0/s_do0/s_o0 and s_q1/s_do1/s_o1 are the two Q/dO/O tile buffers;
 // s_nl and s_nd hold -L / scale and -D of each buffer's 64 rows.
-template <bool CAUSAL, bool SEQLEN, bool BMASK>
+template <bool CAUSAL, bool SEQLEN, bool BMASK, bool DROP>
 __device__ __forceinline__ void dkdv_role(const BwdArgs& a, int item, uint16_t* s_q0,
                                           uint16_t* s_do0, uint16_t* s_o0, uint16_t* s_q1,
                                           uint16_t* s_do1, uint16_t* s_o1,
@@ -385,6 +410,7 @@ __device__ __forceinline__ void dkdv_role(const BwdArgs& a, int item, uint16_t* 
       f32x16 sc_[2], dp[2];
       uint32_t pkp[4][4], pkd[4][4];  // bf16 pairs of P and dS per step
       bf16x8 opa[32];
+      [[maybe_unused]] DropBlock zb[2];  // keep bytes of the two halves
       // A operand of slot t.
       auto load_a = [&](int t) FA_INLINE {
         if (t < 16) {
@@ -403,11 +429,19 @@ __device__ __forceinline__ void dkdv_role(const BwdArgs& a, int item, uint16_t* 
         for (int j = 0; j < 4; ++j) {
           const int row = 32 * qb + 8 * j + 4 * hl;
           const f32x4 l4 = *reinterpret_cast<const f32x4*>(&s_nl[buf][row]);
-          const f32x4 d4 = *reinterpret_cast<const f32x4*>(&s_nd[buf][row]);
+          if constexpr (DROP) {
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            sc_[qb][4 * j + i] = l4[i];
-            dp[qb][4 * j + i] = d4[i];
+            for (int i = 0; i < 4; ++i) {
+              sc_[qb][4 * j + i] = l4[i];
+              dp[qb][4 * j + i] = 0.f;
+            }
+          } else {
+            const f32x4 d4 = *reinterpret_cast<const f32x4*>(&s_nd[buf][row]);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              sc_[qb][4 * j + i] = l4[i];
+              dp[qb][4 * j + i] = d4[i];
+            }
           }
         }
       };
@@ -415,6 +449,10 @@ __device__ __forceinline__ void dkdv_role(const BwdArgs& a, int item, uint16_t* 
       // dS = P (dP - D), each pair rounded to bf16.
       auto probs = [&](int qb, int ch) FA_INLINE {
         float pv[2], dv2[2];
+        [[maybe_unused]] float2 nd2;
+        if constexpr (DROP)  // -D of the pair's two query rows
+          nd2 = *reinterpret_cast<const float2*>(
+              &s_nd[buf][32 * qb + 8 * (ch >> 1) + 4 * hl + 2 * (ch & 1)]);
 #pragma unroll
         for (int x = 0; x < 2; ++x) {
           const int e = 2 * ch + x;
@@ -423,7 +461,14 @@ __device__ __forceinline__ void dkdv_role(const BwdArgs& a, int item, uint16_t* 
             if (32 * qb + 8 * (e >> 2) + (e & 3) < key_lim - qs) sv = -kInf;
           }
           pv[x] = fast_exp2(sv);
-          dv2[x] = dp[qb][e] * pv[x];
+          if constexpr (DROP) {
+            const bool keep = drop_keep(zb[qb], e, a.drop.t);
+            const float nd = x ? nd2.y : nd2.x;
+            dv2[x] = pv[x] * ((keep ? a.drop.scale * dp[qb][e] : 0.f) + nd);
+            pv[x] = keep ? pv[x] : 0.f;
+          } else {
+            dv2[x] = dp[qb][e] * pv[x];
+          }
         }
         pkp[2 * qb + (ch >> 2)][ch & 3] = pack2(pv[0], pv[1]);
         pkd[2 * qb + (ch >> 2)][ch & 3] = pack2(dv2[0], dv2[1]);
@@ -455,6 +500,18 @@ __device__ __forceinline__ void dkdv_role(const BwdArgs& a, int item, uint16_t* 
             dvt[db] = mfma32(opa[t], bop, dvt[db]);
         }
         if (t >= 8 && t < 24) probs((t - 8) >> 3, (t - 8) & 7);
+        if constexpr (DROP) {  // half t / 4, in slots 0..7
+          if (t < 8) {
+            DropBlock& z = zb[t >> 2];
+            if ((t & 3) == 0)
+              drop_start(z, (uint32_t)(kj >> 2),
+                         (uint32_t)((qs >> 2) + 8 * (t >> 2) + 2 * (lane & 3) + hl),
+                         (uint32_t)bh, a.drop.offset);
+            const int r0 = (10 * (t & 3)) >> 2, r1 = (10 * ((t & 3) + 1)) >> 2;
+            philox_rounds(z.v, a.drop.seed_lo, a.drop.seed_hi, r0, r1);
+            if ((t & 3) == 3) drop_finish<true>(z, lane);
+          }
+        }
         FA_FENCE();
       }
     };
@@ -508,7 +565,7 @@ __device__ __forceinline__ void dkdv_role(const BwdArgs& a, int item, uint16_t* 
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           k4[i] = (__bf16)(dkt[db][4 * j + i] * a.scale);
-          v4[i] = (__bf16)dvt[db][4 * j + i];
+          v4[i] = (__bf16)(DROP ? dvt[db][4 * j + i] * a.drop.scale : dvt[db][4 * j + i]);
         }
         *reinterpret_cast<bf16x4*>(kout + 32 * db + 8 * j + 4 * hl) = k4;
         *reinterpret_cast<bf16x4*>(vout + 32 * db + 8 * j + 4 * hl) = v4;
@@ -519,7 +576,7 @@ __device__ __forceinline__ void dkdv_role(const BwdArgs& a, int item, uint16_t* 
 // The fused backward kernel.  Work items: query tiles for the dQ role and
 // key tiles for the dK/dV role (each times B*H), each role in its own
 // heavy-first order.
-template <bool CAUSAL, bool SEQLEN, bool BMASK>
+template <bool CAUSAL, bool SEQLEN, bool BMASK, bool DROP>
 __global__ __launch_bounds__(256) void bwd_kernel(BwdArgs a, int phases) {
   // Six tile arrays: the dQ role uses two per buffer (K, V), the dK/dV role
   // three (Q, dO, O).  Separate arrays, so that the copies into one buffer
@@ -562,13 +619,13 @@ __global__ __launch_bounds__(256) void bwd_kernel(BwdArgs a, int phases) {
     item = id;
   }
   if (dkdv)
-    dkdv_role<CAUSAL, SEQLEN, BMASK>(a, item, s_a0, s_b0, s_c0, s_a1, s_b1, s_c1, s_nl, s_nd,
+    dkdv_role<CAUSAL, SEQLEN, BMASK, DROP>(a, item, s_a0, s_b0, s_c0, s_a1, s_b1, s_c1, s_nl, s_nd,
                                      s_list, s_scan);
   else
-    dq_role<CAUSAL, SEQLEN, BMASK>(a, item, s_a0, s_b0, s_a1, s_b1, s_list, s_scan);
+    dq_role<CAUSAL, SEQLEN, BMASK, DROP>(a, item, s_a0, s_b0, s_a1, s_b1, s_list, s_scan);
 }
 
-template <bool C, bool S, bool M>
+template <bool C, bool S, bool M, bool D>
 hipError_t launch(const BwdArgs& a, int phases, hipStream_t stream) {
   static_assert(kBQ == kBK, "the interleaved grid pairs one query tile with one key tile");
   BwdArgs copy = a;
@@ -581,21 +638,26 @@ hipError_t launch(const BwdArgs& a, int phases, hipStream_t stream) {
   else if (phases == kPhaseDQ || phases == kPhaseDKDV)
     n = per_role;
   if (n == 0) return hipSuccess;
-  return hipLaunchKernel((const void*)&bwd_kernel<C, S, M>, dim3((unsigned)n), dim3(256), args,
-                         0, stream);
+  return hipLaunchKernel((const void*)&bwd_kernel<C, S, M, D>, dim3((unsigned)n), dim3(256),
+                         args, 0, stream);
+}
+
+template <bool D>
+hipError_t dispatch(const BwdArgs& a, bool causal, int p, hipStream_t stream) {
+  const bool s = a.seqlens != nullptr, m = a.bmask != nullptr;
+  if (causal) {
+    if (s) return m ? launch<true, true, true, D>(a, p, stream) : launch<true, true, false, D>(a, p, stream);
+    return m ? launch<true, false, true, D>(a, p, stream) : launch<true, false, false, D>(a, p, stream);
+  }
+  if (s) return m ? launch<false, true, true, D>(a, p, stream) : launch<false, true, false, D>(a, p, stream);
+  return m ? launch<false, false, true, D>(a, p, stream) : launch<false, false, false, D>(a, p, stream);
 }
 
 }  // namespace
 
 hipError_t launch_bwd_bf16(const BwdArgs& a, bool causal, int phases, hipStream_t stream) {
-  const bool s = a.seqlens != nullptr, m = a.bmask != nullptr;
-  const int p = phases;
-  if (causal) {
-    if (s) return m ? launch<true, true, true>(a, p, stream) : launch<true, true, false>(a, p, stream);
-    return m ? launch<true, false, true>(a, p, stream) : launch<true, false, false>(a, p, stream);
-  }
-  if (s) return m ? launch<false, true, true>(a, p, stream) : launch<false, true, false>(a, p, stream);
-  return m ? launch<false, false, true>(a, p, stream) : launch<false, false, false>(a, p, stream);
+  return a.drop.t < 256 ? dispatch<true>(a, causal, phases, stream)
+                        : dispatch<false>(a, causal, phases, stream);
 }
 
 }  // namespace fa

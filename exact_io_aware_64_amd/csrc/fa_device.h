@@ -18,11 +18,6 @@ constexpr float kInf = __builtin_inff();
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
-// Row stride (in 16-bit elements) of a row-major 64x64 tile in LDS.  The pad
-// of 8 elements spreads the 16-byte reads of 16 consecutive rows over all
-// banks.
-constexpr int kRowStride = 72;
-
 __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
   // D[32x32] += A[32x16] * B[16x32].  Lane l supplies row (l % 32) of A and
   // column (l % 32) of B, both at contraction slots 8*(l/32) .. 8*(l/32)+7, and
@@ -109,39 +104,7 @@ __device__ __forceinline__ uint32_t slice_bytes(int n, int64_t ss, int esize) {
 
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 u) { return __builtin_bit_cast(bf16x8, u); }
 
-// 8 bf16 of one LDS row (16-byte aligned).
-__device__ __forceinline__ bf16x8 lds_row8(const uint16_t* p) {
-  return *reinterpret_cast<const bf16x8*>(p);
-}
-
 typedef short i16x4 __attribute__((ext_vector_type(4)));
-
-// Per-lane offset (in elements) for tr_operand over a row-major tile with row
-// stride kRowStride.
-__device__ __forceinline__ int tr_lane_offset(int lane) {
-  const int j = lane & 15, g = lane >> 4;
-  return (4 * (g >> 1) + (j >> 2)) * kRowStride + 16 * (g & 1) + 4 * (j & 3);
-}
-
-// A operand of a 32x32x16 MFMA whose contraction runs over the ROWS of a
-// row-major LDS tile X: lane (r, hl) receives X[rbase + 4 hl + t][cbase + r]
-// in slots t = 0..3 and X[rbase + 8 + 4 hl + t][cbase + r] in slots 4..7.
-// Built from two ds_read_b64_tr_b16: within each 16-lane group, lane i
-// receives element 16 t + i (t = 0..3) of the 64 elements the group reads,
-// so source lane j reads X[row0 + j / 4][col0 + 4 (j % 4) .. +3].
-// `p` = tile + tr_lane_offset(lane) + rbase * kRowStride + cbase.
-__device__ __forceinline__ bf16x8 tr_operand(const uint16_t* p) {
-  typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
-  const lds_i16x4* lo = (const lds_i16x4*)(p);
-  const lds_i16x4* hi = (const lds_i16x4*)(p + 8 * kRowStride);
-  const i16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16(const_cast<lds_i16x4*>(lo));
-  const i16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16(const_cast<lds_i16x4*>(hi));
-  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7));
-}
-
-__device__ __forceinline__ void store_row16(uint16_t* t, int row, int c, uint4 a) {
-  *reinterpret_cast<uint4*>(t + row * kRowStride + 8 * c) = a;
-}
 
 // ---------------------------------------------------------------------------
 // Swizzled 64 x 64 bf16 tiles in LDS.
@@ -279,6 +242,116 @@ __device__ __forceinline__ int build_tile_list(uint16_t* list, int* scratch4,
     __syncthreads();
   }
   return base;
+}
+
+// ---------------------------------------------------------------------------
+// Dropout keep bytes.
+//
+// Every (query i, key j) pair of head slice bh gets an 8-bit uniform number
+// from Philox4x32 with 10 rounds (Salmon, Moraes, Dror and Shaw, SC'11),
+// keyed by the 64-bit seed: the call with counter (j / 4, i / 4, bh, offset)
+// covers the 4 x 4 block of pairs with those quotients, output word i % 4
+// holding the four keys of query i in its bytes (key j % 4 in byte j % 4,
+// least significant first).  A pair is kept iff its byte is below the
+// threshold t, so the forward and backward passes regenerate the same mask
+// without storing it.
+
+// Rounds r0 .. r1-1 of Philox4x32 on counter x with key (k0, k1); a call
+// split over several schedule slots runs its rounds in pieces.  The empty asm
+// makes the key opaque, so the round keys are formed on the scalar ALU where
+// they are used instead of being hoisted out of the tile loop, where the ten
+// pairs would occupy twenty scalar registers for the whole kernel.
+__device__ __forceinline__ void philox_rounds(uint32_t (&x)[4], uint32_t k0, uint32_t k1,
+                                              int r0, int r1) {
+  __asm__("" : "+s"(k0), "+s"(k1));
+#pragma unroll
+  for (int r = r0; r < r1; ++r) {
+    const uint32_t ka = k0 + (uint32_t)r * 0x9E3779B9u;  // Weyl key schedule
+    const uint32_t kb = k1 + (uint32_t)r * 0xBB67AE85u;
+    const uint64_t p0 = (uint64_t)0xD2511F53u * x[0];
+    const uint64_t p1 = (uint64_t)0xCD9E8D57u * x[2];
+    const uint32_t y0 = (uint32_t)(p1 >> 32) ^ x[1] ^ ka;
+    const uint32_t y2 = (uint32_t)(p0 >> 32) ^ x[3] ^ kb;
+    x[1] = (uint32_t)p1;
+    x[3] = (uint32_t)p0;
+    x[0] = y0;
+    x[2] = y2;
+  }
+}
+
+__device__ __forceinline__ uint32_t quad_xor1_u(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0xB1, 0xF, 0xF, true);
+}
+__device__ __forceinline__ uint32_t quad_xor2_u(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x4E, 0xF, 0xF, true);
+}
+
+// In every aligned group of four lanes, lane x ends with v[g] = (v[x] of lane
+// g): a 4 x 4 transpose of words over the group, in two butterfly stages
+// that each swap the off-diagonal halves with the partner lane.
+__device__ __forceinline__ void quad_transpose(uint32_t (&v)[4], int lane) {
+  const bool b0 = lane & 1, b1 = lane & 2;
+#pragma unroll
+  for (int w = 0; w < 4; w += 2) {
+    const uint32_t got = quad_xor1_u(b0 ? v[w] : v[w + 1]);
+    if (b0)
+      v[w] = got;
+    else
+      v[w + 1] = got;
+  }
+#pragma unroll
+  for (int w = 0; w < 2; ++w) {
+    const uint32_t got = quad_xor2_u(b1 ? v[w] : v[w + 2]);
+    if (b1)
+      v[w] = got;
+    else
+      v[w + 2] = got;
+  }
+}
+
+// 4 x 4 byte transpose within one lane: byte y of word x <- byte x of word y.
+__device__ __forceinline__ void byte_transpose(uint32_t (&v)[4]) {
+  uint32_t t[4];
+#pragma unroll
+  for (int x = 0; x < 4; ++x)
+    t[x] = ((v[0] >> (8 * x)) & 0xFFu) | (((v[1] >> (8 * x)) & 0xFFu) << 8) |
+           (((v[2] >> (8 * x)) & 0xFFu) << 16) | (((v[3] >> (8 * x)) & 0xFFu) << 24);
+#pragma unroll
+  for (int x = 0; x < 4; ++x) v[x] = t[x];
+}
+
+// Keep bytes of one lane for a 32 x 32 block of pairs in the MFMA
+// accumulator layout, where the lane holds element 4 g + y at "row"
+// 8 g + 4 hl + y of the block (g, y = 0..3) and one fixed "column":
+//  * query-major (forward, dQ): the column is the lane's query qi and rows
+//    are keys from kb0; the lane's call is the block (qi / 4,
+//    kb0 / 4 + 2 (lane % 4) + hl), and after the quad transpose v[g] is
+//    word qi % 4 of block g, i.e. the bytes of keys kb0 + 8 g + 4 hl + 0..3.
+//  * key-major (dK/dV): the column is the lane's key kj and rows are queries
+//    from qb0; the lane's call is the block (qb0 / 4 + 2 (lane % 4) + hl,
+//    kj / 4); after the byte transpose word x holds key 4 (kj / 4) + x of
+//    the block's four queries, and after the quad transpose v[g] holds
+//    key kj of queries qb0 + 8 g + 4 hl + 0..3.
+// Either way byte y of v[g] belongs to element 4 g + y.  The Philox rounds
+// run between `start` and `finish` so that callers can spread them.
+struct DropBlock {
+  uint32_t v[4];
+};
+__device__ __forceinline__ void drop_start(DropBlock& d, uint32_t key_quad,
+                                           uint32_t query_quad, uint32_t bh, uint32_t offset) {
+  d.v[0] = key_quad;
+  d.v[1] = query_quad;
+  d.v[2] = bh;
+  d.v[3] = offset;
+}
+template <bool KEY_MAJOR>
+__device__ __forceinline__ void drop_finish(DropBlock& d, int lane) {
+  if constexpr (KEY_MAJOR) byte_transpose(d.v);
+  quad_transpose(d.v, lane);
+}
+// Is element e (0..15) of the block kept?
+__device__ __forceinline__ bool drop_keep(const DropBlock& d, int e, uint32_t t) {
+  return ((d.v[e >> 2] >> (8 * (e & 3))) & 0xFFu) < t;
 }
 
 }  // namespace fa

@@ -8,7 +8,10 @@
 // owns one query (forward, dQ) or one key (dK/dV); every thread of a
 // workgroup reads the same LDS row at the same time (a broadcast).  This path
 // serves full-precision callers and small problems; the bf16 MFMA kernels are
-// the throughput path.
+// the throughput path.  With dropout, each thread makes one Philox call per
+// four consecutive pairs of its loop: the block of query i and keys j..j+3
+// gives key j % 4's byte of word i % 4 (forward, dQ); the block of queries
+// i..i+3 and key j gives byte j % 4 of each word (dK/dV).
 #include "fa_device.h"
 
 namespace fa {
@@ -54,6 +57,28 @@ __device__ __forceinline__ float dot_lds(const float* x, const float* lds_row) {
   return acc;
 }
 
+// The Philox call of pairs (queries 4 qq .. +3, keys 4 kq .. +3) of slice bh.
+__device__ __forceinline__ void drop_call(uint32_t (&w)[4], const Dropout& d, int qq, int kq,
+                                          int bh) {
+  w[0] = (uint32_t)kq;
+  w[1] = (uint32_t)qq;
+  w[2] = (uint32_t)bh;
+  w[3] = d.offset;
+  philox_rounds(w, d.seed_lo, d.seed_hi, 0, 10);
+}
+
+__device__ __forceinline__ bool keep_byte(uint32_t word, int byte, uint32_t t) {
+  return ((word >> (8 * byte)) & 0xFFu) < t;
+}
+
+// w[i] for a run-time i, by selects (an indexed private array would live in
+// scratch memory).
+__device__ __forceinline__ uint32_t pick4(const uint32_t (&w)[4], int i) {
+  const uint32_t lo = (i & 1) ? w[1] : w[0], hi = (i & 1) ? w[3] : w[2];
+  return (i & 2) ? hi : lo;
+}
+
+template <bool DROP>
 __global__ __launch_bounds__(64) void fwd_f32_kernel(FwdArgs a, int causal) {
   __shared__ __attribute__((aligned(16))) float s_k[kTile * kD];
   __shared__ __attribute__((aligned(16))) float s_v[kTile * kD];
@@ -83,6 +108,20 @@ __global__ __launch_bounds__(64) void fwd_f32_kernel(FwdArgs a, int causal) {
     stage_row(s_k + tid * kD, K + (int64_t)kk * a.sk.s, kk < a.N);
     stage_row(s_v + tid * kD, V + (int64_t)kk * a.sv.s, kk < a.N);
     __syncthreads();
+    // keep bit j of this query and key k0 + j (all ones without dropout)
+    uint64_t keep = ~0ull;
+    if constexpr (DROP) {
+      keep = 0;
+#pragma unroll 1
+      for (int g = 0; g < kTile / 4; ++g) {
+        uint32_t w[4];
+        drop_call(w, a.drop, qi >> 2, (k0 >> 2) + g, bh);
+        const uint32_t word = pick4(w, qi & 3);
+#pragma unroll
+        for (int y = 0; y < 4; ++y)
+          if (keep_byte(word, y, a.drop.t)) keep |= 1ull << (4 * g + y);
+      }
+    }
     float s[kTile];
     float mx = -kInf;
 #pragma unroll
@@ -100,8 +139,9 @@ __global__ __launch_bounds__(64) void fwd_f32_kernel(FwdArgs a, int causal) {
     for (int e = 0; e < kD; ++e) o[e] *= alpha;
 #pragma unroll
     for (int j = 0; j < kTile; ++j) {
-      const float p = fast_exp2(__builtin_fmaf(s[j], c, -m_use));
+      float p = fast_exp2(__builtin_fmaf(s[j], c, -m_use));
       l += p;
+      if constexpr (DROP) p = ((keep >> j) & 1) ? p : 0.f;
 #pragma unroll
       for (int e = 0; e < kD; ++e) o[e] = __builtin_fmaf(p, s_v[j * kD + e], o[e]);
     }
@@ -110,12 +150,13 @@ __global__ __launch_bounds__(64) void fwd_f32_kernel(FwdArgs a, int causal) {
   }
   if (qi < a.N) {
     store_row((float*)a.o + b * a.so.b + hh * a.so.h + (int64_t)qi * a.so.s, o,
-              l > 0.f ? 1.f / l : 0.f);
+              l > 0.f ? (DROP ? a.drop.scale : 1.f) / l : 0.f);
     a.lse[(int64_t)bh * a.N + qi] = l > 0.f ? (m + __builtin_amdgcn_logf(l)) * kLn2 : -kInf;
   }
 }
 
 // dQ for one query per thread.
+template <bool DROP>
 __global__ __launch_bounds__(64) void dq_f32_kernel(BwdArgs a, int causal) {
   __shared__ __attribute__((aligned(16))) float s_k[kTile * kD];
   __shared__ __attribute__((aligned(16))) float s_v[kTile * kD];
@@ -152,12 +193,17 @@ __global__ __launch_bounds__(64) void dq_f32_kernel(BwdArgs a, int causal) {
     stage_row(s_k + tid * kD, K + (int64_t)kk * a.sk.s, kk < a.N);
     stage_row(s_v + tid * kD, V + (int64_t)kk * a.sv.s, kk < a.N);
     __syncthreads();
+    [[maybe_unused]] uint32_t zw[4] = {0u, 0u, 0u, 0u};
     for (int j = 0; j < kTile; ++j) {
       const int key = k0 + j;
       const bool vis = key < kv_len && (!causal || key <= qi);
       const float s = dot_lds(q, s_k + j * kD);
       const float p = vis ? fast_exp2(__builtin_fmaf(s, c, -L2)) : 0.f;
-      const float dp = dot_lds(g, s_v + j * kD);
+      float dp = dot_lds(g, s_v + j * kD);
+      if constexpr (DROP) {
+        if ((j & 3) == 0) drop_call(zw, a.drop, qi >> 2, key >> 2, bh);
+        dp = keep_byte(pick4(zw, qi & 3), j & 3, a.drop.t) ? a.drop.scale * dp : 0.f;
+      }
       const float ds = p * (dp - D);
 #pragma unroll
       for (int e = 0; e < kD; ++e) acc[e] = __builtin_fmaf(ds, s_k[j * kD + e], acc[e]);
@@ -170,6 +216,7 @@ __global__ __launch_bounds__(64) void dq_f32_kernel(BwdArgs a, int causal) {
 
 // dK, dV for one key per thread.  Each staged query row also gets its
 // D_i = dot(dO_i, O_i), computed by the thread that stages it.
+template <bool DROP>
 __global__ __launch_bounds__(64) void dkdv_f32_kernel(BwdArgs a, int causal) {
   __shared__ __attribute__((aligned(16))) float s_q[kTile * kD];
   __shared__ __attribute__((aligned(16))) float s_g[kTile * kD];
@@ -211,16 +258,24 @@ __global__ __launch_bounds__(64) void dkdv_f32_kernel(BwdArgs a, int causal) {
       }
       s_d[tid] = dd;
       __syncthreads();
+      [[maybe_unused]] uint32_t zw[4] = {0u, 0u, 0u, 0u};
       for (int i = 0; i < kTile; ++i) {
         const int q = qs + i;
         const bool vis = kj < kv_len && (!causal || kj <= q);
         const float s = dot_lds(kr, s_q + i * kD);
-        const float p = vis ? fast_exp2(__builtin_fmaf(s, c, -s_l2[i])) : 0.f;
-        const float dp = dot_lds(vr, s_g + i * kD);
+        float p = vis ? fast_exp2(__builtin_fmaf(s, c, -s_l2[i])) : 0.f;
+        float dp = dot_lds(vr, s_g + i * kD);
+        float pv = p;  // the weight of dO_i in dV
+        if constexpr (DROP) {
+          if ((i & 3) == 0) drop_call(zw, a.drop, q >> 2, kj >> 2, bh);
+          const bool keep = keep_byte(pick4(zw, i & 3), kj & 3, a.drop.t);
+          dp = keep ? a.drop.scale * dp : 0.f;
+          pv = keep ? p : 0.f;
+        }
         const float ds = p * (dp - s_d[i]);
 #pragma unroll
         for (int e = 0; e < kD; ++e) {
-          dv[e] = __builtin_fmaf(p, s_g[i * kD + e], dv[e]);
+          dv[e] = __builtin_fmaf(pv, s_g[i * kD + e], dv[e]);
           dk[e] = __builtin_fmaf(ds, s_q[i * kD + e], dk[e]);
         }
       }
@@ -229,7 +284,8 @@ __global__ __launch_bounds__(64) void dkdv_f32_kernel(BwdArgs a, int causal) {
   }
   if (kj < a.N) {
     store_row((float*)a.dk + b * a.sdk.b + hh * a.sdk.h + (int64_t)kj * a.sdk.s, dk, a.scale);
-    store_row((float*)a.dv + b * a.sdv.b + hh * a.sdv.h + (int64_t)kj * a.sdv.s, dv, 1.f);
+    store_row((float*)a.dv + b * a.sdv.b + hh * a.sdv.h + (int64_t)kj * a.sdv.s, dv,
+              DROP ? a.drop.scale : 1.f);
   }
 }
 
@@ -240,7 +296,9 @@ hipError_t launch_fwd_f32(const FwdArgs& a, bool causal, hipStream_t stream) {
   int cz = causal ? 1 : 0;
   void* args[] = {&copy, &cz};
   dim3 grid((unsigned)(((a.N + kTile - 1) / kTile) * a.B * a.H)), block(64);
-  return hipLaunchKernel((const void*)&fwd_f32_kernel, grid, block, args, 0, stream);
+  const void* fn = a.drop.t < 256 ? (const void*)&fwd_f32_kernel<true>
+                                  : (const void*)&fwd_f32_kernel<false>;
+  return hipLaunchKernel(fn, grid, block, args, 0, stream);
 }
 
 hipError_t launch_bwd_f32(const BwdArgs& a, bool causal, int phases, hipStream_t stream) {
@@ -248,12 +306,17 @@ hipError_t launch_bwd_f32(const BwdArgs& a, bool causal, int phases, hipStream_t
   int cz = causal ? 1 : 0;
   void* args[] = {&copy, &cz};
   dim3 grid((unsigned)(((a.N + kTile - 1) / kTile) * a.B * a.H)), block(64);
+  const bool drop = a.drop.t < 256;
   if (phases & kPhaseDQ) {
-    hipError_t e = hipLaunchKernel((const void*)&dq_f32_kernel, grid, block, args, 0, stream);
+    const void* fn = drop ? (const void*)&dq_f32_kernel<true> : (const void*)&dq_f32_kernel<false>;
+    hipError_t e = hipLaunchKernel(fn, grid, block, args, 0, stream);
     if (e != hipSuccess) return e;
   }
-  if (phases & kPhaseDKDV)
-    return hipLaunchKernel((const void*)&dkdv_f32_kernel, grid, block, args, 0, stream);
+  if (phases & kPhaseDKDV) {
+    const void* fn =
+        drop ? (const void*)&dkdv_f32_kernel<true> : (const void*)&dkdv_f32_kernel<false>;
+    return hipLaunchKernel(fn, grid, block, args, 0, stream);
+  }
   return hipSuccess;
 }
 

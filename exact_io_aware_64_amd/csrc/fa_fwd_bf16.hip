@@ -31,6 +31,14 @@
 // Tiles that the mask removes entirely are never loaded: causal and key
 // padding shrink the key range, and a block mask is compacted into a list of
 // kept tiles (suanlizi.com, "block-sparse attention").
+//
+// Dropout (DROP): the pages count dropout among the element-wise operations
+// the fused kernel absorbs (suanlizi.com, per-component timing figure of
+// "kernel fusion").  The keep bytes of each 32-key half come from one Philox
+// call per lane, run in the MFMA-only slots before the half's probabilities
+// are formed; a dropped probability still counts in l (L is the statistic of
+// the undropped softmax) but enters O^T += V^T P^T as zero, and the keep
+// scale is applied with 1 / l at the end.
 #include <type_traits>
 
 #include "fa_device.h"
@@ -41,7 +49,7 @@ namespace {
 constexpr int kBR = 128;               // query rows per workgroup
 constexpr float kSumLimit = 4096.f;    // largest partial sum the fast path accepts
 
-template <bool CAUSAL, bool SEQLEN, bool BMASK>
+template <bool CAUSAL, bool SEQLEN, bool BMASK, bool DROP>
 __global__ __launch_bounds__(256) void fwd_bf16_kernel(FwdArgs a) {
   // Two buffers, each a K tile and a V tile; separate arrays so that the
   // copies into one buffer and the reads of the other never alias.
@@ -141,7 +149,7 @@ __global__ __launch_bounds__(256) void fwd_bf16_kernel(FwdArgs a) {
   };
 
   // One 64-key tile as 16 MFMA issue slots separated by scheduling fences:
-  //   slots  0.. 3  S^T of keys  0..31                 (MFMA)
+  //   slots  0.. 3  S^T of keys  0..31                 (MFMA) | [keep bytes]
   //   slots  4.. 7  S^T of keys 32..63                 (MFMA) | P of keys 0..31
   //   slots  8..11  O^T += V^T P^T, keys 0..31         (MFMA) | P of keys 32..63
   //   slots 12..15  O^T += V^T P^T, keys 32..63        (MFMA)
@@ -152,6 +160,7 @@ __global__ __launch_bounds__(256) void fwd_bf16_kernel(FwdArgs a) {
     bf16x8 ka[2][4], va[4][2];
     uint32_t pk[4][4];   // bf16 pairs of P for PV steps 0..3
     float ps[2] = {0.f, 0.f};
+    [[maybe_unused]] DropBlock zb[2];  // keep bytes of the two halves
     // element e of half kb holds key k0 + 32 kb + 8 (e / 4) + 4 hl + e % 4;
     // visible iff 32 kb + 8 (e / 4) + e % 4 <= lim
     [[maybe_unused]] int lim = 0;
@@ -168,6 +177,7 @@ __global__ __launch_bounds__(256) void fwd_bf16_kernel(FwdArgs a) {
         }
         p[x] = fast_exp2(__builtin_fmaf(sv, c, -m));
         ps[kb] += p[x];
+        if constexpr (DROP) p[x] = drop_keep(zb[kb], e, a.drop.t) ? p[x] : 0.f;
       }
       const int st = 2 * kb + (e0 >> 3), wd = (e0 & 7) >> 1;
       pk[st][wd] = pack2(p[0], p[1]);
@@ -185,9 +195,13 @@ __global__ __launch_bounds__(256) void fwd_bf16_kernel(FwdArgs a) {
       ps[kb] = 0.f;
 #pragma unroll
       for (int e = 0; e < 16; e += 2) {
-        const float p0 = fast_exp2(__builtin_fmaf(s[kb][e], c, -m_use));
-        const float p1 = fast_exp2(__builtin_fmaf(s[kb][e + 1], c, -m_use));
+        float p0 = fast_exp2(__builtin_fmaf(s[kb][e], c, -m_use));
+        float p1 = fast_exp2(__builtin_fmaf(s[kb][e + 1], c, -m_use));
         ps[kb] += p0 + p1;
+        if constexpr (DROP) {
+          p0 = drop_keep(zb[kb], e, a.drop.t) ? p0 : 0.f;
+          p1 = drop_keep(zb[kb], e + 1, a.drop.t) ? p1 : 0.f;
+        }
         pk[2 * kb + (e >> 3)][(e & 7) >> 1] = pack2(p0, p1);
       }
     };
@@ -199,6 +213,14 @@ __global__ __launch_bounds__(256) void fwd_bf16_kernel(FwdArgs a) {
     for (int ks = 0; ks < 4; ++ks) {  // slots 0..3
       s[0] = mfma32(ka[0][ks], qf[ks], s[0]);
       ka[1][ks] = tile_row8(kt, 2048 + roff[ks]);
+      if constexpr (DROP) {  // half ks / 2: rounds 0..4 in even slots, 5..9 in odd
+        DropBlock& z = zb[ks >> 1];
+        if ((ks & 1) == 0)
+          drop_start(z, (uint32_t)((k0 >> 2) + 8 * (ks >> 1) + 2 * (lane & 3) + hl),
+                     (uint32_t)(qi >> 2), (uint32_t)bh, a.drop.offset);
+        philox_rounds(z.v, a.drop.seed_lo, a.drop.seed_hi, 5 * (ks & 1), 5 * (ks & 1) + 5);
+        if (ks & 1) drop_finish<false>(z, lane);
+      }
       FA_FENCE();
     }
 #pragma unroll
@@ -266,7 +288,8 @@ __global__ __launch_bounds__(256) void fwd_bf16_kernel(FwdArgs a) {
 
   const float lt = half_sum(l);
   if (qi < a.N) {
-    const float inv = lt > 0.f ? 1.f / lt : 0.f;
+    float inv = lt > 0.f ? 1.f / lt : 0.f;
+    if constexpr (DROP) inv *= a.drop.scale;
     uint16_t* op = (uint16_t*)a.o + b * a.so.b + hh * a.so.h + (int64_t)qi * a.so.s;
 #pragma unroll
     for (int db = 0; db < 2; ++db)
@@ -283,25 +306,30 @@ __global__ __launch_bounds__(256) void fwd_bf16_kernel(FwdArgs a) {
   }
 }
 
-template <bool C, bool S, bool M>
+template <bool C, bool S, bool M, bool D>
 hipError_t launch(const FwdArgs& a, hipStream_t stream) {
   const int nqt = (a.N + kBR - 1) / kBR;
   dim3 grid((unsigned)(nqt * a.B * a.H)), block(256);
   FwdArgs copy = a;
   void* args[] = {&copy};
-  return hipLaunchKernel((const void*)&fwd_bf16_kernel<C, S, M>, grid, block, args, 0, stream);
+  return hipLaunchKernel((const void*)&fwd_bf16_kernel<C, S, M, D>, grid, block, args, 0, stream);
+}
+
+template <bool D>
+hipError_t dispatch(const FwdArgs& a, bool causal, hipStream_t stream) {
+  const bool s = a.seqlens != nullptr, m = a.bmask != nullptr;
+  if (causal) {
+    if (s) return m ? launch<true, true, true, D>(a, stream) : launch<true, true, false, D>(a, stream);
+    return m ? launch<true, false, true, D>(a, stream) : launch<true, false, false, D>(a, stream);
+  }
+  if (s) return m ? launch<false, true, true, D>(a, stream) : launch<false, true, false, D>(a, stream);
+  return m ? launch<false, false, true, D>(a, stream) : launch<false, false, false, D>(a, stream);
 }
 
 }  // namespace
 
 hipError_t launch_fwd_bf16(const FwdArgs& a, bool causal, hipStream_t stream) {
-  const bool s = a.seqlens != nullptr, m = a.bmask != nullptr;
-  if (causal) {
-    if (s) return m ? launch<true, true, true>(a, stream) : launch<true, true, false>(a, stream);
-    return m ? launch<true, false, true>(a, stream) : launch<true, false, false>(a, stream);
-  }
-  if (s) return m ? launch<false, true, true>(a, stream) : launch<false, true, false>(a, stream);
-  return m ? launch<false, false, true>(a, stream) : launch<false, false, false>(a, stream);
+  return a.drop.t < 256 ? dispatch<true>(a, causal, stream) : dispatch<false>(a, causal, stream);
 }
 
 }  // namespace fa

@@ -16,6 +16,16 @@ struct Strides {
   int64_t b, h, s;
 };
 
+// Dropout on the probabilities: a pair is kept iff its Philox byte is below
+// t, and kept probabilities are multiplied by scale = 256 / t.  t = 256 keeps
+// every pair (no dropout).
+struct Dropout {
+  uint32_t t;
+  float scale;
+  uint32_t seed_lo, seed_hi;
+  uint32_t offset;
+};
+
 struct FwdArgs {
   const void* q;
   const void* k;
@@ -30,6 +40,7 @@ struct FwdArgs {
   const uint8_t* bmask;
   int mask_block;
   int n_mask_tiles;
+  Dropout drop;
 };
 
 struct BwdArgs {
@@ -50,6 +61,7 @@ struct BwdArgs {
   const uint8_t* bmask;
   int mask_block;
   int n_mask_tiles;
+  Dropout drop;
 };
 
 // Backward roles: kPhaseDQ writes dQ, kPhaseDKDV writes dK and dV.  They are

@@ -55,7 +55,7 @@ typedef enum fa_dtype {
 typedef enum fa_status {
   FA_OK = 0,
   FA_ERR_INVALID_ARG = 1, /* null pointer, bad size, stride or alignment, scale <= 0,
-                             workspace too small, bad mask_block */
+                             workspace too small, bad mask_block, bad dropout_p */
   FA_ERR_UNSUPPORTED = 2, /* valid request this build does not implement (d != 64,
                              too many mask tiles) */
   FA_ERR_HIP = 3          /* a HIP launch reported an error */
@@ -179,6 +179,66 @@ fa_status fa_bwd_dkdv(fa_dtype dtype,
                       const int32_t* seqlens_k,
                       const uint8_t* block_mask, int mask_block,
                       hipStream_t stream);
+
+/*
+ * fa_fwd_dropout, fa_bwd_dropout -- fa_fwd and fa_bwd with dropout applied
+ * to the probabilities.  The pages list dropout among the element-wise
+ * operations that standard attention runs as separate kernels and that the
+ * fused kernel absorbs (suanlizi.com summary, per-component timing figure of
+ * "kernel fusion"); they give no formula, so the definition is:
+ *
+ *   O_i = sum_{visible j} s Z_ij exp(s_ij - L_i) v_j,   L_i as for fa_fwd
+ *
+ * (L stays the logsumexp of the undropped scores), with keep indicator Z_ij
+ * and keep scale s = 256 / t, where t = floor(256 (1 - dropout_p) + 1/2)
+ * computed in double.  Z_ij = 1 iff u_ij < t, u_ij being the pair's 8-bit
+ * uniform number from Philox4x32 with 10 rounds (Salmon, Moraes, Dror and
+ * Shaw, "Parallel random numbers: as easy as 1, 2, 3", SC'11) keyed by
+ * (seed & 0xffffffff, seed >> 32): the call with counter
+ * (j / 4, i / 4, b * H + h, offset) yields four 32-bit words, and u_ij is
+ * byte j % 4 (least significant first) of word i % 4.  The effective drop
+ * probability is therefore 1 - t / 256.  fa_bwd_dropout returns the
+ * gradients of sum(dO * O) with the mask held fixed, and needs the same
+ * dropout_p, seed and offset as the forward call (the mask is regenerated,
+ * never stored).
+ *
+ *   dropout_p    in [0, 1); 0 gives exactly fa_fwd / fa_bwd.  A value that
+ *                rounds to t = 0 is rejected (FA_ERR_INVALID_ARG).
+ *   seed         64-bit Philox key.
+ *   offset       fourth counter word: distinct offsets give independent
+ *                masks under one seed.
+ *   remaining arguments, validation and errors as for fa_fwd / fa_bwd.
+ */
+fa_status fa_fwd_dropout(fa_dtype dtype,
+                         const void* q, fa_strides q_strides,
+                         const void* k, fa_strides k_strides,
+                         const void* v, fa_strides v_strides,
+                         void* o, fa_strides o_strides,
+                         float* lse,
+                         int B, int H, int N, int d,
+                         float scale, int causal,
+                         const int32_t* seqlens_k,
+                         const uint8_t* block_mask, int mask_block,
+                         float dropout_p, uint64_t seed, uint32_t offset,
+                         hipStream_t stream);
+
+fa_status fa_bwd_dropout(fa_dtype dtype,
+                         const void* q, fa_strides q_strides,
+                         const void* k, fa_strides k_strides,
+                         const void* v, fa_strides v_strides,
+                         const void* o, fa_strides o_strides,
+                         const void* dout, fa_strides dout_strides,
+                         const float* lse,
+                         void* dq, fa_strides dq_strides,
+                         void* dk, fa_strides dk_strides,
+                         void* dv, fa_strides dv_strides,
+                         void* workspace, size_t workspace_bytes,
+                         int B, int H, int N, int d,
+                         float scale, int causal,
+                         const int32_t* seqlens_k,
+                         const uint8_t* block_mask, int mask_block,
+                         float dropout_p, uint64_t seed, uint32_t offset,
+                         hipStream_t stream);
 
 /* Static, human-readable name of a status code. */
 const char* fa_status_string(fa_status status);

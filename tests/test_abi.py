@@ -161,3 +161,44 @@ def _load_fresh(path):
         return bnd.load_library(path)
     finally:
         bnd._lib = saved
+
+
+def _fwd_drop(**kw):
+    lib = fa.load_library()
+    args = dict(dtype=0, q=A, sq=S, k=A, sk=S, v=A, sv=S, o=A, so=S, lse=A, B=1, H=1, N=1024,
+                d=64, scale=0.125, causal=1, seqlens=None, bmask=None, mb=128, p=0.1, seed=1,
+                offset=0, stream=None)
+    args.update(kw)
+    return lib.fa_fwd_dropout(*args.values())
+
+
+def _bwd_drop(**kw):
+    lib = fa.load_library()
+    args = dict(dtype=0, q=A, sq=S, k=A, sk=S, v=A, sv=S, o=A, so=S, do=A, sdo=S, lse=A,
+                dq=A, sdq=S, dk=A, sdk=S, dv=A, sdv=S, ws=None, wsb=0, B=1, H=1, N=1024,
+                d=64, scale=0.125, causal=0, seqlens=None, bmask=None, mb=128, p=0.1, seed=1,
+                offset=0, stream=None)
+    args.update(kw)
+    return lib.fa_bwd_dropout(*args.values())
+
+
+BAD_DROPOUT = [
+    (dict(p=1.0), 1, "dropout_p must lie in [0, 1)"),
+    (dict(p=-0.1), 1, "dropout_p must lie in [0, 1)"),
+    (dict(p=float("nan")), 1, "dropout_p must lie in [0, 1)"),
+    (dict(p=0.999), 1, "rounds to dropping every pair"),
+    (dict(p=0.1, q=None), 1, "q is NULL"),
+    (dict(p=0.1, d=32), 2, "head dimension"),
+]
+
+
+@pytest.mark.parametrize("kw,status,msg", BAD_DROPOUT)
+def test_fwd_dropout_rejects_bad_arguments(kw, status, msg):
+    assert _fwd_drop(**kw) == status
+    assert msg in fa.fa_last_error()
+
+
+@pytest.mark.parametrize("kw,status,msg", BAD_DROPOUT + [(dict(dq=None), 1, "dq is NULL")])
+def test_bwd_dropout_rejects_bad_arguments(kw, status, msg):
+    assert _bwd_drop(**kw) == status
+    assert msg in fa.fa_last_error()
