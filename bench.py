@@ -11,7 +11,11 @@ the dominant kernel and the fp64 CPU oracle timed on the host as a baseline.
 FLOP convention (algorithmic work over visible (query, key) pairs; masked-out
 tiles are never credited): forward 4*d*pairs, backward 10*d*pairs.
 
-    python bench.py [--steps K] [--warmup W] [--workload NAME] [--cpu-baseline off]
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--dropout P]
+                    [--cpu-baseline off]
+
+--dropout P times fa_fwd_dropout / fa_bwd_dropout (keep mask regenerated in
+every kernel from Philox4x32-10) on the same workload and FLOP count.
 
 HBM traffic of the dominant kernel comes from rocprofv3 counter runs kept in
 profiles/hbm_traffic_<workload>.json (written by --pmc-summary from a
@@ -97,9 +101,17 @@ def kernel_flops(d, pairs):
 # ------------------------------------------------------------------- timing
 
 KERNELS = ("fwd_bf16_kernel", "bwd_kernel")
+DROPOUT_SEED = 2024  # Philox key of the --dropout runs (offset 0)
 
 
-def run_gpu(w: wl.Workload, inp: dict, steps: int, warmup: int, prewarm_s: float = 1.0):
+def measure_key(workload: str, dropout_p: float) -> str:
+    """Name of the profiles/ records of a run: the workload, plus the drop
+    probability when dropout is on (a different kernel variant)."""
+    return workload if dropout_p <= 0 else f"{workload}_dropout{dropout_p:g}"
+
+
+def run_gpu(w: wl.Workload, inp: dict, steps: int, warmup: int, prewarm_s: float = 1.0,
+            dropout_p: float = 0.0):
     """Times `steps` steps after `warmup` untimed ones.  One step is fa_fwd
     then fa_bwd, each a single kernel launch on the current stream; HIP
     events recorded on that stream around the launches give each kernel's
@@ -122,7 +134,8 @@ def run_gpu(w: wl.Workload, inp: dict, steps: int, warmup: int, prewarm_s: float
     o = torch.empty_like(q)
     lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
-    kw = dict(scale=w.scale, causal=w.causal, seqlens_k=sl, block_mask=bm, mask_block=128)
+    kw = dict(scale=w.scale, causal=w.causal, seqlens_k=sl, block_mask=bm, mask_block=128,
+              dropout_p=dropout_p, seed=DROPOUT_SEED, offset=0)
     stream = torch.cuda.current_stream(dev)
     # argument marshalling done once, so the host keeps ahead of the GPU
     fwd = fa.prepare_fwd(q, k, v, o, lse, **kw)
@@ -161,7 +174,7 @@ def run_gpu(w: wl.Workload, inp: dict, steps: int, warmup: int, prewarm_s: float
 
 
 def cpu_baseline(w: wl.Workload, inp: dict, outs: dict, flops_fb: float,
-                 budget_s: float = 10.0):
+                 budget_s: float = 10.0, dropout_p: float = 0.0):
     """The fp64 oracle as it stands, on the host cores, on the same inputs.
 
     Sample: whole (batch, head) slices of the workload -- all heads when one
@@ -169,20 +182,26 @@ def cpu_baseline(w: wl.Workload, inp: dict, outs: dict, flops_fb: float,
     ``budget_s`` seconds of CPU work; the value is scaled by the FLOPs of what
     was computed."""
     from oracle import attention_ref as ref
+    from oracle import dropout_ref as dref
     try:
         from threadpoolctl import threadpool_info
         cores = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
     except Exception:  # pragma: no cover
         cores = len(os.sched_getaffinity(0))
-    args = dict(scale=w.scale, causal=w.causal, seqlens=inp["seqlens"],
-                block_mask=inp["block_mask"], mask_block=128)
+    args = dict(causal=w.causal, seqlens=inp["seqlens"], block_mask=inp["block_mask"],
+                mask_block=128)
     H = w.H
     sub = lambda x, hs: x[:, :hs]  # noqa: E731
 
     def one_pass(hs):
-        O, L = ref.forward(sub(inp["q"], hs), sub(inp["k"], hs), sub(inp["v"], hs), **args)
-        G = ref.backward(sub(inp["q"], hs), sub(inp["k"], hs), sub(inp["v"], hs),
-                         sub(inp["do"], hs), **args)
+        q, k, v, do = (sub(inp[n], hs) for n in ("q", "k", "v", "do"))
+        if dropout_p > 0:  # mask index b * H + h with the workload's H
+            dkw = dict(args, n_heads=H)
+            O, L = dref.forward(q, k, v, w.scale, dropout_p, DROPOUT_SEED, 0, **dkw)
+            G = dref.backward(q, k, v, do, w.scale, dropout_p, DROPOUT_SEED, 0, **dkw)
+            return O, L, G
+        O, L = ref.forward(q, k, v, w.scale, **args)
+        G = ref.backward(q, k, v, do, w.scale, **args)
         return O, L, G
 
     t0 = time.perf_counter()
@@ -358,6 +377,9 @@ def main(argv=None):
     ap.add_argument("--prewarm-s", type=float, default=1.0,
                     help="seconds of untimed steps before the warmup steps (clock ramp)")
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=wl.WORKLOAD_ORDER)
+    ap.add_argument("--dropout", type=float, default=0.0,
+                    help="drop probability on P (fa_fwd_dropout / fa_bwd_dropout); the FLOP "
+                         "count is the same as without dropout")
     ap.add_argument("--cpu-baseline", default="on", choices=["on", "off"])
     ap.add_argument("--mode", default="attention", choices=["attention", "copy"],
                     help="copy: time a plain 1 GiB device copy (counter calibration)")
@@ -372,16 +394,17 @@ def main(argv=None):
                     help="write profiles/kernel_trace_<workload>.md from a rocprofv3 "
                          "--kernel-trace --stats run of this script")
     args = ap.parse_args(argv)
+    key = measure_key(args.workload, args.dropout)
     if args.trace_summary:
-        md = trace_summary(*args.trace_summary, workload=args.workload, command=args.pmc_command)
-        with open(os.path.join(ROOT, "profiles", f"kernel_trace_{args.workload}.md"), "w") as fh:
+        md = trace_summary(*args.trace_summary, workload=key, command=args.pmc_command)
+        with open(os.path.join(ROOT, "profiles", f"kernel_trace_{key}.md"), "w") as fh:
             fh.write(md)
         print(md)
         return 0
     if args.pmc_summary:
-        rec = pmc_summary(*args.pmc_summary, workload=args.workload,
+        rec = pmc_summary(*args.pmc_summary, workload=key,
                           copy_bytes=args.copy_mib << 20, command=args.pmc_command)
-        out = os.path.join(ROOT, "profiles", f"hbm_traffic_{args.workload}.json")
+        out = os.path.join(ROOT, "profiles", f"hbm_traffic_{key}.json")
         with open(out, "w") as fh:
             json.dump(rec, fh, indent=1)
         print(json.dumps(rec["kernels"]), flush=True)
@@ -402,7 +425,8 @@ def main(argv=None):
     flops_b = 10.0 * w.d * pairs
     esize = 2 if w.dtype == "bf16" else 4
 
-    wall_ms, kernel_ms, props, outs = run_gpu(w, inp, args.steps, args.warmup, args.prewarm_s)
+    wall_ms, kernel_ms, props, outs = run_gpu(w, inp, args.steps, args.warmup, args.prewarm_s,
+                                               args.dropout)
     fwd_ms = kernel_ms["fwd_bf16_kernel"]
     bwd_ms = kernel_ms["bwd_kernel"]
     peak = PEAK_TFLOPS[w.dtype]
@@ -427,13 +451,13 @@ def main(argv=None):
         ach = kbytes[dom] / (ms * 1e-3) / 1e9
         roofline = dict(kernel=dom, bound="hbm", achieved=ach, peak=PEAK_HBM_GBS, unit="GB/s",
                         frac=ach / PEAK_HBM_GBS)
-    roofline.update(traffic=traffic_for(dom, w.name), flops_per_launch=kflops[dom],
+    roofline.update(traffic=traffic_for(dom, key), flops_per_launch=kflops[dom],
                     compulsory_bytes_per_launch=kbytes[dom], launch_ms=ms)
 
     base = None
     parity = None
     if args.cpu_baseline == "on":
-        base, parity = cpu_baseline(w, inp, outs, flops_f + flops_b)
+        base, parity = cpu_baseline(w, inp, outs, flops_f + flops_b, dropout_p=args.dropout)
 
     line = {
         "metric": METRIC,
@@ -452,7 +476,8 @@ def main(argv=None):
         if w.dtype == "bf16" else "synthetic: seeded iid normal fp32 inputs",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d,
                    "causal": w.causal, "key_padding": inp["seqlens"] is not None,
-                   "block_sparse": inp["block_mask"] is not None, "pairs": pairs},
+                   "block_sparse": inp["block_mask"] is not None, "pairs": pairs,
+                   "dropout_p": args.dropout},
         "fwd_tflops": tf_f,
         "bwd_tflops": tf_b,
         "fwd_ms": fwd_ms,

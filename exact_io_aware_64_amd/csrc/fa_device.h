@@ -270,8 +270,9 @@ __device__ __forceinline__ void philox_rounds(uint32_t (&x)[4], uint32_t k0, uin
     const uint32_t kb = k1 + (uint32_t)r * 0xBB67AE85u;
     const uint64_t p0 = (uint64_t)0xD2511F53u * x[0];
     const uint64_t p1 = (uint64_t)0xCD9E8D57u * x[2];
-    const uint32_t y0 = (uint32_t)(p1 >> 32) ^ x[1] ^ ka;
-    const uint32_t y2 = (uint32_t)(p0 >> 32) ^ x[3] ^ kb;
+    // three-input xor in one gfx950 bitop3 (truth table 0x96 = a ^ b ^ c)
+    const uint32_t y0 = __builtin_amdgcn_bitop3_b32((uint32_t)(p1 >> 32), x[1], ka, 0x96);
+    const uint32_t y2 = __builtin_amdgcn_bitop3_b32((uint32_t)(p0 >> 32), x[3], kb, 0x96);
     x[1] = (uint32_t)p1;
     x[3] = (uint32_t)p0;
     x[0] = y0;

@@ -110,11 +110,15 @@ def keep_mask(rows, n_keys: int, bh: int, p: float, seed: int, offset: int) -> n
 
 
 def forward(q, k, v, scale, p, seed, offset=0, causal=False, seqlens=None, block_mask=None,
-            mask_block=128, rows=None):
+            mask_block=128, rows=None, n_heads=None):
     """Attention forward with dropout on P.  Shapes as in
-    ``attention_ref.forward``; returns O and L (L of the undropped softmax)."""
+    ``attention_ref.forward``; returns O and L (L of the undropped softmax).
+    ``n_heads``: the head count that the mask index b H + h uses (default:
+    the tensors' own; larger when the tensors are the first heads of a
+    problem)."""
     q, k, v = _as64(q), _as64(k), _as64(v)
     B, H, N, _ = q.shape
+    Hm = H if n_heads is None else n_heads
     s = 256.0 / keep_threshold(p)
     R = N if rows is None else rows.shape[-1]
     O = np.zeros((B, H, R, v.shape[-1]))
@@ -127,19 +131,20 @@ def forward(q, k, v, scale, p, seed, offset=0, causal=False, seqlens=None, block
                 idx = rr[c0:c0 + ROW_CHUNK]
                 vis = visible(idx, N, causal, sl, block_mask, mask_block)
                 pr, lse = _probabilities(q[b, h, idx], k[b, h], vis, scale)
-                z = keep_mask(idx, N, b * H + h, p, seed, offset)
+                z = keep_mask(idx, N, b * Hm + h, p, seed, offset)
                 O[b, h, c0:c0 + idx.size] = (s * z * pr) @ v[b, h]
                 L[b, h, c0:c0 + idx.size] = lse
     return O, L
 
 
 def backward(q, k, v, do, scale, p, seed, offset=0, causal=False, seqlens=None,
-             block_mask=None, mask_block=128, rows=None):
+             block_mask=None, mask_block=128, rows=None, n_heads=None):
     """Gradients of f = sum(dO * O) for attention with dropout (the mask held
     fixed).  ``rows`` as in ``attention_ref.backward``: dQ of the sampled rows,
     dK and dV of the problem with dO zero outside them."""
     q, k, v, do = _as64(q), _as64(k), _as64(v), _as64(do)
     B, H, N, d = q.shape
+    Hm = H if n_heads is None else n_heads
     s = 256.0 / keep_threshold(p)
     R = N if rows is None else rows.shape[-1]
     dQ = np.zeros((B, H, R, d))
@@ -155,7 +160,7 @@ def backward(q, k, v, do, scale, p, seed, offset=0, causal=False, seqlens=None,
                 vis = visible(idx, N, causal, sl, block_mask, mask_block)
                 qc, doc = q[b, h, idx], do[b, h, idx]
                 pr, _ = _probabilities(qc, kb, vis, scale)
-                sz = s * keep_mask(idx, N, b * H + h, p, seed, offset)
+                sz = s * keep_mask(idx, N, b * Hm + h, p, seed, offset)
                 dV[b, h] += (sz * pr).T @ doc
                 dp = sz * (doc @ vb.T)
                 D = (pr * dp).sum(axis=1)
