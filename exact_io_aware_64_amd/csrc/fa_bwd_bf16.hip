@@ -576,8 +576,13 @@ __device__ __forceinline__ void dkdv_role(const BwdArgs& a, int item, uint16_t* 
 // The fused backward kernel.  Work items: query tiles for the dQ role and
 // key tiles for the dK/dV role (each times B*H), each role in its own
 // heavy-first order.
+// Two waves per SIMD are asked for explicitly: left to itself the compiler
+// gives some dropout variants 256 VGPRs plus AGPR spill slots (one wave per
+// SIMD, a third slower); with the bound they fit in 256 registers, and the
+// other variants compile unchanged.
 template <bool CAUSAL, bool SEQLEN, bool BMASK, bool DROP>
-__global__ __launch_bounds__(256) void bwd_kernel(BwdArgs a, int phases) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void bwd_kernel(
+    BwdArgs a, int phases) {
   // Six tile arrays: the dQ role uses two per buffer (K, V), the dK/dV role
   // three (Q, dO, O).  Separate arrays, so that the copies into one buffer
   // and the reads of the other never alias.
