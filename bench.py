@@ -255,6 +255,141 @@ def copy_calibration(mib: int, steps: int, warmup: int) -> int:
     return 0
 
 
+# ------------------------------------------------------------ IO sweep
+
+SWEEP_N = (1024, 2048, 4096, 8192, 16384, 32768)
+SWEEP_BQ = (64, 128, 256)
+SWEEP_B, SWEEP_H, SWEEP_D = 1, 16, 64
+SWEEP_SEED = 6
+SWEEP_REPS = 3
+
+
+def sweep_model(N: int, block_q: int, H: int = SWEEP_H, d: int = SWEEP_D) -> dict:
+    """Bytes of one dense (non-causal) bf16 forward of B = 1: the compulsory
+    traffic (Q, K, V read once, O written once, L) and the K/V bytes the
+    kernel streams through LDS, once per query tile: (N / block_q) * 2 N d * 2
+    per head, the N^2 d / Br term of the pages' IO count."""
+    t = N * d * 2
+    nqt = -(-N // block_q)
+    return dict(compulsory=H * (4 * t + 4 * N), compulsory_read=H * 3 * t,
+                kv_streamed=H * nqt * 2 * t, q_read=H * t)
+
+
+def io_sweep_run(ns, bqs, reps: int) -> int:
+    """Dense bf16 forward (B=1, H=16, d=64) for every N and query-tile height:
+    one untimed and `reps` event-timed fa_fwd_tiled launches each, in a fixed
+    order, one JSON line per configuration.  Under rocprofv3 --pmc the
+    dispatches are told apart by workgroup size (block_q / 32 waves) and grid
+    size (N / block_q * H workgroups)."""
+    import torch
+    import exact_io_aware_64_amd as fa
+    dev = torch.device("cuda:0")
+    rng = np.random.default_rng(SWEEP_SEED)
+    nmax = max(ns)
+    full = [torch.from_numpy(x).to(torch.bfloat16).to(dev)
+            for x in wl.draw_tensors(rng, SWEEP_B, SWEEP_H, nmax, SWEEP_D, "bf16", count=3)]
+    stream = torch.cuda.current_stream(dev)
+    for N in ns:
+        q, k, v = (x[:, :, :N] for x in full)
+        o = torch.empty((SWEEP_B, SWEEP_H, N, SWEEP_D), dtype=torch.bfloat16, device=dev)
+        lse = torch.empty((SWEEP_B, SWEEP_H, N), dtype=torch.float32, device=dev)
+        for bq in bqs:
+            call = fa.prepare_fwd_tiled(q, k, v, o, lse, scale=1 / 8, block_q=bq)
+            call()
+            evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                   for _ in range(reps)]
+            for a, b in evs:
+                a.record(stream)
+                call()
+                b.record(stream)
+            torch.cuda.synchronize()
+            ms = float(np.median([a.elapsed_time(b) for a, b in evs]))
+            flops = 4.0 * SWEEP_D * N * N * SWEEP_H * SWEEP_B
+            print(json.dumps(dict(mode="io-sweep", N=N, block_q=bq, ms=ms,
+                                  tflops=flops / (ms * 1e-3) / 1e12,
+                                  workgroups=-(-N // bq) * SWEEP_H * SWEEP_B,
+                                  threads=2 * bq, **sweep_model(N, bq))), flush=True)
+    return 0
+
+
+def _per_dispatch(path: str, counters):
+    """{dispatch id: dict(kernel, grid, wg, counter values summed over
+    dimensions)} from a rocprofv3 counter_collection.csv."""
+    out = {}
+    with open(path) as fh:
+        for row in csv.DictReader(fh):
+            if row["Counter_Name"] not in counters:
+                continue
+            d = out.setdefault(int(row["Dispatch_Id"]), dict(
+                kernel=_short_kernel_name(row["Kernel_Name"]), name=row["Kernel_Name"],
+                grid=int(row["Grid_Size"]), wg=int(row["Workgroup_Size"])))
+            d[row["Counter_Name"]] = d.get(row["Counter_Name"], 0.0) + float(row["Counter_Value"])
+    return out
+
+
+def _sweep_config(d):
+    """(N, block_q) of a sweep dispatch from its launch shape."""
+    bq = d["wg"] // 2
+    nwg = d["grid"] // d["wg"]
+    return (nwg // (SWEEP_H * SWEEP_B)) * bq, bq
+
+
+def io_sweep_summary(fetch_csv, write_csv, l2_csv, cfetch_csv, cwrite_csv, cl2_csv, log,
+                     command, copy_bytes) -> str:
+    """profiles/io_sweep.md: measured bytes per launch of every sweep
+    configuration (means over its dispatches), against the model."""
+    def copy_max(path, counter):
+        vals = [v[counter] for v in _per_dispatch(path, (counter,)).values()]
+        return max(vals)
+    f_fetch = copy_bytes / (copy_max(cfetch_csv, "FETCH_SIZE") * 1024.0)
+    f_write = copy_bytes / (copy_max(cwrite_csv, "WRITE_SIZE") * 1024.0)
+    f_sect = copy_bytes / copy_max(cl2_csv, "TCC_READ_SECTORS_sum")
+    meas = {}
+    for path, counters in ((fetch_csv, ("FETCH_SIZE",)), (write_csv, ("WRITE_SIZE",)),
+                           (l2_csv, ("TCC_READ_SECTORS_sum", "TCC_HIT_sum", "TCC_MISS_sum"))):
+        for d in _per_dispatch(path, counters).values():
+            if d["kernel"] != "fwd_bf16_kernel":
+                continue
+            acc = meas.setdefault(_sweep_config(d), {})
+            for c in counters:
+                acc.setdefault(c, []).append(d.get(c, 0.0))
+    timing = {}
+    with open(log) as fh:
+        for line in fh:
+            if line.startswith("{") and '"io-sweep"' in line:
+                r = json.loads(line)
+                timing[(r["N"], r["block_q"])] = r
+    rows = []
+    for (N, bq) in sorted(meas):
+        m = {c: float(np.mean(v)) for c, v in meas[(N, bq)].items()}
+        mod = sweep_model(N, bq)
+        fetch = m["FETCH_SIZE"] * 1024.0 * f_fetch
+        write = m["WRITE_SIZE"] * 1024.0 * f_write
+        l2 = m["TCC_READ_SECTORS_sum"] * f_sect
+        hit = m["TCC_HIT_sum"] / max(1.0, m["TCC_HIT_sum"] + m["TCC_MISS_sum"])
+        t = timing.get((N, bq), {})
+        rows.append((N, bq, mod["compulsory"] / 1e6, (mod["q_read"] + mod["kv_streamed"]) / 1e6,
+                     l2 / 1e6, fetch / 1e6, write / 1e6, fetch / mod["compulsory_read"], hit,
+                     t.get("ms", float("nan")) * 1e3, t.get("tflops", float("nan"))))
+    out = ["# IO sweep: dense bf16 forward, B=1 H=16 d=64, query tile height x N", "",
+           "Command (repository root, MI355X, `TMPDIR=/tmp`):", "", "```", command, "```", "",
+           "Model (per launch): *compulsory* = Q, K, V read once + O written once + L; "
+           "*streamed* = Q + K/V read once per query tile, (N / Br) * 2 N d * 2 bytes per "
+           "head -- the N^2 d / Br term of the pages' IO count.  Measured: *L2 read* = "
+           "TCC_READ_SECTORS (bytes the CUs read from L2), *fetch* = FETCH_SIZE (bytes L2 "
+           "read from memory, Infinity Cache hits included), *write* = WRITE_SIZE; each "
+           f"scaled by the same counter over a {copy_bytes >> 20} MiB device copy "
+           f"(factors: sectors x {f_sect:.2f} B, fetch x {f_fetch:.3f}, write x {f_write:.3f}). "
+           "Time: median of event-timed launches in the same run.", "",
+           "| N | Br | compulsory MB | streamed MB (model) | L2 read MB | fetch MB | write MB "
+           "| fetch / compulsory read | L2 hit rate | us | TFLOP/s |",
+           "|---|---|---|---|---|---|---|---|---|---|---|"]
+    for r in rows:
+        out.append("| %d | %d | %.1f | %.1f | %.1f | %.1f | %.1f | %.2f | %.3f | %.1f | %.0f |"
+                   % r)
+    return "\n".join(out) + "\n"
+
+
 # ------------------------------------------------------------ HBM traffic
 
 KERNEL_SOURCES = {
@@ -381,8 +516,14 @@ def main(argv=None):
                     help="drop probability on P (fa_fwd_dropout / fa_bwd_dropout); the FLOP "
                          "count is the same as without dropout")
     ap.add_argument("--cpu-baseline", default="on", choices=["on", "off"])
-    ap.add_argument("--mode", default="attention", choices=["attention", "copy"],
-                    help="copy: time a plain 1 GiB device copy (counter calibration)")
+    ap.add_argument("--mode", default="attention", choices=["attention", "copy", "io-sweep"],
+                    help="copy: time a plain 1 GiB device copy (counter calibration); "
+                         "io-sweep: dense forward over N x query-tile height (fa_fwd_tiled)")
+    ap.add_argument("--sweep-n", default=",".join(str(n) for n in SWEEP_N))
+    ap.add_argument("--io-summary", nargs=7, metavar=("FETCH_CSV", "WRITE_CSV", "L2_CSV",
+                                                     "COPY_FETCH_CSV", "COPY_WRITE_CSV",
+                                                     "COPY_L2_CSV", "SWEEP_LOG"),
+                    help="write profiles/io_sweep.md from rocprofv3 runs of --mode io-sweep")
     ap.add_argument("--copy-mib", type=int, default=1024)
     ap.add_argument("--pmc-summary", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV",
                                                      "COPY_FETCH_CSV", "COPY_WRITE_CSV"),
@@ -395,6 +536,13 @@ def main(argv=None):
                          "--kernel-trace --stats run of this script")
     args = ap.parse_args(argv)
     key = measure_key(args.workload, args.dropout)
+    if args.io_summary:
+        md = io_sweep_summary(*args.io_summary, command=args.pmc_command,
+                              copy_bytes=args.copy_mib << 20)
+        with open(os.path.join(ROOT, "profiles", "io_sweep.md"), "w") as fh:
+            fh.write(md)
+        print(md)
+        return 0
     if args.trace_summary:
         md = trace_summary(*args.trace_summary, workload=key, command=args.pmc_command)
         with open(os.path.join(ROOT, "profiles", f"kernel_trace_{key}.md"), "w") as fh:
@@ -417,6 +565,8 @@ def main(argv=None):
         return 2
     if args.mode == "copy":
         return copy_calibration(args.copy_mib, args.steps, args.warmup)
+    if args.mode == "io-sweep":
+        return io_sweep_run([int(x) for x in args.sweep_n.split(",")], SWEEP_BQ, SWEEP_REPS)
 
     w = wl.WORKLOADS[args.workload]
     inp = wl.make_inputs(w)

@@ -17,10 +17,12 @@ from ._binding import (  # noqa: F401
     fa_bwd_workspace_bytes,
     fa_fwd,
     fa_fwd_dropout,
+    fa_fwd_tiled,
     fa_last_error,
     fa_status_string,
     forward,
     load_library,
     prepare_bwd,
     prepare_fwd,
+    prepare_fwd_tiled,
 )

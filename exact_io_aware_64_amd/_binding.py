@@ -23,7 +23,8 @@ FA_ERR_HIP = 3
 
 # Public entry points declared in include/fa.h.
 EXPORTED = ("fa_fwd", "fa_bwd", "fa_bwd_dq", "fa_bwd_dkdv", "fa_fwd_dropout",
-            "fa_bwd_dropout", "fa_bwd_workspace_bytes", "fa_status_string", "fa_last_error")
+            "fa_bwd_dropout", "fa_fwd_tiled", "fa_bwd_workspace_bytes", "fa_status_string",
+            "fa_last_error")
 
 
 class FaError(RuntimeError):
@@ -61,6 +62,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.fa_bwd_dkdv.argtypes = [I, P, S, P, S, P, S, P, S, P, S, P, P, S, P, S, P,
                                 ctypes.c_size_t, I, I, I, I, F, I, P, P, I, P]
     U64, U32 = ctypes.c_uint64, ctypes.c_uint32
+    lib.fa_fwd_tiled.restype = I
+    lib.fa_fwd_tiled.argtypes = [I, P, S, P, S, P, S, P, S, P, I, I, I, I, F, I, P, P, I, I, P]
     lib.fa_fwd_dropout.restype = I
     lib.fa_fwd_dropout.argtypes = [I, P, S, P, S, P, S, P, S, P, I, I, I, I, F, I, P, P, I,
                                    F, U64, U32, P]
@@ -153,6 +156,24 @@ def fa_fwd(q, k, v, o, lse, *, scale: float, causal: bool = False, seqlens_k=Non
     lib = load_library()
     args = _fwd_args(q, k, v, o, lse, scale, causal, seqlens_k, block_mask, mask_block)
     _check(lib.fa_fwd(*args, _stream(q, stream)))
+
+
+def fa_fwd_tiled(q, k, v, o, lse, *, scale: float, block_q: int, causal: bool = False,
+                 seqlens_k=None, block_mask=None, mask_block: int = 128, stream=None) -> None:
+    """Calls fa_fwd_tiled (fa_fwd with block_q query rows per workgroup)."""
+    lib = load_library()
+    args = _fwd_args(q, k, v, o, lse, scale, causal, seqlens_k, block_mask, mask_block)
+    _check(lib.fa_fwd_tiled(*args, int(block_q), _stream(q, stream)))
+
+
+def prepare_fwd_tiled(q, k, v, o, lse, *, scale: float, block_q: int, causal: bool = False,
+                      seqlens_k=None, block_mask=None, mask_block: int = 128,
+                      stream=None) -> "Prepared":
+    """fa_fwd_tiled with fixed arguments."""
+    lib = load_library()
+    args = _fwd_args(q, k, v, o, lse, scale, causal, seqlens_k, block_mask, mask_block)
+    return Prepared(lib.fa_fwd_tiled, args + (int(block_q), _stream(q, stream)),
+                    (q, k, v, o, lse, seqlens_k, block_mask))
 
 
 def fa_fwd_dropout(q, k, v, o, lse, *, scale: float, dropout_p: float, seed: int,

@@ -94,7 +94,7 @@ fa_status fwd_impl(fa_dtype dtype, const void* q, fa_strides q_strides, const vo
                    fa_strides o_strides, float* lse, int B, int H, int N, int d, float scale,
                    int causal, const int32_t* seqlens_k, const uint8_t* block_mask,
                    int mask_block, float dropout_p, uint64_t seed, uint32_t offset,
-                   hipStream_t stream) {
+                   int block_q, hipStream_t stream) {
   int al = 0;
   fa_status st = check_common(dtype, B, H, N, d, scale, block_mask, mask_block, &al);
   if (st != FA_OK) return st;
@@ -108,6 +108,13 @@ fa_status fwd_impl(fa_dtype dtype, const void* q, fa_strides q_strides, const vo
     return fail(FA_ERR_INVALID_ARG, "seqlens_k is not 4-byte aligned");
   fa::Dropout drop{};
   if ((st = make_dropout(dropout_p, seed, offset, &drop)) != FA_OK) return st;
+  if (block_q != 64 && block_q != 128 && block_q != 256)
+    return fail(FA_ERR_INVALID_ARG, "block_q must be 64, 128 or 256 (got %d)", block_q);
+  if (block_q != 128 && dtype != FA_BF16)
+    return fail(FA_ERR_UNSUPPORTED, "block_q other than 128 is built for bf16 only");
+  if (block_mask != nullptr && mask_block % block_q != 0)
+    return fail(FA_ERR_UNSUPPORTED, "block_q %d does not divide mask_block %d", block_q,
+                mask_block);
 
   fa::FwdArgs a{};
   a.q = q;
@@ -129,7 +136,7 @@ fa_status fwd_impl(fa_dtype dtype, const void* q, fa_strides q_strides, const vo
   a.mask_block = block_mask ? mask_block : 128;
   a.n_mask_tiles = (N + a.mask_block - 1) / a.mask_block;
   a.drop = drop;
-  const hipError_t e = dtype == FA_BF16 ? fa::launch_fwd_bf16(a, causal != 0, stream)
+  const hipError_t e = dtype == FA_BF16 ? fa::launch_fwd_bf16(a, causal != 0, block_q, stream)
                                         : fa::launch_fwd_f32(a, causal != 0, stream);
   return hip_status(e);
 }
@@ -144,7 +151,17 @@ fa_status fa_fwd(fa_dtype dtype, const void* q, fa_strides q_strides, const void
                  int causal, const int32_t* seqlens_k, const uint8_t* block_mask,
                  int mask_block, hipStream_t stream) {
   return fwd_impl(dtype, q, q_strides, k, k_strides, v, v_strides, o, o_strides, lse, B, H, N,
-                  d, scale, causal, seqlens_k, block_mask, mask_block, 0.f, 0, 0, stream);
+                  d, scale, causal, seqlens_k, block_mask, mask_block, 0.f, 0, 0, 128, stream);
+}
+
+fa_status fa_fwd_tiled(fa_dtype dtype, const void* q, fa_strides q_strides, const void* k,
+                       fa_strides k_strides, const void* v, fa_strides v_strides, void* o,
+                       fa_strides o_strides, float* lse, int B, int H, int N, int d, float scale,
+                       int causal, const int32_t* seqlens_k, const uint8_t* block_mask,
+                       int mask_block, int block_q, hipStream_t stream) {
+  return fwd_impl(dtype, q, q_strides, k, k_strides, v, v_strides, o, o_strides, lse, B, H, N,
+                  d, scale, causal, seqlens_k, block_mask, mask_block, 0.f, 0, 0, block_q,
+                  stream);
 }
 
 fa_status fa_fwd_dropout(fa_dtype dtype, const void* q, fa_strides q_strides, const void* k,
@@ -155,7 +172,7 @@ fa_status fa_fwd_dropout(fa_dtype dtype, const void* q, fa_strides q_strides, co
                          uint64_t seed, uint32_t offset, hipStream_t stream) {
   return fwd_impl(dtype, q, q_strides, k, k_strides, v, v_strides, o, o_strides, lse, B, H, N,
                   d, scale, causal, seqlens_k, block_mask, mask_block, dropout_p, seed, offset,
-                  stream);
+                  128, stream);
 }
 
 size_t fa_bwd_workspace_bytes(fa_dtype dtype, int B, int H, int N, int d) {

@@ -134,25 +134,28 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 // `stride_b`, buffer resource `rs`) straight from memory into the swizzled
 // tile, without passing through registers: buffer_load_dwordx4 ... lds puts
 // lane l's 16 bytes at the wave's LDS base + 16 l, so lane l fetches the
-// logical chunk that belongs at physical chunk l % 8 of row l / 8.  Wave w
-// copies rows 8 w .. 8 w + 7 and 8 w + 32 .. 8 w + 39 (stage_rows); the
-// swizzle repeats every 32 rows, so both instructions share one per-lane
-// offset and the second adds 32 rows to the uniform offset.  Rows past the
-// end of the slice read as zeros.  Completion is tracked by the wave's
-// vmcnt.
+// logical chunk that belongs at physical chunk l % 8 of row l / 8.  In a
+// workgroup of W waves, wave w copies rows 8 (w + W u) .. +7 for u < 8 / W
+// (with four waves: rows 8 w .. 8 w + 7 and 8 w + 32 .. 8 w + 39, stage_row);
+// those rows are 16 apart or more and the swizzle repeats every 16 rows, so
+// all the wave's instructions share one per-lane offset and step the uniform
+// offset.  Rows past the end of the slice read as zeros.  Completion is
+// tracked by the wave's vmcnt.
 __device__ __forceinline__ int stage_row(int w, int lane, int u) {
   return 8 * w + 32 * u + (lane >> 3);
 }
 
+template <int W = 4>
 __device__ __forceinline__ void stage_tile(__amdgpu_buffer_rsrc_t rs, int row0, int stride_b,
                                            uint16_t* tile, int w, int lane) {
-  const int row = stage_row(w, lane, 0);
+  static_assert(W == 2 || W == 4 || W == 8, "a tile is copied by 2, 4 or 8 waves");
+  const int row = 8 * w + (lane >> 3);
   const int voff = row * stride_b + (((lane & 7) ^ swz(row)) << 4);
 #pragma unroll
-  for (int u = 0; u < 2; ++u)
+  for (int u = 0; u < 8 / W; ++u)
     __builtin_amdgcn_raw_ptr_buffer_load_lds(
-        rs, (lds_void_t*)(tile + (8 * w + 32 * u) * 64), 16, voff,
-        __builtin_amdgcn_readfirstlane((row0 + 32 * u) * stride_b), 0, 0);
+        rs, (lds_void_t*)(tile + (8 * w + 8 * W * u) * 64), 16, voff,
+        __builtin_amdgcn_readfirstlane((row0 + 8 * W * u) * stride_b), 0, 0);
 }
 
 // 8 consecutive bf16 of a tile row (a 16-byte aligned chunk).
@@ -208,9 +211,10 @@ __device__ __forceinline__ int wave_incl_scan(int x) {
 
 // Builds, in LDS, the list of 64-row tiles t in [t_lo, t_hi) whose mask tile
 // (t / per_mask) is kept: mask entry J lives at mask[J * stride].  Called by
-// all 256 threads of the block; returns the list length (same in every
-// thread).  The list is sorted ascending.
-__device__ __forceinline__ int build_tile_list(uint16_t* list, int* scratch4,
+// all NT threads of the block (scratch holds NT / 64 ints); returns the list
+// length (same in every thread).  The list is sorted ascending.
+template <int NT = 256>
+__device__ __forceinline__ int build_tile_list(uint16_t* list, int* scratch,
                                                const uint8_t* mask, int64_t stride,
                                                int n_mask_tiles, int per_mask, int t_lo,
                                                int t_hi) {
@@ -218,7 +222,7 @@ __device__ __forceinline__ int build_tile_list(uint16_t* list, int* scratch4,
   int base = 0;
   const int j_lo = t_lo / per_mask;
   const int j_hi = (t_hi + per_mask - 1) / per_mask;  // exclusive
-  for (int c0 = j_lo; c0 < j_hi; c0 += 256) {
+  for (int c0 = j_lo; c0 < j_hi; c0 += NT) {
     const int J = c0 + tid;
     int first = 0, cnt = 0;
     if (J < j_hi && J < n_mask_tiles && mask[(int64_t)J * stride] != 0) {
@@ -227,12 +231,12 @@ __device__ __forceinline__ int build_tile_list(uint16_t* list, int* scratch4,
       cnt = max(0, last - first);
     }
     const int incl = wave_incl_scan(cnt);
-    if (lane == 63) scratch4[w] = incl;
+    if (lane == 63) scratch[w] = incl;
     __syncthreads();
     int woff = 0, total = 0;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int v = scratch4[i];
+    for (int i = 0; i < NT / 64; ++i) {
+      const int v = scratch[i];
       woff += (i < w) ? v : 0;
       total += v;
     }

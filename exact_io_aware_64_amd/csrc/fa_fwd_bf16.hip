@@ -2,6 +2,9 @@
 //
 // One workgroup (4 waves) owns 128 query rows of one (batch, head); each wave
 // owns 32 of them and keeps its Q fragment in registers for the whole kernel.
+// (Workgroups of 2 or 8 waves, 64 or 256 query rows, are also built: the
+// query tile height sets how often K and V are streamed, the quantity in the
+// pages' IO analysis -- researchpapers.dev, "tiling and recomputation".)
 // Key/value tiles of 64 rows stream through LDS, double-buffered and copied
 // straight from memory into LDS (the copy of tile t+1 is in flight while
 // tile t is computed), so each K/V element is read from HBM/L2 once per
@@ -46,11 +49,12 @@
 namespace fa {
 namespace {
 
-constexpr int kBR = 128;               // query rows per workgroup
 constexpr float kSumLimit = 4096.f;    // largest partial sum the fast path accepts
 
-template <bool CAUSAL, bool SEQLEN, bool BMASK, bool DROP>
-__global__ __launch_bounds__(256) void fwd_bf16_kernel(FwdArgs a) {
+// W waves, 32 W query rows per workgroup.
+template <int W, bool CAUSAL, bool SEQLEN, bool BMASK, bool DROP>
+__global__ __launch_bounds__(64 * W) void fwd_bf16_kernel(FwdArgs a) {
+  constexpr int kBR = 32 * W;
   // Two buffers, each a K tile and a V tile; separate arrays so that the
   // copies into one buffer and the reads of the other never alias.
   __shared__ __attribute__((aligned(16))) uint16_t s_k0[kTileElems];
@@ -83,11 +87,11 @@ __global__ __launch_bounds__(256) void fwd_bf16_kernel(FwdArgs a) {
   [[maybe_unused]] uint16_t* tlist = nullptr;
   if constexpr (BMASK) {
     __shared__ uint16_t s_list[kMaxListTiles];
-    __shared__ int s_scan[4];
+    __shared__ int s_scan[W];
     tlist = s_list;
-    const int row = q0 / a.mask_block;
-    nlist = build_tile_list(s_list, s_scan, a.bmask + (int64_t)row * a.n_mask_tiles, 1,
-                            a.n_mask_tiles, a.mask_block / kTile, 0, ntk);
+    const int row = q0 / a.mask_block;  // the host makes the query tile divide mask_block
+    nlist = build_tile_list<64 * W>(s_list, s_scan, a.bmask + (int64_t)row * a.n_mask_tiles,
+                                    1, a.n_mask_tiles, a.mask_block / kTile, 0, ntk);
   }
 
   const __amdgpu_buffer_rsrc_t rq =
@@ -127,8 +131,8 @@ __global__ __launch_bounds__(256) void fwd_bf16_kernel(FwdArgs a) {
     return it;
   };
   auto stage = [&](int t, uint16_t* kt, uint16_t* vt) FA_INLINE {
-    stage_tile(rk, t * kTile, ssk, kt, w, lane);
-    stage_tile(rv, t * kTile, ssv, vt, w, lane);
+    stage_tile<W>(rk, t * kTile, ssk, kt, w, lane);
+    stage_tile<W>(rv, t * kTile, ssv, vt, w, lane);
   };
 
   // Raises m to cover the scores of half kb, rescales acc and l, and
@@ -306,30 +310,36 @@ __global__ __launch_bounds__(256) void fwd_bf16_kernel(FwdArgs a) {
   }
 }
 
-template <bool C, bool S, bool M, bool D>
+template <int W, bool C, bool S, bool M, bool D>
 hipError_t launch(const FwdArgs& a, hipStream_t stream) {
-  const int nqt = (a.N + kBR - 1) / kBR;
-  dim3 grid((unsigned)(nqt * a.B * a.H)), block(256);
+  const int nqt = (a.N + 32 * W - 1) / (32 * W);
+  dim3 grid((unsigned)(nqt * a.B * a.H)), block(64 * W);
   FwdArgs copy = a;
   void* args[] = {&copy};
-  return hipLaunchKernel((const void*)&fwd_bf16_kernel<C, S, M, D>, grid, block, args, 0, stream);
+  return hipLaunchKernel((const void*)&fwd_bf16_kernel<W, C, S, M, D>, grid, block, args, 0,
+                         stream);
 }
 
-template <bool D>
+template <int W, bool D>
 hipError_t dispatch(const FwdArgs& a, bool causal, hipStream_t stream) {
   const bool s = a.seqlens != nullptr, m = a.bmask != nullptr;
   if (causal) {
-    if (s) return m ? launch<true, true, true, D>(a, stream) : launch<true, true, false, D>(a, stream);
-    return m ? launch<true, false, true, D>(a, stream) : launch<true, false, false, D>(a, stream);
+    if (s)
+      return m ? launch<W, true, true, true, D>(a, stream) : launch<W, true, true, false, D>(a, stream);
+    return m ? launch<W, true, false, true, D>(a, stream) : launch<W, true, false, false, D>(a, stream);
   }
-  if (s) return m ? launch<false, true, true, D>(a, stream) : launch<false, true, false, D>(a, stream);
-  return m ? launch<false, false, true, D>(a, stream) : launch<false, false, false, D>(a, stream);
+  if (s)
+    return m ? launch<W, false, true, true, D>(a, stream) : launch<W, false, true, false, D>(a, stream);
+  return m ? launch<W, false, false, true, D>(a, stream) : launch<W, false, false, false, D>(a, stream);
 }
 
 }  // namespace
 
-hipError_t launch_fwd_bf16(const FwdArgs& a, bool causal, hipStream_t stream) {
-  return a.drop.t < 256 ? dispatch<true>(a, causal, stream) : dispatch<false>(a, causal, stream);
+hipError_t launch_fwd_bf16(const FwdArgs& a, bool causal, int block_q, hipStream_t stream) {
+  if (a.drop.t < 256) return dispatch<4, true>(a, causal, stream);  // host: block_q == 128
+  if (block_q == 64) return dispatch<2, false>(a, causal, stream);
+  if (block_q == 256) return dispatch<8, false>(a, causal, stream);
+  return dispatch<4, false>(a, causal, stream);
 }
 
 }  // namespace fa

@@ -181,6 +181,34 @@ fa_status fa_bwd_dkdv(fa_dtype dtype,
                       hipStream_t stream);
 
 /*
+ * fa_fwd_tiled -- fa_fwd with a chosen query-tile height (bf16 only): each
+ * workgroup owns block_q query rows (block_q / 32 waves) and streams the
+ * visible K/V tiles of its (b, h) once, so the K/V bytes read from memory
+ * scale like N^2 d / block_q.  This is the tile-size dependence of the pages'
+ * IO analysis (researchpapers.dev explainer, "tiling and recomputation":
+ * the on-chip tile bounds how often K and V are re-read), exposed for
+ * measurement; fa_fwd uses 128.  Results equal fa_fwd's up to summation
+ * order (block_q = 128 is the same kernel, bit for bit).
+ *
+ *   block_q      64, 128 or 256 (FA_ERR_INVALID_ARG otherwise).  With a
+ *                block mask it must divide mask_block (FA_ERR_UNSUPPORTED).
+ *                FA_F32 supports only 128 (FA_ERR_UNSUPPORTED).
+ *   remaining arguments, validation and errors as for fa_fwd.
+ */
+fa_status fa_fwd_tiled(fa_dtype dtype,
+                       const void* q, fa_strides q_strides,
+                       const void* k, fa_strides k_strides,
+                       const void* v, fa_strides v_strides,
+                       void* o, fa_strides o_strides,
+                       float* lse,
+                       int B, int H, int N, int d,
+                       float scale, int causal,
+                       const int32_t* seqlens_k,
+                       const uint8_t* block_mask, int mask_block,
+                       int block_q,
+                       hipStream_t stream);
+
+/*
  * fa_fwd_dropout, fa_bwd_dropout -- fa_fwd and fa_bwd with dropout applied
  * to the probabilities.  The pages list dropout among the element-wise
  * operations that standard attention runs as separate kernels and that the

@@ -202,3 +202,24 @@ def test_fwd_dropout_rejects_bad_arguments(kw, status, msg):
 def test_bwd_dropout_rejects_bad_arguments(kw, status, msg):
     assert _bwd_drop(**kw) == status
     assert msg in fa.fa_last_error()
+
+
+def _fwd_tiled(**kw):
+    lib = fa.load_library()
+    args = dict(dtype=0, q=A, sq=S, k=A, sk=S, v=A, sv=S, o=A, so=S, lse=A, B=1, H=1, N=1024,
+                d=64, scale=0.125, causal=1, seqlens=None, bmask=None, mb=128, bq=64,
+                stream=None)
+    args.update(kw)
+    return lib.fa_fwd_tiled(*args.values())
+
+
+@pytest.mark.parametrize("kw,status,msg", [
+    (dict(bq=100), 1, "block_q must be 64, 128 or 256"),
+    (dict(bq=32), 1, "block_q must be 64, 128 or 256"),
+    (dict(bq=64, dtype=1), 2, "bf16 only"),
+    (dict(bq=256, bmask=A, mb=128), 2, "does not divide mask_block"),
+    (dict(bq=256, q=None), 1, "q is NULL"),
+])
+def test_fwd_tiled_rejects_bad_arguments(kw, status, msg):
+    assert _fwd_tiled(**kw) == status
+    assert msg in fa.fa_last_error()

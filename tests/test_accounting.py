@@ -55,3 +55,18 @@ def test_kernel_flops_are_the_method():
 def test_more_than_one_gpu_is_refused(capsys):
     assert bench.main(["--gpus", "2"]) == 2
     assert "one GPU" in capsys.readouterr().err
+
+
+def test_io_sweep_model_and_dispatch_mapping():
+    import bench
+    m = bench.sweep_model(1024, 128, H=16, d=64)
+    t = 1024 * 64 * 2
+    assert m["compulsory"] == 16 * (4 * t + 4 * 1024)
+    assert m["kv_streamed"] == 16 * 8 * 2 * t          # 8 query tiles of 128 rows
+    assert bench.sweep_model(1024, 64)["kv_streamed"] == 2 * m["kv_streamed"]
+    assert bench.sweep_model(1024, 256)["kv_streamed"] * 2 == m["kv_streamed"]
+    for N in bench.SWEEP_N:
+        for bq in bench.SWEEP_BQ:
+            threads = 2 * bq                              # bq / 32 waves of 64 lanes
+            grid = (N // bq) * bench.SWEEP_H * threads    # Grid_Size counts work-items
+            assert bench._sweep_config(dict(wg=threads, grid=grid)) == (N, bq)
