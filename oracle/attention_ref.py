@@ -32,7 +32,11 @@ differentiating the definitions above for f = sum(dO * O):
 
 Readings where the pages are silent (each also listed in the design notes):
 rows with no visible key give O_i = 0, L_i = -inf and no gradient; keys past a
-sequence's length get dK = dV = 0; L is the natural-log logsumexp.
+sequence's length get dK = dV = 0; L is the natural-log logsumexp.  The pages
+only treat square problems; with N_q queries and N_k keys (the queries being
+the last N_q positions of a sequence whose first N_k - N_q keys are already
+cached), causal visibility is j <= i + (N_k - N_q), so the last query sees
+every key, and the tile mask is [ceil(N_q / mb)][ceil(N_k / mb)].
 
 Every function here is pinned by tests that do not re-use its formula:
 closed forms, invariants, a hand-worked fixture, central finite differences,
@@ -47,13 +51,15 @@ ROW_CHUNK = 256
 
 
 def visible(rows: np.ndarray, n_keys: int, causal: bool, seqlen, block_mask,
-            mask_block: int) -> np.ndarray:
-    """bool ``[len(rows), n_keys]``: True where query ``rows[r]`` may attend key j."""
+            mask_block: int, n_queries=None) -> np.ndarray:
+    """bool ``[len(rows), n_keys]``: True where query ``rows[r]`` may attend key
+    j.  ``n_queries`` (default n_keys) sets the causal offset N_k - N_q."""
     rows = np.asarray(rows, dtype=np.int64)
     j = np.arange(n_keys, dtype=np.int64)
+    off = 0 if n_queries is None else n_keys - n_queries
     vis = np.ones((rows.size, n_keys), dtype=bool)
     if causal:
-        vis &= j[None, :] <= rows[:, None]
+        vis &= j[None, :] <= rows[:, None] + off
     if seqlen is not None:
         vis &= j[None, :] < int(seqlen)
     if block_mask is not None:
@@ -89,12 +95,14 @@ def forward(q, k, v, scale, causal=False, seqlens=None, block_mask=None,
             mask_block=128, rows=None):
     """Standard attention forward.
 
-    q, k, v: ``[B, H, N, d]`` (any float dtype; computed in float64).
+    q: ``[B, H, N_q, d]``; k, v: ``[B, H, N_k, d]`` (any float dtype;
+    computed in float64).
     rows: None (all rows) or int ``[B, H, R]`` query rows to evaluate.
-    Returns O ``[B, H, R, d]`` and L ``[B, H, R]`` (R = N when rows is None).
+    Returns O ``[B, H, R, d]`` and L ``[B, H, R]`` (R = N_q when rows is None).
     """
     q, k, v = _as64(q), _as64(k), _as64(v)
     B, H, N, _ = q.shape
+    Nk = k.shape[2]
     dv = v.shape[-1]
     R = N if rows is None else rows.shape[-1]
     O = np.zeros((B, H, R, dv))
@@ -105,7 +113,7 @@ def forward(q, k, v, scale, causal=False, seqlens=None, block_mask=None,
             rr = _rows_for(None if rows is None else rows[b, h], N)
             for c0 in range(0, R, ROW_CHUNK):
                 idx = rr[c0:c0 + ROW_CHUNK]
-                vis = visible(idx, N, causal, sl, block_mask, mask_block)
+                vis = visible(idx, Nk, causal, sl, block_mask, mask_block, N)
                 p, lse = _probabilities(q[b, h, idx], k[b, h], vis, scale)
                 O[b, h, c0:c0 + idx.size] = p @ v[b, h]
                 L[b, h, c0:c0 + idx.size] = lse
@@ -116,17 +124,18 @@ def backward(q, k, v, do, scale, causal=False, seqlens=None, block_mask=None,
              mask_block=128, rows=None):
     """Gradients of f = sum(dO * O) with respect to Q, K and V.
 
-    rows None: full gradients dQ, dK, dV, each ``[B, H, N, d]``.
+    rows None: full gradients dQ ``[B, H, N_q, d]``, dK, dV ``[B, H, N_k, d]``.
     rows ``[B, H, R]``: dQ ``[B, H, R, d]`` for those rows (exact full-problem
-    values, since dQ_i depends on row i of dO only) and dK, dV ``[B, H, N, d]``
+    values, since dQ_i depends on row i of dO only) and dK, dV ``[B, H, N_k, d]``
     of the restricted problem in which dO is zero outside the sampled rows.
     """
     q, k, v, do = _as64(q), _as64(k), _as64(v), _as64(do)
     B, H, N, d = q.shape
+    Nk = k.shape[2]
     R = N if rows is None else rows.shape[-1]
     dQ = np.zeros((B, H, R, d))
-    dK = np.zeros((B, H, N, d))
-    dV = np.zeros((B, H, N, v.shape[-1]))
+    dK = np.zeros((B, H, Nk, d))
+    dV = np.zeros((B, H, Nk, v.shape[-1]))
     for b in range(B):
         sl = None if seqlens is None else int(seqlens[b])
         for h in range(H):
@@ -134,7 +143,7 @@ def backward(q, k, v, do, scale, causal=False, seqlens=None, block_mask=None,
             kb, vb = k[b, h], v[b, h]
             for c0 in range(0, R, ROW_CHUNK):
                 idx = rr[c0:c0 + ROW_CHUNK]
-                vis = visible(idx, N, causal, sl, block_mask, mask_block)
+                vis = visible(idx, Nk, causal, sl, block_mask, mask_block, N)
                 qc, doc = q[b, h, idx], do[b, h, idx]
                 p, _ = _probabilities(qc, kb, vis, scale)
                 dV[b, h] += p.T @ doc
@@ -159,6 +168,7 @@ def forward_online(q, k, v, scale, causal=False, seqlens=None, block_mask=None,
     """
     q, k, v = _as64(q), _as64(k), _as64(v)
     B, H, N, _ = q.shape
+    Nk = k.shape[2]
     d = v.shape[-1]
     O = np.zeros((B, H, N, d))
     L = np.zeros((B, H, N))
@@ -169,9 +179,9 @@ def forward_online(q, k, v, scale, causal=False, seqlens=None, block_mask=None,
             m = np.full(N, -np.inf)
             l = np.zeros(N)
             acc = np.zeros((N, d))
-            for j0 in range(0, N, key_block):
-                j1 = min(N, j0 + key_block)
-                vis = visible(rows, N, causal, sl, block_mask, mask_block)[:, j0:j1]
+            for j0 in range(0, Nk, key_block):
+                j1 = min(Nk, j0 + key_block)
+                vis = visible(rows, Nk, causal, sl, block_mask, mask_block, N)[:, j0:j1]
                 s = scale * (q[b, h] @ k[b, h, j0:j1].T)
                 s = np.where(vis, s, -np.inf)
                 m_new = np.maximum(m, s.max(axis=1))
@@ -190,11 +200,12 @@ def forward_online(q, k, v, scale, causal=False, seqlens=None, block_mask=None,
 
 
 def visible_pair_count(N, causal=False, seqlens=None, block_mask=None, mask_block=128,
-                       B=1):
+                       B=1, N_k=None):
     """Brute-force count of visible (query, key) pairs summed over the batch
-    (per head), by materialising the mask."""
+    (per head), by materialising the mask (N queries, N_k keys, default N)."""
+    Nk = N if N_k is None else N_k
     total = 0
     for b in range(B):
         sl = None if seqlens is None else int(seqlens[b])
-        total += int(visible(np.arange(N), N, causal, sl, block_mask, mask_block).sum())
+        total += int(visible(np.arange(N), Nk, causal, sl, block_mask, mask_block, N).sum())
     return total

@@ -118,6 +118,7 @@ def forward(q, k, v, scale, p, seed, offset=0, causal=False, seqlens=None, block
     problem)."""
     q, k, v = _as64(q), _as64(k), _as64(v)
     B, H, N, _ = q.shape
+    Nk = k.shape[2]
     Hm = H if n_heads is None else n_heads
     s = 256.0 / keep_threshold(p)
     R = N if rows is None else rows.shape[-1]
@@ -129,9 +130,9 @@ def forward(q, k, v, scale, p, seed, offset=0, causal=False, seqlens=None, block
             rr = _rows_for(None if rows is None else rows[b, h], N)
             for c0 in range(0, R, ROW_CHUNK):
                 idx = rr[c0:c0 + ROW_CHUNK]
-                vis = visible(idx, N, causal, sl, block_mask, mask_block)
+                vis = visible(idx, Nk, causal, sl, block_mask, mask_block, N)
                 pr, lse = _probabilities(q[b, h, idx], k[b, h], vis, scale)
-                z = keep_mask(idx, N, b * Hm + h, p, seed, offset)
+                z = keep_mask(idx, Nk, b * Hm + h, p, seed, offset)
                 O[b, h, c0:c0 + idx.size] = (s * z * pr) @ v[b, h]
                 L[b, h, c0:c0 + idx.size] = lse
     return O, L
@@ -144,12 +145,13 @@ def backward(q, k, v, do, scale, p, seed, offset=0, causal=False, seqlens=None,
     dK and dV of the problem with dO zero outside them."""
     q, k, v, do = _as64(q), _as64(k), _as64(v), _as64(do)
     B, H, N, d = q.shape
+    Nk = k.shape[2]
     Hm = H if n_heads is None else n_heads
     s = 256.0 / keep_threshold(p)
     R = N if rows is None else rows.shape[-1]
     dQ = np.zeros((B, H, R, d))
-    dK = np.zeros((B, H, N, d))
-    dV = np.zeros((B, H, N, v.shape[-1]))
+    dK = np.zeros((B, H, Nk, d))
+    dV = np.zeros((B, H, Nk, v.shape[-1]))
     for b in range(B):
         sl = None if seqlens is None else int(seqlens[b])
         for h in range(H):
@@ -157,10 +159,10 @@ def backward(q, k, v, do, scale, p, seed, offset=0, causal=False, seqlens=None,
             kb, vb = k[b, h], v[b, h]
             for c0 in range(0, R, ROW_CHUNK):
                 idx = rr[c0:c0 + ROW_CHUNK]
-                vis = visible(idx, N, causal, sl, block_mask, mask_block)
+                vis = visible(idx, Nk, causal, sl, block_mask, mask_block, N)
                 qc, doc = q[b, h, idx], do[b, h, idx]
                 pr, _ = _probabilities(qc, kb, vis, scale)
-                sz = s * keep_mask(idx, N, b * Hm + h, p, seed, offset)
+                sz = s * keep_mask(idx, Nk, b * Hm + h, p, seed, offset)
                 dV[b, h] += (sz * pr).T @ doc
                 dp = sz * (doc @ vb.T)
                 D = (pr * dp).sum(axis=1)

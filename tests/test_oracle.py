@@ -357,3 +357,108 @@ def test_matches_torch_float64_sdpa_and_autograd(kind):
     np.testing.assert_allclose(dq, tq.grad.numpy(), atol=1e-12)
     np.testing.assert_allclose(dk, tk.grad.numpy(), atol=1e-12)
     np.testing.assert_allclose(dv, tv.grad.numpy(), atol=1e-12)
+
+
+# ------------------------------------------------- N_q != N_k (cached keys)
+
+def _rect(Nq, Nk, kind, seed=0, d=4, B=1, H=2, mask_block=4):
+    rng = np.random.default_rng(seed)
+    q = rng.standard_normal((B, H, Nq, d))
+    k, v = (rng.standard_normal((B, H, Nk, d)) for _ in range(2))
+    do = rng.standard_normal((B, H, Nq, d))
+    causal = kind in ("causal", "causal_padded_block")
+    seqlens = None
+    block = None
+    if kind in ("padded", "causal_padded_block"):
+        seqlens = rng.integers(max(1, Nk // 2), Nk + 1, size=B).astype(np.int32)
+    if kind in ("block", "causal_padded_block"):
+        tq, tk = -(-Nq // mask_block), -(-Nk // mask_block)
+        block = (rng.random((tq, tk)) < 0.6).astype(np.uint8)
+    return dict(q=q, k=k, v=v, do=do, scale=0.7, causal=causal, seqlens=seqlens,
+                block_mask=block, mask_block=mask_block)
+
+
+def _mk(c):
+    return dict(causal=c["causal"], seqlens=c["seqlens"], block_mask=c["block_mask"],
+                mask_block=c["mask_block"])
+
+
+@pytest.mark.parametrize("Nq", [1, 3, 7])
+def test_cached_keys_equal_the_suffix_of_the_square_problem(Nq):
+    """Causal with N_q < N_k: the N_q queries are the last positions of a
+    sequence of N_k, so their outputs are the last rows of the square causal
+    problem; gradients likewise, with dO zero on the earlier rows."""
+    Nk = 11
+    rng = np.random.default_rng(Nq)
+    qf, k, v, dof = (rng.standard_normal((1, 2, Nk, 5)) for _ in range(4))
+    dof[:, :, :Nk - Nq] = 0.0
+    Of, Lf = ref.forward(qf, k, v, 0.6, causal=True)
+    O, L = ref.forward(qf[:, :, Nk - Nq:], k, v, 0.6, causal=True)
+    np.testing.assert_allclose(O, Of[:, :, Nk - Nq:], rtol=0, atol=1e-14)
+    np.testing.assert_allclose(L, Lf[:, :, Nk - Nq:], rtol=0, atol=1e-14)
+    gf = ref.backward(qf, k, v, dof, 0.6, causal=True)
+    g = ref.backward(qf[:, :, Nk - Nq:], k, v, dof[:, :, Nk - Nq:], 0.6, causal=True)
+    np.testing.assert_allclose(g[0], gf[0][:, :, Nk - Nq:], rtol=0, atol=1e-13)
+    np.testing.assert_allclose(g[1], gf[1], rtol=0, atol=1e-13)
+    np.testing.assert_allclose(g[2], gf[2], rtol=0, atol=1e-13)
+
+
+def test_decode_row_sees_every_key():
+    c = _rect(1, 9, "none", seed=3)
+    O1, L1 = ref.forward(c["q"], c["k"], c["v"], c["scale"], causal=True)
+    O0, L0 = ref.forward(c["q"], c["k"], c["v"], c["scale"], causal=False)
+    np.testing.assert_array_equal(O1, O0)
+    np.testing.assert_array_equal(L1, L0)
+
+
+def test_more_queries_than_keys_leaves_leading_rows_dead():
+    """Causal with N_q > N_k: query i sees keys j <= i - (N_q - N_k), so the
+    first N_q - N_k rows see nothing and the rest are the square problem."""
+    Nq, Nk = 9, 5
+    c = _rect(Nq, Nk, "none", seed=4)
+    O, L = ref.forward(c["q"], c["k"], c["v"], c["scale"], causal=True)
+    assert np.all(O[:, :, :Nq - Nk] == 0) and np.all(np.isneginf(L[:, :, :Nq - Nk]))
+    Os, Ls = ref.forward(c["q"][:, :, Nq - Nk:], c["k"], c["v"], c["scale"], causal=True)
+    np.testing.assert_allclose(O[:, :, Nq - Nk:], Os, rtol=0, atol=1e-15)
+    np.testing.assert_allclose(L[:, :, Nq - Nk:], Ls, rtol=0, atol=1e-15)
+    dq, dk, dv = ref.backward(c["q"], c["k"], c["v"], c["do"], c["scale"], causal=True)
+    assert np.all(dq[:, :, :Nq - Nk] == 0)
+
+
+@pytest.mark.parametrize("Nq,Nk", [(5, 9), (9, 5)])
+@pytest.mark.parametrize("kind", MASK_KINDS)
+def test_rectangular_online_and_finite_differences(Nq, Nk, kind):
+    c = _rect(Nq, Nk, kind, seed=Nq * 10 + Nk)
+    kw = _mk(c)
+    O, L = ref.forward(c["q"], c["k"], c["v"], c["scale"], **kw)
+    O2, L2 = ref.forward_online(c["q"], c["k"], c["v"], c["scale"], key_block=3, **kw)
+    np.testing.assert_allclose(O2, O, rtol=0, atol=1e-12)
+    live = np.isfinite(L)
+    np.testing.assert_allclose(L2[live], L[live], rtol=0, atol=1e-12)
+    dq, dk, dv = ref.backward(c["q"], c["k"], c["v"], c["do"], c["scale"], **kw)
+    assert dq.shape == c["q"].shape and dk.shape == c["k"].shape
+
+    def f(q, k, v):
+        return float((c["do"] * ref.forward(q, k, v, c["scale"], **kw)[0]).sum())
+
+    h = 1e-6
+    for name, g in (("q", dq), ("k", dk), ("v", dv)):
+        x = {n: c[n].copy() for n in ("q", "k", "v")}
+        num = np.zeros_like(g)
+        it = np.nditer(x[name], flags=["multi_index"])
+        for _ in it:
+            idx = it.multi_index
+            x[name][idx] += h
+            fp = f(x["q"], x["k"], x["v"])
+            x[name][idx] -= 2 * h
+            fm = f(x["q"], x["k"], x["v"])
+            x[name][idx] += h
+            num[idx] = (fp - fm) / (2 * h)
+        np.testing.assert_allclose(g, num, rtol=1e-6, atol=1e-7, err_msg=name)
+
+
+def test_rectangular_pair_count():
+    # causal, N_q = 3 cached after 5 keys: rows see 6, 7, 8 keys
+    assert ref.visible_pair_count(3, causal=True, N_k=8) == 6 + 7 + 8
+    # N_q = 8 over N_k = 3: rows 5, 6, 7 see 1, 2, 3 keys
+    assert ref.visible_pair_count(8, causal=True, N_k=3) == 1 + 2 + 3
