@@ -50,14 +50,19 @@ DEFAULT_WORKLOAD = "gpt2s_causal_b8h12n1024"
 # --------------------------------------------------------------- accounting
 
 def visible_pairs(N: int, H: int, causal: bool, seqlens, block_mask, mask_block: int = 128,
-                  B: int = 1) -> int:
-    """Number of visible (query, key) pairs summed over batch and heads."""
-    lens = [N] * B if seqlens is None else [int(min(max(s, 0), N)) for s in seqlens]
+                  B: int = 1, Nk=None) -> int:
+    """Number of visible (query, key) pairs summed over batch and heads: N
+    queries, Nk keys (default N), causal key j visible to query i iff
+    j <= i + Nk - N."""
+    Nk = N if Nk is None else Nk
+    off = Nk - N
+    lens = [Nk] * B if seqlens is None else [int(min(max(s, 0), Nk)) for s in seqlens]
     total = 0
     for L in lens:
         if block_mask is None:
             if causal:
-                total += L * (L + 1) // 2 + (N - L) * L
+                i = np.arange(N, dtype=np.int64)
+                total += int(np.clip(np.minimum(i + 1 + off, L), 0, None).sum())
             else:
                 total += N * L
             continue
@@ -73,20 +78,23 @@ def visible_pairs(N: int, H: int, causal: bool, seqlens, block_mask, mask_block:
         else:
             for a, b_, c, e in zip(r0, r1, c0, c1):
                 i = np.arange(a, b_)
-                total += int(np.clip(np.minimum(i + 1, e) - c, 0, None).sum())
+                total += int(np.clip(np.minimum(i + 1 + off, e) - c, 0, None).sum())
     return total * H
 
 
-def kernel_bytes(B, H, N, d, esize, seqlens):
+def kernel_bytes(B, H, N, d, esize, seqlens, Nk=None):
     """Compulsory HBM bytes per launch of each kernel: every tensor the kernel
     must read or write once (keys and values only up to each sequence's key
-    length), plus the fp32 row statistic L."""
+    length), plus the fp32 row statistic L.  N queries, Nk keys (default N)."""
+    Nk = N if Nk is None else Nk
     t = B * H * N * d * esize
-    kv_valid = H * d * esize * (B * N if seqlens is None else int(np.minimum(seqlens, N).sum()))
+    tk = B * H * Nk * d * esize
+    kv_valid = H * d * esize * (B * Nk if seqlens is None
+                                else int(np.minimum(seqlens, Nk).sum()))
     rowstat = B * H * N * 4
     return {
-        "fwd_bf16_kernel": 2 * t + 2 * kv_valid + rowstat,     # Q, O; K, V; L
-        "bwd_kernel": 6 * t + 2 * kv_valid + rowstat,          # Q, O, dO, dQ, dK, dV; K, V; L
+        "fwd_bf16_kernel": 2 * t + 2 * kv_valid + rowstat,    # Q, O; K, V; L
+        "bwd_kernel": 4 * t + 2 * tk + 2 * kv_valid + rowstat,  # Q, O, dO, dQ; dK, dV; K, V; L
     }
 
 
@@ -133,7 +141,7 @@ def run_gpu(w: wl.Workload, inp: dict, steps: int, warmup: int, prewarm_s: float
     bm = None if inp["block_mask"] is None else torch.from_numpy(inp["block_mask"]).to(dev)
     o = torch.empty_like(q)
     lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
-    dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     kw = dict(scale=w.scale, causal=w.causal, seqlens_k=sl, block_mask=bm, mask_block=128,
               dropout_p=dropout_p, seed=DROPOUT_SEED, offset=0)
     stream = torch.cuda.current_stream(dev)
@@ -570,7 +578,8 @@ def main(argv=None):
 
     w = wl.WORKLOADS[args.workload]
     inp = wl.make_inputs(w)
-    pairs = visible_pairs(w.N, w.H, w.causal, inp["seqlens"], inp["block_mask"], 128, w.B)
+    pairs = visible_pairs(w.N, w.H, w.causal, inp["seqlens"], inp["block_mask"], 128, w.B,
+                          Nk=w.n_keys)
     flops_f = 4.0 * w.d * pairs
     flops_b = 10.0 * w.d * pairs
     esize = 2 if w.dtype == "bf16" else 4
@@ -588,7 +597,7 @@ def main(argv=None):
     # algorithmic FLOPs and compulsory bytes per launch against its own
     # event-timed duration.
     kflops = kernel_flops(w.d, pairs)
-    kbytes = kernel_bytes(w.B, w.H, w.N, w.d, esize, inp["seqlens"])
+    kbytes = kernel_bytes(w.B, w.H, w.N, w.d, esize, inp["seqlens"], Nk=w.n_keys)
     dom = max(KERNELS, key=lambda n: kernel_ms[n])
     ms = kernel_ms[dom]
     t_mfma = kflops[dom] / (peak * 1e12)
@@ -624,7 +633,7 @@ def main(argv=None):
         "dtype": w.dtype,
         "data": "synthetic: seeded iid normal inputs, bf16-rounded (RNE)"
         if w.dtype == "bf16" else "synthetic: seeded iid normal fp32 inputs",
-        "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d,
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "N_k": w.n_keys, "d": w.d,
                    "causal": w.causal, "key_padding": inp["seqlens"] is not None,
                    "block_sparse": inp["block_mask"] is not None, "pairs": pairs,
                    "dropout_p": args.dropout},

@@ -13,10 +13,12 @@ from ._binding import (  # noqa: F401
     fa_bwd,
     fa_bwd_dkdv,
     fa_bwd_dq,
+    fa_bwd_qk,
     fa_bwd_dropout,
     fa_bwd_workspace_bytes,
     fa_fwd,
     fa_fwd_dropout,
+    fa_fwd_qk,
     fa_fwd_tiled,
     fa_last_error,
     fa_status_string,

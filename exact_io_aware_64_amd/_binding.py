@@ -23,8 +23,8 @@ FA_ERR_HIP = 3
 
 # Public entry points declared in include/fa.h.
 EXPORTED = ("fa_fwd", "fa_bwd", "fa_bwd_dq", "fa_bwd_dkdv", "fa_fwd_dropout",
-            "fa_bwd_dropout", "fa_fwd_tiled", "fa_bwd_workspace_bytes", "fa_status_string",
-            "fa_last_error")
+            "fa_bwd_dropout", "fa_fwd_tiled", "fa_fwd_qk", "fa_bwd_qk",
+            "fa_bwd_workspace_bytes", "fa_status_string", "fa_last_error")
 
 
 class FaError(RuntimeError):
@@ -62,6 +62,12 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.fa_bwd_dkdv.argtypes = [I, P, S, P, S, P, S, P, S, P, S, P, P, S, P, S, P,
                                 ctypes.c_size_t, I, I, I, I, F, I, P, P, I, P]
     U64, U32 = ctypes.c_uint64, ctypes.c_uint32
+    lib.fa_fwd_qk.restype = I
+    lib.fa_fwd_qk.argtypes = [I, P, S, P, S, P, S, P, S, P, I, I, I, I, I, F, I, P, P, I,
+                              F, U64, U32, P]
+    lib.fa_bwd_qk.restype = I
+    lib.fa_bwd_qk.argtypes = [I, P, S, P, S, P, S, P, S, P, S, P, P, S, P, S, P, S, P,
+                              ctypes.c_size_t, I, I, I, I, I, F, I, P, P, I, F, U64, U32, P]
     lib.fa_fwd_tiled.restype = I
     lib.fa_fwd_tiled.argtypes = [I, P, S, P, S, P, S, P, S, P, I, I, I, I, F, I, P, P, I, I, P]
     lib.fa_fwd_dropout.restype = I
@@ -142,6 +148,52 @@ def _fwd_args(q, k, v, o, lse, scale, causal, seqlens_k, block_mask, mask_block)
     return (_dtype_code(q), _ptr(q), _strides(q), _ptr(k), _strides(k), _ptr(v), _strides(v),
             _ptr(o), _strides(o), _ptr(lse), B, H, N, d, float(scale), int(bool(causal)),
             _ptr(seqlens_k), _ptr(block_mask), int(mask_block))
+
+
+def _check_qk(q, k, qside, kside):
+    """Shapes [B, H, N_q, d] (q and qside) and [B, H, N_k, d] (k and kside),
+    one dtype; returns B, H, N_q, N_k, d."""
+    B, H, Nq, d = q.shape
+    Nk = k.shape[2]
+    for name, t in qside:
+        if tuple(t.shape) != (B, H, Nq, d) or t.dtype != q.dtype:
+            raise ValueError(f"{name} must be [B, H, N_q, d] like q")
+    for name, t in (("k", k),) + tuple(kside):
+        if tuple(t.shape) != (B, H, Nk, d) or t.dtype != q.dtype:
+            raise ValueError(f"{name} must be [B, H, N_k, d] like k")
+    return B, H, Nq, Nk, d
+
+
+def fa_fwd_qk(q, k, v, o, lse, *, scale: float, causal: bool = False, seqlens_k=None,
+              block_mask=None, mask_block: int = 128, dropout_p: float = 0.0, seed: int = 0,
+              offset: int = 0, stream=None) -> None:
+    """Calls fa_fwd_qk: q, o [B, H, N_q, d]; k, v [B, H, N_k, d]; causal keys
+    j <= i + N_k - N_q."""
+    lib = load_library()
+    B, H, Nq, Nk, d = _check_qk(q, k, (("o", o),), (("v", v),))
+    if tuple(lse.shape) != (B, H, Nq) or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous fp32 [B, H, N_q] tensor")
+    st = lib.fa_fwd_qk(_dtype_code(q), _ptr(q), _strides(q), _ptr(k), _strides(k), _ptr(v),
+                       _strides(v), _ptr(o), _strides(o), _ptr(lse), B, H, Nq, Nk, d,
+                       float(scale), int(bool(causal)), _ptr(seqlens_k), _ptr(block_mask),
+                       int(mask_block), *_drop_args(dropout_p, seed, offset), _stream(q, stream))
+    _check(st)
+
+
+def fa_bwd_qk(q, k, v, o, dout, lse, dq, dk, dv, workspace=None, *, scale: float,
+              causal: bool = False, seqlens_k=None, block_mask=None, mask_block: int = 128,
+              dropout_p: float = 0.0, seed: int = 0, offset: int = 0, stream=None) -> None:
+    """Calls fa_bwd_qk (the forward call's lengths, masks and dropout)."""
+    lib = load_library()
+    B, H, Nq, Nk, d = _check_qk(q, k, (("o", o), ("dout", dout), ("dq", dq)),
+                                (("v", v), ("dk", dk), ("dv", dv)))
+    st = lib.fa_bwd_qk(_dtype_code(q), _ptr(q), _strides(q), _ptr(k), _strides(k), _ptr(v),
+                       _strides(v), _ptr(o), _strides(o), _ptr(dout), _strides(dout), _ptr(lse),
+                       _ptr(dq), _strides(dq), _ptr(dk), _strides(dk), _ptr(dv), _strides(dv),
+                       _ptr(workspace), _nbytes(workspace), B, H, Nq, Nk, d, float(scale),
+                       int(bool(causal)), _ptr(seqlens_k), _ptr(block_mask), int(mask_block),
+                       *_drop_args(dropout_p, seed, offset), _stream(q, stream))
+    _check(st)
 
 
 def _drop_args(dropout_p, seed, offset):
@@ -276,10 +328,18 @@ class Prepared:
 def prepare_fwd(q, k, v, o, lse, *, scale: float, causal: bool = False, seqlens_k=None,
                 block_mask=None, mask_block: int = 128, dropout_p: float = 0.0, seed: int = 0,
                 offset: int = 0, stream=None) -> Prepared:
-    """fa_fwd (or fa_fwd_dropout when dropout_p > 0) with fixed arguments."""
+    """fa_fwd (or fa_fwd_dropout when dropout_p > 0, fa_fwd_qk when k has
+    another length) with fixed arguments."""
     lib = load_library()
-    args = _fwd_args(q, k, v, o, lse, scale, causal, seqlens_k, block_mask, mask_block)
     keep = (q, k, v, o, lse, seqlens_k, block_mask)
+    if k.shape[2] != q.shape[2]:
+        B, H, Nq, Nk, d = _check_qk(q, k, (("o", o),), (("v", v),))
+        args = (_dtype_code(q), _ptr(q), _strides(q), _ptr(k), _strides(k), _ptr(v),
+                _strides(v), _ptr(o), _strides(o), _ptr(lse), B, H, Nq, Nk, d, float(scale),
+                int(bool(causal)), _ptr(seqlens_k), _ptr(block_mask), int(mask_block))
+        return Prepared(lib.fa_fwd_qk,
+                        args + _drop_args(dropout_p, seed, offset) + (_stream(q, stream),), keep)
+    args = _fwd_args(q, k, v, o, lse, scale, causal, seqlens_k, block_mask, mask_block)
     if dropout_p > 0:
         return Prepared(lib.fa_fwd_dropout,
                         args + _drop_args(dropout_p, seed, offset) + (_stream(q, stream),), keep)
@@ -290,11 +350,22 @@ def prepare_bwd(q, k, v, o, dout, lse, dq, dk, dv, workspace=None, *, scale: flo
                 causal: bool = False, seqlens_k=None, block_mask=None, mask_block: int = 128,
                 dropout_p: float = 0.0, seed: int = 0, offset: int = 0,
                 stream=None) -> Prepared:
-    """fa_bwd (or fa_bwd_dropout when dropout_p > 0) with fixed arguments."""
+    """fa_bwd (or fa_bwd_dropout when dropout_p > 0, fa_bwd_qk when k has
+    another length) with fixed arguments."""
     lib = load_library()
+    keep = (q, k, v, o, dout, lse, dq, dk, dv, workspace, seqlens_k, block_mask)
+    if k.shape[2] != q.shape[2]:
+        B, H, Nq, Nk, d = _check_qk(q, k, (("o", o), ("dout", dout), ("dq", dq)),
+                                    (("v", v), ("dk", dk), ("dv", dv)))
+        args = (_dtype_code(q), _ptr(q), _strides(q), _ptr(k), _strides(k), _ptr(v),
+                _strides(v), _ptr(o), _strides(o), _ptr(dout), _strides(dout), _ptr(lse),
+                _ptr(dq), _strides(dq), _ptr(dk), _strides(dk), _ptr(dv), _strides(dv),
+                _ptr(workspace), _nbytes(workspace), B, H, Nq, Nk, d, float(scale),
+                int(bool(causal)), _ptr(seqlens_k), _ptr(block_mask), int(mask_block))
+        return Prepared(lib.fa_bwd_qk,
+                        args + _drop_args(dropout_p, seed, offset) + (_stream(q, stream),), keep)
     args = _bwd_args(q, k, v, o, dout, lse, dq, dk, dv, workspace, scale, causal, seqlens_k,
                      block_mask, mask_block)
-    keep = (q, k, v, o, dout, lse, dq, dk, dv, workspace, seqlens_k, block_mask)
     if dropout_p > 0:
         return Prepared(lib.fa_bwd_dropout,
                         args + _drop_args(dropout_p, seed, offset) + (_stream(q, stream),), keep)
@@ -306,14 +377,16 @@ def prepare_bwd(q, k, v, o, dout, lse, dq, dk, dv, workspace=None, *, scale: flo
 def forward(q, k, v, *, scale: float, causal: bool = False, seqlens_k=None, block_mask=None,
             mask_block: int = 128, dropout_p: float = 0.0, seed: int = 0, offset: int = 0):
     """Allocates O (contiguous [B, H, N, d]) and L, then calls fa_fwd (or
-    fa_fwd_dropout when dropout_p > 0)."""
+    fa_fwd_dropout when dropout_p > 0, fa_fwd_qk when k has another length)."""
     torch = _torch()
     B, H, N, d = q.shape
     o = torch.empty((B, H, N, d), dtype=q.dtype, device=q.device)
     lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
     kw = dict(scale=scale, causal=causal, seqlens_k=seqlens_k, block_mask=block_mask,
               mask_block=mask_block)
-    if dropout_p > 0:
+    if k.shape[2] != N:
+        fa_fwd_qk(q, k, v, o, lse, dropout_p=dropout_p, seed=seed, offset=offset, **kw)
+    elif dropout_p > 0:
         fa_fwd_dropout(q, k, v, o, lse, dropout_p=dropout_p, seed=seed, offset=offset, **kw)
     else:
         fa_fwd(q, k, v, o, lse, **kw)
@@ -324,18 +397,22 @@ def backward(q, k, v, o, dout, lse, *, scale: float, causal: bool = False, seqle
              block_mask=None, mask_block: int = 128, workspace=None, dropout_p: float = 0.0,
              seed: int = 0, offset: int = 0):
     """Allocates dQ, dK, dV (and the workspace unless given), then calls fa_bwd
-    (or fa_bwd_dropout when dropout_p > 0)."""
+    (or fa_bwd_dropout when dropout_p > 0, fa_bwd_qk when k has another length)."""
     torch = _torch()
     B, H, N, d = q.shape
+    Nk = k.shape[2]
     dq = torch.empty((B, H, N, d), dtype=q.dtype, device=q.device)
-    dk = torch.empty_like(dq)
-    dv = torch.empty_like(dq)
+    dk = torch.empty((B, H, Nk, d), dtype=q.dtype, device=q.device)
+    dv = torch.empty_like(dk)
     if workspace is None:
-        nb = fa_bwd_workspace_bytes(_dtype_code(q), B, H, N, d)
+        nb = fa_bwd_workspace_bytes(_dtype_code(q), B, H, max(N, Nk), d)
         workspace = torch.empty(nb, dtype=torch.uint8, device=q.device) if nb else None
     kw = dict(scale=scale, causal=causal, seqlens_k=seqlens_k, block_mask=block_mask,
               mask_block=mask_block)
-    if dropout_p > 0:
+    if Nk != N:
+        fa_bwd_qk(q, k, v, o, dout, lse, dq, dk, dv, workspace, dropout_p=dropout_p,
+                  seed=seed, offset=offset, **kw)
+    elif dropout_p > 0:
         fa_bwd_dropout(q, k, v, o, dout, lse, dq, dk, dv, workspace, dropout_p=dropout_p,
                        seed=seed, offset=offset, **kw)
     else:

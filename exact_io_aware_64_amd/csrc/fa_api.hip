@@ -40,24 +40,26 @@ fa_status check_tensor(const char* name, const void* p, fa_strides s, int elem_a
   return FA_OK;
 }
 
-fa_status check_common(fa_dtype dtype, int B, int H, int N, int d, float scale,
+fa_status check_common(fa_dtype dtype, int B, int H, int N, int Nk, int d, float scale,
                        const uint8_t* block_mask, int mask_block, int* elem_align) {
   if (dtype != FA_BF16 && dtype != FA_F32)
     return fail(FA_ERR_INVALID_ARG, "unknown dtype %d", (int)dtype);
   if (B <= 0 || H <= 0 || N <= 0)
     return fail(FA_ERR_INVALID_ARG, "B, H and N must be positive (got %d, %d, %d)", B, H, N);
+  if (Nk <= 0) return fail(FA_ERR_INVALID_ARG, "N_k must be positive (got %d)", Nk);
   if (d != 64) return fail(FA_ERR_UNSUPPORTED, "head dimension %d is not supported (only 64)", d);
   if (!(scale > 0.f) || !isfinite(scale))
     return fail(FA_ERR_INVALID_ARG, "scale must be positive and finite");
-  const long long tiles = ((long long)N + fa::kTile - 1) / fa::kTile;
-  if (tiles * (long long)B * H > 0x7fffffffLL)
+  const long long tiles = ((long long)(N > Nk ? N : Nk) + fa::kTile - 1) / fa::kTile;
+  if (2 * tiles * (long long)B * H > 0x7fffffffLL)
     return fail(FA_ERR_UNSUPPORTED, "problem too large for one launch grid");
   if (block_mask != nullptr) {
     if (mask_block <= 0 || mask_block % 128 != 0)
       return fail(FA_ERR_INVALID_ARG, "mask_block must be a positive multiple of 128 (got %d)",
                   mask_block);
     if (tiles > fa::kMaxListTiles)
-      return fail(FA_ERR_UNSUPPORTED, "block mask supports N <= %d", fa::kMaxListTiles * 64);
+      return fail(FA_ERR_UNSUPPORTED, "block mask supports N, N_k <= %d",
+                  fa::kMaxListTiles * 64);
   }
   *elem_align = dtype == FA_BF16 ? 8 : 4;
   return FA_OK;
@@ -91,16 +93,16 @@ fa_status hip_status(hipError_t e) {
 
 fa_status fwd_impl(fa_dtype dtype, const void* q, fa_strides q_strides, const void* k,
                    fa_strides k_strides, const void* v, fa_strides v_strides, void* o,
-                   fa_strides o_strides, float* lse, int B, int H, int N, int d, float scale,
-                   int causal, const int32_t* seqlens_k, const uint8_t* block_mask,
-                   int mask_block, float dropout_p, uint64_t seed, uint32_t offset,
-                   int block_q, hipStream_t stream) {
+                   fa_strides o_strides, float* lse, int B, int H, int N, int Nk, int d,
+                   float scale, int causal, const int32_t* seqlens_k,
+                   const uint8_t* block_mask, int mask_block, float dropout_p, uint64_t seed,
+                   uint32_t offset, int block_q, hipStream_t stream) {
   int al = 0;
-  fa_status st = check_common(dtype, B, H, N, d, scale, block_mask, mask_block, &al);
+  fa_status st = check_common(dtype, B, H, N, Nk, d, scale, block_mask, mask_block, &al);
   if (st != FA_OK) return st;
   if ((st = check_tensor("q", q, q_strides, al, N)) != FA_OK) return st;
-  if ((st = check_tensor("k", k, k_strides, al, N)) != FA_OK) return st;
-  if ((st = check_tensor("v", v, v_strides, al, N)) != FA_OK) return st;
+  if ((st = check_tensor("k", k, k_strides, al, Nk)) != FA_OK) return st;
+  if ((st = check_tensor("v", v, v_strides, al, Nk)) != FA_OK) return st;
   if ((st = check_tensor("o", o, o_strides, al, N)) != FA_OK) return st;
   if (lse == nullptr) return fail(FA_ERR_INVALID_ARG, "lse is NULL");
   if (!aligned16(lse)) return fail(FA_ERR_INVALID_ARG, "lse is not 16-byte aligned");
@@ -129,12 +131,15 @@ fa_status fwd_impl(fa_dtype dtype, const void* q, fa_strides q_strides, const vo
   a.B = B;
   a.H = H;
   a.N = N;
+  a.Nk = Nk;
+  a.coff = Nk - N;
   a.scale = scale;
   a.scale_log2 = (float)((double)scale * 1.4426950408889634);
   a.seqlens = seqlens_k;
   a.bmask = block_mask;
   a.mask_block = block_mask ? mask_block : 128;
-  a.n_mask_tiles = (N + a.mask_block - 1) / a.mask_block;
+  a.n_mask_q = (N + a.mask_block - 1) / a.mask_block;
+  a.n_mask_k = (Nk + a.mask_block - 1) / a.mask_block;
   a.drop = drop;
   const hipError_t e = dtype == FA_BF16 ? fa::launch_fwd_bf16(a, causal != 0, block_q, stream)
                                         : fa::launch_fwd_f32(a, causal != 0, stream);
@@ -151,7 +156,7 @@ fa_status fa_fwd(fa_dtype dtype, const void* q, fa_strides q_strides, const void
                  int causal, const int32_t* seqlens_k, const uint8_t* block_mask,
                  int mask_block, hipStream_t stream) {
   return fwd_impl(dtype, q, q_strides, k, k_strides, v, v_strides, o, o_strides, lse, B, H, N,
-                  d, scale, causal, seqlens_k, block_mask, mask_block, 0.f, 0, 0, 128, stream);
+                  N, d, scale, causal, seqlens_k, block_mask, mask_block, 0.f, 0, 0, 128, stream);
 }
 
 fa_status fa_fwd_tiled(fa_dtype dtype, const void* q, fa_strides q_strides, const void* k,
@@ -160,8 +165,19 @@ fa_status fa_fwd_tiled(fa_dtype dtype, const void* q, fa_strides q_strides, cons
                        int causal, const int32_t* seqlens_k, const uint8_t* block_mask,
                        int mask_block, int block_q, hipStream_t stream) {
   return fwd_impl(dtype, q, q_strides, k, k_strides, v, v_strides, o, o_strides, lse, B, H, N,
-                  d, scale, causal, seqlens_k, block_mask, mask_block, 0.f, 0, 0, block_q,
+                  N, d, scale, causal, seqlens_k, block_mask, mask_block, 0.f, 0, 0, block_q,
                   stream);
+}
+
+fa_status fa_fwd_qk(fa_dtype dtype, const void* q, fa_strides q_strides, const void* k,
+                    fa_strides k_strides, const void* v, fa_strides v_strides, void* o,
+                    fa_strides o_strides, float* lse, int B, int H, int N_q, int N_k, int d,
+                    float scale, int causal, const int32_t* seqlens_k,
+                    const uint8_t* block_mask, int mask_block, float dropout_p, uint64_t seed,
+                    uint32_t offset, hipStream_t stream) {
+  return fwd_impl(dtype, q, q_strides, k, k_strides, v, v_strides, o, o_strides, lse, B, H, N_q,
+                  N_k, d, scale, causal, seqlens_k, block_mask, mask_block, dropout_p, seed,
+                  offset, 128, stream);
 }
 
 fa_status fa_fwd_dropout(fa_dtype dtype, const void* q, fa_strides q_strides, const void* k,
@@ -171,7 +187,7 @@ fa_status fa_fwd_dropout(fa_dtype dtype, const void* q, fa_strides q_strides, co
                          const uint8_t* block_mask, int mask_block, float dropout_p,
                          uint64_t seed, uint32_t offset, hipStream_t stream) {
   return fwd_impl(dtype, q, q_strides, k, k_strides, v, v_strides, o, o_strides, lse, B, H, N,
-                  d, scale, causal, seqlens_k, block_mask, mask_block, dropout_p, seed, offset,
+                  N, d, scale, causal, seqlens_k, block_mask, mask_block, dropout_p, seed, offset,
                   128, stream);
 }
 
@@ -194,24 +210,24 @@ fa_status bwd_impl(int phases, fa_dtype dtype, const void* q, fa_strides q_strid
                    const void* o, fa_strides o_strides, const void* dout,
                    fa_strides dout_strides, const float* lse, void* dq, fa_strides dq_strides,
                    void* dk, fa_strides dk_strides, void* dv, fa_strides dv_strides,
-                   void* workspace, size_t workspace_bytes, int B, int H, int N, int d,
+                   void* workspace, size_t workspace_bytes, int B, int H, int N, int Nk, int d,
                    float scale, int causal, const int32_t* seqlens_k,
                    const uint8_t* block_mask, int mask_block, float dropout_p, uint64_t seed,
                    uint32_t offset, hipStream_t stream) {
   int al = 0;
-  fa_status st = check_common(dtype, B, H, N, d, scale, block_mask, mask_block, &al);
+  fa_status st = check_common(dtype, B, H, N, Nk, d, scale, block_mask, mask_block, &al);
   if (st != FA_OK) return st;
   if ((st = check_tensor("q", q, q_strides, al, N)) != FA_OK) return st;
-  if ((st = check_tensor("k", k, k_strides, al, N)) != FA_OK) return st;
-  if ((st = check_tensor("v", v, v_strides, al, N)) != FA_OK) return st;
+  if ((st = check_tensor("k", k, k_strides, al, Nk)) != FA_OK) return st;
+  if ((st = check_tensor("v", v, v_strides, al, Nk)) != FA_OK) return st;
   if ((st = check_tensor("o", o, o_strides, al, N)) != FA_OK) return st;
   if (phases & fa::kPhaseDQ) {
     if ((st = check_tensor("dq", dq, dq_strides, al, N)) != FA_OK) return st;
   }
   if ((st = check_tensor("dout", dout, dout_strides, al, N)) != FA_OK) return st;
   if (phases & fa::kPhaseDKDV) {
-    if ((st = check_tensor("dk", dk, dk_strides, al, N)) != FA_OK) return st;
-    if ((st = check_tensor("dv", dv, dv_strides, al, N)) != FA_OK) return st;
+    if ((st = check_tensor("dk", dk, dk_strides, al, Nk)) != FA_OK) return st;
+    if ((st = check_tensor("dv", dv, dv_strides, al, Nk)) != FA_OK) return st;
   }
   if (lse == nullptr) return fail(FA_ERR_INVALID_ARG, "lse is NULL");
   if (!aligned16(lse)) return fail(FA_ERR_INVALID_ARG, "lse is not 16-byte aligned");
@@ -250,12 +266,15 @@ fa_status bwd_impl(int phases, fa_dtype dtype, const void* q, fa_strides q_strid
   a.B = B;
   a.H = H;
   a.N = N;
+  a.Nk = Nk;
+  a.coff = Nk - N;
   a.scale = scale;
   a.scale_log2 = (float)((double)scale * 1.4426950408889634);
   a.seqlens = seqlens_k;
   a.bmask = block_mask;
   a.mask_block = block_mask ? mask_block : 128;
-  a.n_mask_tiles = (N + a.mask_block - 1) / a.mask_block;
+  a.n_mask_q = (N + a.mask_block - 1) / a.mask_block;
+  a.n_mask_k = (Nk + a.mask_block - 1) / a.mask_block;
   a.drop = drop;
   const hipError_t e = dtype == FA_BF16 ? fa::launch_bwd_bf16(a, causal != 0, phases, stream)
                                         : fa::launch_bwd_f32(a, causal != 0, phases, stream);
@@ -276,8 +295,24 @@ fa_status fa_bwd(fa_dtype dtype, const void* q, fa_strides q_strides, const void
                  hipStream_t stream) {
   return bwd_impl(fa::kPhaseDQ | fa::kPhaseDKDV, dtype, q, q_strides, k, k_strides, v,
                   v_strides, o, o_strides, dout, dout_strides, lse, dq, dq_strides, dk,
-                  dk_strides, dv, dv_strides, workspace, workspace_bytes, B, H, N, d, scale,
+                  dk_strides, dv, dv_strides, workspace, workspace_bytes, B, H, N, N, d, scale,
                   causal, seqlens_k, block_mask, mask_block, 0.f, 0, 0, stream);
+}
+
+fa_status fa_bwd_qk(fa_dtype dtype, const void* q, fa_strides q_strides, const void* k,
+                    fa_strides k_strides, const void* v, fa_strides v_strides, const void* o,
+                    fa_strides o_strides, const void* dout, fa_strides dout_strides,
+                    const float* lse, void* dq, fa_strides dq_strides, void* dk,
+                    fa_strides dk_strides, void* dv, fa_strides dv_strides, void* workspace,
+                    size_t workspace_bytes, int B, int H, int N_q, int N_k, int d, float scale,
+                    int causal, const int32_t* seqlens_k, const uint8_t* block_mask,
+                    int mask_block, float dropout_p, uint64_t seed, uint32_t offset,
+                    hipStream_t stream) {
+  return bwd_impl(fa::kPhaseDQ | fa::kPhaseDKDV, dtype, q, q_strides, k, k_strides, v,
+                  v_strides, o, o_strides, dout, dout_strides, lse, dq, dq_strides, dk,
+                  dk_strides, dv, dv_strides, workspace, workspace_bytes, B, H, N_q, N_k, d,
+                  scale, causal, seqlens_k, block_mask, mask_block, dropout_p, seed, offset,
+                  stream);
 }
 
 fa_status fa_bwd_dropout(fa_dtype dtype, const void* q, fa_strides q_strides, const void* k,
@@ -291,7 +326,7 @@ fa_status fa_bwd_dropout(fa_dtype dtype, const void* q, fa_strides q_strides, co
                          float dropout_p, uint64_t seed, uint32_t offset, hipStream_t stream) {
   return bwd_impl(fa::kPhaseDQ | fa::kPhaseDKDV, dtype, q, q_strides, k, k_strides, v,
                   v_strides, o, o_strides, dout, dout_strides, lse, dq, dq_strides, dk,
-                  dk_strides, dv, dv_strides, workspace, workspace_bytes, B, H, N, d, scale,
+                  dk_strides, dv, dv_strides, workspace, workspace_bytes, B, H, N, N, d, scale,
                   causal, seqlens_k, block_mask, mask_block, dropout_p, seed, offset, stream);
 }
 
@@ -305,7 +340,7 @@ fa_status fa_bwd_dq(fa_dtype dtype, const void* q, fa_strides q_strides, const v
   const fa_strides none{0, 0, 0};
   return bwd_impl(fa::kPhaseDQ, dtype, q, q_strides, k, k_strides, v, v_strides, o,
                   o_strides, dout, dout_strides, lse, dq, dq_strides, nullptr, none, nullptr,
-                  none, workspace, workspace_bytes, B, H, N, d, scale, causal, seqlens_k,
+                  none, workspace, workspace_bytes, B, H, N, N, d, scale, causal, seqlens_k,
                   block_mask, mask_block, 0.f, 0, 0, stream);
 }
 
@@ -320,7 +355,7 @@ fa_status fa_bwd_dkdv(fa_dtype dtype, const void* q, fa_strides q_strides, const
   const fa_strides none{0, 0, 0};
   return bwd_impl(fa::kPhaseDKDV, dtype, q, q_strides, k, k_strides, v, v_strides, o,
                   o_strides, dout, dout_strides, lse, nullptr, none, dk, dk_strides, dv,
-                  dv_strides, workspace, workspace_bytes, B, H, N, d, scale, causal, seqlens_k,
+                  dv_strides, workspace, workspace_bytes, B, H, N, N, d, scale, causal, seqlens_k,
                   block_mask, mask_block, 0.f, 0, 0, stream);
 }
 

@@ -61,10 +61,10 @@ __device__ __forceinline__ void dq_role(const BwdArgs& a, int item, uint16_t* s_
   const int qw = q0 + 32 * w;
   const int qi = qw + r;
 
-  int kv_len = a.N;
-  if constexpr (SEQLEN) kv_len = min(max(a.seqlens[b], 0), a.N);
+  int kv_len = a.Nk;
+  if constexpr (SEQLEN) kv_len = min(max(a.seqlens[b], 0), a.Nk);
   int kend = kv_len;
-  if constexpr (CAUSAL) kend = min(kend, q0 + kBQ);
+  if constexpr (CAUSAL) kend = max(0, min(kend, q0 + kBQ + a.coff));
   const int ntk = (kend + kTile - 1) / kTile;
 
   int nlist = ntk;
@@ -72,16 +72,16 @@ __device__ __forceinline__ void dq_role(const BwdArgs& a, int item, uint16_t* s_
   if constexpr (BMASK) {
     tlist = s_list;
     const int row = q0 / a.mask_block;
-    nlist = build_tile_list(s_list, s_scan, a.bmask + (int64_t)row * a.n_mask_tiles, 1,
-                            a.n_mask_tiles, a.mask_block / kTile, 0, ntk);
+    nlist = build_tile_list(s_list, s_scan, a.bmask + (int64_t)row * a.n_mask_k, 1,
+                            a.n_mask_k, a.mask_block / kTile, 0, ntk);
   }
 
   const __amdgpu_buffer_rsrc_t rq =
       make_rsrc((const uint16_t*)a.q + b * a.sq.b + hh * a.sq.h, slice_bytes(a.N, a.sq.s, 2));
   const __amdgpu_buffer_rsrc_t rk =
-      make_rsrc((const uint16_t*)a.k + b * a.sk.b + hh * a.sk.h, slice_bytes(a.N, a.sk.s, 2));
+      make_rsrc((const uint16_t*)a.k + b * a.sk.b + hh * a.sk.h, slice_bytes(a.Nk, a.sk.s, 2));
   const __amdgpu_buffer_rsrc_t rv =
-      make_rsrc((const uint16_t*)a.v + b * a.sv.b + hh * a.sv.h, slice_bytes(a.N, a.sv.s, 2));
+      make_rsrc((const uint16_t*)a.v + b * a.sv.b + hh * a.sv.h, slice_bytes(a.Nk, a.sv.s, 2));
   const __amdgpu_buffer_rsrc_t ro =
       make_rsrc((const uint16_t*)a.o + b * a.so.b + hh * a.so.h, slice_bytes(a.N, a.so.s, 2));
   const __amdgpu_buffer_rsrc_t rdo = make_rsrc(
@@ -149,7 +149,7 @@ __device__ __forceinline__ void dq_role(const BwdArgs& a, int item, uint16_t* s_
     bf16x8 opa[24];
     [[maybe_unused]] DropBlock zb[2];  // keep bytes of the two halves
     [[maybe_unused]] int lim = 0;
-    if constexpr (MASK) lim = (CAUSAL ? min(kv_len - 1, qi) : kv_len - 1) - k0 - 4 * hl;
+    if constexpr (MASK) lim = (CAUSAL ? min(kv_len - 1, qi + a.coff) : kv_len - 1) - k0 - 4 * hl;
     // A operand of slot t
     auto load_a = [&](int t) FA_INLINE {
       if (t < 16) {
@@ -221,9 +221,9 @@ __device__ __forceinline__ void dq_role(const BwdArgs& a, int item, uint16_t* s_
 
   auto compute = [&](int it, const uint16_t* kt, const uint16_t* vt) FA_INLINE {
     const int k0 = tile_at(it) * kTile;
-    const bool active = !CAUSAL || (k0 <= qw + 31);
+    const bool active = !CAUSAL || (k0 <= qw + 31 + a.coff);
     if (active) {
-      const bool need_mask = (k0 + kTile > kv_len) || (CAUSAL && k0 + kTile - 1 > qw);
+      const bool need_mask = (k0 + kTile > kv_len) || (CAUSAL && k0 + kTile - 1 > qw + a.coff);
       if (need_mask)
         body(std::true_type{}, kt, vt, k0);
       else
@@ -287,8 +287,8 @@ __device__ __forceinline__ void dkdv_role(const BwdArgs& a, int item, uint16_t* 
   const int kw = k0 + 32 * w;  // first key of this wave
   const int kj = kw + r;       // this lane's key
 
-  int kv_len = a.N;
-  if constexpr (SEQLEN) kv_len = min(max(a.seqlens[b], 0), a.N);
+  int kv_len = a.Nk;
+  if constexpr (SEQLEN) kv_len = min(max(a.seqlens[b], 0), a.Nk);
 
   uint16_t* dK = (uint16_t*)a.dk + b * a.sdk.b + hh * a.sdk.h;
   uint16_t* dV = (uint16_t*)a.dv + b * a.sdv.b + hh * a.sdv.h;
@@ -298,22 +298,23 @@ __device__ __forceinline__ void dkdv_role(const BwdArgs& a, int item, uint16_t* 
 
   if (k0 < kv_len) {
     const int nq = (a.N + kTile - 1) / kTile;
-    const int qt_lo = CAUSAL ? k0 / kTile : 0;
+    // causal: the first query that sees key k0 is k0 - coff
+    const int qt_lo = CAUSAL ? max(0, k0 - a.coff) / kTile : 0;
     int nlist = nq - qt_lo;
     [[maybe_unused]] uint16_t* tlist = nullptr;
     if constexpr (BMASK) {
       tlist = s_list;
       const int col = k0 / a.mask_block;
-      nlist = build_tile_list(s_list, s_scan, a.bmask + col, a.n_mask_tiles, a.n_mask_tiles,
+      nlist = build_tile_list(s_list, s_scan, a.bmask + col, a.n_mask_k, a.n_mask_q,
                               a.mask_block / kTile, qt_lo, nq);
     }
 
     const __amdgpu_buffer_rsrc_t rq =
         make_rsrc((const uint16_t*)a.q + b * a.sq.b + hh * a.sq.h, slice_bytes(a.N, a.sq.s, 2));
     const __amdgpu_buffer_rsrc_t rk =
-        make_rsrc((const uint16_t*)a.k + b * a.sk.b + hh * a.sk.h, slice_bytes(a.N, a.sk.s, 2));
+        make_rsrc((const uint16_t*)a.k + b * a.sk.b + hh * a.sk.h, slice_bytes(a.Nk, a.sk.s, 2));
     const __amdgpu_buffer_rsrc_t rv =
-        make_rsrc((const uint16_t*)a.v + b * a.sv.b + hh * a.sv.h, slice_bytes(a.N, a.sv.s, 2));
+        make_rsrc((const uint16_t*)a.v + b * a.sv.b + hh * a.sv.h, slice_bytes(a.Nk, a.sv.s, 2));
     const __amdgpu_buffer_rsrc_t rdo = make_rsrc(
         (const uint16_t*)a.dout + b * a.sdo.b + hh * a.sdo.h, slice_bytes(a.N, a.sdo.s, 2));
     const __amdgpu_buffer_rsrc_t ro = make_rsrc(
@@ -337,7 +338,8 @@ __device__ __forceinline__ void dkdv_role(const BwdArgs& a, int item, uint16_t* 
     const float inv_scale = 1.f / a.scale;
     // Causal: element e of block qb holds query qs + 4*hl + off(qb, e) and is
     // visible iff off >= qs_lim - qs; keys past the sequence see nothing.
-    const int key_lim = (kj < kv_len) ? (CAUSAL ? kj - 4 * hl : -(1 << 30)) : (1 << 30);
+    const int key_lim =
+        (kj < kv_len) ? (CAUSAL ? kj - a.coff - 4 * hl : -(1 << 30)) : (1 << 30);
 
     // Per-lane LDS offsets: Q and dO rows (A operands of S and dP) and Q^T,
     // dO^T transpose reads (A operands of dK^T and dV^T).
@@ -518,9 +520,9 @@ __device__ __forceinline__ void dkdv_role(const BwdArgs& a, int item, uint16_t* 
 
     auto compute = [&](int it, int buf, const uint16_t* qs_, const uint16_t* ds_) FA_INLINE {
       const int qs = tile_at(it) * kTile;
-      const bool active = !CAUSAL || (qs + kTile - 1 >= kw);
+      const bool active = !CAUSAL || (qs + kTile - 1 >= kw - a.coff);
       if (active) {
-        const bool need_mask = (kw + 32 > kv_len) || (CAUSAL && kw + 31 > qs);
+        const bool need_mask = (kw + 32 > kv_len) || (CAUSAL && kw + 31 - a.coff > qs);
         if (need_mask)
           tile(std::true_type{}, buf, qs_, ds_, qs);
         else
@@ -554,7 +556,7 @@ __device__ __forceinline__ void dkdv_role(const BwdArgs& a, int item, uint16_t* 
     }
   }
 
-  if (kj < a.N) {
+  if (kj < a.Nk) {
     uint16_t* kout = dK + (int64_t)kj * a.sdk.s;
     uint16_t* vout = dV + (int64_t)kj * a.sdv.s;
 #pragma unroll
@@ -610,15 +612,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   bool dkdv;
   int item;
   if (phases == (kPhaseDQ | kPhaseDKDV)) {
+    // The role whose items are heavier goes first: a dK/dV item sweeps the
+    // queries, a dQ item the keys.
+    const bool dq_first = a.Nk > a.N;
+    const int nfirst = dq_first ? (a.N + kBQ - 1) / kBQ : (a.Nk + kBK - 1) / kBK;
+    bool first;
     if ((BH & 7) == 0) {
       const int hpx = BH >> 3, x = id & 7, j = id >> 3;
-      const int m = j / hpx, nt = (a.N + kBQ - 1) / kBQ;
-      dkdv = m < nt;
-      item = (dkdv ? m : m - nt) * BH + x + 8 * (j % hpx);
+      const int m = j / hpx;
+      first = m < nfirst;
+      item = (first ? m : m - nfirst) * BH + x + 8 * (j % hpx);
     } else {
-      dkdv = (id & 1) == 0;
-      item = id >> 1;
+      first = id < nfirst * BH;
+      item = first ? id : id - nfirst * BH;
     }
+    dkdv = first != dq_first;
   } else {
     dkdv = phases == kPhaseDKDV;
     item = id;
@@ -632,16 +640,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 
 template <bool C, bool S, bool M, bool D>
 hipError_t launch(const BwdArgs& a, int phases, hipStream_t stream) {
-  static_assert(kBQ == kBK, "the interleaved grid pairs one query tile with one key tile");
   BwdArgs copy = a;
   int ph = phases;
   void* args[] = {&copy, &ph};
-  const int per_role = ((a.N + kBQ - 1) / kBQ) * a.B * a.H;
+  const int n_dq = ((a.N + kBQ - 1) / kBQ) * a.B * a.H;
+  const int n_dkdv = ((a.Nk + kBK - 1) / kBK) * a.B * a.H;
   int n = 0;
-  if (phases == (kPhaseDQ | kPhaseDKDV))
-    n = 2 * per_role;
-  else if (phases == kPhaseDQ || phases == kPhaseDKDV)
-    n = per_role;
+  if (phases & kPhaseDQ) n += n_dq;
+  if (phases & kPhaseDKDV) n += n_dkdv;
   if (n == 0) return hipSuccess;
   return hipLaunchKernel((const void*)&bwd_kernel<C, S, M, D>, dim3((unsigned)n), dim3(256),
                          args, 0, stream);

@@ -19,10 +19,10 @@ namespace {
 
 constexpr int kD = 64;
 
-__device__ __forceinline__ bool tile_kept(const uint8_t* bmask, int n_mask_tiles,
-                                          int mask_block, int qrow, int kcol) {
+__device__ __forceinline__ bool tile_kept(const uint8_t* bmask, int n_mask_k, int mask_block,
+                                          int qrow, int kcol) {
   return bmask == nullptr ||
-         bmask[(int64_t)(qrow / mask_block) * n_mask_tiles + kcol / mask_block] != 0;
+         bmask[(int64_t)(qrow / mask_block) * n_mask_k + kcol / mask_block] != 0;
 }
 
 __device__ __forceinline__ void load_row(float* dst, const float* src) {
@@ -87,9 +87,9 @@ __global__ __launch_bounds__(64) void fwd_f32_kernel(FwdArgs a, int causal) {
   const int qt = blockIdx.x / BH, bh = blockIdx.x % BH;
   const int b = bh / a.H, hh = bh % a.H;
   const int q0 = qt * kTile, qi = q0 + tid;
-  int kv_len = a.N;
-  if (a.seqlens) kv_len = min(max(a.seqlens[b], 0), a.N);
-  const int kend = causal ? min(kv_len, q0 + kTile) : kv_len;
+  int kv_len = a.Nk;
+  if (a.seqlens) kv_len = min(max(a.seqlens[b], 0), a.Nk);
+  const int kend = causal ? min(kv_len, q0 + kTile + a.coff) : kv_len;
   const float* Q = (const float*)a.q + b * a.sq.b + hh * a.sq.h;
   const float* K = (const float*)a.k + b * a.sk.b + hh * a.sk.h;
   const float* V = (const float*)a.v + b * a.sv.b + hh * a.sv.h;
@@ -103,10 +103,10 @@ __global__ __launch_bounds__(64) void fwd_f32_kernel(FwdArgs a, int causal) {
   const float c = a.scale_log2;
 
   for (int k0 = 0; k0 < kend; k0 += kTile) {
-    if (!tile_kept(a.bmask, a.n_mask_tiles, a.mask_block, q0, k0)) continue;
+    if (!tile_kept(a.bmask, a.n_mask_k, a.mask_block, q0, k0)) continue;
     const int kk = k0 + tid;
-    stage_row(s_k + tid * kD, K + (int64_t)kk * a.sk.s, kk < a.N);
-    stage_row(s_v + tid * kD, V + (int64_t)kk * a.sv.s, kk < a.N);
+    stage_row(s_k + tid * kD, K + (int64_t)kk * a.sk.s, kk < a.Nk);
+    stage_row(s_v + tid * kD, V + (int64_t)kk * a.sv.s, kk < a.Nk);
     __syncthreads();
     // keep bit j of this query and key k0 + j (all ones without dropout)
     uint64_t keep = ~0ull;
@@ -127,7 +127,7 @@ __global__ __launch_bounds__(64) void fwd_f32_kernel(FwdArgs a, int causal) {
 #pragma unroll
     for (int j = 0; j < kTile; ++j) {
       const int key = k0 + j;
-      const bool vis = key < kv_len && (!causal || key <= qi);
+      const bool vis = key < kv_len && (!causal || key <= qi + a.coff);
       s[j] = vis ? dot_lds(q, s_k + j * kD) : -kInf;
       mx = fmaxf(mx, s[j]);
     }
@@ -165,9 +165,9 @@ __global__ __launch_bounds__(64) void dq_f32_kernel(BwdArgs a, int causal) {
   const int qt = blockIdx.x / BH, bh = blockIdx.x % BH;
   const int b = bh / a.H, hh = bh % a.H;
   const int q0 = qt * kTile, qi = q0 + tid;
-  int kv_len = a.N;
-  if (a.seqlens) kv_len = min(max(a.seqlens[b], 0), a.N);
-  const int kend = causal ? min(kv_len, q0 + kTile) : kv_len;
+  int kv_len = a.Nk;
+  if (a.seqlens) kv_len = min(max(a.seqlens[b], 0), a.Nk);
+  const int kend = causal ? min(kv_len, q0 + kTile + a.coff) : kv_len;
   const float* K = (const float*)a.k + b * a.sk.b + hh * a.sk.h;
   const float* V = (const float*)a.v + b * a.sv.b + hh * a.sv.h;
 
@@ -188,15 +188,15 @@ __global__ __launch_bounds__(64) void dq_f32_kernel(BwdArgs a, int causal) {
   const float c = a.scale_log2;
 
   for (int k0 = 0; k0 < kend; k0 += kTile) {
-    if (!tile_kept(a.bmask, a.n_mask_tiles, a.mask_block, q0, k0)) continue;
+    if (!tile_kept(a.bmask, a.n_mask_k, a.mask_block, q0, k0)) continue;
     const int kk = k0 + tid;
-    stage_row(s_k + tid * kD, K + (int64_t)kk * a.sk.s, kk < a.N);
-    stage_row(s_v + tid * kD, V + (int64_t)kk * a.sv.s, kk < a.N);
+    stage_row(s_k + tid * kD, K + (int64_t)kk * a.sk.s, kk < a.Nk);
+    stage_row(s_v + tid * kD, V + (int64_t)kk * a.sv.s, kk < a.Nk);
     __syncthreads();
     [[maybe_unused]] uint32_t zw[4] = {0u, 0u, 0u, 0u};
     for (int j = 0; j < kTile; ++j) {
       const int key = k0 + j;
-      const bool vis = key < kv_len && (!causal || key <= qi);
+      const bool vis = key < kv_len && (!causal || key <= qi + a.coff);
       const float s = dot_lds(q, s_k + j * kD);
       const float p = vis ? fast_exp2(__builtin_fmaf(s, c, -L2)) : 0.f;
       float dp = dot_lds(g, s_v + j * kD);
@@ -226,14 +226,14 @@ __global__ __launch_bounds__(64) void dkdv_f32_kernel(BwdArgs a, int causal) {
   const int kt = blockIdx.x / BH, bh = blockIdx.x % BH;
   const int b = bh / a.H, hh = bh % a.H;
   const int k0 = kt * kTile, kj = k0 + tid;
-  int kv_len = a.N;
-  if (a.seqlens) kv_len = min(max(a.seqlens[b], 0), a.N);
+  int kv_len = a.Nk;
+  if (a.seqlens) kv_len = min(max(a.seqlens[b], 0), a.Nk);
   const float* Q = (const float*)a.q + b * a.sq.b + hh * a.sq.h;
   const float* G = (const float*)a.dout + b * a.sdo.b + hh * a.sdo.h;
   const float* O = (const float*)a.o + b * a.so.b + hh * a.so.h;
 
   float kr[kD], vr[kD], dk[kD], dv[kD];
-  if (kj < a.N) {
+  if (kj < a.Nk) {
     load_row(kr, (const float*)a.k + b * a.sk.b + hh * a.sk.h + (int64_t)kj * a.sk.s);
     load_row(vr, (const float*)a.v + b * a.sv.b + hh * a.sv.h + (int64_t)kj * a.sv.s);
   } else {
@@ -243,8 +243,9 @@ __global__ __launch_bounds__(64) void dkdv_f32_kernel(BwdArgs a, int causal) {
   const float c = a.scale_log2;
 
   if (k0 < kv_len) {
-    for (int qs = causal ? k0 : 0; qs < a.N; qs += kTile) {
-      if (!tile_kept(a.bmask, a.n_mask_tiles, a.mask_block, qs, k0)) continue;
+    // causal: the first query that sees key k0 is k0 - coff
+    for (int qs = causal ? max(0, k0 - a.coff) / kTile * kTile : 0; qs < a.N; qs += kTile) {
+      if (!tile_kept(a.bmask, a.n_mask_k, a.mask_block, qs, k0)) continue;
       const int qq = qs + tid;
       stage_row(s_q + tid * kD, Q + (int64_t)qq * a.sq.s, qq < a.N);
       stage_row(s_g + tid * kD, G + (int64_t)qq * a.sdo.s, qq < a.N);
@@ -261,7 +262,7 @@ __global__ __launch_bounds__(64) void dkdv_f32_kernel(BwdArgs a, int causal) {
       [[maybe_unused]] uint32_t zw[4] = {0u, 0u, 0u, 0u};
       for (int i = 0; i < kTile; ++i) {
         const int q = qs + i;
-        const bool vis = kj < kv_len && (!causal || kj <= q);
+        const bool vis = kj < kv_len && (!causal || kj <= q + a.coff);
         const float s = dot_lds(kr, s_q + i * kD);
         float p = vis ? fast_exp2(__builtin_fmaf(s, c, -s_l2[i])) : 0.f;
         float dp = dot_lds(vr, s_g + i * kD);
@@ -282,7 +283,7 @@ __global__ __launch_bounds__(64) void dkdv_f32_kernel(BwdArgs a, int causal) {
       __syncthreads();
     }
   }
-  if (kj < a.N) {
+  if (kj < a.Nk) {
     store_row((float*)a.dk + b * a.sdk.b + hh * a.sdk.h + (int64_t)kj * a.sdk.s, dk, a.scale);
     store_row((float*)a.dv + b * a.sdv.b + hh * a.sdv.h + (int64_t)kj * a.sdv.s, dv,
               DROP ? a.drop.scale : 1.f);
@@ -305,14 +306,16 @@ hipError_t launch_bwd_f32(const BwdArgs& a, bool causal, int phases, hipStream_t
   BwdArgs copy = a;
   int cz = causal ? 1 : 0;
   void* args[] = {&copy, &cz};
-  dim3 grid((unsigned)(((a.N + kTile - 1) / kTile) * a.B * a.H)), block(64);
+  const dim3 block(64);
   const bool drop = a.drop.t < 256;
   if (phases & kPhaseDQ) {
+    const dim3 grid((unsigned)(((a.N + kTile - 1) / kTile) * a.B * a.H));
     const void* fn = drop ? (const void*)&dq_f32_kernel<true> : (const void*)&dq_f32_kernel<false>;
     hipError_t e = hipLaunchKernel(fn, grid, block, args, 0, stream);
     if (e != hipSuccess) return e;
   }
   if (phases & kPhaseDKDV) {
+    const dim3 grid((unsigned)(((a.Nk + kTile - 1) / kTile) * a.B * a.H));
     const void* fn =
         drop ? (const void*)&dkdv_f32_kernel<true> : (const void*)&dkdv_f32_kernel<false>;
     return hipLaunchKernel(fn, grid, block, args, 0, stream);

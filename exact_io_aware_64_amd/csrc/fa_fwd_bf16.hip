@@ -77,10 +77,10 @@ __global__ __launch_bounds__(64 * W) void fwd_bf16_kernel(FwdArgs a) {
   const int qw = q0 + 32 * w;  // first query of this wave
   const int qi = qw + r;       // this lane's query
 
-  int kv_len = a.N;
-  if constexpr (SEQLEN) kv_len = min(max(a.seqlens[b], 0), a.N);
+  int kv_len = a.Nk;
+  if constexpr (SEQLEN) kv_len = min(max(a.seqlens[b], 0), a.Nk);
   int kend = kv_len;
-  if constexpr (CAUSAL) kend = min(kend, q0 + kBR);
+  if constexpr (CAUSAL) kend = max(0, min(kend, q0 + kBR + a.coff));
   const int ntk = (kend + kTile - 1) / kTile;
 
   int nlist = ntk;
@@ -90,16 +90,16 @@ __global__ __launch_bounds__(64 * W) void fwd_bf16_kernel(FwdArgs a) {
     __shared__ int s_scan[W];
     tlist = s_list;
     const int row = q0 / a.mask_block;  // the host makes the query tile divide mask_block
-    nlist = build_tile_list<64 * W>(s_list, s_scan, a.bmask + (int64_t)row * a.n_mask_tiles,
-                                    1, a.n_mask_tiles, a.mask_block / kTile, 0, ntk);
+    nlist = build_tile_list<64 * W>(s_list, s_scan, a.bmask + (int64_t)row * a.n_mask_k, 1,
+                                    a.n_mask_k, a.mask_block / kTile, 0, ntk);
   }
 
   const __amdgpu_buffer_rsrc_t rq =
       make_rsrc((const uint16_t*)a.q + b * a.sq.b + hh * a.sq.h, slice_bytes(a.N, a.sq.s, 2));
   const __amdgpu_buffer_rsrc_t rk =
-      make_rsrc((const uint16_t*)a.k + b * a.sk.b + hh * a.sk.h, slice_bytes(a.N, a.sk.s, 2));
+      make_rsrc((const uint16_t*)a.k + b * a.sk.b + hh * a.sk.h, slice_bytes(a.Nk, a.sk.s, 2));
   const __amdgpu_buffer_rsrc_t rv =
-      make_rsrc((const uint16_t*)a.v + b * a.sv.b + hh * a.sv.h, slice_bytes(a.N, a.sv.s, 2));
+      make_rsrc((const uint16_t*)a.v + b * a.sv.b + hh * a.sv.h, slice_bytes(a.Nk, a.sv.s, 2));
   const int ssk = (int)a.sk.s * 2, ssv = (int)a.sv.s * 2;
 
   // Q fragment: B operand of S^T = K Q^T, lane (r, hl) holds
@@ -168,7 +168,7 @@ __global__ __launch_bounds__(64 * W) void fwd_bf16_kernel(FwdArgs a) {
     // element e of half kb holds key k0 + 32 kb + 8 (e / 4) + 4 hl + e % 4;
     // visible iff 32 kb + 8 (e / 4) + e % 4 <= lim
     [[maybe_unused]] int lim = 0;
-    if constexpr (MASK) lim = (CAUSAL ? min(kv_len - 1, qi) : kv_len - 1) - k0 - 4 * hl;
+    if constexpr (MASK) lim = (CAUSAL ? min(kv_len - 1, qi + a.coff) : kv_len - 1) - k0 - 4 * hl;
 
     auto probs = [&](int kb, int e0) FA_INLINE {  // elements e0 .. e0+3 of half kb
       float p[4];
@@ -261,9 +261,9 @@ __global__ __launch_bounds__(64 * W) void fwd_bf16_kernel(FwdArgs a) {
 
   auto compute = [&](int it, const uint16_t* kt, const uint16_t* vt) FA_INLINE {
     const int k0 = tile_at(it) * kTile;
-    const bool active = !CAUSAL || (k0 <= qw + 31);
+    const bool active = !CAUSAL || (k0 <= qw + 31 + a.coff);
     if (active) {
-      const bool need_mask = (k0 + kTile > kv_len) || (CAUSAL && k0 + kTile - 1 > qw);
+      const bool need_mask = (k0 + kTile > kv_len) || (CAUSAL && k0 + kTile - 1 > qw + a.coff);
       if (need_mask)
         body(std::true_type{}, kt, vt, k0);
       else

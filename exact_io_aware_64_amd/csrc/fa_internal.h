@@ -33,13 +33,16 @@ struct FwdArgs {
   void* o;
   float* lse;
   Strides sq, sk, sv, so;
-  int B, H, N;
+  int B, H;
+  int N;     // queries
+  int Nk;    // keys
+  int coff;  // causal offset Nk - N: key j is visible to query i iff j <= i + coff
   float scale;       // softmax scale
   float scale_log2;  // scale * log2(e): scores enter exp2 directly
   const int32_t* seqlens;
-  const uint8_t* bmask;
+  const uint8_t* bmask;  // [n_mask_q][n_mask_k]
   int mask_block;
-  int n_mask_tiles;
+  int n_mask_q, n_mask_k;
   Dropout drop;
 };
 
@@ -54,13 +57,16 @@ struct BwdArgs {
   void* dk;
   void* dv;
   Strides sq, sk, sv, so, sdo, sdq, sdk, sdv;
-  int B, H, N;
+  int B, H;
+  int N;     // queries (Q, O, dO, dQ, L rows)
+  int Nk;    // keys (K, V, dK, dV rows)
+  int coff;  // causal offset Nk - N
   float scale;
   float scale_log2;
   const int32_t* seqlens;
-  const uint8_t* bmask;
+  const uint8_t* bmask;  // [n_mask_q][n_mask_k]
   int mask_block;
-  int n_mask_tiles;
+  int n_mask_q, n_mask_k;
   Dropout drop;
 };
 

@@ -268,6 +268,59 @@ fa_status fa_bwd_dropout(fa_dtype dtype,
                          float dropout_p, uint64_t seed, uint32_t offset,
                          hipStream_t stream);
 
+/*
+ * fa_fwd_qk, fa_bwd_qk -- the general forms: N_q queries attend to N_k keys
+ * (every other entry point is the special case N_q = N_k, and fa_fwd /
+ * fa_bwd also dropout_p = 0).  The pages only treat square problems; the
+ * queries are read as the last N_q positions of a sequence whose first
+ * N_k - N_q keys are already held (a key/value cache), so
+ *
+ *   causal: key j is visible to query i iff j <= i + (N_k - N_q)
+ *
+ * -- the last query sees every key, a single query (N_q = 1) sees all of
+ * them, and with N_q > N_k the first N_q - N_k queries see none (O = 0,
+ * L = -inf).  With N_q = N_k this is j <= i.
+ *
+ *   q, o, dout, dq   [B][H][N_q][d] through their strides; lse [B*H*N_q].
+ *   k, v, dk, dv     [B][H][N_k][d] through their strides.
+ *   seqlens_k        as before, clamped to [0, N_k].
+ *   block_mask       uint8[ceil(N_q / mask_block) * ceil(N_k / mask_block)],
+ *                    row-major [query tile][key tile].
+ *   dropout_p, seed, offset  as for fa_fwd_dropout (0 = no dropout).
+ *   remaining arguments, validation and errors as for fa_fwd / fa_bwd; N_k
+ *   must be positive.
+ */
+fa_status fa_fwd_qk(fa_dtype dtype,
+                    const void* q, fa_strides q_strides,
+                    const void* k, fa_strides k_strides,
+                    const void* v, fa_strides v_strides,
+                    void* o, fa_strides o_strides,
+                    float* lse,
+                    int B, int H, int N_q, int N_k, int d,
+                    float scale, int causal,
+                    const int32_t* seqlens_k,
+                    const uint8_t* block_mask, int mask_block,
+                    float dropout_p, uint64_t seed, uint32_t offset,
+                    hipStream_t stream);
+
+fa_status fa_bwd_qk(fa_dtype dtype,
+                    const void* q, fa_strides q_strides,
+                    const void* k, fa_strides k_strides,
+                    const void* v, fa_strides v_strides,
+                    const void* o, fa_strides o_strides,
+                    const void* dout, fa_strides dout_strides,
+                    const float* lse,
+                    void* dq, fa_strides dq_strides,
+                    void* dk, fa_strides dk_strides,
+                    void* dv, fa_strides dv_strides,
+                    void* workspace, size_t workspace_bytes,
+                    int B, int H, int N_q, int N_k, int d,
+                    float scale, int causal,
+                    const int32_t* seqlens_k,
+                    const uint8_t* block_mask, int mask_block,
+                    float dropout_p, uint64_t seed, uint32_t offset,
+                    hipStream_t stream);
+
 /* Static, human-readable name of a status code. */
 const char* fa_status_string(fa_status status);
 

@@ -51,6 +51,15 @@ def maxabs(a, b) -> float:
     return float(np.nanmax(np.where(np.isnan(d), np.inf, d)))
 
 
+def excess_over(o, ostar, abs_tol: float, rel: float = 2.0 ** -8) -> float:
+    """Largest |o - o*| - (abs_tol + rel |o*|) over the elements (<= 0 passes):
+    an absolute budget plus the rounding of the stored value, at most half
+    an ulp of bf16 (2^-8 of its magnitude)."""
+    o = np.asarray(o, np.float64)
+    ostar = np.asarray(ostar, np.float64)
+    return float(np.max(np.abs(o - ostar) - (abs_tol + rel * np.abs(ostar))))
+
+
 def relfro(g, gstar) -> float:
     g = np.asarray(g, np.float64)
     gstar = np.asarray(gstar, np.float64)

@@ -223,3 +223,27 @@ def _fwd_tiled(**kw):
 def test_fwd_tiled_rejects_bad_arguments(kw, status, msg):
     assert _fwd_tiled(**kw) == status
     assert msg in fa.fa_last_error()
+
+
+def _fwd_qk(**kw):
+    lib = fa.load_library()
+    args = dict(dtype=0, q=A, sq=S, k=A, sk=S, v=A, sv=S, o=A, so=S, lse=A, B=1, H=1, Nq=16,
+                Nk=1024, d=64, scale=0.125, causal=1, seqlens=None, bmask=None, mb=128, p=0.0,
+                seed=0, offset=0, stream=None)
+    args.update(kw)
+    return lib.fa_fwd_qk(*args.values())
+
+
+@pytest.mark.parametrize("kw,status,msg", [
+    (dict(Nk=0), 1, "N_k must be positive"),
+    (dict(Nq=0), 1, "must be positive"),
+    (dict(Nk=-3), 1, "N_k must be positive"),
+    (dict(k=None), 1, "k is NULL"),
+    (dict(sk=bnd.fa_strides(0, 0, 1 << 20), Nk=1024), 2, "2 GiB"),
+    (dict(bmask=A, mb=64), 1, "mask_block"),
+    (dict(bmask=A, Nk=300000), 2, "block mask"),
+    (dict(p=1.5), 1, "dropout_p"),
+])
+def test_fwd_qk_rejects_bad_arguments(kw, status, msg):
+    assert _fwd_qk(**kw) == status
+    assert msg in fa.fa_last_error()

@@ -70,3 +70,29 @@ def test_io_sweep_model_and_dispatch_mapping():
             threads = 2 * bq                              # bq / 32 waves of 64 lanes
             grid = (N // bq) * bench.SWEEP_H * threads    # Grid_Size counts work-items
             assert bench._sweep_config(dict(wg=threads, grid=grid)) == (N, bq)
+
+
+@pytest.mark.parametrize("N,Nk,causal,seqlens,p", [
+    (100, 300, True, None, None),
+    (300, 100, True, None, None),
+    (130, 500, True, [400, 20], 0.5),
+    (500, 130, True, [130, 60], 0.5),
+    (200, 450, False, [450, 300], 0.4),
+])
+def test_rectangular_pairs_match_brute_force(N, Nk, causal, seqlens, p):
+    rng = np.random.default_rng(N + Nk)
+    bm = None
+    if p:
+        bm = (rng.random((-(-N // 128), -(-Nk // 128))) < p).astype(np.uint8)
+    B = 1 if seqlens is None else len(seqlens)
+    sl = None if seqlens is None else np.array(seqlens, np.int32)
+    got = bench.visible_pairs(N, 2, causal, sl, bm, 128, B, Nk=Nk)
+    want = 2 * ref.visible_pair_count(N, causal, sl, bm, 128, B, N_k=Nk)
+    assert got == want
+
+
+def test_rectangular_kernel_bytes():
+    kb = bench.kernel_bytes(1, 2, 100, 64, 2, None, Nk=300)
+    tq, tk = 2 * 100 * 64 * 2, 2 * 300 * 64 * 2
+    assert kb["fwd_bf16_kernel"] == 2 * tq + 2 * tk + 2 * 100 * 4
+    assert kb["bwd_kernel"] == 4 * tq + 4 * tk + 2 * 100 * 4

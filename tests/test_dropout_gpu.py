@@ -14,10 +14,11 @@ output:
   * dK/dV role, dS path: the same with K = 0 and Q one-hot over a query
     window, read from the sign of dK.
 Random inputs are then compared with the oracle to the usual tolerances,
-except that the O bound is multiplied by the keep scale s = 256 / t: kept
-values are s times larger, and so is the rounding of the stored bf16 O (a
-row with a single visible key reaches |O| = s |v|, whose half-ulp exceeds
-the plain bound once it passes 4).
+except for O: each element may differ by the plain bound times the keep
+scale s = 256 / t (kept values are s times larger) plus the rounding of the
+stored bf16 value itself, 2^-8 of its magnitude (a row with a single visible
+key reaches |O| = s |v|, whose half-ulp exceeds the plain bound once it
+passes 4).
 """
 import sys
 
@@ -26,7 +27,8 @@ import pytest
 
 import workloads as wl
 from oracle import dropout_ref as dref
-from tests.gpu_util import TOL, device_inputs, maxabs, opt_dev, relfro, to_dev, to_np
+from tests.gpu_util import (TOL, device_inputs, excess_over, maxabs, opt_dev, relfro, to_dev,
+                            to_np)
 
 pytestmark = pytest.mark.gpu
 
@@ -162,7 +164,8 @@ def _check_random(case, p, seed, offset, tag):
     for name, g, gs in (("dQ", dq, gq), ("dK", dk, gk), ("dV", dv, gv)):
         errs[name] = relfro(to_np(g), gs)
     _say(f"[dropout parity] {tag} {errs}")
-    assert errs["O"] <= tol["O"] * _keep_scale(p) and errs["L"] <= tol["L"], errs
+    assert excess_over(to_np(o), O, tol["O"] * _keep_scale(p)) <= 0, errs
+    assert errs["L"] <= tol["L"], errs
     for name in ("dQ", "dK", "dV"):
         assert errs[name] <= tol["G"], (name, errs)
 
@@ -251,6 +254,7 @@ def test_sampled_full_size_gpt2_with_dropout():
     errs["dV"] = relfro(to_np(dv_r), gv)
     _say(f"[dropout sampled] {errs}")
     tol = TOL["bf16"]
-    assert errs["O"] <= tol["O"] * _keep_scale(p) and errs["L"] <= tol["L"], errs
+    assert excess_over(to_np(o)[idx], O, tol["O"] * _keep_scale(p)) <= 0, errs
+    assert errs["L"] <= tol["L"], errs
     for name in ("dQ", "dK", "dV"):
         assert errs[name] <= tol["G"], (name, errs)

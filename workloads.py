@@ -11,8 +11,9 @@ suanlizi.com page, "core idea"; researchpapers.dev page, "key results").  No
 dataset item is used: every tensor is iid Gaussian noise.
 
 Draw order for one workload (one ``numpy.random.default_rng(seed)``, PCG64):
-Q, K, V, dO (each ``[B, H, N, d]``, fp32 standard normals times ``std``), then
-the per-sequence key lengths or the tile mask, then the sampled query rows.
+Q, K, V, dO (each ``[B, H, N, d]``, fp32 standard normals times ``std``; K and
+V have ``N_k`` rows where a workload sets a key length of its own), then the
+per-sequence key lengths or the tile mask, then the sampled query rows.
 bf16 workloads round every tensor to bf16 with round-to-nearest-even and keep
 it as float32 values that are exactly representable in bf16.
 """
@@ -43,6 +44,11 @@ class Workload:
     sample_rows: Optional[int] = None  # query rows per (b, h) checked against the oracle
     backward: bool = True
     summary: str = field(default="", compare=False)
+    Nk: Optional[int] = None   # keys, when not N (the queries are the last N positions)
+
+    @property
+    def n_keys(self) -> int:
+        return self.N if self.Nk is None else self.Nk
 
 
 WORKLOADS = {
@@ -62,6 +68,10 @@ WORKLOADS = {
         Workload("blocksparse_b1h8n65536", 1, 8, 65536, 64, "bf16", False, 1 / 8, 5,
                  block_keep_p=1 / 16, sample_rows=512,
                  summary="block-sparse attention, 128x128 tiles, bf16"),
+        Workload("prefill_causal_b1h16q2048k16384", 1, 16, 2048, 64, "bf16", True, 1 / 8, 7,
+                 std=0.5, sample_rows=512, Nk=16384,
+                 summary="chunked prefill: 2048 new queries over 16384 keys (14336 cached), "
+                         "causal aligned to the last query, bf16"),
     ]
 }
 WORKLOAD_ORDER = list(WORKLOADS)
@@ -119,7 +129,12 @@ def draw_tensors(rng: np.random.Generator, B: int, H: int, N: int, d: int,
 def make_inputs(w: Workload, seed: Optional[int] = None) -> dict:
     """All inputs of one workload, drawn in the documented order."""
     rng = np.random.default_rng(w.seed if seed is None else seed)
-    q, k, v, do = draw_tensors(rng, w.B, w.H, w.N, w.d, w.dtype, w.std)
+    if w.Nk is None:
+        q, k, v, do = draw_tensors(rng, w.B, w.H, w.N, w.d, w.dtype, w.std)
+    else:
+        (q,) = draw_tensors(rng, w.B, w.H, w.N, w.d, w.dtype, w.std, count=1)
+        k, v = draw_tensors(rng, w.B, w.H, w.Nk, w.d, w.dtype, w.std, count=2)
+        (do,) = draw_tensors(rng, w.B, w.H, w.N, w.d, w.dtype, w.std, count=1)
     seqlens = None
     block_mask = None
     if w.padded_min is not None:
