@@ -121,7 +121,8 @@ def measure_key(workload: str, dropout_p: float) -> str:
 def run_gpu(w: wl.Workload, inp: dict, steps: int, warmup: int, prewarm_s: float = 1.0,
             dropout_p: float = 0.0):
     """Times `steps` steps after `warmup` untimed ones.  One step is fa_fwd
-    then fa_bwd, each a single kernel launch on the current stream; HIP
+    then fa_bwd (fa_fwd alone for a forward-only workload), each a single
+    kernel launch on the current stream; HIP
     events recorded on that stream around the launches give each kernel's
     device time, and the wall clock around the whole timed region gives the
     step time.
@@ -147,7 +148,8 @@ def run_gpu(w: wl.Workload, inp: dict, steps: int, warmup: int, prewarm_s: float
     stream = torch.cuda.current_stream(dev)
     # argument marshalling done once, so the host keeps ahead of the GPU
     fwd = fa.prepare_fwd(q, k, v, o, lse, **kw)
-    bwd = fa.prepare_bwd(q, k, v, o, do, lse, dq, dk, dv, **kw)
+    bwd = fa.prepare_bwd(q, k, v, o, do, lse, dq, dk, dv, **kw) if w.backward else None
+    kernels = KERNELS if w.backward else KERNELS[:1]
 
     def step(ev=None):
         if ev is not None:
@@ -155,9 +157,10 @@ def run_gpu(w: wl.Workload, inp: dict, steps: int, warmup: int, prewarm_s: float
         fwd()
         if ev is not None:
             ev[1].record(stream)
-        bwd()
-        if ev is not None:
-            ev[2].record(stream)
+        if bwd is not None:
+            bwd()
+            if ev is not None:
+                ev[2].record(stream)
 
     torch.cuda.synchronize()
     t_end = time.perf_counter() + prewarm_s
@@ -167,7 +170,8 @@ def run_gpu(w: wl.Workload, inp: dict, steps: int, warmup: int, prewarm_s: float
         torch.cuda.synchronize()
     for _ in range(warmup):
         step()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(kernels) + 1)]
+           for _ in range(steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for e in evs:
@@ -175,7 +179,7 @@ def run_gpu(w: wl.Workload, inp: dict, steps: int, warmup: int, prewarm_s: float
     torch.cuda.synchronize()
     wall_ms = (time.perf_counter() - t0) * 1e3 / steps
     kernel_ms = {name: float(np.mean([e[i].elapsed_time(e[i + 1]) for e in evs]))
-                 for i, name in enumerate(KERNELS)}
+                 for i, name in enumerate(kernels)}
     props = torch.cuda.get_device_properties(dev)
     outs = dict(o=o, lse=lse, dq=dq, dk=dk, dv=dv)
     return wall_ms, kernel_ms, props, outs
@@ -209,7 +213,7 @@ def cpu_baseline(w: wl.Workload, inp: dict, outs: dict, flops_fb: float,
             G = dref.backward(q, k, v, do, w.scale, dropout_p, DROPOUT_SEED, 0, **dkw)
             return O, L, G
         O, L = ref.forward(q, k, v, w.scale, **args)
-        G = ref.backward(q, k, v, do, w.scale, **args)
+        G = ref.backward(q, k, v, do, w.scale, **args) if w.backward else ()
         return O, L, G
 
     t0 = time.perf_counter()
@@ -235,7 +239,8 @@ def cpu_baseline(w: wl.Workload, inp: dict, outs: dict, flops_fb: float,
         parity[f"{name}_relfro"] = float(np.linalg.norm(npf(outs["d" + name[1].lower()]) - g)
                                          / np.linalg.norm(g))
     base = dict(value=tflops, unit="TFLOP/s", cores=int(cores), kind="oracle",
-                sample=f"fp64 NumPy oracle fwd+bwd on {hs} of {H} heads x batch {w.B} "
+                sample=f"fp64 NumPy oracle {'fwd+bwd' if w.backward else 'fwd'} on {hs} of "
+                       f"{H} heads x batch {w.B} "
                        f"(whole sequences), {passes} pass(es) in {secs:.1f} s; value scaled "
                        f"by the FLOPs of the sample",
                 seconds=secs)
@@ -505,9 +510,12 @@ def trace_summary(stats_csv: str, bench_log: str, workload: str, command: str) -
         km = {k: round(v * 1e3, 2) for k, v in line["kernel_ms"].items()}
         out += ["", "Bench line of the same run (HIP events on the launch stream, us per launch):",
                 "", f"- kernels: {km}",
-                f"- fwd {line['fwd_tflops']:.1f} TFLOP/s, bwd {line['bwd_tflops']:.1f} TFLOP/s, "
-                f"fwd+bwd {line['value']:.1f} TFLOP/s ({100 * line['fwdbwd_frac_peak']:.1f} % of "
-                f"{line['peak_tflops']})",
+                (f"- fwd {line['fwd_tflops']:.1f} TFLOP/s, bwd {line['bwd_tflops']:.1f} "
+                 f"TFLOP/s, fwd+bwd {line['value']:.1f} TFLOP/s "
+                 f"({100 * line['fwdbwd_frac_peak']:.1f} % of {line['peak_tflops']})")
+                if line.get("bwd_tflops") is not None else
+                (f"- forward-only step: fwd {line['fwd_tflops']:.1f} TFLOP/s "
+                 f"({100 * line['fwd_frac_peak']:.1f} % of {line['peak_tflops']})"),
                 f"- roofline: {json.dumps(line['roofline'])}"]
     return "\n".join(out) + "\n"
 
@@ -581,24 +589,24 @@ def main(argv=None):
     pairs = visible_pairs(w.N, w.H, w.causal, inp["seqlens"], inp["block_mask"], 128, w.B,
                           Nk=w.n_keys)
     flops_f = 4.0 * w.d * pairs
-    flops_b = 10.0 * w.d * pairs
+    flops_b = 10.0 * w.d * pairs if w.backward else 0.0
     esize = 2 if w.dtype == "bf16" else 4
 
     wall_ms, kernel_ms, props, outs = run_gpu(w, inp, args.steps, args.warmup, args.prewarm_s,
                                                args.dropout)
     fwd_ms = kernel_ms["fwd_bf16_kernel"]
-    bwd_ms = kernel_ms["bwd_kernel"]
+    bwd_ms = kernel_ms.get("bwd_kernel")
     peak = PEAK_TFLOPS[w.dtype]
     tf_fb = (flops_f + flops_b) / (wall_ms * 1e-3) / 1e12
     tf_f = flops_f / (fwd_ms * 1e-3) / 1e12
-    tf_b = flops_b / (bwd_ms * 1e-3) / 1e12
+    tf_b = flops_b / (bwd_ms * 1e-3) / 1e12 if bwd_ms else None
 
     # Roofline of the dominant kernel (largest device time per step): its
     # algorithmic FLOPs and compulsory bytes per launch against its own
     # event-timed duration.
     kflops = kernel_flops(w.d, pairs)
     kbytes = kernel_bytes(w.B, w.H, w.N, w.d, esize, inp["seqlens"], Nk=w.n_keys)
-    dom = max(KERNELS, key=lambda n: kernel_ms[n])
+    dom = max(kernel_ms, key=lambda n: kernel_ms[n])
     ms = kernel_ms[dom]
     t_mfma = kflops[dom] / (peak * 1e12)
     t_hbm = kbytes[dom] / (PEAK_HBM_GBS * 1e9)
@@ -636,7 +644,7 @@ def main(argv=None):
         "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "N_k": w.n_keys, "d": w.d,
                    "causal": w.causal, "key_padding": inp["seqlens"] is not None,
                    "block_sparse": inp["block_mask"] is not None, "pairs": pairs,
-                   "dropout_p": args.dropout},
+                   "dropout_p": args.dropout, "step": "fwd+bwd" if w.backward else "fwd"},
         "fwd_tflops": tf_f,
         "bwd_tflops": tf_b,
         "fwd_ms": fwd_ms,

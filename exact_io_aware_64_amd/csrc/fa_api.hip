@@ -47,7 +47,8 @@ fa_status check_common(fa_dtype dtype, int B, int H, int N, int Nk, int d, float
   if (B <= 0 || H <= 0 || N <= 0)
     return fail(FA_ERR_INVALID_ARG, "B, H and N must be positive (got %d, %d, %d)", B, H, N);
   if (Nk <= 0) return fail(FA_ERR_INVALID_ARG, "N_k must be positive (got %d)", Nk);
-  if (d != 64) return fail(FA_ERR_UNSUPPORTED, "head dimension %d is not supported (only 64)", d);
+  if (d != 32 && d != 64 && d != 128)
+    return fail(FA_ERR_UNSUPPORTED, "head dimension %d is not supported (32, 64, 128)", d);
   if (!(scale > 0.f) || !isfinite(scale))
     return fail(FA_ERR_INVALID_ARG, "scale must be positive and finite");
   const long long tiles = ((long long)(N > Nk ? N : Nk) + fa::kTile - 1) / fa::kTile;
@@ -112,6 +113,10 @@ fa_status fwd_impl(fa_dtype dtype, const void* q, fa_strides q_strides, const vo
   if ((st = make_dropout(dropout_p, seed, offset, &drop)) != FA_OK) return st;
   if (block_q != 64 && block_q != 128 && block_q != 256)
     return fail(FA_ERR_INVALID_ARG, "block_q must be 64, 128 or 256 (got %d)", block_q);
+  if (d != 64 && (dtype != FA_BF16 || drop.t < 256 || block_q != 128))
+    return fail(FA_ERR_UNSUPPORTED,
+                "head dimension %d is built for the bf16 forward pass without dropout and "
+                "with block_q 128 only", d);
   if (block_q != 128 && dtype != FA_BF16)
     return fail(FA_ERR_UNSUPPORTED, "block_q other than 128 is built for bf16 only");
   if (block_mask != nullptr && mask_block % block_q != 0)
@@ -141,7 +146,7 @@ fa_status fwd_impl(fa_dtype dtype, const void* q, fa_strides q_strides, const vo
   a.n_mask_q = (N + a.mask_block - 1) / a.mask_block;
   a.n_mask_k = (Nk + a.mask_block - 1) / a.mask_block;
   a.drop = drop;
-  const hipError_t e = dtype == FA_BF16 ? fa::launch_fwd_bf16(a, causal != 0, block_q, stream)
+  const hipError_t e = dtype == FA_BF16 ? fa::launch_fwd_bf16(a, causal != 0, block_q, d, stream)
                                         : fa::launch_fwd_f32(a, causal != 0, stream);
   return hip_status(e);
 }
@@ -217,6 +222,9 @@ fa_status bwd_impl(int phases, fa_dtype dtype, const void* q, fa_strides q_strid
   int al = 0;
   fa_status st = check_common(dtype, B, H, N, Nk, d, scale, block_mask, mask_block, &al);
   if (st != FA_OK) return st;
+  if (d != 64)
+    return fail(FA_ERR_UNSUPPORTED, "the backward pass supports head dimension 64 only (got %d)",
+                d);
   if ((st = check_tensor("q", q, q_strides, al, N)) != FA_OK) return st;
   if ((st = check_tensor("k", k, k_strides, al, Nk)) != FA_OK) return st;
   if ((st = check_tensor("v", v, v_strides, al, Nk)) != FA_OK) return st;

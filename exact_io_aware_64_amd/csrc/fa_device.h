@@ -97,9 +97,9 @@ __device__ __forceinline__ uint4 ldb16(__amdgpu_buffer_rsrc_t r, int byte_off) {
   return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0));
 }
 
-// Bytes spanned by rows 0..n-1 of 64 elements with row stride `ss` (elements).
-__device__ __forceinline__ uint32_t slice_bytes(int n, int64_t ss, int esize) {
-  return (uint32_t)(((int64_t)(n - 1) * ss + 64) * esize);
+// Bytes spanned by rows 0..n-1 of `row` elements with row stride `ss` (elements).
+__device__ __forceinline__ uint32_t slice_bytes(int n, int64_t ss, int esize, int row = 64) {
+  return (uint32_t)(((int64_t)(n - 1) * ss + row) * esize);
 }
 
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 u) { return __builtin_bit_cast(bf16x8, u); }
@@ -145,12 +145,14 @@ __device__ __forceinline__ int stage_row(int w, int lane, int u) {
   return 8 * w + 32 * u + (lane >> 3);
 }
 
+// col_b: byte offset of the tile's first column within a row (a 64-column
+// block of a wider row).
 template <int W = 4>
 __device__ __forceinline__ void stage_tile(__amdgpu_buffer_rsrc_t rs, int row0, int stride_b,
-                                           uint16_t* tile, int w, int lane) {
+                                           uint16_t* tile, int w, int lane, int col_b = 0) {
   static_assert(W == 2 || W == 4 || W == 8, "a tile is copied by 2, 4 or 8 waves");
   const int row = 8 * w + (lane >> 3);
-  const int voff = row * stride_b + (((lane & 7) ^ swz(row)) << 4);
+  const int voff = row * stride_b + col_b + (((lane & 7) ^ swz(row)) << 4);
 #pragma unroll
   for (int u = 0; u < 8 / W; ++u)
     __builtin_amdgcn_raw_ptr_buffer_load_lds(

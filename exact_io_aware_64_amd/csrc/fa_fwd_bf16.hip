@@ -51,16 +51,26 @@ namespace {
 
 constexpr float kSumLimit = 4096.f;    // largest partial sum the fast path accepts
 
-// W waves, 32 W query rows per workgroup.
-template <int W, bool CAUSAL, bool SEQLEN, bool BMASK, bool DROP>
+// W waves, 32 W query rows per workgroup; head dimension D = 32, 64 or 128.
+// A K or V tile of 64 rows is held as KB = max(1, D / 64) swizzled 64 x 64
+// blocks (columns 64 j .. 64 j + 63 in block j; with D = 32 only the first
+// four chunks of each row are used), so every LDS read keeps the
+// conflict-free pattern of the 64-column tile.
+template <int W, int D, bool CAUSAL, bool SEQLEN, bool BMASK, bool DROP>
 __global__ __launch_bounds__(64 * W) void fwd_bf16_kernel(FwdArgs a) {
+  static_assert(D == 32 || D == 64 || D == 128, "head dimension 32, 64 or 128");
+  static_assert(!DROP || D == 64, "dropout is built for D = 64");
   constexpr int kBR = 32 * W;
+  constexpr int KB = D > 64 ? D / 64 : 1;  // 64-column blocks per tile
+  constexpr int KS = D / 16;               // contraction steps of S^T; slots per phase
+  constexpr int DB = D / 32;               // 32-row blocks of O^T
+  constexpr int LEAD = KS < 4 ? KS : 4;    // slots between an operand's read and its use
   // Two buffers, each a K tile and a V tile; separate arrays so that the
   // copies into one buffer and the reads of the other never alias.
-  __shared__ __attribute__((aligned(16))) uint16_t s_k0[kTileElems];
-  __shared__ __attribute__((aligned(16))) uint16_t s_v0[kTileElems];
-  __shared__ __attribute__((aligned(16))) uint16_t s_k1[kTileElems];
-  __shared__ __attribute__((aligned(16))) uint16_t s_v1[kTileElems];
+  __shared__ __attribute__((aligned(16))) uint16_t s_k0[KB * kTileElems];
+  __shared__ __attribute__((aligned(16))) uint16_t s_v0[KB * kTileElems];
+  __shared__ __attribute__((aligned(16))) uint16_t s_k1[KB * kTileElems];
+  __shared__ __attribute__((aligned(16))) uint16_t s_v1[KB * kTileElems];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int r = lane & 31, hl = lane >> 5;
@@ -94,24 +104,26 @@ __global__ __launch_bounds__(64 * W) void fwd_bf16_kernel(FwdArgs a) {
                                     a.n_mask_k, a.mask_block / kTile, 0, ntk);
   }
 
-  const __amdgpu_buffer_rsrc_t rq =
-      make_rsrc((const uint16_t*)a.q + b * a.sq.b + hh * a.sq.h, slice_bytes(a.N, a.sq.s, 2));
-  const __amdgpu_buffer_rsrc_t rk =
-      make_rsrc((const uint16_t*)a.k + b * a.sk.b + hh * a.sk.h, slice_bytes(a.Nk, a.sk.s, 2));
-  const __amdgpu_buffer_rsrc_t rv =
-      make_rsrc((const uint16_t*)a.v + b * a.sv.b + hh * a.sv.h, slice_bytes(a.Nk, a.sv.s, 2));
+  const __amdgpu_buffer_rsrc_t rq = make_rsrc(
+      (const uint16_t*)a.q + b * a.sq.b + hh * a.sq.h, slice_bytes(a.N, a.sq.s, 2, D));
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(
+      (const uint16_t*)a.k + b * a.sk.b + hh * a.sk.h, slice_bytes(a.Nk, a.sk.s, 2, D));
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(
+      (const uint16_t*)a.v + b * a.sv.b + hh * a.sv.h, slice_bytes(a.Nk, a.sv.s, 2, D));
   const int ssk = (int)a.sk.s * 2, ssv = (int)a.sv.s * 2;
 
   // Q fragment: B operand of S^T = K Q^T, lane (r, hl) holds
   // Q[qi][16 ks + 8 hl .. +7].  Rows past N read as zeros.
-  bf16x8 qf[4];
+  bf16x8 qf[KS];
   {
     const int off = qi * (int)a.sq.s * 2 + 16 * hl;
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) qf[ks] = as_bf16x8(ldb16(rq, off + 32 * ks));
+    for (int ks = 0; ks < KS; ++ks) qf[ks] = as_bf16x8(ldb16(rq, off + 32 * ks));
   }
 
-  f32x16 o[2] = {zero16(), zero16()};
+  f32x16 o[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) o[db] = zero16();
   float m = -kInf, l = 0.f;
   const float c = a.scale_log2;
 
@@ -131,8 +143,11 @@ __global__ __launch_bounds__(64 * W) void fwd_bf16_kernel(FwdArgs a) {
     return it;
   };
   auto stage = [&](int t, uint16_t* kt, uint16_t* vt) FA_INLINE {
-    stage_tile<W>(rk, t * kTile, ssk, kt, w, lane);
-    stage_tile<W>(rv, t * kTile, ssv, vt, w, lane);
+#pragma unroll
+    for (int j = 0; j < KB; ++j) {
+      stage_tile<W>(rk, t * kTile, ssk, kt + j * kTileElems, w, lane, 128 * j);
+      stage_tile<W>(rv, t * kTile, ssv, vt + j * kTileElems, w, lane, 128 * j);
+    }
   };
 
   // Raises m to cover the scores of half kb, rescales acc and l, and
@@ -146,22 +161,25 @@ __global__ __launch_bounds__(64 * W) void fwd_bf16_kernel(FwdArgs a) {
     const float alpha = (m_new == m) ? 1.f : fast_exp2(m - m_new);
     l *= alpha;
 #pragma unroll
-    for (int db = 0; db < 2; ++db)
+    for (int db = 0; db < DB; ++db)
 #pragma unroll
       for (int e = 0; e < 16; ++e) o[db][e] *= alpha;
     m = m_new;
   };
 
-  // One 64-key tile as 16 MFMA issue slots separated by scheduling fences:
-  //   slots  0.. 3  S^T of keys  0..31                 (MFMA) | [keep bytes]
-  //   slots  4.. 7  S^T of keys 32..63                 (MFMA) | P of keys 0..31
-  //   slots  8..11  O^T += V^T P^T, keys 0..31         (MFMA) | P of keys 32..63
-  //   slots 12..15  O^T += V^T P^T, keys 32..63        (MFMA)
-  // with the LDS reads of each operand issued a few slots ahead.
+  // One 64-key tile as 4 KS MFMA issue slots (16 for D = 64) in four phases
+  // of KS slots, separated by scheduling fences:
+  //   phase 0  S^T of keys  0..31, KS steps             (MFMA) | [keep bytes]
+  //   phase 1  S^T of keys 32..63                       (MFMA) | P of keys 0..31
+  //   phase 2  O^T += V^T P^T, keys 0..31: 2 x DB steps (MFMA) | P of keys 32..63
+  //   phase 3  O^T += V^T P^T, keys 32..63              (MFMA)
+  // Each slot issues the LDS read of the operand LEAD slots ahead (for
+  // D <= 64 the same position of the next phase); the first LEAD operands are
+  // read before the first slot.
   auto body = [&](auto mask_c, const uint16_t* kt, const uint16_t* vt, int k0) FA_INLINE {
     constexpr bool MASK = decltype(mask_c)::value;
     f32x16 s[2] = {zero16(), zero16()};
-    bf16x8 ka[2][4], va[4][2];
+    bf16x8 opa[4 * KS];  // A operand of each slot
     uint32_t pk[4][4];   // bf16 pairs of P for PV steps 0..3
     float ps[2] = {0.f, 0.f};
     [[maybe_unused]] DropBlock zb[2];  // keep bytes of the two halves
@@ -210,52 +228,55 @@ __global__ __launch_bounds__(64 * W) void fwd_bf16_kernel(FwdArgs a) {
       }
     };
 
+    // A operand of slot t: K rows (phases 0, 1) or V^T transpose reads
+    // (phases 2, 3: key step st, output block db).
+    auto load_a = [&](int t) FA_INLINE {
+      const int ph = t / KS, i = t % KS;
+      if (ph < 2) {
+        opa[t] = tile_row8(kt + (i >> 2) * kTileElems, 2048 * ph + roff[i & 3]);
+      } else {
+        const int st = 2 * (ph - 2) + i / DB, db = i % DB;
+        opa[t] = tr_read(vt + (db >> 1) * kTileElems + 1024 * st, troff[0][db & 1],
+                         troff[1][db & 1]);
+      }
+    };
+
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) ka[0][ks] = tile_row8(kt, roff[ks]);
+    for (int t = 0; t < LEAD; ++t) load_a(t);
     FA_FENCE();
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {  // slots 0..3
-      s[0] = mfma32(ka[0][ks], qf[ks], s[0]);
-      ka[1][ks] = tile_row8(kt, 2048 + roff[ks]);
-      if constexpr (DROP) {  // half ks / 2: rounds 0..4 in even slots, 5..9 in odd
-        DropBlock& z = zb[ks >> 1];
-        if ((ks & 1) == 0)
-          drop_start(z, (uint32_t)((k0 >> 2) + 8 * (ks >> 1) + 2 * (lane & 3) + hl),
-                     (uint32_t)(qi >> 2), (uint32_t)bh, a.drop.offset);
-        philox_rounds(z.v, a.drop.seed_lo, a.drop.seed_hi, 5 * (ks & 1), 5 * (ks & 1) + 5);
-        if (ks & 1) drop_finish<false>(z, lane);
+    for (int t = 0; t < 4 * KS; ++t) {
+      const int ph = t / KS, i = t % KS;
+      if (ph < 2) {
+        s[ph] = mfma32(opa[t], qf[i], s[ph]);
+      } else {
+        const int st = 2 * (ph - 2) + i / DB, db = i % DB;
+        o[db] = mfma32(opa[t], words_to_bf16x8(pk[st][0], pk[st][1], pk[st][2], pk[st][3]),
+                       o[db]);
+      }
+      if (t + LEAD < 4 * KS) load_a(t + LEAD);
+      if constexpr (DROP) {  // half i / 2: rounds 0..4 in even slots, 5..9 in odd
+        if (ph == 0) {
+          DropBlock& z = zb[i >> 1];
+          if ((i & 1) == 0)
+            drop_start(z, (uint32_t)((k0 >> 2) + 8 * (i >> 1) + 2 * (lane & 3) + hl),
+                       (uint32_t)(qi >> 2), (uint32_t)bh, a.drop.offset);
+          philox_rounds(z.v, a.drop.seed_lo, a.drop.seed_hi, 5 * (i & 1), 5 * (i & 1) + 5);
+          if (i & 1) drop_finish<false>(z, lane);
+        }
+      }
+      if (ph == 1 || ph == 2) {  // P of half ph - 1, four elements per call
+#pragma unroll
+        for (int cc = 0; cc < 4; ++cc)
+          if ((cc * KS) / 4 == i) probs(ph - 1, 4 * cc);
       }
       FA_FENCE();
-    }
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {  // slots 4..7
-      s[1] = mfma32(ka[1][ks], qf[ks], s[1]);
-      const int st = ks >> 1, db = ks & 1;
-      va[st][db] = tr_read(vt + 1024 * st, troff[0][db], troff[1][db]);
-      probs(0, 4 * ks);
-      FA_FENCE();
-    }
-    if (__any(!(ps[0] <= kSumLimit))) fix_half(0);
-    l += ps[0];
-    FA_FENCE();
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {  // slots 8..11
-      const int st = i >> 1, db = i & 1;
-      o[db] = mfma32(va[st][db], words_to_bf16x8(pk[st][0], pk[st][1], pk[st][2], pk[st][3]),
-                     o[db]);
-      va[2 + st][db] = tr_read(vt + 1024 * (2 + st), troff[0][db], troff[1][db]);
-      probs(1, 4 * i);
-      FA_FENCE();
-    }
-    if (__any(!(ps[1] <= kSumLimit))) fix_half(1);
-    l += ps[1];
-    FA_FENCE();
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {  // slots 12..15
-      const int st = 2 + (i >> 1), db = i & 1;
-      o[db] = mfma32(va[st][db], words_to_bf16x8(pk[st][0], pk[st][1], pk[st][2], pk[st][3]),
-                     o[db]);
-      FA_FENCE();
+      if (t == 2 * KS - 1 || t == 3 * KS - 1) {
+        const int kb = (t == 2 * KS - 1) ? 0 : 1;
+        if (__any(!(ps[kb] <= kSumLimit))) fix_half(kb);
+        l += ps[kb];
+        FA_FENCE();
+      }
     }
   };
 
@@ -296,7 +317,7 @@ __global__ __launch_bounds__(64 * W) void fwd_bf16_kernel(FwdArgs a) {
     if constexpr (DROP) inv *= a.drop.scale;
     uint16_t* op = (uint16_t*)a.o + b * a.so.b + hh * a.so.h + (int64_t)qi * a.so.s;
 #pragma unroll
-    for (int db = 0; db < 2; ++db)
+    for (int db = 0; db < DB; ++db)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         bf16x4 v4;
@@ -310,36 +331,44 @@ __global__ __launch_bounds__(64 * W) void fwd_bf16_kernel(FwdArgs a) {
   }
 }
 
-template <int W, bool C, bool S, bool M, bool D>
+template <int W, int HD, bool C, bool S, bool M, bool D>
 hipError_t launch(const FwdArgs& a, hipStream_t stream) {
   const int nqt = (a.N + 32 * W - 1) / (32 * W);
   dim3 grid((unsigned)(nqt * a.B * a.H)), block(64 * W);
   FwdArgs copy = a;
   void* args[] = {&copy};
-  return hipLaunchKernel((const void*)&fwd_bf16_kernel<W, C, S, M, D>, grid, block, args, 0,
-                         stream);
+  return hipLaunchKernel((const void*)&fwd_bf16_kernel<W, HD, C, S, M, D>, grid, block, args,
+                         0, stream);
 }
 
-template <int W, bool D>
+template <int W, int HD, bool D>
 hipError_t dispatch(const FwdArgs& a, bool causal, hipStream_t stream) {
   const bool s = a.seqlens != nullptr, m = a.bmask != nullptr;
   if (causal) {
     if (s)
-      return m ? launch<W, true, true, true, D>(a, stream) : launch<W, true, true, false, D>(a, stream);
-    return m ? launch<W, true, false, true, D>(a, stream) : launch<W, true, false, false, D>(a, stream);
+      return m ? launch<W, HD, true, true, true, D>(a, stream)
+               : launch<W, HD, true, true, false, D>(a, stream);
+    return m ? launch<W, HD, true, false, true, D>(a, stream)
+             : launch<W, HD, true, false, false, D>(a, stream);
   }
   if (s)
-    return m ? launch<W, false, true, true, D>(a, stream) : launch<W, false, true, false, D>(a, stream);
-  return m ? launch<W, false, false, true, D>(a, stream) : launch<W, false, false, false, D>(a, stream);
+    return m ? launch<W, HD, false, true, true, D>(a, stream)
+             : launch<W, HD, false, true, false, D>(a, stream);
+  return m ? launch<W, HD, false, false, true, D>(a, stream)
+           : launch<W, HD, false, false, false, D>(a, stream);
 }
 
 }  // namespace
 
-hipError_t launch_fwd_bf16(const FwdArgs& a, bool causal, int block_q, hipStream_t stream) {
-  if (a.drop.t < 256) return dispatch<4, true>(a, causal, stream);  // host: block_q == 128
-  if (block_q == 64) return dispatch<2, false>(a, causal, stream);
-  if (block_q == 256) return dispatch<8, false>(a, causal, stream);
-  return dispatch<4, false>(a, causal, stream);
+hipError_t launch_fwd_bf16(const FwdArgs& a, bool causal, int block_q, int d,
+                           hipStream_t stream) {
+  // the host allows d != 64 only without dropout and with block_q = 128
+  if (d == 32) return dispatch<4, 32, false>(a, causal, stream);
+  if (d == 128) return dispatch<4, 128, false>(a, causal, stream);
+  if (a.drop.t < 256) return dispatch<4, 64, true>(a, causal, stream);  // block_q == 128
+  if (block_q == 64) return dispatch<2, 64, false>(a, causal, stream);
+  if (block_q == 256) return dispatch<8, 64, false>(a, causal, stream);
+  return dispatch<4, 64, false>(a, causal, stream);
 }
 
 }  // namespace fa

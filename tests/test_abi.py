@@ -78,7 +78,9 @@ def _bwd(**kw):
     (dict(v=A + 8), 1, "v is not 16-byte aligned"),
     (dict(B=0), 1, "must be positive"),
     (dict(N=-5), 1, "must be positive"),
-    (dict(d=128), 2, "head dimension"),
+    (dict(d=96), 2, "head dimension"),
+    (dict(d=128, dtype=1), 2, "head dimension"),
+    (dict(d=32, dtype=1), 2, "head dimension"),
     (dict(scale=0.0), 1, "scale"),
     (dict(scale=float("nan")), 1, "scale"),
     (dict(dtype=7), 1, "dtype"),

@@ -1,0 +1,110 @@
+"""GPU parity of the bf16 forward pass with head dimensions 32 and 128 (the
+kernel family is templated on d; d = 64 has its own tests) against the fp64
+oracle: edge lengths, causal, key lengths, tile masks, both layouts and
+separate query / key lengths.  The backward pass is built for d = 64 and
+rejects other head dimensions."""
+import sys
+
+import numpy as np
+import pytest
+
+import workloads as wl
+from oracle import attention_ref as ref
+from tests.gpu_util import (TOL, device_inputs, gpu_forward, maxabs, oracle_args, opt_dev,
+                            to_dev, to_np)
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def _check(case, tag, layout="bhsd"):
+    _say(f"[headdim] {tag}")
+    q, k, v, _, sl, bm = device_inputs(case, layout)
+    o, lse = gpu_forward(case, q, k, v, sl, bm)
+    O, L = ref.forward(case["q"], case["k"], case["v"], **oracle_args(case))
+    eo, el = maxabs(to_np(o), O), maxabs(to_np(lse), L)
+    assert np.array_equal(np.isinf(to_np(lse)), np.isinf(L)), "dead rows differ"
+    assert eo <= TOL["bf16"]["O"] and el <= TOL["bf16"]["L"], (eo, el)
+    _say(f"[headdim] {tag} ok O={eo:.2e} L={el:.2e}")
+
+
+@pytest.mark.parametrize("d", [32, 128])
+@pytest.mark.parametrize("N", [1, 17, 63, 64, 65, 300, 1000])
+@pytest.mark.parametrize("causal", [False, True])
+def test_headdim_dense(d, N, causal):
+    case = wl.random_case(2, 3, N, d, seed=N + d + causal, causal=causal)
+    _check(case, f"d={d} N={N} causal={causal}")
+
+
+@pytest.mark.parametrize("d", [32, 128])
+@pytest.mark.parametrize("masks", ["seqlens", "block", "both"])
+def test_headdim_masks(d, masks):
+    seqlens = "random" if masks in ("seqlens", "both") else None
+    keep = 0.5 if masks in ("block", "both") else None
+    case = wl.random_case(3, 2, 700, d, seed=d, causal=True, seqlens=seqlens,
+                          block_keep_p=keep)
+    _check(case, f"d={d} masks={masks}")
+
+
+@pytest.mark.parametrize("d", [32, 128])
+def test_headdim_strided_layout(d):
+    case = wl.random_case(2, 4, 257, d, seed=3 * d, causal=True)
+    _check(case, f"d={d} bshd", layout="bshd")
+
+
+@pytest.mark.parametrize("d", [32, 128])
+@pytest.mark.parametrize("Nq,Nk", [(1, 900), (200, 900), (900, 200)])
+def test_headdim_separate_lengths(d, Nq, Nk):
+    import exact_io_aware_64_amd as fa
+    rng = np.random.default_rng(Nq + Nk + d)
+    (q,) = wl.draw_tensors(rng, 2, 2, Nq, d, "bf16", count=1)
+    k, v = wl.draw_tensors(rng, 2, 2, Nk, d, "bf16", count=2)
+    _say(f"[headdim] d={d} Nq={Nq} Nk={Nk}")
+    o, lse = fa.forward(to_dev(q, "bf16"), to_dev(k, "bf16"), to_dev(v, "bf16"),
+                        scale=d ** -0.5, causal=True)
+    O, L = ref.forward(q, k, v, d ** -0.5, causal=True)
+    eo, el = maxabs(to_np(o), O), maxabs(to_np(lse), L)
+    assert eo <= TOL["bf16"]["O"] and el <= TOL["bf16"]["L"], (eo, el)
+
+
+@pytest.mark.parametrize("d", [32, 128])
+def test_headdim_full_size(d):
+    """B=4, H=16, N=2048 causal (a 7B-model-like attention shape for d=128)."""
+    case = wl.random_case(4, 16, 2048, d, seed=99 + d, causal=True)
+    rows = wl.sample_rows(np.random.default_rng(d), 4, 16, 2048, 256)
+    _say(f"[headdim] full size d={d}")
+    q, k, v, _, sl, bm = device_inputs(case)
+    o, lse = gpu_forward(case, q, k, v, sl, bm)
+    O, L = ref.forward(case["q"], case["k"], case["v"], rows=rows, **oracle_args(case))
+    idx = (np.arange(4)[:, None, None], np.arange(16)[None, :, None], rows)
+    eo, el = maxabs(to_np(o)[idx], O), maxabs(to_np(lse)[idx], L)
+    assert eo <= TOL["bf16"]["O"] and el <= TOL["bf16"]["L"], (eo, el)
+
+
+def test_backward_rejects_other_head_dims():
+    import exact_io_aware_64_amd as fa
+    case = wl.random_case(1, 1, 64, 128, seed=1)
+    q, k, v, do, _, _ = device_inputs(case)
+    o, lse = fa.forward(q, k, v, scale=0.1)
+    with pytest.raises(fa.FaError, match="head dimension 64 only"):
+        fa.backward(q, k, v, o, do, lse, scale=0.1)
+
+
+def test_d128_workload_sampled():
+    """The benchmarked d = 128 workload at full size, sampled rows."""
+    w = wl.WORKLOADS["causal_b2h32n4096d128"]
+    case = wl.make_inputs(w)
+    case["mask_block"] = 128
+    rows = case["rows"]
+    _say(f"[headdim] {w.name} sampled")
+    q, k, v, _, sl, bm = device_inputs(case)
+    o, lse = gpu_forward(case, q, k, v, sl, bm)
+    O, L = ref.forward(case["q"], case["k"], case["v"], rows=rows, **oracle_args(case))
+    idx = (np.arange(w.B)[:, None, None], np.arange(w.H)[None, :, None], rows)
+    eo, el = maxabs(to_np(o)[idx], O), maxabs(to_np(lse)[idx], L)
+    assert eo <= TOL["bf16"]["O"] and el <= TOL["bf16"]["L"], (eo, el)
+    _say(f"[headdim] {w.name} ok O={eo:.2e} L={el:.2e}")
