@@ -222,9 +222,8 @@ fa_status bwd_impl(int phases, fa_dtype dtype, const void* q, fa_strides q_strid
   int al = 0;
   fa_status st = check_common(dtype, B, H, N, Nk, d, scale, block_mask, mask_block, &al);
   if (st != FA_OK) return st;
-  if (d != 64)
-    return fail(FA_ERR_UNSUPPORTED, "the backward pass supports head dimension 64 only (got %d)",
-                d);
+  if (d != 64 && dtype != FA_BF16)
+    return fail(FA_ERR_UNSUPPORTED, "head dimension %d is built for bf16 only", d);
   if ((st = check_tensor("q", q, q_strides, al, N)) != FA_OK) return st;
   if ((st = check_tensor("k", k, k_strides, al, Nk)) != FA_OK) return st;
   if ((st = check_tensor("v", v, v_strides, al, Nk)) != FA_OK) return st;
@@ -252,6 +251,8 @@ fa_status bwd_impl(int phases, fa_dtype dtype, const void* q, fa_strides q_strid
     return fail(FA_ERR_INVALID_ARG, "seqlens_k is not 4-byte aligned");
   fa::Dropout drop{};
   if ((st = make_dropout(dropout_p, seed, offset, &drop)) != FA_OK) return st;
+  if (d != 64 && drop.t < 256)
+    return fail(FA_ERR_UNSUPPORTED, "head dimension %d is built without dropout only", d);
 
   fa::BwdArgs a{};
   a.q = q;
@@ -284,7 +285,7 @@ fa_status bwd_impl(int phases, fa_dtype dtype, const void* q, fa_strides q_strid
   a.n_mask_q = (N + a.mask_block - 1) / a.mask_block;
   a.n_mask_k = (Nk + a.mask_block - 1) / a.mask_block;
   a.drop = drop;
-  const hipError_t e = dtype == FA_BF16 ? fa::launch_bwd_bf16(a, causal != 0, phases, stream)
+  const hipError_t e = dtype == FA_BF16 ? fa::launch_bwd_bf16(a, causal != 0, phases, d, stream)
                                         : fa::launch_bwd_f32(a, causal != 0, phases, stream);
   return hip_status(e);
 }

@@ -41,14 +41,34 @@ namespace {
 constexpr int kBQ = 128;   // dQ role: query rows per workgroup
 constexpr int kBK = 128;   // dK/dV role: key rows per workgroup
 
+// dK/dV work items per key tile: with D = 128 each item accumulates 32 of
+// the output columns (recomputing S and dP), which keeps the role within the
+// register file; otherwise one item per tile.
+constexpr int dkdv_splits(int d) { return d > 64 ? d / 32 : 1; }
+
+// Issues, at slot t, the chunks c (0..7) of a half tile that are spread over
+// the nw slots starting at t0, chunk c in slot t0 + c nw / 8: the chunks with
+// c nw / 8 == t - t0 (8 / nw of them when nw < 8, else at most one).
+template <int T0, int NW, class F>
+__device__ __forceinline__ void spread_chunks(int t, F&& f) {
+  const int u = t - T0;
+  if (u < 0 || u >= NW) return;
+  const int c_lo = (8 * u + NW - 1) / NW, c_hi = (8 * (u + 1) + NW - 1) / NW;
+#pragma unroll
+  for (int cc = 0; cc < (8 + NW - 1) / NW; ++cc)
+    if (c_lo + cc < c_hi && c_lo + cc < 8) f(c_lo + cc);
+}
+
 // ------------------------------------------------------------------ dQ (+D)
 
 // dQ for the 128 queries of work item `item` (query tile, batch, head).
 // s_k0/s_v0 and s_k1/s_v1 are the two K/V tile buffers.
-template <bool CAUSAL, bool SEQLEN, bool BMASK, bool DROP>
+template <int D, bool CAUSAL, bool SEQLEN, bool BMASK, bool DROP>
 __device__ __forceinline__ void dq_role(const BwdArgs& a, int item, uint16_t* s_k0,
                                         uint16_t* s_v0, uint16_t* s_k1, uint16_t* s_v1,
                                         uint16_t* s_list, int* s_scan) {
+  constexpr int KS = D / 16;  // contraction steps over d
+  constexpr int DB = D / 32;  // 32-row blocks of dQ^T
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = tid >> 6;
   const int r = lane & 31, hl = lane >> 5;
@@ -76,28 +96,28 @@ __device__ __forceinline__ void dq_role(const BwdArgs& a, int item, uint16_t* s_
                             a.n_mask_k, a.mask_block / kTile, 0, ntk);
   }
 
-  const __amdgpu_buffer_rsrc_t rq =
-      make_rsrc((const uint16_t*)a.q + b * a.sq.b + hh * a.sq.h, slice_bytes(a.N, a.sq.s, 2));
-  const __amdgpu_buffer_rsrc_t rk =
-      make_rsrc((const uint16_t*)a.k + b * a.sk.b + hh * a.sk.h, slice_bytes(a.Nk, a.sk.s, 2));
-  const __amdgpu_buffer_rsrc_t rv =
-      make_rsrc((const uint16_t*)a.v + b * a.sv.b + hh * a.sv.h, slice_bytes(a.Nk, a.sv.s, 2));
-  const __amdgpu_buffer_rsrc_t ro =
-      make_rsrc((const uint16_t*)a.o + b * a.so.b + hh * a.so.h, slice_bytes(a.N, a.so.s, 2));
+  const __amdgpu_buffer_rsrc_t rq = make_rsrc(
+      (const uint16_t*)a.q + b * a.sq.b + hh * a.sq.h, slice_bytes(a.N, a.sq.s, 2, D));
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(
+      (const uint16_t*)a.k + b * a.sk.b + hh * a.sk.h, slice_bytes(a.Nk, a.sk.s, 2, D));
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(
+      (const uint16_t*)a.v + b * a.sv.b + hh * a.sv.h, slice_bytes(a.Nk, a.sv.s, 2, D));
+  const __amdgpu_buffer_rsrc_t ro = make_rsrc(
+      (const uint16_t*)a.o + b * a.so.b + hh * a.so.h, slice_bytes(a.N, a.so.s, 2, D));
   const __amdgpu_buffer_rsrc_t rdo = make_rsrc(
-      (const uint16_t*)a.dout + b * a.sdo.b + hh * a.sdo.h, slice_bytes(a.N, a.sdo.s, 2));
+      (const uint16_t*)a.dout + b * a.sdo.b + hh * a.sdo.h, slice_bytes(a.N, a.sdo.s, 2, D));
   const int ssk = (int)a.sk.s * 2, ssv = (int)a.sv.s * 2;
 
   // Q and dO fragments (B operands, lane (r, hl) holds row qi, columns
   // 16 ks + 8 hl .. +7) and D_i = dot(dO_i, O_i) over the two wave halves.
-  bf16x8 qf[4], dof[4];
+  bf16x8 qf[KS], dof[KS];
   float Dq = 0.f;
   {
     const int oq = qi * (int)a.sq.s * 2 + 16 * hl;
     const int odo = qi * (int)a.sdo.s * 2 + 16 * hl;
     const int oo = qi * (int)a.so.s * 2 + 16 * hl;
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
+    for (int ks = 0; ks < KS; ++ks) {
       qf[ks] = as_bf16x8(ldb16(rq, oq + 32 * ks));
       dof[ks] = as_bf16x8(ldb16(rdo, odo + 32 * ks));
       const bf16x8 of = as_bf16x8(ldb16(ro, oo + 32 * ks));
@@ -113,7 +133,9 @@ __device__ __forceinline__ void dq_role(const BwdArgs& a, int item, uint16_t* s_
   }
   const float c = a.scale_log2;
 
-  f32x16 acc[2] = {zero16(), zero16()};
+  f32x16 acc[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) acc[db] = zero16();
 
   // Per-lane LDS offsets: K and V rows (A operands of S^T and dP^T) and K^T
   // transpose reads (A operand of dQ^T).
@@ -125,39 +147,49 @@ __device__ __forceinline__ void dq_role(const BwdArgs& a, int item, uint16_t* s_
   for (int hi = 0; hi < 2; ++hi)
 #pragma unroll
     for (int db = 0; db < 2; ++db) troff[hi][db] = tr_off(lane, hi, db);
+  static_assert(!DROP || D == 64, "dropout is built for D = 64");
 
   auto tile_at = [&](int it) FA_INLINE -> int {
     if constexpr (BMASK) return tlist[it];
     return it;
   };
   auto stage = [&](int t, uint16_t* kt, uint16_t* vt) FA_INLINE {
-    stage_tile(rk, t * kTile, ssk, kt, w, lane);
-    stage_tile(rv, t * kTile, ssv, vt, w, lane);
+#pragma unroll
+    for (int j = 0; j < (D > 64 ? D / 64 : 1); ++j) {
+      stage_tile(rk, t * kTile, ssk, kt + j * kTileElems, w, lane, 128 * j);
+      stage_tile(rv, t * kTile, ssv, vt + j * kTileElems, w, lane, 128 * j);
+    }
   };
 
-  // One 64-key tile as 24 MFMA issue slots separated by scheduling fences:
+  // One 64-key tile as 6 KS MFMA issue slots separated by scheduling fences
+  // (for D = 64:
   //   slots  0.. 7  S^T, dP^T of keys  0..31                 (MFMA)
   //   slots  8..15  S^T, dP^T of keys 32..63                 (MFMA) | P, dS of keys 0..31
-  //   slots 16..23  dQ^T += K^T dS^T (steps 0..3)            (MFMA) | P, dS of keys 32..63
+  //   slots 16..23  dQ^T += K^T dS^T (steps 0..3)            (MFMA) | P, dS of keys 32..63)
   // with each LDS operand read four slots ahead.  dS of keys 32..47 is done
   // by slot 19 and of 48..63 by slot 21, ahead of the steps that use them.
+  // Other D: 4 KS slots of S^T and dP^T, then 4 DB of dQ^T, the dS chunks of
+  // each half spread evenly over the slots that follow the half.
   auto body = [&](auto mask_c, const uint16_t* kt, const uint16_t* vt, int k0) FA_INLINE {
     constexpr bool MASK = decltype(mask_c)::value;
     constexpr int kLead = 4;
+    constexpr int NS = 6 * KS;
     f32x16 st[2] = {zero16(), zero16()}, dpt[2] = {zero16(), zero16()};
     uint32_t pkd[4][4];  // bf16 pairs of dS per step
-    bf16x8 opa[24];
+    bf16x8 opa[NS];
     [[maybe_unused]] DropBlock zb[2];  // keep bytes of the two halves
     [[maybe_unused]] int lim = 0;
     if constexpr (MASK) lim = (CAUSAL ? min(kv_len - 1, qi + a.coff) : kv_len - 1) - k0 - 4 * hl;
     // A operand of slot t
     auto load_a = [&](int t) FA_INLINE {
-      if (t < 16) {
-        const int kb = t >> 3, ks = (t & 7) >> 1;
-        opa[t] = tile_row8((t & 1) ? vt : kt, 2048 * kb + roff[ks]);
+      if (t < 4 * KS) {
+        const int kb = t / (2 * KS), ks = (t % (2 * KS)) >> 1;
+        opa[t] = tile_row8(((t & 1) ? vt : kt) + (ks >> 2) * kTileElems,
+                           2048 * kb + roff[ks & 3]);
       } else {
-        const int stp = (t - 16) >> 1, db = t & 1;
-        opa[t] = tr_read(kt + 1024 * stp, troff[0][db], troff[1][db]);
+        const int stp = (t - 4 * KS) / DB, db = (t - 4 * KS) % DB;
+        opa[t] = tr_read(kt + (db >> 1) * kTileElems + 1024 * stp, troff[0][db & 1],
+                         troff[1][db & 1]);
       }
     };
     // elements 2 ch, 2 ch + 1 of half kb: P = 2^(S c - L log2 e), dS = P (dP - D)
@@ -185,25 +217,32 @@ __device__ __forceinline__ void dq_role(const BwdArgs& a, int item, uint16_t* s_
     for (int t = 0; t < kLead; ++t) load_a(t);
     FA_FENCE();
 #pragma unroll
-    for (int t = 0; t < 24; ++t) {
-      if (t + kLead < 24) load_a(t + kLead);
-      if (t < 16) {
-        const int kb = t >> 3, ks = (t & 7) >> 1;
+    for (int t = 0; t < NS; ++t) {
+      if (t + kLead < NS) load_a(t + kLead);
+      if (t < 4 * KS) {
+        const int kb = t / (2 * KS), ks = (t % (2 * KS)) >> 1;
         if (t & 1)
           dpt[kb] = mfma32(opa[t], dof[ks], dpt[kb]);
         else
           st[kb] = mfma32(opa[t], qf[ks], st[kb]);
       } else {
-        const int stp = (t - 16) >> 1, db = t & 1;
+        const int stp = (t - 4 * KS) / DB, db = (t - 4 * KS) % DB;
         acc[db] = mfma32(opa[t], words_to_bf16x8(pkd[stp][0], pkd[stp][1], pkd[stp][2],
                                                  pkd[stp][3]), acc[db]);
       }
-      if (t >= 8 && t < 16) probs(0, t - 8);
-      if (t >= 16 && t < 20) {  // chunks 0..5 of half 1 over four slots
-        probs(1, (3 * (t - 16)) >> 1);
-        if ((t - 16) & 1) probs(1, ((3 * (t - 16)) >> 1) + 1);
+      if constexpr (D == 64) {
+        if (t >= 8 && t < 16) probs(0, t - 8);
+        if (t >= 16 && t < 20) {  // chunks 0..5 of half 1 over four slots
+          probs(1, (3 * (t - 16)) >> 1);
+          if ((t - 16) & 1) probs(1, ((3 * (t - 16)) >> 1) + 1);
+        }
+        if (t == 20 || t == 21) probs(1, t - 14);
+      } else {
+        // half 0 over the 2 KS slots of half 1's S^T, dP^T; half 1 over the
+        // first 2 DB dQ^T slots (its first steps are needed at 4 KS + 2 DB)
+        spread_chunks<2 * KS, 2 * KS>(t, [&](int cc) FA_INLINE { probs(0, cc); });
+        spread_chunks<4 * KS, 2 * DB>(t, [&](int cc) FA_INLINE { probs(1, cc); });
       }
-      if (t == 20 || t == 21) probs(1, t - 14);
       if constexpr (DROP) {  // half t / 4, in the MFMA-only slots 0..7
         if (t < 8) {
           DropBlock& z = zb[t >> 2];
@@ -253,7 +292,7 @@ __device__ __forceinline__ void dq_role(const BwdArgs& a, int item, uint16_t* s_
   if (qi < a.N) {
     uint16_t* out = (uint16_t*)a.dq + b * a.sdq.b + hh * a.sdq.h + (int64_t)qi * a.sdq.s;
 #pragma unroll
-    for (int db = 0; db < 2; ++db)
+    for (int db = 0; db < DB; ++db)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         bf16x4 v4;
@@ -266,10 +305,13 @@ __device__ __forceinline__ void dq_role(const BwdArgs& a, int item, uint16_t* s_
 
 // ---------------------------------------------------------------- dK, dV
 
-// dK, dV for the 128 keys of work item `item` (key tile, batch, head).
-// s_q0/s_do0/s_o0 and s_q1/s_do1/s_o1 are the two Q/dO/O tile buffers;
-// s_nl and s_nd hold -L / scale and -D of each buffer's 64 rows.
-template <bool CAUSAL, bool SEQLEN, bool BMASK, bool DROP>
+// dK, dV for the 128 keys of work item `item` (key tile, batch, head; with
+// D = 128 also which 32 of the D output columns: the item recomputes S and dP
+// in full and accumulates a quarter of dK^T and dV^T, which keeps the role
+// within the register file).  s_q0/s_do0/s_o0 and s_q1/s_do1/s_o1 are the two
+// Q/dO/O tile buffers; s_nl and s_nd hold -L / scale and -D of each buffer's
+// 64 rows.
+template <int D, bool CAUSAL, bool SEQLEN, bool BMASK, bool DROP>
 __device__ __forceinline__ void dkdv_role(const BwdArgs& a, int item, uint16_t* s_q0,
                                           uint16_t* s_do0, uint16_t* s_o0, uint16_t* s_q1,
                                           uint16_t* s_do1, uint16_t* s_o1,
@@ -279,8 +321,13 @@ __device__ __forceinline__ void dkdv_role(const BwdArgs& a, int item, uint16_t* 
   const int w = tid >> 6;
   const int r = lane & 31, hl = lane >> 5;
   const int BH = a.B * a.H;
+  constexpr int KS = D / 16;                  // contraction steps over d
+  constexpr int NDH = dkdv_splits(D);         // items per key tile
+  constexpr int DBo = D / 32 / NDH;           // 32-row blocks of dK^T, dV^T per item
+  static_assert(!DROP || D == 64, "dropout is built for D = 64");
   // Causal: key tile 0 sees every query, so ascending items are heaviest first.
-  const int kt = item / BH;
+  const int kt = NDH > 1 ? item / BH / NDH : item / BH;
+  const int dh = NDH > 1 ? item / BH % NDH : 0;  // output columns 32 DBo dh ..
   const int bh = item % BH;
   const int b = bh / a.H, hh = bh % a.H;
   const int k0 = kt * kBK;
@@ -293,8 +340,9 @@ __device__ __forceinline__ void dkdv_role(const BwdArgs& a, int item, uint16_t* 
   uint16_t* dK = (uint16_t*)a.dk + b * a.sdk.b + hh * a.sdk.h;
   uint16_t* dV = (uint16_t*)a.dv + b * a.sdv.b + hh * a.sdv.h;
 
-  f32x16 dkt[2] = {zero16(), zero16()};
-  f32x16 dvt[2] = {zero16(), zero16()};
+  f32x16 dkt[DBo], dvt[DBo];
+#pragma unroll
+  for (int db = 0; db < DBo; ++db) dkt[db] = dvt[db] = zero16();
 
   if (k0 < kv_len) {
     const int nq = (a.N + kTile - 1) / kTile;
@@ -310,26 +358,26 @@ __device__ __forceinline__ void dkdv_role(const BwdArgs& a, int item, uint16_t* 
     }
 
     const __amdgpu_buffer_rsrc_t rq =
-        make_rsrc((const uint16_t*)a.q + b * a.sq.b + hh * a.sq.h, slice_bytes(a.N, a.sq.s, 2));
+        make_rsrc((const uint16_t*)a.q + b * a.sq.b + hh * a.sq.h, slice_bytes(a.N, a.sq.s, 2, D));
     const __amdgpu_buffer_rsrc_t rk =
-        make_rsrc((const uint16_t*)a.k + b * a.sk.b + hh * a.sk.h, slice_bytes(a.Nk, a.sk.s, 2));
+        make_rsrc((const uint16_t*)a.k + b * a.sk.b + hh * a.sk.h, slice_bytes(a.Nk, a.sk.s, 2, D));
     const __amdgpu_buffer_rsrc_t rv =
-        make_rsrc((const uint16_t*)a.v + b * a.sv.b + hh * a.sv.h, slice_bytes(a.Nk, a.sv.s, 2));
+        make_rsrc((const uint16_t*)a.v + b * a.sv.b + hh * a.sv.h, slice_bytes(a.Nk, a.sv.s, 2, D));
     const __amdgpu_buffer_rsrc_t rdo = make_rsrc(
-        (const uint16_t*)a.dout + b * a.sdo.b + hh * a.sdo.h, slice_bytes(a.N, a.sdo.s, 2));
+        (const uint16_t*)a.dout + b * a.sdo.b + hh * a.sdo.h, slice_bytes(a.N, a.sdo.s, 2, D));
     const __amdgpu_buffer_rsrc_t ro = make_rsrc(
-        (const uint16_t*)a.o + b * a.so.b + hh * a.so.h, slice_bytes(a.N, a.so.s, 2));
+        (const uint16_t*)a.o + b * a.so.b + hh * a.so.h, slice_bytes(a.N, a.so.s, 2, D));
     const float* lse = a.lse + (int64_t)bh * a.N;
     const int ssq = (int)a.sq.s * 2, ssdo = (int)a.sdo.s * 2, sso = (int)a.so.s * 2;
 
     // K and V fragments (B operands): lane (r, hl) holds row kj, columns
     // 16 ks + 8 hl .. +7.
-    bf16x8 kf[4], vf[4];
+    bf16x8 kf[KS], vf[KS];
     {
       const int ok = kj * (int)a.sk.s * 2 + 16 * hl;
       const int ov = kj * (int)a.sv.s * 2 + 16 * hl;
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
+      for (int ks = 0; ks < KS; ++ks) {
         kf[ks] = as_bf16x8(ldb16(rk, ok + 32 * ks));
         vf[ks] = as_bf16x8(ldb16(rv, ov + 32 * ks));
       }
@@ -365,9 +413,12 @@ __device__ __forceinline__ void dkdv_role(const BwdArgs& a, int item, uint16_t* 
     // Q, dO and O tiles go straight to LDS; L through registers.
     auto gload = [&](int t, uint16_t* qt_, uint16_t* dt_, uint16_t* ot_) FA_INLINE {
       const int qs = t * kTile;
-      stage_tile(rq, qs, ssq, qt_, w, lane);
-      stage_tile(rdo, qs, ssdo, dt_, w, lane);
-      stage_tile(ro, qs, sso, ot_, w, lane);
+#pragma unroll
+      for (int j = 0; j < (D > 64 ? D / 64 : 1); ++j) {
+        stage_tile(rq, qs, ssq, qt_ + j * kTileElems, w, lane, 128 * j);
+        stage_tile(rdo, qs, ssdo, dt_ + j * kTileElems, w, lane, 128 * j);
+        stage_tile(ro, qs, sso, ot_ + j * kTileElems, w, lane, 128 * j);
+      }
       if (tid < kTile) {
         lrow = qs + tid;
         lraw = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rl, 4 * lrow, 0, 0));
@@ -386,10 +437,17 @@ __device__ __forceinline__ void dkdv_role(const BwdArgs& a, int item, uint16_t* 
       // lanes 0..31: rows 8 w .. 8 w + 7, lanes 32..63: rows 8 w + 32 .. + 39
       const int rl = stage_row(w, lane >> 2 << 3 & 63, lane >> 5), qq = lane & 3;
       float acc = 0.f;
-#pragma unroll
-      for (int cc = 0; cc < 2; ++cc) {
-        const int off = toff(rl, 16 * qq + 8 * cc);
+      if constexpr (D == 32) {  // 8 columns per lane
+        const int off = toff(rl, 8 * qq);
         acc = dot8_bf16(tile_row8(dt_, off), tile_row8(ot_, off), acc);
+      } else {  // 16 columns per lane in each 64-column block
+#pragma unroll
+        for (int j = 0; j < D / 64; ++j)
+#pragma unroll
+          for (int cc = 0; cc < 2; ++cc) {
+            const int off = j * kTileElems + toff(rl, 16 * qq + 8 * cc);
+            acc = dot8_bf16(tile_row8(dt_, off), tile_row8(ot_, off), acc);
+          }
       }
       acc += quad_xor1(acc);
       acc += quad_xor2(acc);
@@ -409,18 +467,22 @@ __device__ __forceinline__ void dkdv_role(const BwdArgs& a, int item, uint16_t* 
         FA_INLINE {
       constexpr bool MASK = decltype(mask_c)::value;
       constexpr int kLead = 2;
+      constexpr int NS = 4 * KS + 8 * DBo;  // 32 for D = 64
       f32x16 sc_[2], dp[2];
       uint32_t pkp[4][4], pkd[4][4];  // bf16 pairs of P and dS per step
-      bf16x8 opa[32];
+      bf16x8 opa[NS];
       [[maybe_unused]] DropBlock zb[2];  // keep bytes of the two halves
       // A operand of slot t.
       auto load_a = [&](int t) FA_INLINE {
-        if (t < 16) {
-          const int qb = t >> 3, ks = (t & 7) >> 1;
-          opa[t] = tile_row8((t & 1) ? ds_ : qs_, 2048 * qb + roff[ks]);
+        if (t < 4 * KS) {
+          const int qb = t / (2 * KS), ks = (t % (2 * KS)) >> 1;
+          opa[t] = tile_row8(((t & 1) ? ds_ : qs_) + (ks >> 2) * kTileElems,
+                             2048 * qb + roff[ks & 3]);
         } else {
-          const int stp = (t - 16) >> 2, u = (t - 16) & 3, db = u >> 1;
-          opa[t] = tr_read(((u & 1) ? qs_ : ds_) + 1024 * stp, troff[0][db], troff[1][db]);
+          const int tb = t - 4 * KS;
+          const int stp = tb / (2 * DBo), u = tb % (2 * DBo), gdb = DBo * dh + (u >> 1);
+          opa[t] = tr_read(((u & 1) ? qs_ : ds_) + (gdb >> 1) * kTileElems + 1024 * stp,
+                           troff[0][gdb & 1], troff[1][gdb & 1]);
         }
       };
       // The accumulators start at the row constants of their elements: S at
@@ -481,17 +543,18 @@ __device__ __forceinline__ void dkdv_role(const BwdArgs& a, int item, uint16_t* 
       for (int t = 0; t < kLead; ++t) load_a(t);
       FA_FENCE();
 #pragma unroll
-      for (int t = 0; t < 32; ++t) {
-        if (t + kLead < 32) load_a(t + kLead);
+      for (int t = 0; t < NS; ++t) {
+        if (t + kLead < NS) load_a(t + kLead);
         if (t == 2) init_acc(1);
-        if (t < 16) {
-          const int qb = t >> 3, ks = (t & 7) >> 1;
+        if (t < 4 * KS) {
+          const int qb = t / (2 * KS), ks = (t % (2 * KS)) >> 1;
           if (t & 1)
             dp[qb] = mfma32(opa[t], vf[ks], dp[qb]);
           else
             sc_[qb] = mfma32(opa[t], kf[ks], sc_[qb]);
         } else {
-          const int stp = (t - 16) >> 2, u = (t - 16) & 3, db = u >> 1;
+          const int tb = t - 4 * KS;
+          const int stp = tb / (2 * DBo), u = tb % (2 * DBo), db = u >> 1;
           const bf16x8 bop = (u & 1) ? words_to_bf16x8(pkd[stp][0], pkd[stp][1], pkd[stp][2],
                                                        pkd[stp][3])
                                      : words_to_bf16x8(pkp[stp][0], pkp[stp][1], pkp[stp][2],
@@ -501,7 +564,15 @@ __device__ __forceinline__ void dkdv_role(const BwdArgs& a, int item, uint16_t* 
           else
             dvt[db] = mfma32(opa[t], bop, dvt[db]);
         }
-        if (t >= 8 && t < 24) probs((t - 8) >> 3, (t - 8) & 7);
+        // P, dS of half 0 over the S, dP slots of half 1, of half 1 over the
+        // first half of the dV, dK slots (one chunk in each of slots 8..23 for
+        // D = 64)
+        if constexpr (D == 64) {
+          if (t >= 8 && t < 24) probs((t - 8) >> 3, (t - 8) & 7);
+        } else {
+          spread_chunks<2 * KS, 2 * KS>(t, [&](int cc) FA_INLINE { probs(0, cc); });
+          spread_chunks<4 * KS, 4 * DBo>(t, [&](int cc) FA_INLINE { probs(1, cc); });
+        }
         if constexpr (DROP) {  // half t / 4, in slots 0..7
           if (t < 8) {
             DropBlock& z = zb[t >> 2];
@@ -557,10 +628,10 @@ __device__ __forceinline__ void dkdv_role(const BwdArgs& a, int item, uint16_t* 
   }
 
   if (kj < a.Nk) {
-    uint16_t* kout = dK + (int64_t)kj * a.sdk.s;
-    uint16_t* vout = dV + (int64_t)kj * a.sdv.s;
+    uint16_t* kout = dK + (int64_t)kj * a.sdk.s + 32 * DBo * dh;
+    uint16_t* vout = dV + (int64_t)kj * a.sdv.s + 32 * DBo * dh;
 #pragma unroll
-    for (int db = 0; db < 2; ++db)
+    for (int db = 0; db < DBo; ++db)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         bf16x4 k4, v4;
@@ -582,18 +653,20 @@ __device__ __forceinline__ void dkdv_role(const BwdArgs& a, int item, uint16_t* 
 // gives some dropout variants 256 VGPRs plus AGPR spill slots (one wave per
 // SIMD, a third slower); with the bound they fit in 256 registers, and the
 // other variants compile unchanged.
-template <bool CAUSAL, bool SEQLEN, bool BMASK, bool DROP>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void bwd_kernel(
+template <int D, bool CAUSAL, bool SEQLEN, bool BMASK, bool DROP>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 64 ? 2 : 1, D == 64 ? 2 : 8))) void bwd_kernel(
     BwdArgs a, int phases) {
+  constexpr int KB = D > 64 ? D / 64 : 1;   // 64-column blocks per LDS tile
+  constexpr int NDH = dkdv_splits(D);       // dK/dV items per key tile
   // Six tile arrays: the dQ role uses two per buffer (K, V), the dK/dV role
   // three (Q, dO, O).  Separate arrays, so that the copies into one buffer
   // and the reads of the other never alias.
-  __shared__ __attribute__((aligned(16))) uint16_t s_a0[kTileElems];
-  __shared__ __attribute__((aligned(16))) uint16_t s_b0[kTileElems];
-  __shared__ __attribute__((aligned(16))) uint16_t s_c0[kTileElems];
-  __shared__ __attribute__((aligned(16))) uint16_t s_a1[kTileElems];
-  __shared__ __attribute__((aligned(16))) uint16_t s_b1[kTileElems];
-  __shared__ __attribute__((aligned(16))) uint16_t s_c1[kTileElems];
+  __shared__ __attribute__((aligned(16))) uint16_t s_a0[KB * kTileElems];
+  __shared__ __attribute__((aligned(16))) uint16_t s_b0[KB * kTileElems];
+  __shared__ __attribute__((aligned(16))) uint16_t s_c0[KB * kTileElems];
+  __shared__ __attribute__((aligned(16))) uint16_t s_a1[KB * kTileElems];
+  __shared__ __attribute__((aligned(16))) uint16_t s_b1[KB * kTileElems];
+  __shared__ __attribute__((aligned(16))) uint16_t s_c1[KB * kTileElems];
   __shared__ __attribute__((aligned(16))) float s_nl[2][kTile];  // -L / scale
   __shared__ __attribute__((aligned(16))) float s_nd[2][kTile];  // -D
   __shared__ uint16_t s_list[BMASK ? kMaxListTiles : 1];
@@ -615,7 +688,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     // The role whose items are heavier goes first: a dK/dV item sweeps the
     // queries, a dQ item the keys.
     const bool dq_first = a.Nk > a.N;
-    const int nfirst = dq_first ? (a.N + kBQ - 1) / kBQ : (a.Nk + kBK - 1) / kBK;
+    const int nfirst = dq_first ? (a.N + kBQ - 1) / kBQ : NDH * ((a.Nk + kBK - 1) / kBK);
     bool first;
     if ((BH & 7) == 0) {
       const int hpx = BH >> 3, x = id & 7, j = id >> 3;
@@ -632,43 +705,53 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     item = id;
   }
   if (dkdv)
-    dkdv_role<CAUSAL, SEQLEN, BMASK, DROP>(a, item, s_a0, s_b0, s_c0, s_a1, s_b1, s_c1, s_nl, s_nd,
-                                     s_list, s_scan);
+    dkdv_role<D, CAUSAL, SEQLEN, BMASK, DROP>(a, item, s_a0, s_b0, s_c0, s_a1, s_b1, s_c1,
+                                              s_nl, s_nd, s_list, s_scan);
   else
-    dq_role<CAUSAL, SEQLEN, BMASK, DROP>(a, item, s_a0, s_b0, s_a1, s_b1, s_list, s_scan);
+    dq_role<D, CAUSAL, SEQLEN, BMASK, DROP>(a, item, s_a0, s_b0, s_a1, s_b1, s_list, s_scan);
 }
 
-template <bool C, bool S, bool M, bool D>
+template <int HD, bool C, bool S, bool M, bool D>
 hipError_t launch(const BwdArgs& a, int phases, hipStream_t stream) {
   BwdArgs copy = a;
   int ph = phases;
   void* args[] = {&copy, &ph};
   const int n_dq = ((a.N + kBQ - 1) / kBQ) * a.B * a.H;
-  const int n_dkdv = ((a.Nk + kBK - 1) / kBK) * a.B * a.H;
+  const int n_dkdv = dkdv_splits(HD) * ((a.Nk + kBK - 1) / kBK) * a.B * a.H;
   int n = 0;
   if (phases & kPhaseDQ) n += n_dq;
   if (phases & kPhaseDKDV) n += n_dkdv;
   if (n == 0) return hipSuccess;
-  return hipLaunchKernel((const void*)&bwd_kernel<C, S, M, D>, dim3((unsigned)n), dim3(256),
-                         args, 0, stream);
+  return hipLaunchKernel((const void*)&bwd_kernel<HD, C, S, M, D>, dim3((unsigned)n),
+                         dim3(256), args, 0, stream);
 }
 
-template <bool D>
+template <int HD, bool D>
 hipError_t dispatch(const BwdArgs& a, bool causal, int p, hipStream_t stream) {
   const bool s = a.seqlens != nullptr, m = a.bmask != nullptr;
   if (causal) {
-    if (s) return m ? launch<true, true, true, D>(a, p, stream) : launch<true, true, false, D>(a, p, stream);
-    return m ? launch<true, false, true, D>(a, p, stream) : launch<true, false, false, D>(a, p, stream);
+    if (s)
+      return m ? launch<HD, true, true, true, D>(a, p, stream)
+               : launch<HD, true, true, false, D>(a, p, stream);
+    return m ? launch<HD, true, false, true, D>(a, p, stream)
+             : launch<HD, true, false, false, D>(a, p, stream);
   }
-  if (s) return m ? launch<false, true, true, D>(a, p, stream) : launch<false, true, false, D>(a, p, stream);
-  return m ? launch<false, false, true, D>(a, p, stream) : launch<false, false, false, D>(a, p, stream);
+  if (s)
+    return m ? launch<HD, false, true, true, D>(a, p, stream)
+             : launch<HD, false, true, false, D>(a, p, stream);
+  return m ? launch<HD, false, false, true, D>(a, p, stream)
+           : launch<HD, false, false, false, D>(a, p, stream);
 }
 
 }  // namespace
 
-hipError_t launch_bwd_bf16(const BwdArgs& a, bool causal, int phases, hipStream_t stream) {
-  return a.drop.t < 256 ? dispatch<true>(a, causal, phases, stream)
-                        : dispatch<false>(a, causal, phases, stream);
+hipError_t launch_bwd_bf16(const BwdArgs& a, bool causal, int phases, int d,
+                           hipStream_t stream) {
+  // the host allows d != 64 only without dropout
+  if (d == 32) return dispatch<32, false>(a, causal, phases, stream);
+  if (d == 128) return dispatch<128, false>(a, causal, phases, stream);
+  return a.drop.t < 256 ? dispatch<64, true>(a, causal, phases, stream)
+                        : dispatch<64, false>(a, causal, phases, stream);
 }
 
 }  // namespace fa

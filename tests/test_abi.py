@@ -102,7 +102,8 @@ def test_fwd_rejects_bad_arguments(kw, status, msg):
     (dict(o=None), 1, "o is NULL"),
     (dict(do=A + 4), 1, "dout is not 16-byte aligned"),
     (dict(dtype=1, sdv=bnd.fa_strides(64, 64, 66)), 1, "multiples of 4"),
-    (dict(d=32), 2, "head dimension"),
+    (dict(d=96), 2, "head dimension"),
+    (dict(d=32, dtype=1), 2, "head dimension"),
 ])
 def test_bwd_rejects_bad_arguments(kw, status, msg):
     assert _bwd(**kw) == status
@@ -144,7 +145,8 @@ def test_bwd_dq_rejects_bad_arguments(kw, status, msg):
     (dict(dv=A + 2), 1, "dv is not 16-byte aligned"),
     (dict(o=None), 1, "o is NULL"),
     (dict(do=None), 1, "dout is NULL"),
-    (dict(d=128), 2, "head dimension"),
+    (dict(d=96), 2, "head dimension"),
+    (dict(d=128, dtype=1), 2, "head dimension"),
 ])
 def test_bwd_dkdv_rejects_bad_arguments(kw, status, msg):
     assert _bwd_dkdv(**kw) == status

@@ -1,8 +1,8 @@
 """GPU parity of the bf16 forward pass with head dimensions 32 and 128 (the
 kernel family is templated on d; d = 64 has its own tests) against the fp64
 oracle: edge lengths, causal, key lengths, tile masks, both layouts and
-separate query / key lengths.  The backward pass is built for d = 64 and
-rejects other head dimensions."""
+separate query / key lengths, for the forward and the backward pass; dropout
+is built for d = 64 only."""
 import sys
 
 import numpy as np
@@ -85,13 +85,60 @@ def test_headdim_full_size(d):
     assert eo <= TOL["bf16"]["O"] and el <= TOL["bf16"]["L"], (eo, el)
 
 
-def test_backward_rejects_other_head_dims():
+def _check_bwd(case, tag):
+    from tests.gpu_util import gpu_backward, relfro
+    _say(f"[headdim bwd] {tag}")
+    q, k, v, do, sl, bm = device_inputs(case)
+    o, lse = gpu_forward(case, q, k, v, sl, bm)
+    dq, dk, dv = gpu_backward(case, q, k, v, o, do, lse, sl, bm)
+    g = ref.backward(case["q"], case["k"], case["v"], case["do"], **oracle_args(case))
+    errs = {n: relfro(to_np(a), b) for n, a, b in zip(("dQ", "dK", "dV"), (dq, dk, dv), g)}
+    for n, e in errs.items():
+        assert e <= TOL["bf16"]["G"], (n, errs)
+        assert np.all(np.isfinite(to_np(dict(dQ=dq, dK=dk, dV=dv)[n])))
+    _say(f"[headdim bwd] {tag} ok {errs}")
+
+
+@pytest.mark.parametrize("d", [32, 128])
+@pytest.mark.parametrize("N", [1, 17, 64, 65, 300, 1000])
+@pytest.mark.parametrize("causal", [False, True])
+def test_headdim_backward_dense(d, N, causal):
+    _check_bwd(wl.random_case(2, 2, N, d, seed=N + d + 5 * causal, causal=causal),
+               f"d={d} N={N} causal={causal}")
+
+
+@pytest.mark.parametrize("d", [32, 128])
+@pytest.mark.parametrize("masks", ["seqlens", "block", "both"])
+def test_headdim_backward_masks(d, masks):
+    seqlens = "random" if masks in ("seqlens", "both") else None
+    keep = 0.5 if masks in ("block", "both") else None
+    _check_bwd(wl.random_case(3, 2, 700, d, seed=d + 1, causal=True, seqlens=seqlens,
+                              block_keep_p=keep), f"d={d} masks={masks}")
+
+
+@pytest.mark.parametrize("d", [32, 128])
+@pytest.mark.parametrize("Nq,Nk", [(200, 900), (900, 200)])
+def test_headdim_backward_separate_lengths(d, Nq, Nk):
+    from tests.gpu_util import relfro
+    import exact_io_aware_64_amd as fa
+    rng = np.random.default_rng(Nq * 3 + Nk + d)
+    q, do = wl.draw_tensors(rng, 2, 2, Nq, d, "bf16", count=2)
+    k, v = wl.draw_tensors(rng, 2, 2, Nk, d, "bf16", count=2)
+    _say(f"[headdim bwd] d={d} Nq={Nq} Nk={Nk}")
+    tq, tk, tv, tdo = (to_dev(x, "bf16") for x in (q, k, v, do))
+    o, lse = fa.forward(tq, tk, tv, scale=d ** -0.5, causal=True)
+    grads = fa.backward(tq, tk, tv, o, tdo, lse, scale=d ** -0.5, causal=True)
+    g = ref.backward(q, k, v, do, d ** -0.5, causal=True)
+    for name, a, b in zip(("dQ", "dK", "dV"), grads, g):
+        assert relfro(to_np(a), b) <= TOL["bf16"]["G"], name
+
+
+def test_other_head_dims_reject_dropout():
     import exact_io_aware_64_amd as fa
     case = wl.random_case(1, 1, 64, 128, seed=1)
     q, k, v, do, _, _ = device_inputs(case)
-    o, lse = fa.forward(q, k, v, scale=0.1)
-    with pytest.raises(fa.FaError, match="head dimension 64 only"):
-        fa.backward(q, k, v, o, do, lse, scale=0.1)
+    with pytest.raises(fa.FaError, match="without dropout"):
+        fa.forward(q, k, v, scale=0.1, dropout_p=0.1, seed=1)
 
 
 def test_d128_workload_sampled():
