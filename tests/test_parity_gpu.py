@@ -75,7 +75,8 @@ def _sampled_inputs(name):
 
 
 @pytest.mark.parametrize("name", ["long_causal_b1h16n16384", "blocksparse_b1h8n65536",
-                                  "prefill_causal_b1h16q2048k16384"])
+                                  "prefill_causal_b1h16q2048k16384",
+                                  "train_causal_b2h16n4096d128"])
 def test_sampled_workload(name):
     """Full-size run checked on sampled query rows (O, L, dQ exact per row),
     a second backward with dO zeroed outside the sample (dK, dV exact for that
