@@ -56,8 +56,9 @@ typedef enum fa_status {
   FA_OK = 0,
   FA_ERR_INVALID_ARG = 1, /* null pointer, bad size, stride or alignment, scale <= 0,
                              workspace too small, bad mask_block, bad dropout_p */
-  FA_ERR_UNSUPPORTED = 2, /* valid request this build does not implement (d != 64,
-                             too many mask tiles) */
+  FA_ERR_UNSUPPORTED = 2, /* valid request this build does not implement (d other than
+                             32/64/128, d != 64 with fp32 or dropout, too many mask
+                             tiles) */
   FA_ERR_HIP = 3          /* a HIP launch reported an error */
 } fa_status;
 
@@ -75,7 +76,9 @@ typedef struct fa_strides {
  *   q, k, v      device pointers, [B][H][N][d] through their strides.
  *   o            device pointer, same element type, written in full.
  *   lse          device fp32 [B*H*N], contiguous, written in full (L above).
- *   B, H, N      >= 1.   d: must be 64.
+ *   B, H, N      >= 1.
+ *   d            head dimension: 64; 32 and 128 for FA_BF16 without dropout
+ *                (FA_ERR_UNSUPPORTED otherwise).
  *   scale        score scale (> 0, finite), typically 1/sqrt(d).
  *   causal       nonzero: key j is visible to query i only if j <= i.
  *   seqlens_k    NULL, or device int32[B]: keys j >= seqlens_k[b] are masked
