@@ -407,7 +407,7 @@ def io_sweep_summary(fetch_csv, write_csv, l2_csv, cfetch_csv, cwrite_csv, cl2_c
 
 KERNEL_SOURCES = {
     "fwd_bf16_kernel": ("fa_fwd_bf16.hip",),
-    "bwd_kernel": ("fa_bwd_bf16.hip",),
+    "bwd_kernel": ("fa_bwd_bf16.h", "fa_bwd_bf16.hip", "fa_bwd_bf16_d128.hip"),
 }
 COMMON_SOURCES = ("fa_device.h", "fa_internal.h")
 
@@ -575,9 +575,9 @@ def main(argv=None):
         return 0
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU only: the attention path needs no collective and "
-              "this build runs on a single MI355X (heads shard across GPUs with no "
-              "communication). Run with --gpus 1.", file=sys.stderr)
+        print("bench.py measures one GPU only: the attention path needs no collective "
+              "(batch and heads shard across GPUs with no communication), so the figure "
+              "is one MI355X's. Run with --gpus 1.", file=sys.stderr)
         return 2
     if args.mode == "copy":
         return copy_calibration(args.copy_mib, args.steps, args.warmup)

@@ -20,14 +20,28 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libfa.so")
 ARCH = "gfx950"
 
-SOURCES = ["fa_api.hip", "fa_fwd_bf16.hip", "fa_bwd_bf16.hip", "fa_f32.hip"]
+SOURCES = ["fa_api.hip", "fa_fwd_bf16.hip", "fa_bwd_bf16.hip", "fa_bwd_bf16_d128.hip",
+           "fa_f32.hip"]
 
 # Packed fp32 instructions are disabled for all device code: the compiler
 # would otherwise pair independent fp32 operations into them.
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
-CFLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall",
-          "-mllvm", "-amdgpu-mfma-vgpr-form",
-          "-Wno-unused-command-line-argument"] + DEVICE_FLAGS
+BASE_FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall",
+              "-Wno-unused-command-line-argument"] + DEVICE_FLAGS
+# MFMA accumulators in the architectural VGPRs: the kernels that run two or
+# more waves per SIMD fit their 256 registers that way.
+VGPR_FORM = ["-mllvm", "-amdgpu-mfma-vgpr-form"]
+# Per-source flags.  The d = 128 backward runs one wave per SIMD and keeps its
+# accumulators in the accumulation registers; its 64-slot tile loop is past
+# the default limit for fully unrolling a loop.
+SOURCE_FLAGS = {
+    "fa_bwd_bf16_d128.hip": ["-mllvm", "-pragma-unroll-threshold=200000"],
+}
+
+
+def source_flags(src: str) -> list:
+    """The compiler flags of one source file."""
+    return BASE_FLAGS + SOURCE_FLAGS.get(src, VGPR_FORM)
 
 
 def hipcc() -> str:
@@ -39,7 +53,7 @@ def hipcc() -> str:
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc(), *CFLAGS, "-Rpass-analysis=kernel-resource-usage",
+    cmd = [hipcc(), *source_flags(src), "-Rpass-analysis=kernel-resource-usage",
            "-I", os.path.join(ROOT, "include"), "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     noise = "is not a recognized feature for this target"

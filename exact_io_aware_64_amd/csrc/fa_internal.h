@@ -82,6 +82,9 @@ hipError_t launch_fwd_bf16(const FwdArgs& a, bool causal, int block_q, int d,
 // d: head dimension, 32, 64 or 128 (64 with dropout).
 hipError_t launch_bwd_bf16(const BwdArgs& a, bool causal, int phases, int d,
                            hipStream_t stream);
+// The d = 128 instantiation of the above, from its own translation unit.
+hipError_t launch_bwd_bf16_d128(const BwdArgs& a, bool causal, int phases,
+                                hipStream_t stream);
 hipError_t launch_fwd_f32(const FwdArgs& a, bool causal, hipStream_t stream);
 hipError_t launch_bwd_f32(const BwdArgs& a, bool causal, int phases, hipStream_t stream);
 

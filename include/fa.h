@@ -56,7 +56,7 @@ typedef enum fa_status {
   FA_OK = 0,
   FA_ERR_INVALID_ARG = 1, /* null pointer, bad size, stride or alignment, scale <= 0,
                              workspace too small, bad mask_block, bad dropout_p */
-  FA_ERR_UNSUPPORTED = 2, /* valid request this build does not implement (d other than
+  FA_ERR_UNSUPPORTED = 2, /* valid request the library does not implement (d other than
                              32/64/128, d != 64 with fp32 or dropout, too many mask
                              tiles) */
   FA_ERR_HIP = 3          /* a HIP launch reported an error */
@@ -106,7 +106,7 @@ fa_status fa_fwd(fa_dtype dtype,
 
 /*
  * fa_bwd_workspace_bytes -- device workspace that fa_bwd, fa_bwd_dq and
- * fa_bwd_dkdv need.  Every kernel of this build keeps its per-row statistics
+ * fa_bwd_dkdv need.  Every kernel of the library keeps its per-row statistics
  * (L, D = dot(dO_i, O_i)) on chip, so the result is 0 for every problem; the
  * workspace arguments are kept so that a future kernel may use them.
  */
@@ -124,7 +124,7 @@ size_t fa_bwd_workspace_bytes(fa_dtype dtype, int B, int H, int N, int d);
  *   dq, dk, dv       outputs, element type dtype, through their strides.
  *   workspace        device buffer of at least fa_bwd_workspace_bytes(...) bytes
  *                    (16-byte aligned); may be NULL when that size is 0, as it is
- *                    in this build.
+ *                    for every problem.
  *   remaining arguments as for fa_fwd and must match the forward call.
  */
 fa_status fa_bwd(fa_dtype dtype,
