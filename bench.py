@@ -22,6 +22,13 @@ profiles/hbm_traffic_<workload>.json (written by --pmc-summary from a
 FETCH_SIZE run and a WRITE_SIZE run of this script, scaled by the same
 counters read on a plain copy of known size, --mode copy); it is reported
 only while the kernel's sources still hash to the value recorded there.
+
+After the timed steps, --cold-reps launches of each kernel are timed again,
+each after a 1 GiB write that evicts L2 and the Infinity Cache (cold-cache
+medians, reported beside the warm back-to-back figures).  --pipe-summary
+turns a rocprofv3 run of SQ/GRBM counters into profiles/pipe_counters_<key>.md
+(MFMA and VALU busy fractions, transcendental instructions, LDS bank
+conflicts).
 """
 from __future__ import annotations
 
@@ -44,6 +51,12 @@ import workloads as wl  # noqa: E402
 METRIC = "attention TFLOP/s (fwd, fwd+bwd) and % of MI355X bf16 MFMA peak"
 PEAK_TFLOPS = {"bf16": 2516.6, "f32": 157.3}   # dense MFMA bf16; fp32 vector/matrix
 PEAK_HBM_GBS = 8000.0
+FLUSH_BYTES = 1 << 30   # cold-cache runs: larger than L2 (8 x 4 MB) + Infinity Cache (256 MB)
+# Counters of one --pmc pass for --pipe-summary (7 SQ + 1 GRBM, within the
+# per-pass limits of the SQ and GRBM blocks).
+PIPE_COUNTERS = ("SQ_VALU_MFMA_BUSY_CYCLES", "SQ_ACTIVE_INST_VALU", "SQ_INSTS_VALU_TRANS_F32",
+                 "SQ_INSTS_MFMA", "SQ_LDS_BANK_CONFLICT", "SQ_LDS_IDX_ACTIVE",
+                 "SQ_BUSY_CU_CYCLES", "GRBM_GUI_ACTIVE")
 DEFAULT_WORKLOAD = "gpt2s_causal_b8h12n1024"
 
 
@@ -119,7 +132,7 @@ def measure_key(workload: str, dropout_p: float) -> str:
 
 
 def run_gpu(w: wl.Workload, inp: dict, steps: int, warmup: int, prewarm_s: float = 1.0,
-            dropout_p: float = 0.0):
+            dropout_p: float = 0.0, cold_reps: int = 0):
     """Times `steps` steps after `warmup` untimed ones.  One step is fa_fwd
     then fa_bwd (fa_fwd alone for a forward-only workload), each a single
     kernel launch on the current stream; HIP
@@ -129,7 +142,12 @@ def run_gpu(w: wl.Workload, inp: dict, steps: int, warmup: int, prewarm_s: float
 
     Before the warmup steps the step runs untimed for `prewarm_s` seconds of
     wall time: an idle MI355X takes a few milliseconds of sustained load to
-    raise its clocks, and a short warmup would otherwise time the ramp."""
+    raise its clocks, and a short warmup would otherwise time the ramp.
+
+    Then, outside the timed region, `cold_reps` launches of each kernel are
+    timed one by one, each right after a FLUSH_BYTES write on the same stream
+    (the kernel then starts with nothing of its inputs in L2 or the Infinity
+    Cache); their medians are returned as cold_ms."""
     import torch
     import exact_io_aware_64_amd as fa
 
@@ -180,9 +198,49 @@ def run_gpu(w: wl.Workload, inp: dict, steps: int, warmup: int, prewarm_s: float
     wall_ms = (time.perf_counter() - t0) * 1e3 / steps
     kernel_ms = {name: float(np.mean([e[i].elapsed_time(e[i + 1]) for e in evs]))
                  for i, name in enumerate(kernels)}
+    median_ms = {name: float(np.median([e[i].elapsed_time(e[i + 1]) for e in evs]))
+                 for i, name in enumerate(kernels)}
+    cold_ms = None
+    if cold_reps > 0:
+        flush = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=dev)
+        launches = [fwd] + ([bwd] if bwd is not None else [])
+        cev = [[torch.cuda.Event(enable_timing=True) for _ in range(2 * len(launches))]
+               for _ in range(cold_reps)]
+        for r, e in enumerate(cev):
+            for i, f in enumerate(launches):
+                flush.fill_(r & 0xFF)
+                e[2 * i].record(stream)
+                f()
+                e[2 * i + 1].record(stream)
+        torch.cuda.synchronize()
+        cold_ms = {name: float(np.median([e[2 * i].elapsed_time(e[2 * i + 1]) for e in cev]))
+                   for i, name in enumerate(kernels)}
+        del flush
     props = torch.cuda.get_device_properties(dev)
     outs = dict(o=o, lse=lse, dq=dq, dk=dk, dv=dv)
-    return wall_ms, kernel_ms, props, outs
+    return wall_ms, kernel_ms, median_ms, cold_ms, props, outs
+
+
+def host_info() -> dict:
+    """CPU model and the BLAS library NumPy runs on (for the CPU baseline)."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:  # pragma: no cover
+        pass
+    blas = None
+    try:
+        from threadpoolctl import threadpool_info
+        libs = [p for p in threadpool_info() if p.get("user_api") == "blas"]
+        if libs:
+            blas = f"{libs[0].get('internal_api')} {libs[0].get('version')}"
+    except Exception:  # pragma: no cover
+        pass
+    return dict(cpu=model, blas=blas)
 
 
 def cpu_baseline(w: wl.Workload, inp: dict, outs: dict, flops_fb: float,
@@ -243,7 +301,7 @@ def cpu_baseline(w: wl.Workload, inp: dict, outs: dict, flops_fb: float,
                        f"{H} heads x batch {w.B} "
                        f"(whole sequences), {passes} pass(es) in {secs:.1f} s; value scaled "
                        f"by the FLOPs of the sample",
-                seconds=secs)
+                seconds=secs, **host_info())
     return base, parity
 
 
@@ -473,6 +531,70 @@ def pmc_summary(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, workload, 
                 kernels=kernels)
 
 
+def pipe_metrics(c: dict, n_cu: int = 256, simd_per_cu: int = 4, n_xcd: int = 8) -> dict:
+    """Busy fractions of one dispatch from its counters, each summed over the
+    GPU's block instances (as rocprofv3 reports them), with rocprofv3's own
+    gfx950 formulas.  GRBM_GUI_ACTIVE counts the dispatch's active cycles once
+    per XCD, so the dispatch lasted gui = GRBM_GUI_ACTIVE / n_xcd cycles.
+    MFMA busy = MFMA busy cycles / (gui x SIMDs); VALU busy = VALU-active
+    quad-cycles / (gui x CUs), the share of SIMD cycles executing a vector
+    instruction; CU busy = CU-busy cycles / (gui x CUs); LDS bank-conflict
+    share = conflict cycles / LDS-active cycles."""
+    gui = c["GRBM_GUI_ACTIVE"] / n_xcd
+    return dict(
+        mfma_busy=c["SQ_VALU_MFMA_BUSY_CYCLES"] / (gui * n_cu * simd_per_cu),
+        valu_busy=c["SQ_ACTIVE_INST_VALU"] / (gui * n_cu),
+        lds_conflict=c["SQ_LDS_BANK_CONFLICT"] / max(1.0, c["SQ_LDS_IDX_ACTIVE"]),
+        trans_per_mfma=c["SQ_INSTS_VALU_TRANS_F32"] / max(1.0, c["SQ_INSTS_MFMA"]),
+        cu_busy=c["SQ_BUSY_CU_CYCLES"] / (gui * n_cu),
+        gui_cycles=gui)
+
+
+def pipe_summary(counter_csv: str, workload: str, command: str) -> str:
+    """Markdown summary of a rocprofv3 --pmc run over PIPE_COUNTERS: per
+    kernel, the counters averaged over its dispatches (each summed over the
+    GPU's instances) and the busy fractions derived from them."""
+    per = {}
+    with open(counter_csv) as fh:
+        for row in csv.DictReader(fh):
+            k = _short_kernel_name(row["Kernel_Name"])
+            if k not in KERNEL_SOURCES:
+                continue
+            d = per.setdefault(k, {}).setdefault(row["Dispatch_Id"], {})
+            d[row["Counter_Name"]] = d.get(row["Counter_Name"], 0.0) + float(row["Counter_Value"])
+            d["_ns"] = float(row["End_Timestamp"]) - float(row["Start_Timestamp"])
+    out = [f"# Pipe counters: {workload}", "",
+           "Command (repository root, MI355X, `TMPDIR=/tmp`):", "", "```", command, "```", "",
+           "Per dispatch, averaged over the dispatches of the run (rocprofv3's gfx950 "
+           "formulas; counters come summed over block instances, GRBM_GUI_ACTIVE once per "
+           "XCD). µs: the dispatch's duration under the profiler; cycles: its active cycles; "
+           "clock: the two divided. MFMA busy: share of SIMD cycles with the matrix core "
+           "busy; VALU busy: share of SIMD cycles executing a vector instruction (MfmaUtil "
+           "and VALUBusy); CU busy: share of CU cycles with waves resident; LDS conflict: "
+           "bank-conflict cycles per LDS-active cycle; trans/MFMA: fp32 transcendental "
+           "(exp2) instructions per MFMA instruction.", "",
+           "| kernel | dispatches | µs | cycles | clock GHz | MFMA busy | VALU busy | CU busy | "
+           "LDS conflict | trans/MFMA |", "|---|---|---|---|---|---|---|---|---|---|"]
+    for k, disp in sorted(per.items()):
+        full = [d for d in disp.values() if all(n in d for n in PIPE_COUNTERS)]
+        if not full:
+            continue
+        mean = {n: float(np.mean([d[n] for d in full])) for n in PIPE_COUNTERS}
+        ns = float(np.mean([d["_ns"] for d in full]))
+        m = pipe_metrics(mean)
+        out.append(f"| {k} | {len(full)} | {ns / 1e3:.1f} | {m['gui_cycles']:.0f} | "
+                   f"{m['gui_cycles'] / ns:.2f} | {100 * m['mfma_busy']:.1f} % | "
+                   f"{100 * m['valu_busy']:.1f} % | {100 * m['cu_busy']:.1f} % | "
+                   f"{100 * m['lds_conflict']:.2f} % | {m['trans_per_mfma']:.2f} |")
+    out += ["", "Raw means per dispatch:", ""]
+    for k, disp in sorted(per.items()):
+        full = [d for d in disp.values() if all(n in d for n in PIPE_COUNTERS)]
+        if full:
+            out.append(f"- {k}: " + ", ".join(
+                f"{n} {np.mean([d[n] for d in full]):.4g}" for n in PIPE_COUNTERS))
+    return "\n".join(out) + "\n"
+
+
 def traffic_for(kernel: str, workload: str):
     """Measured HBM bytes per launch of `kernel` on `workload`, or None when
     no record exists or the kernel changed since the counters were taken."""
@@ -532,6 +654,9 @@ def main(argv=None):
                     help="drop probability on P (fa_fwd_dropout / fa_bwd_dropout); the FLOP "
                          "count is the same as without dropout")
     ap.add_argument("--cpu-baseline", default="on", choices=["on", "off"])
+    ap.add_argument("--cold-reps", type=int, default=50,
+                    help="launches of each kernel timed after a 1 GiB cache-evicting write "
+                         "(0: none)")
     ap.add_argument("--mode", default="attention", choices=["attention", "copy", "io-sweep"],
                     help="copy: time a plain 1 GiB device copy (counter calibration); "
                          "io-sweep: dense forward over N x query-tile height (fa_fwd_tiled)")
@@ -547,6 +672,9 @@ def main(argv=None):
                          "(attention and --mode copy) into profiles/hbm_traffic_<workload>.json")
     ap.add_argument("--pmc-command", default="",
                     help="the rocprofv3 commands that produced the --pmc-summary inputs")
+    ap.add_argument("--pipe-summary", metavar="COUNTER_CSV",
+                    help="write profiles/pipe_counters_<workload>.md from a rocprofv3 "
+                         "--pmc run of this script over PIPE_COUNTERS")
     ap.add_argument("--trace-summary", nargs=2, metavar=("KERNEL_STATS_CSV", "BENCH_LOG"),
                     help="write profiles/kernel_trace_<workload>.md from a rocprofv3 "
                          "--kernel-trace --stats run of this script")
@@ -562,6 +690,12 @@ def main(argv=None):
     if args.trace_summary:
         md = trace_summary(*args.trace_summary, workload=key, command=args.pmc_command)
         with open(os.path.join(ROOT, "profiles", f"kernel_trace_{key}.md"), "w") as fh:
+            fh.write(md)
+        print(md)
+        return 0
+    if args.pipe_summary:
+        md = pipe_summary(args.pipe_summary, workload=key, command=args.pmc_command)
+        with open(os.path.join(ROOT, "profiles", f"pipe_counters_{key}.md"), "w") as fh:
             fh.write(md)
         print(md)
         return 0
@@ -592,8 +726,8 @@ def main(argv=None):
     flops_b = 10.0 * w.d * pairs if w.backward else 0.0
     esize = 2 if w.dtype == "bf16" else 4
 
-    wall_ms, kernel_ms, props, outs = run_gpu(w, inp, args.steps, args.warmup, args.prewarm_s,
-                                               args.dropout)
+    wall_ms, kernel_ms, median_ms, cold_ms, props, outs = run_gpu(
+        w, inp, args.steps, args.warmup, args.prewarm_s, args.dropout, args.cold_reps)
     fwd_ms = kernel_ms["fwd_bf16_kernel"]
     bwd_ms = kernel_ms.get("bwd_kernel")
     peak = PEAK_TFLOPS[w.dtype]
@@ -650,6 +784,9 @@ def main(argv=None):
         "fwd_ms": fwd_ms,
         "bwd_ms": bwd_ms,
         "kernel_ms": kernel_ms,
+        "kernel_ms_median": median_ms,
+        "cold_kernel_ms": cold_ms,
+        "cold_reps": args.cold_reps,
         "fwd_frac_peak": tf_f / peak,
         "fwdbwd_frac_peak": tf_fb / peak,
         "peak_tflops": peak,

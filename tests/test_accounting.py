@@ -96,3 +96,24 @@ def test_rectangular_kernel_bytes():
     tq, tk = 2 * 100 * 64 * 2, 2 * 300 * 64 * 2
     assert kb["fwd_bf16_kernel"] == 2 * tq + 2 * tk + 2 * 100 * 4
     assert kb["bwd_kernel"] == 4 * tq + 4 * tk + 2 * 100 * 4
+
+
+def test_pipe_metrics_formulas():
+    # A dispatch of 1000 GPU-active cycles on 256 CUs x 4 SIMDs in which every
+    # SIMD has its matrix core busy for 400 cycles and a vector instruction
+    # executing for 600 (counted in quad-cycles per CU: 4 SIMDs x 600 / 4).
+    # GRBM_GUI_ACTIVE comes summed over the 8 XCDs.
+    c = dict(GRBM_GUI_ACTIVE=8 * 1000.0, SQ_VALU_MFMA_BUSY_CYCLES=1024 * 400.0,
+             SQ_ACTIVE_INST_VALU=256 * 600.0, SQ_BUSY_CU_CYCLES=256 * 1000.0,
+             SQ_LDS_BANK_CONFLICT=5.0, SQ_LDS_IDX_ACTIVE=100.0,
+             SQ_INSTS_VALU_TRANS_F32=300.0, SQ_INSTS_MFMA=1200.0)
+    m = bench.pipe_metrics(c)
+    assert m["mfma_busy"] == pytest.approx(0.4)
+    assert m["valu_busy"] == pytest.approx(0.6)
+    assert m["cu_busy"] == pytest.approx(1.0)
+    assert m["lds_conflict"] == pytest.approx(0.05)
+    assert m["trans_per_mfma"] == pytest.approx(0.25)
+    assert m["gui_cycles"] == pytest.approx(1000.0)
+    assert len(bench.PIPE_COUNTERS) == 8
+    assert sum(n.startswith("SQ_") for n in bench.PIPE_COUNTERS) <= 8
+    assert sum(n.startswith("GRBM_") for n in bench.PIPE_COUNTERS) <= 2
