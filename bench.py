@@ -137,8 +137,9 @@ def run_gpu(w: wl.Workload, inp: dict, steps: int, warmup: int, prewarm_s: float
     then fa_bwd (fa_fwd alone for a forward-only workload), each a single
     kernel launch on the current stream; HIP
     events recorded on that stream around the launches give each kernel's
-    device time, and the wall clock around the whole timed region gives the
-    step time.
+    device time (one event after each launch: the event that ends a step
+    also starts the next), and the wall clock around the whole timed region
+    gives the step time.
 
     Before the warmup steps the step runs untimed for `prewarm_s` seconds of
     wall time: an idle MI355X takes a few milliseconds of sustained load to
@@ -169,16 +170,18 @@ def run_gpu(w: wl.Workload, inp: dict, steps: int, warmup: int, prewarm_s: float
     bwd = fa.prepare_bwd(q, k, v, o, do, lse, dq, dk, dv, **kw) if w.backward else None
     kernels = KERNELS if w.backward else KERNELS[:1]
 
+    # Events: one after each launch.  The event after a step's last launch is
+    # also the start of the next step's first launch (nothing else runs on
+    # the stream in between), so a step records one event per kernel; each
+    # event packet costs the stream a few microseconds.
     def step(ev=None):
-        if ev is not None:
-            ev[0].record(stream)
         fwd()
         if ev is not None:
-            ev[1].record(stream)
+            ev[0].record(stream)
         if bwd is not None:
             bwd()
             if ev is not None:
-                ev[2].record(stream)
+                ev[1].record(stream)
 
     torch.cuda.synchronize()
     t_end = time.perf_counter() + prewarm_s
@@ -188,18 +191,22 @@ def run_gpu(w: wl.Workload, inp: dict, steps: int, warmup: int, prewarm_s: float
         torch.cuda.synchronize()
     for _ in range(warmup):
         step()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(kernels) + 1)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(kernels))]
            for _ in range(steps)]
+    start = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    start.record(stream)
     for e in evs:
         step(e)
     torch.cuda.synchronize()
     wall_ms = (time.perf_counter() - t0) * 1e3 / steps
-    kernel_ms = {name: float(np.mean([e[i].elapsed_time(e[i + 1]) for e in evs]))
-                 for i, name in enumerate(kernels)}
-    median_ms = {name: float(np.median([e[i].elapsed_time(e[i + 1]) for e in evs]))
-                 for i, name in enumerate(kernels)}
+    # bounds[i] = [start of step i's first launch, end of each launch ...]
+    bounds = [[start if i == 0 else evs[i - 1][-1]] + e for i, e in enumerate(evs)]
+    durs = {name: [b[j].elapsed_time(b[j + 1]) for b in bounds]
+            for j, name in enumerate(kernels)}
+    kernel_ms = {name: float(np.mean(d)) for name, d in durs.items()}
+    median_ms = {name: float(np.median(d)) for name, d in durs.items()}
     cold_ms = None
     if cold_reps > 0:
         flush = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=dev)
