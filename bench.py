@@ -201,10 +201,7 @@ def run_gpu(w: wl.Workload, inp: dict, steps: int, warmup: int, prewarm_s: float
         step(e)
     torch.cuda.synchronize()
     wall_ms = (time.perf_counter() - t0) * 1e3 / steps
-    # bounds[i] = [start of step i's first launch, end of each launch ...]
-    bounds = [[start if i == 0 else evs[i - 1][-1]] + e for i, e in enumerate(evs)]
-    durs = {name: [b[j].elapsed_time(b[j + 1]) for b in bounds]
-            for j, name in enumerate(kernels)}
+    durs = launch_durations(start, evs, kernels)
     kernel_ms = {name: float(np.mean(d)) for name, d in durs.items()}
     median_ms = {name: float(np.median(d)) for name, d in durs.items()}
     cold_ms = None
@@ -226,6 +223,20 @@ def run_gpu(w: wl.Workload, inp: dict, steps: int, warmup: int, prewarm_s: float
     props = torch.cuda.get_device_properties(dev)
     outs = dict(o=o, lse=lse, dq=dq, dk=dk, dv=dv)
     return wall_ms, kernel_ms, median_ms, cold_ms, props, outs
+
+
+def launch_durations(start, evs, kernels) -> dict:
+    """Per-kernel durations (ms) from chained events: evs[i][j] was recorded
+    right after launch j of step i, and `start` right before step 0, so launch
+    j of step i ran between the previous event on the stream (evs[i][j-1], or
+    the last event of step i-1, or `start`) and evs[i][j]."""
+    durs = {name: [] for name in kernels}
+    prev = start
+    for e in evs:
+        for j, name in enumerate(kernels):
+            durs[name].append(prev.elapsed_time(e[j]))
+            prev = e[j]
+    return durs
 
 
 def host_info() -> dict:

@@ -117,3 +117,21 @@ def test_pipe_metrics_formulas():
     assert len(bench.PIPE_COUNTERS) == 8
     assert sum(n.startswith("SQ_") for n in bench.PIPE_COUNTERS) <= 8
     assert sum(n.startswith("GRBM_") for n in bench.PIPE_COUNTERS) <= 2
+
+
+def test_launch_durations_chain_events():
+    class Ev:
+        def __init__(self, t):
+            self.t = t
+
+        def elapsed_time(self, other):
+            return other.t - self.t
+
+    # two steps of (fwd 2 ms, bwd 5 ms) after a 1 ms gap, then (3, 4)
+    start = Ev(0.0)
+    evs = [[Ev(3.0), Ev(8.0)], [Ev(11.0), Ev(15.0)]]
+    d = bench.launch_durations(start, evs, ("fwd", "bwd"))
+    assert d == {"fwd": [3.0, 3.0], "bwd": [5.0, 4.0]}
+    # forward-only steps: one event per step
+    d = bench.launch_durations(start, [[Ev(2.0)], [Ev(5.0)]], ("fwd",))
+    assert d == {"fwd": [2.0, 3.0]}
