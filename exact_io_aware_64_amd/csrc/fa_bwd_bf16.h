@@ -21,8 +21,8 @@
 //    come out with one key per lane, which is exactly the B operand of
 //    dV^T = dO^T P and dK^T = Q^T dS.
 // One launch carries both roles, heaviest work first, so that the GPU stays
-// busy to the end without a second kernel's launch gap and tail.  Masked tiles are skipped exactly as
-// in the forward pass.
+// busy to the end without a second kernel's launch gap and tail.  Masked
+// tiles are skipped exactly as in the forward pass.
 //
 // Dropout (DROP), with keep indicator Z and keep scale s:
 //   dV = (s Z P)^T dO,  dP = s Z (dO V^T),  dS = P (dP - D),  D_i = dot(dO_i, O_i).
@@ -643,10 +643,12 @@ __device__ __forceinline__ void dkdv_role(const BwdArgs& a, int item, uint16_t* 
 // The fused backward kernel.  Work items: query tiles for the dQ role and
 // key tiles for the dK/dV role (each times B*H), each role in its own
 // heavy-first order.
-// Two waves per SIMD are asked for explicitly: left to itself the compiler
-// gives some dropout variants 256 VGPRs plus AGPR spill slots (one wave per
-// SIMD, a third slower); with the bound they fit in 256 registers, and the
-// other variants compile unchanged.
+// D = 32, 64: two waves per SIMD are asked for explicitly: left to itself the
+// compiler gives some dropout variants 256 VGPRs plus AGPR spill slots (one
+// wave per SIMD, a third slower); with the bound they fit in 256 registers,
+// and the other variants compile unchanged.  D = 128 runs one wave per SIMD:
+// its dK/dV accumulators alone take 128 registers per lane, and its
+// translation unit keeps them in the accumulation registers.
 template <int D, bool CAUSAL, bool SEQLEN, bool BMASK, bool DROP>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 64 ? 2 : 1, D == 64 ? 2 : 8))) void bwd_kernel(
     BwdArgs a, int phases) {
