@@ -314,12 +314,18 @@ def cpu_baseline(w: wl.Workload, inp: dict, outs: dict, flops_fb: float,
     for name, g in zip(("dQ", "dK", "dV"), G):
         parity[f"{name}_relfro"] = float(np.linalg.norm(npf(outs["d" + name[1].lower()]) - g)
                                          / np.linalg.norm(g))
+    # the whole workload at the sample's rate (an extrapolation unless the
+    # sample was every head)
+    full_s = flops_fb / (tflops * 1e12)
     base = dict(value=tflops, unit="TFLOP/s", cores=int(cores), kind="oracle",
                 sample=f"fp64 NumPy oracle {'fwd+bwd' if w.backward else 'fwd'} on {hs} of "
                        f"{H} heads x batch {w.B} "
                        f"(whole sequences), {passes} pass(es) in {secs:.1f} s; value scaled "
                        f"by the FLOPs of the sample",
-                seconds=secs, **host_info())
+                seconds=secs,
+                full_problem_s=full_s,
+                full_problem_s_kind="measured" if hs == H else "extrapolated from the sample",
+                **host_info())
     return base, parity
 
 

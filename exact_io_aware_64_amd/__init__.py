@@ -10,6 +10,7 @@ from ._binding import (  # noqa: F401
     FA_F32,
     FaError,
     backward,
+    bwd,
     fa_bwd,
     fa_bwd_dkdv,
     fa_bwd_dq,
@@ -23,6 +24,7 @@ from ._binding import (  # noqa: F401
     fa_last_error,
     fa_status_string,
     forward,
+    fwd,
     load_library,
     prepare_bwd,
     prepare_fwd,

@@ -418,3 +418,9 @@ def backward(q, k, v, o, dout, lse, *, scale: float, causal: bool = False, seqle
     else:
         fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, workspace, **kw)
     return dq, dk, dv
+
+
+# Short names of the two allocating calls: fwd(q, k, v, ...) -> (o, lse) and
+# bwd(q, k, v, o, dout, lse, ...) -> (dq, dk, dv).
+fwd = forward
+bwd = backward

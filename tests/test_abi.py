@@ -251,3 +251,8 @@ def _fwd_qk(**kw):
 def test_fwd_qk_rejects_bad_arguments(kw, status, msg):
     assert _fwd_qk(**kw) == status
     assert msg in fa.fa_last_error()
+
+
+def test_short_python_names():
+    # fa.fwd / fa.bwd are the allocating calls under their short names
+    assert fa.fwd is fa.forward and fa.bwd is fa.backward
