@@ -132,14 +132,16 @@ def measure_key(workload: str, dropout_p: float) -> str:
 
 
 def run_gpu(w: wl.Workload, inp: dict, steps: int, warmup: int, prewarm_s: float = 1.0,
-            dropout_p: float = 0.0, cold_reps: int = 0):
+            dropout_p: float = 0.0, cold_reps: int = 0, event_every: int = 4):
     """Times `steps` steps after `warmup` untimed ones.  One step is fa_fwd
     then fa_bwd (fa_fwd alone for a forward-only workload), each a single
     kernel launch on the current stream; HIP
     events recorded on that stream around the launches give each kernel's
-    device time (one event after each launch: the event that ends a step
-    also starts the next), and the wall clock around the whole timed region
-    gives the step time.
+    device time, and the wall clock around the whole timed region gives the
+    step time.  Every `event_every`-th timed step carries the events (one
+    before its first launch and one after each launch); each event packet
+    costs the stream a few microseconds, so timing every step would slow the
+    step it measures.
 
     Before the warmup steps the step runs untimed for `prewarm_s` seconds of
     wall time: an idle MI355X takes a few milliseconds of sustained load to
@@ -170,18 +172,17 @@ def run_gpu(w: wl.Workload, inp: dict, steps: int, warmup: int, prewarm_s: float
     bwd = fa.prepare_bwd(q, k, v, o, do, lse, dq, dk, dv, **kw) if w.backward else None
     kernels = KERNELS if w.backward else KERNELS[:1]
 
-    # Events: one after each launch.  The event after a step's last launch is
-    # also the start of the next step's first launch (nothing else runs on
-    # the stream in between), so a step records one event per kernel; each
-    # event packet costs the stream a few microseconds.
+    # ev: [start, after launch 0, after launch 1, ...] of a sampled step
     def step(ev=None):
-        fwd()
         if ev is not None:
             ev[0].record(stream)
+        fwd()
+        if ev is not None:
+            ev[1].record(stream)
         if bwd is not None:
             bwd()
             if ev is not None:
-                ev[1].record(stream)
+                ev[2].record(stream)
 
     torch.cuda.synchronize()
     t_end = time.perf_counter() + prewarm_s
@@ -191,17 +192,16 @@ def run_gpu(w: wl.Workload, inp: dict, steps: int, warmup: int, prewarm_s: float
         torch.cuda.synchronize()
     for _ in range(warmup):
         step()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(kernels))]
-           for _ in range(steps)]
-    start = torch.cuda.Event(enable_timing=True)
+    every = max(1, event_every)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(kernels) + 1)]
+           if i % every == 0 else None for i in range(steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    start.record(stream)
     for e in evs:
         step(e)
     torch.cuda.synchronize()
     wall_ms = (time.perf_counter() - t0) * 1e3 / steps
-    durs = launch_durations(start, evs, kernels)
+    durs = launch_durations([e for e in evs if e is not None], kernels)
     kernel_ms = {name: float(np.mean(d)) for name, d in durs.items()}
     median_ms = {name: float(np.median(d)) for name, d in durs.items()}
     cold_ms = None
@@ -225,17 +225,15 @@ def run_gpu(w: wl.Workload, inp: dict, steps: int, warmup: int, prewarm_s: float
     return wall_ms, kernel_ms, median_ms, cold_ms, props, outs
 
 
-def launch_durations(start, evs, kernels) -> dict:
-    """Per-kernel durations (ms) from chained events: evs[i][j] was recorded
-    right after launch j of step i, and `start` right before step 0, so launch
-    j of step i ran between the previous event on the stream (evs[i][j-1], or
-    the last event of step i-1, or `start`) and evs[i][j]."""
+def launch_durations(samples, kernels) -> dict:
+    """Per-kernel durations (ms) of the sampled steps: samples[i][0] was
+    recorded right before the step's first launch and samples[i][j + 1] right
+    after its launch j, so launch j ran between samples[i][j] and
+    samples[i][j + 1]."""
     durs = {name: [] for name in kernels}
-    prev = start
-    for e in evs:
+    for e in samples:
         for j, name in enumerate(kernels):
-            durs[name].append(prev.elapsed_time(e[j]))
-            prev = e[j]
+            durs[name].append(e[j].elapsed_time(e[j + 1]))
     return durs
 
 
@@ -678,6 +676,8 @@ def main(argv=None):
                     help="drop probability on P (fa_fwd_dropout / fa_bwd_dropout); the FLOP "
                          "count is the same as without dropout")
     ap.add_argument("--cpu-baseline", default="on", choices=["on", "off"])
+    ap.add_argument("--event-every", type=int, default=4,
+                    help="time the kernels with HIP events on every N-th timed step")
     ap.add_argument("--cold-reps", type=int, default=50,
                     help="launches of each kernel timed after a 1 GiB cache-evicting write "
                          "(0: none)")
@@ -751,7 +751,8 @@ def main(argv=None):
     esize = 2 if w.dtype == "bf16" else 4
 
     wall_ms, kernel_ms, median_ms, cold_ms, props, outs = run_gpu(
-        w, inp, args.steps, args.warmup, args.prewarm_s, args.dropout, args.cold_reps)
+        w, inp, args.steps, args.warmup, args.prewarm_s, args.dropout, args.cold_reps,
+        args.event_every)
     fwd_ms = kernel_ms["fwd_bf16_kernel"]
     bwd_ms = kernel_ms.get("bwd_kernel")
     peak = PEAK_TFLOPS[w.dtype]
@@ -811,6 +812,7 @@ def main(argv=None):
         "kernel_ms_median": median_ms,
         "cold_kernel_ms": cold_ms,
         "cold_reps": args.cold_reps,
+        "event_steps": len(range(0, args.steps, max(1, args.event_every))),
         "fwd_frac_peak": tf_f / peak,
         "fwdbwd_frac_peak": tf_fb / peak,
         "peak_tflops": peak,

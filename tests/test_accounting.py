@@ -119,7 +119,7 @@ def test_pipe_metrics_formulas():
     assert sum(n.startswith("GRBM_") for n in bench.PIPE_COUNTERS) <= 2
 
 
-def test_launch_durations_chain_events():
+def test_launch_durations_of_sampled_steps():
     class Ev:
         def __init__(self, t):
             self.t = t
@@ -127,11 +127,10 @@ def test_launch_durations_chain_events():
         def elapsed_time(self, other):
             return other.t - self.t
 
-    # two steps of (fwd 2 ms, bwd 5 ms) after a 1 ms gap, then (3, 4)
-    start = Ev(0.0)
-    evs = [[Ev(3.0), Ev(8.0)], [Ev(11.0), Ev(15.0)]]
-    d = bench.launch_durations(start, evs, ("fwd", "bwd"))
-    assert d == {"fwd": [3.0, 3.0], "bwd": [5.0, 4.0]}
-    # forward-only steps: one event per step
-    d = bench.launch_durations(start, [[Ev(2.0)], [Ev(5.0)]], ("fwd",))
+    # two sampled steps: (fwd 2 ms, bwd 5 ms) and (3, 4)
+    samples = [[Ev(1.0), Ev(3.0), Ev(8.0)], [Ev(20.0), Ev(23.0), Ev(27.0)]]
+    d = bench.launch_durations(samples, ("fwd", "bwd"))
+    assert d == {"fwd": [2.0, 3.0], "bwd": [5.0, 4.0]}
+    # forward-only steps: a start and one launch
+    d = bench.launch_durations([[Ev(0.0), Ev(2.0)], [Ev(5.0), Ev(8.0)]], ("fwd",))
     assert d == {"fwd": [2.0, 3.0]}
