@@ -200,6 +200,23 @@ __device__ __forceinline__ bf16x8 words_to_bf16x8(uint32_t a, uint32_t b, uint32
 // spill the captured state to scratch memory.
 #define FA_INLINE __attribute__((always_inline))
 
+// Workgroup ids are dealt to the 8 XCDs round robin, and within an XCD to its
+// 32 CUs in order, so the k-th id of an XCD lands on CU k mod 32 in the first
+// pass.  For a list ordered heaviest first, this makes CU 0 take items 0, 32,
+// 64, ... of its XCD and CU 31 items 31, 63, 95, ...: every CU's share is
+// skewed the same way.  snake_id turns every second run of 32 ids of an XCD
+// around (items 0, 63, 64, ... on CU 0; 31, 32, 95, ... on CU 31), which
+// evens out the co-resident items of a CU.  A bijection on [0, G) that keeps
+// each id on its XCD and in its run of 32.
+__device__ __forceinline__ int snake_id(int id, int G) {
+  const int x = id & 7, k = id >> 3;
+  const int cnt = (G - x + 7) >> 3;  // ids of XCD x
+  const int r0 = k & ~31;
+  const int len = min(32, cnt - r0);
+  const int kk = ((k >> 5) & 1) ? r0 + len - 1 - (k - r0) : k;
+  return kk * 8 + x;
+}
+
 // Inclusive prefix sum over the 64 lanes of a wave.
 __device__ __forceinline__ int wave_incl_scan(int x) {
   const int lane = threadIdx.x & 63;

@@ -76,10 +76,13 @@ __global__ __launch_bounds__(64 * W) void fwd_bf16_kernel(FwdArgs a) {
   const int r = lane & 31, hl = lane >> 5;
   const int BH = a.B * a.H;
   const int nqt = (a.N + kBR - 1) / kBR;
-  const int id = blockIdx.x;
-  // Causal: the longest query tiles are dispatched first.  Consecutive ids
-  // walk the heads, so with B*H a multiple of 8 all tiles of one head land
-  // on the same XCD and share its L2.
+  // Causal: the longest query tiles are dispatched first; with four waves
+  // (two or three workgroups resident per CU) they are dealt to the CUs of
+  // an XCD in snake order, which measured 1-5 % faster there and slower for
+  // the 2- and 8-wave workgroups.  Consecutive ids walk the heads, so with
+  // B*H a multiple of 8 all tiles of one head land on the same XCD and share
+  // its L2.
+  const int id = (CAUSAL && W == 4) ? snake_id(blockIdx.x, gridDim.x) : blockIdx.x;
   const int qt = CAUSAL ? (nqt - 1 - id / BH) : (id / BH);
   const int bh = id % BH;
   const int b = bh / a.H, hh = bh % a.H;
