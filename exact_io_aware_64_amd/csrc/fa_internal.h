@@ -37,6 +37,7 @@ struct FwdArgs {
   int N;     // queries
   int Nk;    // keys
   int coff;  // causal offset Nk - N: key j is visible to query i iff j <= i + coff
+             // (the bf16 forward runs non-causal calls with coff = Nk)
   float scale;       // softmax scale
   float scale_log2;  // scale * log2(e): scores enter exp2 directly
   const int32_t* seqlens;
