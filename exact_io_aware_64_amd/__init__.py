@@ -19,6 +19,7 @@ from ._binding import (  # noqa: F401
     fa_bwd_workspace_bytes,
     fa_fwd,
     fa_fwd_dropout,
+    fa_fwd_key_groups,
     fa_fwd_qk,
     fa_fwd_tiled,
     fa_last_error,

@@ -24,7 +24,8 @@ FA_ERR_HIP = 3
 # Public entry points declared in include/fa.h.
 EXPORTED = ("fa_fwd", "fa_bwd", "fa_bwd_dq", "fa_bwd_dkdv", "fa_fwd_dropout",
             "fa_bwd_dropout", "fa_fwd_tiled", "fa_fwd_qk", "fa_bwd_qk",
-            "fa_bwd_workspace_bytes", "fa_status_string", "fa_last_error")
+            "fa_bwd_workspace_bytes", "fa_fwd_key_groups", "fa_status_string",
+            "fa_last_error")
 
 
 class FaError(RuntimeError):
@@ -78,6 +79,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                                    ctypes.c_size_t, I, I, I, I, F, I, P, P, I, F, U64, U32, P]
     lib.fa_bwd_workspace_bytes.restype = ctypes.c_size_t
     lib.fa_bwd_workspace_bytes.argtypes = [I, I, I, I, I]
+    lib.fa_fwd_key_groups.restype = I
+    lib.fa_fwd_key_groups.argtypes = [I, I, I, I, I, I, I]
     lib.fa_status_string.restype = ctypes.c_char_p
     lib.fa_status_string.argtypes = [I]
     lib.fa_last_error.restype = ctypes.c_char_p
@@ -96,6 +99,11 @@ def fa_last_error() -> str:
 
 def fa_bwd_workspace_bytes(dtype: int, B: int, H: int, N: int, d: int) -> int:
     return int(load_library().fa_bwd_workspace_bytes(dtype, B, H, N, d))
+
+
+def fa_fwd_key_groups(dtype: int, B: int, H: int, N: int, N_k: int, d: int,
+                      block_q: int = 128) -> int:
+    return int(load_library().fa_fwd_key_groups(dtype, B, H, N, N_k, d, block_q))
 
 
 # ------------------------------------------------------------ marshalling

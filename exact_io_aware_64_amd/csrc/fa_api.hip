@@ -206,6 +206,11 @@ size_t fa_bwd_workspace_bytes(fa_dtype dtype, int B, int H, int N, int d) {
   return 0;
 }
 
+int fa_fwd_key_groups(fa_dtype dtype, int B, int H, int N, int N_k, int d, int block_q) {
+  if (dtype != FA_BF16 || B <= 0 || H <= 0 || N <= 0 || N_k <= 0) return 1;
+  return fa::fwd_key_groups(B, H, N, N_k, d, block_q);
+}
+
 }  // extern "C"
 
 namespace {

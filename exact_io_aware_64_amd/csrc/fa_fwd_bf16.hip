@@ -66,8 +66,15 @@ constexpr float kSumLimit = 4096.f;    // largest partial sum the fast path acce
 // The 4-wave D = 64 kernels are held to three waves per SIMD (168 VGPRs):
 // the variants without dropout need 160-162, the dropout ones 165, which
 // measured 7-10 % faster than their 172-register, two-wave build.
-template <int W, int D, bool SEQLEN, bool BMASK, bool DROP>
-__global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu((D == 64 && W == 4) ? 3 : 1, 8))) void fwd_bf16_kernel(FwdArgs a) {
+//
+// G > 1 splits the key range of the query tile over G groups of W waves
+// (group g takes the g-th of G equal runs of the tile list, each with its
+// own K/V buffers); at the end the groups' (m, l, acc) are merged through
+// LDS by the online-softmax rescaling and group 0 writes the outputs.  It is
+// used when the grid has no more query tiles than the GPU has CUs, where a
+// single group would leave one wave per SIMD.
+template <int W, int G, int D, bool SEQLEN, bool BMASK, bool DROP>
+__global__ __launch_bounds__(64 * W * G) __attribute__((amdgpu_waves_per_eu((D == 64 && W <= 4) ? 3 : 1, 8))) void fwd_bf16_kernel(FwdArgs a) {
   static_assert(D == 32 || D == 64 || D == 128, "head dimension 32, 64 or 128");
   static_assert(!DROP || D == 64, "dropout is built for D = 64");
   constexpr int kBR = 32 * W;
@@ -75,14 +82,22 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu((D == 64
   constexpr int KS = D / 16;               // contraction steps of S^T; slots per phase
   constexpr int DB = D / 32;               // 32-row blocks of O^T
   constexpr int LEAD = KS < 4 ? KS : 4;    // slots between an operand's read and its use
-  // Two buffers, each a K tile and a V tile; separate arrays so that the
-  // copies into one buffer and the reads of the other never alias.
-  __shared__ __attribute__((aligned(16))) uint16_t s_k0[KB * kTileElems];
-  __shared__ __attribute__((aligned(16))) uint16_t s_v0[KB * kTileElems];
-  __shared__ __attribute__((aligned(16))) uint16_t s_k1[KB * kTileElems];
-  __shared__ __attribute__((aligned(16))) uint16_t s_v1[KB * kTileElems];
+  static_assert(G == 1 || (W == 4 && G <= 3), "key-range groups of 4 waves");
+  // Two buffers per group, each a K tile and a V tile; separate arrays so
+  // that the copies into one buffer and the reads of the other never alias.
+  __shared__ __attribute__((aligned(16))) uint16_t s_k0g[G][KB * kTileElems];
+  __shared__ __attribute__((aligned(16))) uint16_t s_v0g[G][KB * kTileElems];
+  __shared__ __attribute__((aligned(16))) uint16_t s_k1g[G][KB * kTileElems];
+  __shared__ __attribute__((aligned(16))) uint16_t s_v1g[G][KB * kTileElems];
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  // key-range group (uniform in a wave: read from the first lane)
+  const int g = G > 1 ? __builtin_amdgcn_readfirstlane((tid >> 6) / W) : 0;
+  const int w = G > 1 ? (tid >> 6) % W : tid >> 6;  // wave within the group
+  uint16_t* const s_k0 = s_k0g[g];
+  uint16_t* const s_v0 = s_v0g[g];
+  uint16_t* const s_k1 = s_k1g[g];
+  uint16_t* const s_v1 = s_v1g[g];
   const int r = lane & 31, hl = lane >> 5;
   const int BH = a.B * a.H;
   const int nqt = (a.N + kBR - 1) / kBR;
@@ -109,12 +124,17 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu((D == 64
   [[maybe_unused]] uint16_t* tlist = nullptr;
   if constexpr (BMASK) {
     __shared__ uint16_t s_list[kMaxListTiles];
-    __shared__ int s_scan[W];
+    __shared__ int s_scan[W * G];
     tlist = s_list;
     const int row = q0 / a.mask_block;  // the host makes the query tile divide mask_block
-    nlist = build_tile_list<64 * W>(s_list, s_scan, a.bmask + (int64_t)row * a.n_mask_k, 1,
-                                    a.n_mask_k, a.mask_block / kTile, 0, ntk);
+    nlist = build_tile_list<64 * W * G>(s_list, s_scan, a.bmask + (int64_t)row * a.n_mask_k, 1,
+                                        a.n_mask_k, a.mask_block / kTile, 0, ntk);
   }
+  // This group's run of the tile list, and the trips every group makes (the
+  // barriers of all groups have to match).
+  const int lo = G > 1 ? g * nlist / G : 0;
+  const int cnt = G > 1 ? (g + 1) * nlist / G - lo : nlist;
+  const int trips = G > 1 ? (nlist + G - 1) / G : nlist;
 
   const __amdgpu_buffer_rsrc_t rq = make_rsrc(
       (const uint16_t*)a.q + b * a.sq.b + hh * a.sq.h, slice_bytes(a.N, a.sq.s, 2, D));
@@ -311,23 +331,66 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu((D == 64
     }
   };
 
-  if (nlist > 0) stage(tile_at(0), s_k0, s_v0);
+  if (cnt > 0) stage(tile_at(lo), s_k0, s_v0);
   // Every load issued so far (Q fragment, first tile) is complete here;
   // saying so also keeps the loop's wait counts from covering them.
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
   // Two tiles per trip so that each buffer is a fixed array.
-  for (int it = 0; it < nlist; it += 2) {
-    if (it + 1 < nlist) stage(tile_at(it + 1), s_k1, s_v1);
-    compute(it, s_k0, s_v0);
+  for (int it = 0; it < trips; it += 2) {
+    if (it + 1 < cnt) stage(tile_at(lo + it + 1), s_k1, s_v1);
+    if (G == 1 || it < cnt) compute(lo + it, s_k0, s_v0);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    if (it + 1 >= nlist) break;
-    if (it + 2 < nlist) stage(tile_at(it + 2), s_k0, s_v0);
-    compute(it + 1, s_k1, s_v1);
+    if (it + 1 >= trips) break;
+    if (it + 2 < cnt) stage(tile_at(lo + it + 2), s_k0, s_v0);
+    if (G == 1 || it + 1 < cnt) compute(lo + it + 1, s_k1, s_v1);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
+  }
+
+  if constexpr (G > 1) {
+    // Groups 1 .. G-1 hand their state to group 0 one at a time, through the
+    // K/V buffers (free: every read of them completed before the last
+    // barrier).  Per wave and lane: acc block db in s_k0g (db < max(1, DB/2))
+    // or s_v0g, then m and l in s_k1g, each float at [element][wave][lane].
+    float* const xo0 = reinterpret_cast<float*>(&s_k0g[0][0]);
+    float* const xo1 = reinterpret_cast<float*>(&s_v0g[0][0]);
+    float* const xml = reinterpret_cast<float*>(&s_k1g[0][0]);
+    constexpr int kHalf = DB > 1 ? DB / 2 : 1;  // acc blocks in xo0
+    const int slot = w * 64 + lane;            // this lane's column
+    auto at = [&](int db, int e) FA_INLINE -> float* {
+      float* base = db < kHalf ? xo0 : xo1;
+      return base + ((db % kHalf) * 16 + e) * (64 * W) + slot;
+    };
+#pragma unroll
+    for (int j = 1; j < G; ++j) {
+      if (g == j) {
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) *at(db, e) = o[db][e];
+        xml[slot] = m;
+        xml[64 * W + slot] = l;
+      }
+      __syncthreads();
+      if (g == 0) {
+        const float mj = xml[slot], lj = xml[64 * W + slot];
+        const float m_new = fmaxf(m, mj);
+        // a dead side (m = -inf, l = 0, acc = 0) gets weight 0, or 1 if both are
+        const float a0 = (m == m_new) ? 1.f : fast_exp2(m - m_new);
+        const float aj = (mj == m_new) ? 1.f : fast_exp2(mj - m_new);
+        l = l * a0 + lj * aj;
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) o[db][e] = o[db][e] * a0 + *at(db, e) * aj;
+        m = m_new;
+      }
+      __syncthreads();
+    }
+    if (g != 0) return;
   }
 
   const float lt = half_sum(l);
@@ -350,39 +413,67 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu((D == 64
   }
 }
 
-template <int W, int HD, bool S, bool M, bool D>
+
+template <int W, int G, int HD, bool S, bool M, bool D>
 hipError_t launch(const FwdArgs& a, hipStream_t stream) {
   const int nqt = (a.N + 32 * W - 1) / (32 * W);
-  dim3 grid((unsigned)(nqt * a.B * a.H)), block(64 * W);
+  dim3 grid((unsigned)(nqt * a.B * a.H)), block(64 * W * G);
   FwdArgs copy = a;
   void* args[] = {&copy};
-  return hipLaunchKernel((const void*)&fwd_bf16_kernel<W, HD, S, M, D>, grid, block, args, 0,
-                         stream);
+  return hipLaunchKernel((const void*)&fwd_bf16_kernel<W, G, HD, S, M, D>, grid, block, args,
+                         0, stream);
+}
+
+template <int W, int G, int HD, bool D>
+hipError_t dispatch_masks(const FwdArgs& c, hipStream_t stream) {
+  const bool s = c.seqlens != nullptr, m = c.bmask != nullptr;
+  if (s)
+    return m ? launch<W, G, HD, true, true, D>(c, stream)
+             : launch<W, G, HD, true, false, D>(c, stream);
+  return m ? launch<W, G, HD, false, true, D>(c, stream)
+           : launch<W, G, HD, false, false, D>(c, stream);
 }
 
 // Non-causal calls run with the causal offset Nk, which makes every key
 // visible to every query.
-template <int W, int HD, bool D>
+template <int W, int HD, bool D, int GS = 1>
 hipError_t dispatch(const FwdArgs& a, bool causal, hipStream_t stream) {
   FwdArgs c = a;
   if (!causal) c.coff = a.Nk;
-  const bool s = a.seqlens != nullptr, m = a.bmask != nullptr;
-  if (s)
-    return m ? launch<W, HD, true, true, D>(c, stream) : launch<W, HD, true, false, D>(c, stream);
-  return m ? launch<W, HD, false, true, D>(c, stream) : launch<W, HD, false, false, D>(c, stream);
+  if constexpr (GS > 1) {
+    if (fwd_key_groups(a.B, a.H, a.N, a.Nk, HD, 32 * W) > 1)
+      return dispatch_masks<W, GS, HD, D>(c, stream);
+  }
+  return dispatch_masks<W, 1, HD, D>(c, stream);
 }
 
 }  // namespace
 
+// CUs of the current device (0 if it cannot be read: no split then).
+static int cu_count() {
+  int dev = 0, n = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return 0;
+  return n;
+}
+
+int fwd_key_groups(int B, int H, int N, int Nk, int d, int block_q) {
+  if (block_q != 128 || Nk < 1024) return 1;
+  const long items = (long)((N + 127) / 128) * B * H;
+  if (items > cu_count()) return 1;
+  return d == 128 ? 2 : 3;
+}
+
 hipError_t launch_fwd_bf16(const FwdArgs& a, bool causal, int block_q, int d,
                            hipStream_t stream) {
   // the host allows d != 64 only without dropout and with block_q = 128
-  if (d == 32) return dispatch<4, 32, false>(a, causal, stream);
-  if (d == 128) return dispatch<4, 128, false>(a, causal, stream);
-  if (a.drop.t < 256) return dispatch<4, 64, true>(a, causal, stream);  // block_q == 128
+  if (d == 32) return dispatch<4, 32, false, 3>(a, causal, stream);
+  if (d == 128) return dispatch<4, 128, false, 2>(a, causal, stream);
+  if (a.drop.t < 256) return dispatch<4, 64, true, 3>(a, causal, stream);  // block_q == 128
   if (block_q == 64) return dispatch<2, 64, false>(a, causal, stream);
   if (block_q == 256) return dispatch<8, 64, false>(a, causal, stream);
-  return dispatch<4, 64, false>(a, causal, stream);
+  return dispatch<4, 64, false, 3>(a, causal, stream);
 }
 
 }  // namespace fa

@@ -80,6 +80,10 @@ constexpr int kPhaseDKDV = 2;
 // d: head dimension, 32, 64 or 128 (64 with dropout or block_q != 128).
 hipError_t launch_fwd_bf16(const FwdArgs& a, bool causal, int block_q, int d,
                            hipStream_t stream);
+// Wave groups per query tile that launch_fwd_bf16 splits the key range over
+// on the current device: 3 (2 for d = 128) when block_q is 128, the keys span
+// at least 1024 rows and the grid holds at most one query tile per CU, else 1.
+int fwd_key_groups(int B, int H, int N, int Nk, int d, int block_q);
 // d: head dimension, 32, 64 or 128 (64 with dropout).
 hipError_t launch_bwd_bf16(const BwdArgs& a, bool causal, int phases, int d,
                            hipStream_t stream);

@@ -113,6 +113,26 @@ fa_status fa_fwd(fa_dtype dtype,
 size_t fa_bwd_workspace_bytes(fa_dtype dtype, int B, int H, int N, int d);
 
 /*
+ * fa_fwd_key_groups -- how many groups of waves a forward call with these
+ * sizes splits each query tile's key range over, on the current device.  A
+ * query tile is one workgroup; when the grid holds no more of them than the
+ * device has CUs, each workgroup would run one wave per SIMD, so the bf16
+ * forward with block_q = 128 and N_k >= 1024 keys gives each query tile 3
+ * groups of 4 waves (2 for d = 128), each taking an equal run of the visible
+ * key tiles with its own LDS buffers, and merges their partial results
+ * (running maximum, sum and unnormalised output) with the online-softmax
+ * rescaling (researchpapers.dev explainer, "tiling and recomputation").
+ * The outputs are the same function of the inputs either way; only the
+ * order of the floating-point sums differs.
+ *
+ *   dtype, B, H, N, N_k, d, block_q  as for fa_fwd_qk / fa_fwd_tiled
+ *                                    (block_q = 128 for fa_fwd).
+ * Returns the group count (1 = no split); it reads the device's CU count and
+ * returns 1 if that fails.  No device memory is touched.
+ */
+int fa_fwd_key_groups(fa_dtype dtype, int B, int H, int N, int N_k, int d, int block_q);
+
+/*
  * fa_bwd -- backward pass: writes dQ, dK and dV in full (zeros for keys that
  * no query sees, e.g. keys past seqlens_k).  The scores and probabilities are
  * recomputed tile by tile from q, k and the forward's lse; nothing of size

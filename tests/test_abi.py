@@ -49,6 +49,14 @@ def test_workspace_bytes():
     assert fa.fa_bwd_workspace_bytes(0, 0, 1, 3, 64) == 0
 
 
+def test_key_groups_without_device_query():
+    # cases decided before the device's CU count is read: no split
+    assert fa.fa_fwd_key_groups(fa.FA_F32, 1, 1, 4096, 4096, 64, 128) == 1
+    assert fa.fa_fwd_key_groups(fa.FA_BF16, 1, 1, 4096, 4096, 64, 64) == 1
+    assert fa.fa_fwd_key_groups(fa.FA_BF16, 1, 1, 4096, 1023, 64, 128) == 1
+    assert fa.fa_fwd_key_groups(fa.FA_BF16, 0, 1, 4096, 4096, 64, 128) == 1
+
+
 # Fake, suitably aligned device addresses: every call below must be rejected
 # by host-side validation, so they are never dereferenced.
 A = 0x10000
