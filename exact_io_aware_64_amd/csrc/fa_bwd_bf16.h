@@ -171,7 +171,12 @@ __device__ __forceinline__ void dq_role(const BwdArgs& a, int item, uint16_t* s_
     constexpr bool MASK = decltype(mask_c)::value;
     constexpr int kLead = 4;
     constexpr int NS = 6 * KS;
-    f32x16 st[2] = {zero16(), zero16()}, dpt[2] = {zero16(), zero16()};
+    // Without dropout dP^T starts at -D, so the MFMAs leave dP - D.
+    f32x16 st[2] = {zero16(), zero16()}, dpt[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) dpt[kb][e] = DROP ? 0.f : -Dq;
     uint32_t pkd[4][4];  // bf16 pairs of dS per step
     bf16x8 opa[NS];
     [[maybe_unused]] DropBlock zb[2];  // keep bytes of the two halves
@@ -204,7 +209,7 @@ __device__ __forceinline__ void dq_role(const BwdArgs& a, int item, uint16_t* s_
           const float dpe = drop_keep(zb[kb], e, a.drop.t) ? a.drop.scale * dpt[kb][e] : 0.f;
           ds[x] = p * (dpe - Dq);
         } else {
-          ds[x] = p * (dpt[kb][e] - Dq);
+          ds[x] = p * dpt[kb][e];
         }
       }
       pkd[2 * kb + (ch >> 2)][ch & 3] = pack2(ds[0], ds[1]);
