@@ -372,8 +372,9 @@ def io_sweep_run(ns, bqs, reps: int) -> int:
     """Dense bf16 forward (B=1, H=16, d=64) for every N and query-tile height:
     one untimed and `reps` event-timed fa_fwd_tiled launches each, in a fixed
     order, one JSON line per configuration.  Under rocprofv3 --pmc the
-    dispatches are told apart by workgroup size (block_q / 32 waves) and grid
-    size (N / block_q * H workgroups)."""
+    dispatches are told apart by workgroup size (block_q / 32 waves per group
+    of waves, times the key-range groups) and grid size (N / block_q * H
+    workgroups), both recorded in the line."""
     import torch
     import exact_io_aware_64_amd as fa
     dev = torch.device("cuda:0")
@@ -398,10 +399,12 @@ def io_sweep_run(ns, bqs, reps: int) -> int:
             torch.cuda.synchronize()
             ms = float(np.median([a.elapsed_time(b) for a, b in evs]))
             flops = 4.0 * SWEEP_D * N * N * SWEEP_H * SWEEP_B
+            groups = fa.fa_fwd_key_groups(fa.FA_BF16, SWEEP_B, SWEEP_H, N, N, SWEEP_D, bq)
             print(json.dumps(dict(mode="io-sweep", N=N, block_q=bq, ms=ms,
                                   tflops=flops / (ms * 1e-3) / 1e12,
                                   workgroups=-(-N // bq) * SWEEP_H * SWEEP_B,
-                                  threads=2 * bq, **sweep_model(N, bq))), flush=True)
+                                  threads=2 * bq * groups, key_groups=groups,
+                                  **sweep_model(N, bq))), flush=True)
     return 0
 
 
@@ -420,11 +423,11 @@ def _per_dispatch(path: str, counters):
     return out
 
 
-def _sweep_config(d):
-    """(N, block_q) of a sweep dispatch from its launch shape."""
-    bq = d["wg"] // 2
-    nwg = d["grid"] // d["wg"]
-    return (nwg // (SWEEP_H * SWEEP_B)) * bq, bq
+def _sweep_config(d, shapes):
+    """(N, block_q) of a sweep dispatch from its launch shape: `shapes` maps
+    (workgroups, threads per workgroup) of each configuration the sweep log
+    records to (N, block_q)."""
+    return shapes[(d["grid"] // d["wg"], d["wg"])]
 
 
 def io_sweep_summary(fetch_csv, write_csv, l2_csv, cfetch_csv, cwrite_csv, cl2_csv, log,
@@ -437,21 +440,22 @@ def io_sweep_summary(fetch_csv, write_csv, l2_csv, cfetch_csv, cwrite_csv, cl2_c
     f_fetch = copy_bytes / (copy_max(cfetch_csv, "FETCH_SIZE") * 1024.0)
     f_write = copy_bytes / (copy_max(cwrite_csv, "WRITE_SIZE") * 1024.0)
     f_sect = copy_bytes / copy_max(cl2_csv, "TCC_READ_SECTORS_sum")
+    timing, shapes = {}, {}
+    with open(log) as fh:
+        for line in fh:
+            if line.startswith("{") and '"io-sweep"' in line:
+                r = json.loads(line)
+                timing[(r["N"], r["block_q"])] = r
+                shapes[(r["workgroups"], r["threads"])] = (r["N"], r["block_q"])
     meas = {}
     for path, counters in ((fetch_csv, ("FETCH_SIZE",)), (write_csv, ("WRITE_SIZE",)),
                            (l2_csv, ("TCC_READ_SECTORS_sum", "TCC_HIT_sum", "TCC_MISS_sum"))):
         for d in _per_dispatch(path, counters).values():
             if d["kernel"] != "fwd_bf16_kernel":
                 continue
-            acc = meas.setdefault(_sweep_config(d), {})
+            acc = meas.setdefault(_sweep_config(d, shapes), {})
             for c in counters:
                 acc.setdefault(c, []).append(d.get(c, 0.0))
-    timing = {}
-    with open(log) as fh:
-        for line in fh:
-            if line.startswith("{") and '"io-sweep"' in line:
-                r = json.loads(line)
-                timing[(r["N"], r["block_q"])] = r
     rows = []
     for (N, bq) in sorted(meas):
         m = {c: float(np.mean(v)) for c, v in meas[(N, bq)].items()}
@@ -461,7 +465,8 @@ def io_sweep_summary(fetch_csv, write_csv, l2_csv, cfetch_csv, cwrite_csv, cl2_c
         l2 = m["TCC_READ_SECTORS_sum"] * f_sect
         hit = m["TCC_HIT_sum"] / max(1.0, m["TCC_HIT_sum"] + m["TCC_MISS_sum"])
         t = timing.get((N, bq), {})
-        rows.append((N, bq, mod["compulsory"] / 1e6, (mod["q_read"] + mod["kv_streamed"]) / 1e6,
+        rows.append((N, bq, t.get("key_groups", 1), mod["compulsory"] / 1e6,
+                     (mod["q_read"] + mod["kv_streamed"]) / 1e6,
                      l2 / 1e6, fetch / 1e6, write / 1e6, fetch / mod["compulsory_read"], hit,
                      t.get("ms", float("nan")) * 1e3, t.get("tflops", float("nan"))))
     out = ["# IO sweep: dense bf16 forward, B=1 H=16 d=64, query tile height x N", "",
@@ -473,12 +478,15 @@ def io_sweep_summary(fetch_csv, write_csv, l2_csv, cfetch_csv, cwrite_csv, cl2_c
            "read from memory, Infinity Cache hits included), *write* = WRITE_SIZE; each "
            f"scaled by the same counter over a {copy_bytes >> 20} MiB device copy "
            f"(factors: sectors x {f_sect:.2f} B, fetch x {f_fetch:.3f}, write x {f_write:.3f}). "
-           "Time: median of event-timed launches in the same run.", "",
-           "| N | Br | compulsory MB | streamed MB (model) | L2 read MB | fetch MB | write MB "
-           "| fetch / compulsory read | L2 hit rate | us | TFLOP/s |",
-           "|---|---|---|---|---|---|---|---|---|---|---|"]
+           "Time: median of event-timed launches in the same run.  Groups: key-range groups "
+           "per query tile (3 when the grid has no more query tiles than the GPU has CUs; "
+           "each still streams its share of K/V once per query tile, so the model holds).",
+           "",
+           "| N | Br | groups | compulsory MB | streamed MB (model) | L2 read MB | fetch MB "
+           "| write MB | fetch / compulsory read | L2 hit rate | us | TFLOP/s |",
+           "|---|---|---|---|---|---|---|---|---|---|---|---|"]
     for r in rows:
-        out.append("| %d | %d | %.1f | %.1f | %.1f | %.1f | %.1f | %.2f | %.3f | %.1f | %.0f |"
+        out.append("| %d | %d | %d | %.1f | %.1f | %.1f | %.1f | %.1f | %.2f | %.3f | %.1f | %.0f |"
                    % r)
     return "\n".join(out) + "\n"
 
