@@ -65,11 +65,19 @@ def test_io_sweep_model_and_dispatch_mapping():
     assert m["kv_streamed"] == 16 * 8 * 2 * t          # 8 query tiles of 128 rows
     assert bench.sweep_model(1024, 64)["kv_streamed"] == 2 * m["kv_streamed"]
     assert bench.sweep_model(1024, 256)["kv_streamed"] * 2 == m["kv_streamed"]
-    for N in bench.SWEEP_N:
-        for bq in bench.SWEEP_BQ:
-            threads = 2 * bq                              # bq / 32 waves of 64 lanes
-            grid = (N // bq) * bench.SWEEP_H * threads    # Grid_Size counts work-items
-            assert bench._sweep_config(dict(wg=threads, grid=grid)) == (N, bq)
+    # every configuration's launch shape is distinct, whether or not the
+    # 128-row tiles split their keys over 3 groups of waves
+    for groups128 in (1, 3):
+        shapes, launches = {}, []
+        for N in bench.SWEEP_N:
+            for bq in bench.SWEEP_BQ:
+                threads = 2 * bq * (groups128 if bq == 128 else 1)  # 64 lanes per wave
+                wgs = (N // bq) * bench.SWEEP_H
+                assert (wgs, threads) not in shapes
+                shapes[(wgs, threads)] = (N, bq)
+                launches.append((dict(wg=threads, grid=wgs * threads), (N, bq)))
+        for d, cfg in launches:                       # Grid_Size counts work-items
+            assert bench._sweep_config(d, shapes) == cfg
 
 
 @pytest.mark.parametrize("N,Nk,causal,seqlens,p", [
