@@ -129,3 +129,25 @@ def test_split_matches_unsplit_grid():
         assert maxabs(to_np(o), O) <= TOL["bf16"]["O"]
         assert maxabs(to_np(lse), L) <= TOL["bf16"]["L"]
     assert maxabs(to_np(l_big[:, :2]), to_np(l_two)) <= 1e-5
+
+
+def test_split_strided_layout_and_edge_lengths():
+    """[B, N, H, d] storage (strided heads) and key lengths 0, 1 and N_k."""
+    import exact_io_aware_64_amd as fa
+    c = _case(3, 2, 1100, 1100, seed=41)
+    c["seqlens"] = np.array([0, 1, 1100], np.int32)
+    assert _groups(c) == 3
+    tol = TOL["bf16"]
+    q, k, v, do = (to_dev(c[n], "bf16", layout="bshd") for n in ("q", "k", "v", "do"))
+    assert not q.is_contiguous()
+    sl = opt_dev(c["seqlens"])
+    kw = dict(scale=0.125, causal=False, seqlens_k=sl)
+    o, lse = fa.forward(q, k, v, **kw)
+    O, L = ref.forward(c["q"], c["k"], c["v"], 0.125, seqlens=c["seqlens"])
+    assert np.array_equal(np.isinf(to_np(lse)), np.isinf(L)), "dead rows differ"
+    assert excess_over(to_np(o), O, tol["O"]) <= 0
+    assert maxabs(to_np(lse), L) <= tol["L"]
+    dq, dk, dv = fa.backward(q, k, v, o, do, lse, **kw)
+    g = ref.backward(c["q"], c["k"], c["v"], c["do"], 0.125, seqlens=c["seqlens"])
+    for a, b in zip((dq, dk, dv), g):
+        assert relfro(to_np(a), b) <= tol["G"]
