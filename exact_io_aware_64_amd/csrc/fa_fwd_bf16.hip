@@ -65,7 +65,8 @@ constexpr float kSumLimit = 4096.f;    // largest partial sum the fast path acce
 // conflict-free pattern of the 64-column tile.
 // The 4-wave D = 64 kernels are held to three waves per SIMD (168 VGPRs):
 // the variants without dropout need 160-162, the dropout ones 165, which
-// measured 7-10 % faster than their 172-register, two-wave build.
+// measured 7-10 % faster than their 172-register, two-wave build.  So are the
+// 2-wave ones without a block mask (with it, LDS allows fewer workgroups).
 //
 // G > 1 splits the key range of the query tile over G groups of W waves
 // (group g takes the g-th of G equal runs of the tile list, each with its
@@ -74,7 +75,7 @@ constexpr float kSumLimit = 4096.f;    // largest partial sum the fast path acce
 // used when the grid has no more query tiles than the GPU has CUs, where a
 // single group would leave one wave per SIMD.
 template <int W, int G, int D, bool SEQLEN, bool BMASK, bool DROP>
-__global__ __launch_bounds__(64 * W * G) __attribute__((amdgpu_waves_per_eu((D == 64 && W <= 4) ? 3 : 1, 8))) void fwd_bf16_kernel(FwdArgs a) {
+__global__ __launch_bounds__(64 * W * G) __attribute__((amdgpu_waves_per_eu((D == 64 && (W == 4 || (W == 2 && !BMASK))) ? 3 : 1, 8))) void fwd_bf16_kernel(FwdArgs a) {
   static_assert(D == 32 || D == 64 || D == 128, "head dimension 32, 64 or 128");
   static_assert(!DROP || D == 64, "dropout is built for D = 64");
   constexpr int kBR = 32 * W;
