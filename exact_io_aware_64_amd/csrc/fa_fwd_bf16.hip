@@ -56,6 +56,10 @@
 namespace fa {
 namespace {
 
+// Key-range groups of a split query tile: as many 4-wave groups as the
+// registers allow at three (d <= 64) or two (d = 128) waves per SIMD.
+constexpr int groups_for_d(int d) { return d == 128 ? 2 : 3; }
+
 constexpr float kSumLimit = 4096.f;    // largest partial sum the fast path accepts
 
 // W waves, 32 W query rows per workgroup; head dimension D = 32, 64 or 128.
@@ -360,6 +364,9 @@ __global__ __launch_bounds__(64 * W * G) __attribute__((amdgpu_waves_per_eu((D =
     float* const xo1 = reinterpret_cast<float*>(&s_v0g[0][0]);
     float* const xml = reinterpret_cast<float*>(&s_k1g[0][0]);
     constexpr int kHalf = DB > 1 ? DB / 2 : 1;  // acc blocks in xo0
+    constexpr int kBufBytes = G * KB * kTileElems * 2;  // bytes of each buffer array
+    static_assert(kHalf * 16 * 64 * W * 4 <= kBufBytes, "acc blocks fit the buffers");
+    static_assert(2 * 64 * W * 4 <= kBufBytes, "m and l fit a buffer");
     const int slot = w * 64 + lane;            // this lane's column
     auto at = [&](int db, int e) FA_INLINE -> float* {
       float* base = db < kHalf ? xo0 : xo1;
@@ -414,7 +421,6 @@ __global__ __launch_bounds__(64 * W * G) __attribute__((amdgpu_waves_per_eu((D =
   }
 }
 
-
 template <int W, int G, int HD, bool S, bool M, bool D>
 hipError_t launch(const FwdArgs& a, hipStream_t stream) {
   const int nqt = (a.N + 32 * W - 1) / (32 * W);
@@ -463,18 +469,19 @@ int fwd_key_groups(int B, int H, int N, int Nk, int d, int block_q) {
   if (block_q != 128 || Nk < 1024) return 1;
   const long items = (long)((N + 127) / 128) * B * H;
   if (items > cu_count()) return 1;
-  return d == 128 ? 2 : 3;
+  return groups_for_d(d);
 }
 
 hipError_t launch_fwd_bf16(const FwdArgs& a, bool causal, int block_q, int d,
                            hipStream_t stream) {
   // the host allows d != 64 only without dropout and with block_q = 128
-  if (d == 32) return dispatch<4, 32, false, 3>(a, causal, stream);
-  if (d == 128) return dispatch<4, 128, false, 2>(a, causal, stream);
-  if (a.drop.t < 256) return dispatch<4, 64, true, 3>(a, causal, stream);  // block_q == 128
+  if (d == 32) return dispatch<4, 32, false, groups_for_d(32)>(a, causal, stream);
+  if (d == 128) return dispatch<4, 128, false, groups_for_d(128)>(a, causal, stream);
+  if (a.drop.t < 256)  // block_q == 128
+    return dispatch<4, 64, true, groups_for_d(64)>(a, causal, stream);
   if (block_q == 64) return dispatch<2, 64, false>(a, causal, stream);
   if (block_q == 256) return dispatch<8, 64, false>(a, causal, stream);
-  return dispatch<4, 64, false, 3>(a, causal, stream);
+  return dispatch<4, 64, false, groups_for_d(64)>(a, causal, stream);
 }
 
 }  // namespace fa
