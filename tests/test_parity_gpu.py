@@ -311,3 +311,13 @@ def test_memory_linear_in_N():
         assert peaks[N] <= 1.1 * expect + (4 << 20), (N, peaks[N], expect)
         del q, k, v, do, o, lse, dq, dk, dv, bm, case
     _say(f"[memory] peaks {peaks}")
+
+
+@pytest.mark.parametrize("B,H", [(5, 8), (3, 8), (2, 12), (3, 5)])
+def test_noncausal_head_groups(B, H):
+    """Non-causal backward grids take each XCD's heads (B*H / 8 of them when
+    B*H is a multiple of 8) in groups of four: 5, 3 and 3 heads per XCD give
+    a short last group or a single one; B*H = 15 takes the plain order."""
+    case = wl.random_case(B, H, 300, 64, seed=B * 100 + H, causal=False, seqlens="random",
+                          block_keep_p=0.7)
+    check_full(case, tag=f"non-causal head groups B={B} H={H}")
