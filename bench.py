@@ -761,6 +761,9 @@ def main(argv=None):
     wall_ms, kernel_ms, median_ms, cold_ms, props, outs = run_gpu(
         w, inp, args.steps, args.warmup, args.prewarm_s, args.dropout, args.cold_reps,
         args.event_every)
+    import exact_io_aware_64_amd as fa
+    key_groups = fa.fa_fwd_key_groups(fa.FA_BF16 if w.dtype == "bf16" else fa.FA_F32, w.B, w.H,
+                                      w.N, w.n_keys, w.d, 128)
     fwd_ms = kernel_ms["fwd_bf16_kernel"]
     bwd_ms = kernel_ms.get("bwd_kernel")
     peak = PEAK_TFLOPS[w.dtype]
@@ -811,7 +814,8 @@ def main(argv=None):
         "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "N_k": w.n_keys, "d": w.d,
                    "causal": w.causal, "key_padding": inp["seqlens"] is not None,
                    "block_sparse": inp["block_mask"] is not None, "pairs": pairs,
-                   "dropout_p": args.dropout, "step": "fwd+bwd" if w.backward else "fwd"},
+                   "dropout_p": args.dropout, "step": "fwd+bwd" if w.backward else "fwd",
+                   "fwd_key_groups": key_groups},
         "fwd_tflops": tf_f,
         "bwd_tflops": tf_b,
         "fwd_ms": fwd_ms,

@@ -49,6 +49,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     if not os.path.exists(path):
         raise RuntimeError(
             f"{path} not found: build it first (python -m exact_io_aware_64_amd.build)")
+    # torch brings its own HIP runtime; it has to be loaded first so that the
+    # library binds to that one (loaded the other way round, the two runtimes
+    # both claim the device and the first launch finds none).
+    import torch  # noqa: F401
     lib = ctypes.CDLL(path)
     P, S, I, F = ctypes.c_void_p, fa_strides, ctypes.c_int, ctypes.c_float
     lib.fa_fwd.restype = I
