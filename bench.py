@@ -57,7 +57,7 @@ FLUSH_BYTES = 1 << 30   # cold-cache runs: larger than L2 (8 x 4 MB) + Infinity 
 PIPE_COUNTERS = ("SQ_VALU_MFMA_BUSY_CYCLES", "SQ_ACTIVE_INST_VALU", "SQ_INSTS_VALU_TRANS_F32",
                  "SQ_INSTS_MFMA", "SQ_LDS_BANK_CONFLICT", "SQ_LDS_IDX_ACTIVE",
                  "SQ_BUSY_CU_CYCLES", "GRBM_GUI_ACTIVE")
-DEFAULT_WORKLOAD = "gpt2s_causal_b8h12n1024"
+DEFAULT_WORKLOAD = "blocksparse_b1h8n65536"
 
 
 # --------------------------------------------------------------- accounting
@@ -132,25 +132,26 @@ def measure_key(workload: str, dropout_p: float) -> str:
 
 
 def run_gpu(w: wl.Workload, inp: dict, steps: int, warmup: int, prewarm_s: float = 1.0,
-            dropout_p: float = 0.0, cold_reps: int = 0, event_every: int = 4):
+            dropout_p: float = 0.0, cold_reps: int = 0, event_reps: int = 50):
     """Times `steps` steps after `warmup` untimed ones.  One step is fa_fwd
     then fa_bwd (fa_fwd alone for a forward-only workload), each a single
-    kernel launch on the current stream; HIP
-    events recorded on that stream around the launches give each kernel's
-    device time, and the wall clock around the whole timed region gives the
-    step time.  Every `event_every`-th timed step carries the events (one
-    before its first launch and one after each launch); each event packet
-    costs the stream a few microseconds, so timing every step would slow the
-    step it measures.
+    kernel launch on the current stream; the wall clock around the timed
+    steps (synchronised on both sides) gives the step time.
 
     Before the warmup steps the step runs untimed for `prewarm_s` seconds of
     wall time: an idle MI355X takes a few milliseconds of sustained load to
     raise its clocks, and a short warmup would otherwise time the ramp.
 
-    Then, outside the timed region, `cold_reps` launches of each kernel are
-    timed one by one, each right after a FLUSH_BYTES write on the same stream
-    (the kernel then starts with nothing of its inputs in L2 or the Infinity
-    Cache); their medians are returned as cold_ms."""
+    Each kernel's device time comes from `event_reps` further steps, run
+    after the timed ones and outside their wall clock, with a HIP event
+    recorded on the launch stream before the step's first launch and after
+    each launch (event packets cost the stream a few microseconds, so they
+    stay out of the timed steps).
+
+    Then `cold_reps` launches of each kernel are timed one by one, each right
+    after a FLUSH_BYTES write on the same stream (the kernel then starts with
+    nothing of its inputs in L2 or the Infinity Cache); their medians are
+    returned as cold_ms."""
     import torch
     import exact_io_aware_64_amd as fa
 
@@ -192,16 +193,18 @@ def run_gpu(w: wl.Workload, inp: dict, steps: int, warmup: int, prewarm_s: float
         torch.cuda.synchronize()
     for _ in range(warmup):
         step()
-    every = max(1, event_every)
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(kernels) + 1)]
-           if i % every == 0 else None for i in range(steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3 / steps
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(kernels) + 1)]
+           for _ in range(max(1, event_reps))]
     for e in evs:
         step(e)
     torch.cuda.synchronize()
-    wall_ms = (time.perf_counter() - t0) * 1e3 / steps
-    durs = launch_durations([e for e in evs if e is not None], kernels)
+    durs = launch_durations(evs, kernels)
     kernel_ms = {name: float(np.mean(d)) for name, d in durs.items()}
     median_ms = {name: float(np.median(d)) for name, d in durs.items()}
     cold_ms = None
@@ -220,8 +223,22 @@ def run_gpu(w: wl.Workload, inp: dict, steps: int, warmup: int, prewarm_s: float
         cold_ms = {name: float(np.median([e[2 * i].elapsed_time(e[2 * i + 1]) for e in cev]))
                    for i, name in enumerate(kernels)}
         del flush
+    # the same outputs again (the last launches wrote them), and for sampled
+    # workloads the backward pass rerun with dO kept on the sampled rows only
+    # (its dK, dV are the oracle's restricted gradients)
+    restricted = None
+    if bwd is not None and inp.get("rows") is not None:
+        rows = torch.from_numpy(inp["rows"]).to(dev)
+        do_r = torch.zeros_like(do)
+        idx = rows[..., None].expand(-1, -1, -1, do.shape[-1])
+        do_r.scatter_(2, idx, do.gather(2, idx))
+        dq_r, dk_r, dv_r = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+        fa.prepare_bwd(q, k, v, o, do_r, lse, dq_r, dk_r, dv_r, **kw)()
+        torch.cuda.synchronize()
+        restricted = dict(dk=dk_r, dv=dv_r)
+        del do_r, dq_r
     props = torch.cuda.get_device_properties(dev)
-    outs = dict(o=o, lse=lse, dq=dq, dk=dk, dv=dv)
+    outs = dict(o=o, lse=lse, dq=dq, dk=dk, dv=dv, restricted=restricted)
     return wall_ms, kernel_ms, median_ms, cold_ms, props, outs
 
 
@@ -259,14 +276,44 @@ def host_info() -> dict:
     return dict(cpu=model, blas=blas)
 
 
+def sampled_pairs(rows, N: int, causal: bool, seqlens, block_mask, mask_block: int = 128,
+                  Nk=None) -> int:
+    """Visible (query, key) pairs of the query rows ``rows`` (int ``[B, H, R]``),
+    summed over batch and heads: N queries, Nk keys (default N), causal key j
+    visible to query i iff j <= i + Nk - N."""
+    Nk = N if Nk is None else Nk
+    rows = np.asarray(rows, dtype=np.int64)
+    B = rows.shape[0]
+    total = 0
+    for b in range(B):
+        L = Nk if seqlens is None else int(min(max(int(seqlens[b]), 0), Nk))
+        r = rows[b].reshape(-1)
+        lim = np.full(r.shape, L, dtype=np.int64)
+        if causal:
+            lim = np.minimum(lim, r + 1 + Nk - N)
+        lim = np.maximum(lim, 0)
+        if block_mask is None:
+            total += int(lim.sum())
+            continue
+        bm = np.asarray(block_mask).astype(bool)
+        c0 = np.arange(bm.shape[1], dtype=np.int64) * mask_block
+        over = np.clip(np.minimum(c0[None, :] + mask_block, lim[:, None]) - c0[None, :], 0, None)
+        total += int((bm[r // mask_block] * over).sum())
+    return total
+
+
 def cpu_baseline(w: wl.Workload, inp: dict, outs: dict, flops_fb: float,
                  budget_s: float = 10.0, dropout_p: float = 0.0):
     """The fp64 oracle as it stands, on the host cores, on the same inputs.
 
-    Sample: whole (batch, head) slices of the workload -- all heads when one
-    pass fits the budget, else the first heads -- repeated until about
-    ``budget_s`` seconds of CPU work; the value is scaled by the FLOPs of what
-    was computed."""
+    Sample: for workloads that name sampled query rows (the 16K and 64K
+    ones), those rows of the first heads -- the oracle's forward and
+    backward restricted to them (O, L, dQ of the rows; dK, dV of the problem
+    with dO kept on the rows only) -- else whole (batch, head) slices; all
+    heads when one pass fits the budget, repeated until about ``budget_s``
+    seconds of CPU work.  The value is the visible-pair FLOPs of what was
+    computed over the time taken; the full-problem time at that rate is an
+    extrapolation unless the sample was the whole workload."""
     from oracle import attention_ref as ref
     from oracle import dropout_ref as dref
     try:
@@ -277,18 +324,29 @@ def cpu_baseline(w: wl.Workload, inp: dict, outs: dict, flops_fb: float,
     args = dict(causal=w.causal, seqlens=inp["seqlens"], block_mask=inp["block_mask"],
                 mask_block=128)
     H = w.H
+    rows = inp.get("rows")
+    sampled = rows is not None
     sub = lambda x, hs: x[:, :hs]  # noqa: E731
+    per_pair = 4.0 * w.d + (10.0 * w.d if w.backward else 0.0)
 
     def one_pass(hs):
         q, k, v, do = (sub(inp[n], hs) for n in ("q", "k", "v", "do"))
+        rkw = dict(args, rows=sub(rows, hs)) if sampled else args
         if dropout_p > 0:  # mask index b * H + h with the workload's H
-            dkw = dict(args, n_heads=H)
+            dkw = dict(rkw, n_heads=H)
             O, L = dref.forward(q, k, v, w.scale, dropout_p, DROPOUT_SEED, 0, **dkw)
-            G = dref.backward(q, k, v, do, w.scale, dropout_p, DROPOUT_SEED, 0, **dkw)
+            G = dref.backward(q, k, v, do, w.scale, dropout_p, DROPOUT_SEED, 0, **dkw) \
+                if w.backward else ()
             return O, L, G
-        O, L = ref.forward(q, k, v, w.scale, **args)
-        G = ref.backward(q, k, v, do, w.scale, **args) if w.backward else ()
+        O, L = ref.forward(q, k, v, w.scale, **rkw)
+        G = ref.backward(q, k, v, do, w.scale, **rkw) if w.backward else ()
         return O, L, G
+
+    def flops_of(hs):
+        if not sampled:
+            return flops_fb * hs / H
+        return per_pair * sampled_pairs(sub(rows, hs), w.N, w.causal, inp["seqlens"],
+                                        inp["block_mask"], 128, Nk=w.n_keys)
 
     t0 = time.perf_counter()
     one_pass(1)
@@ -302,27 +360,49 @@ def cpu_baseline(w: wl.Workload, inp: dict, outs: dict, flops_fb: float,
         secs = time.perf_counter() - t0
         if secs >= budget_s or passes >= 50:
             break
-    tflops = flops_fb * (hs / H) * passes / secs / 1e12
+    tflops = flops_of(hs) * passes / secs / 1e12
     # the same sample doubles as a parity spot check of the GPU outputs
     npf = lambda t: t[:, :hs].float().cpu().numpy().astype(np.float64)  # noqa: E731
-    lg = npf(outs["lse"])
+
+    def at_rows(t):
+        x = npf(t)
+        if not sampled:
+            return x
+        r = sub(rows, hs)
+        if x.ndim == 3:
+            return np.take_along_axis(x, r, axis=2)
+        return np.take_along_axis(x, r[..., None], axis=2)
+
+    lg = at_rows(outs["lse"])
     fin = np.isfinite(L)
-    parity = dict(O_maxabs=float(np.abs(npf(outs["o"]) - O).max()),
+    parity = dict(O_maxabs=float(np.abs(at_rows(outs["o"]) - O).max()),
                   L_maxabs=float(np.abs(lg[fin] - L[fin]).max()) if fin.any() else 0.0)
-    for name, g in zip(("dQ", "dK", "dV"), G):
-        parity[f"{name}_relfro"] = float(np.linalg.norm(npf(outs["d" + name[1].lower()]) - g)
-                                         / np.linalg.norm(g))
-    # the whole workload at the sample's rate (an extrapolation unless the
-    # sample was every head)
+    if G:
+        gpu = dict(dQ=at_rows(outs["dq"]))
+        if sampled:
+            res = outs.get("restricted")
+            if res is not None:
+                gpu.update(dK=npf(res["dk"]), dV=npf(res["dv"]))
+        else:
+            gpu.update(dK=npf(outs["dk"]), dV=npf(outs["dv"]))
+        for name, g in zip(("dQ", "dK", "dV"), G):
+            if name in gpu:
+                parity[f"{name}_relfro"] = float(np.linalg.norm(gpu[name] - g)
+                                                 / np.linalg.norm(g))
+        if sampled:
+            parity["sample"] = (f"{rows.shape[-1]} query rows per head on {hs} heads; dK, dV "
+                                f"from the backward rerun with dO kept on those rows")
     full_s = flops_fb / (tflops * 1e12)
+    whole = (not sampled) and hs == H
+    what = (f"{rows.shape[-1]} sampled query rows per head (dK, dV of dO restricted to them)"
+            if sampled else "whole sequences")
     base = dict(value=tflops, unit="TFLOP/s", cores=int(cores), kind="oracle",
                 sample=f"fp64 NumPy oracle {'fwd+bwd' if w.backward else 'fwd'} on {hs} of "
-                       f"{H} heads x batch {w.B} "
-                       f"(whole sequences), {passes} pass(es) in {secs:.1f} s; value scaled "
-                       f"by the FLOPs of the sample",
+                       f"{H} heads x batch {w.B}, {what}, {passes} pass(es) in {secs:.1f} s; "
+                       f"value = visible-pair FLOPs of the sample / time",
                 seconds=secs,
                 full_problem_s=full_s,
-                full_problem_s_kind="measured" if hs == H else "extrapolated from the sample",
+                full_problem_s_kind="measured" if whole else "extrapolated from the sample",
                 **host_info())
     return base, parity
 
@@ -684,8 +764,9 @@ def main(argv=None):
                     help="drop probability on P (fa_fwd_dropout / fa_bwd_dropout); the FLOP "
                          "count is the same as without dropout")
     ap.add_argument("--cpu-baseline", default="on", choices=["on", "off"])
-    ap.add_argument("--event-every", type=int, default=4,
-                    help="time the kernels with HIP events on every N-th timed step")
+    ap.add_argument("--event-reps", type=int, default=50,
+                    help="steps after the timed ones whose launches are bracketed by HIP "
+                         "events (per-kernel device time)")
     ap.add_argument("--cold-reps", type=int, default=50,
                     help="launches of each kernel timed after a 1 GiB cache-evicting write "
                          "(0: none)")
@@ -760,7 +841,7 @@ def main(argv=None):
 
     wall_ms, kernel_ms, median_ms, cold_ms, props, outs = run_gpu(
         w, inp, args.steps, args.warmup, args.prewarm_s, args.dropout, args.cold_reps,
-        args.event_every)
+        args.event_reps)
     import exact_io_aware_64_amd as fa
     key_groups = fa.fa_fwd_key_groups(fa.FA_BF16 if w.dtype == "bf16" else fa.FA_F32, w.B, w.H,
                                       w.N, w.n_keys, w.d, 128)
@@ -824,7 +905,7 @@ def main(argv=None):
         "kernel_ms_median": median_ms,
         "cold_kernel_ms": cold_ms,
         "cold_reps": args.cold_reps,
-        "event_steps": len(range(0, args.steps, max(1, args.event_every))),
+        "event_reps": max(1, args.event_reps),
         "fwd_frac_peak": tf_f / peak,
         "fwdbwd_frac_peak": tf_fb / peak,
         "peak_tflops": peak,

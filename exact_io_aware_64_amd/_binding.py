@@ -153,10 +153,45 @@ def _check(st: int):
         raise FaError(st, fa_last_error())
 
 
+def _check_aux(q, Nq: int, Nk: int, lse, seqlens_k, block_mask, mask_block: int, tensors):
+    """Checks what the library reads through raw pointers without knowing
+    their types or sizes, before any C call: lse fp32 contiguous [B, H, N_q];
+    seqlens_k int32 contiguous [B]; block_mask uint8 or bool contiguous
+    [ceil(N_q / mask_block), ceil(N_k / mask_block)]; and every tensor
+    (`tensors` are the [B, H, *, d] operands) on q's GPU."""
+    torch = _torch()
+    B, H = q.shape[0], q.shape[1]
+    if lse is None or lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, Nq) \
+            or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous fp32 [B, H, N_q] tensor")
+    if seqlens_k is not None:
+        if seqlens_k.dtype != torch.int32:
+            raise ValueError(f"seqlens_k must be int32 (got {seqlens_k.dtype})")
+        if tuple(seqlens_k.shape) != (B,) or not seqlens_k.is_contiguous():
+            raise ValueError(f"seqlens_k must be a contiguous [B] = [{B}] tensor "
+                             f"(got shape {tuple(seqlens_k.shape)})")
+    if block_mask is not None:
+        if block_mask.dtype not in (torch.uint8, torch.bool):
+            raise ValueError(f"block_mask must be uint8 or bool (got {block_mask.dtype})")
+        mb = int(mask_block)
+        if mb <= 0:
+            raise ValueError(f"mask_block must be positive (got {mb})")
+        want = (-(-Nq // mb), -(-Nk // mb))
+        if tuple(block_mask.shape) != want or not block_mask.is_contiguous():
+            raise ValueError(f"block_mask must be a contiguous {want[0]} x {want[1]} tensor "
+                             f"(got shape {tuple(block_mask.shape)})")
+    if q.device.type != "cuda":
+        raise ValueError(f"q must be on a GPU device (got {q.device})")
+    named = [("lse", lse), ("seqlens_k", seqlens_k), ("block_mask", block_mask)]
+    for name, t in list(tensors) + named:
+        if t is not None and t.device != q.device:
+            raise ValueError(f"{name} must be on {q.device} like q (got {t.device})")
+
+
 def _fwd_args(q, k, v, o, lse, scale, causal, seqlens_k, block_mask, mask_block):
     B, H, N, d = _check_like(q, (("k", k), ("v", v), ("o", o)))
-    if tuple(lse.shape) != (B, H, N) or not lse.is_contiguous():
-        raise ValueError("lse must be a contiguous fp32 [B, H, N] tensor")
+    _check_aux(q, N, N, lse, seqlens_k, block_mask, mask_block,
+               (("k", k), ("v", v), ("o", o)))
     return (_dtype_code(q), _ptr(q), _strides(q), _ptr(k), _strides(k), _ptr(v), _strides(v),
             _ptr(o), _strides(o), _ptr(lse), B, H, N, d, float(scale), int(bool(causal)),
             _ptr(seqlens_k), _ptr(block_mask), int(mask_block))
@@ -183,8 +218,8 @@ def fa_fwd_qk(q, k, v, o, lse, *, scale: float, causal: bool = False, seqlens_k=
     j <= i + N_k - N_q."""
     lib = load_library()
     B, H, Nq, Nk, d = _check_qk(q, k, (("o", o),), (("v", v),))
-    if tuple(lse.shape) != (B, H, Nq) or not lse.is_contiguous():
-        raise ValueError("lse must be a contiguous fp32 [B, H, N_q] tensor")
+    _check_aux(q, Nq, Nk, lse, seqlens_k, block_mask, mask_block,
+               (("k", k), ("v", v), ("o", o)))
     st = lib.fa_fwd_qk(_dtype_code(q), _ptr(q), _strides(q), _ptr(k), _strides(k), _ptr(v),
                        _strides(v), _ptr(o), _strides(o), _ptr(lse), B, H, Nq, Nk, d,
                        float(scale), int(bool(causal)), _ptr(seqlens_k), _ptr(block_mask),
@@ -199,6 +234,9 @@ def fa_bwd_qk(q, k, v, o, dout, lse, dq, dk, dv, workspace=None, *, scale: float
     lib = load_library()
     B, H, Nq, Nk, d = _check_qk(q, k, (("o", o), ("dout", dout), ("dq", dq)),
                                 (("v", v), ("dk", dk), ("dv", dv)))
+    _check_aux(q, Nq, Nk, lse, seqlens_k, block_mask, mask_block,
+               (("k", k), ("v", v), ("o", o), ("dout", dout), ("dq", dq), ("dk", dk),
+                ("dv", dv), ("workspace", workspace)))
     st = lib.fa_bwd_qk(_dtype_code(q), _ptr(q), _strides(q), _ptr(k), _strides(k), _ptr(v),
                        _strides(v), _ptr(o), _strides(o), _ptr(dout), _strides(dout), _ptr(lse),
                        _ptr(dq), _strides(dq), _ptr(dk), _strides(dk), _ptr(dv), _strides(dv),
@@ -259,8 +297,10 @@ def _check_like(q, named):
 
 def _bwd_args(q, k, v, o, dout, lse, dq, dk, dv, workspace, scale, causal, seqlens_k,
               block_mask, mask_block):
-    B, H, N, d = _check_like(q, (("k", k), ("v", v), ("o", o), ("dout", dout), ("dq", dq),
-                                 ("dk", dk), ("dv", dv)))
+    named = (("k", k), ("v", v), ("o", o), ("dout", dout), ("dq", dq), ("dk", dk), ("dv", dv))
+    B, H, N, d = _check_like(q, named)
+    _check_aux(q, N, N, lse, seqlens_k, block_mask, mask_block,
+               named + (("workspace", workspace),))
     return (_dtype_code(q), _ptr(q), _strides(q), _ptr(k), _strides(k), _ptr(v), _strides(v),
             _ptr(o), _strides(o), _ptr(dout), _strides(dout), _ptr(lse), _ptr(dq), _strides(dq),
             _ptr(dk), _strides(dk), _ptr(dv), _strides(dv), _ptr(workspace), _nbytes(workspace),
@@ -294,7 +334,10 @@ def fa_bwd_dq(q, k, v, o, dout, lse, dq, workspace=None, *, scale: float,
               stream=None) -> None:
     """Calls fa_bwd_dq: writes dq in full."""
     lib = load_library()
-    B, H, N, d = _check_like(q, (("k", k), ("v", v), ("o", o), ("dout", dout), ("dq", dq)))
+    named = (("k", k), ("v", v), ("o", o), ("dout", dout), ("dq", dq))
+    B, H, N, d = _check_like(q, named)
+    _check_aux(q, N, N, lse, seqlens_k, block_mask, mask_block,
+               named + (("workspace", workspace),))
     nbytes = _nbytes(workspace)
     st = lib.fa_bwd_dq(_dtype_code(q), _ptr(q), _strides(q), _ptr(k), _strides(k), _ptr(v),
                        _strides(v), _ptr(o), _strides(o), _ptr(dout), _strides(dout),
@@ -309,8 +352,10 @@ def fa_bwd_dkdv(q, k, v, o, dout, lse, dk, dv, workspace=None, *, scale: float,
                 stream=None) -> None:
     """Calls fa_bwd_dkdv: writes dk and dv in full."""
     lib = load_library()
-    B, H, N, d = _check_like(q, (("k", k), ("v", v), ("o", o), ("dout", dout), ("dk", dk),
-                                 ("dv", dv)))
+    named = (("k", k), ("v", v), ("o", o), ("dout", dout), ("dk", dk), ("dv", dv))
+    B, H, N, d = _check_like(q, named)
+    _check_aux(q, N, N, lse, seqlens_k, block_mask, mask_block,
+               named + (("workspace", workspace),))
     nbytes = _nbytes(workspace)
     st = lib.fa_bwd_dkdv(_dtype_code(q), _ptr(q), _strides(q), _ptr(k), _strides(k), _ptr(v),
                          _strides(v), _ptr(o), _strides(o), _ptr(dout), _strides(dout),
@@ -346,6 +391,8 @@ def prepare_fwd(q, k, v, o, lse, *, scale: float, causal: bool = False, seqlens_
     keep = (q, k, v, o, lse, seqlens_k, block_mask)
     if k.shape[2] != q.shape[2]:
         B, H, Nq, Nk, d = _check_qk(q, k, (("o", o),), (("v", v),))
+        _check_aux(q, Nq, Nk, lse, seqlens_k, block_mask, mask_block,
+                   (("k", k), ("v", v), ("o", o)))
         args = (_dtype_code(q), _ptr(q), _strides(q), _ptr(k), _strides(k), _ptr(v),
                 _strides(v), _ptr(o), _strides(o), _ptr(lse), B, H, Nq, Nk, d, float(scale),
                 int(bool(causal)), _ptr(seqlens_k), _ptr(block_mask), int(mask_block))
@@ -369,6 +416,9 @@ def prepare_bwd(q, k, v, o, dout, lse, dq, dk, dv, workspace=None, *, scale: flo
     if k.shape[2] != q.shape[2]:
         B, H, Nq, Nk, d = _check_qk(q, k, (("o", o), ("dout", dout), ("dq", dq)),
                                     (("v", v), ("dk", dk), ("dv", dv)))
+        _check_aux(q, Nq, Nk, lse, seqlens_k, block_mask, mask_block,
+                   (("k", k), ("v", v), ("o", o), ("dout", dout), ("dq", dq), ("dk", dk),
+                    ("dv", dv), ("workspace", workspace)))
         args = (_dtype_code(q), _ptr(q), _strides(q), _ptr(k), _strides(k), _ptr(v),
                 _strides(v), _ptr(o), _strides(o), _ptr(dout), _strides(dout), _ptr(lse),
                 _ptr(dq), _strides(dq), _ptr(dk), _strides(dk), _ptr(dv), _strides(dv),

@@ -49,6 +49,7 @@
 // are formed; a dropped probability still counts in l (L is the statistic of
 // the undropped softmax) but enters O^T += V^T P^T as zero, and the keep
 // scale is applied with 1 / l at the end.
+#include <atomic>
 #include <type_traits>
 
 #include "fa_device.h"
@@ -456,12 +457,18 @@ hipError_t dispatch(const FwdArgs& a, bool causal, hipStream_t stream) {
 
 }  // namespace
 
-// CUs of the current device (0 if it cannot be read: no split then).
+// CUs of the current device (0 if it cannot be read: no split then), read
+// from the runtime once per device and kept in a small table.
 static int cu_count() {
+  constexpr int kMaxDevices = 64;
+  static std::atomic<int> cached[kMaxDevices];  // 0: not read yet
   int dev = 0, n = 0;
-  if (hipGetDevice(&dev) != hipSuccess ||
-      hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (dev >= 0 && dev < kMaxDevices && (n = cached[dev].load(std::memory_order_relaxed)) > 0)
+    return n;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
     return 0;
+  if (dev >= 0 && dev < kMaxDevices && n > 0) cached[dev].store(n, std::memory_order_relaxed);
   return n;
 }
 

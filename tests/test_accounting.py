@@ -142,3 +142,26 @@ def test_launch_durations_of_sampled_steps():
     # forward-only steps: a start and one launch
     d = bench.launch_durations([[Ev(0.0), Ev(2.0)], [Ev(5.0), Ev(8.0)]], ("fwd",))
     assert d == {"fwd": [2.0, 3.0]}
+
+
+@pytest.mark.parametrize("N,Nk,causal,seqlens,p", [
+    (300, 300, True, [100, 300], 0.4),
+    (512, 512, False, None, 0.3),
+    (200, 700, True, None, None),
+    (260, 130, True, [5, 130], 0.5),
+    (384, 384, False, [384, 200], None),
+])
+def test_sampled_pairs_match_brute_force(N, Nk, causal, seqlens, p):
+    rng = np.random.default_rng(N + Nk)
+    bm = None
+    if p:
+        bm = (rng.random((-(-N // 128), -(-Nk // 128))) < p).astype(np.uint8)
+    B, H = (1 if seqlens is None else len(seqlens)), 3
+    sl = None if seqlens is None else np.array(seqlens, np.int32)
+    rows = wl.sample_rows(rng, B, H, N, min(N, 37))
+    want = 0
+    for b in range(B):
+        for h in range(H):
+            vis = ref.visible(rows[b, h], Nk, causal, None if sl is None else sl[b], bm, 128, N)
+            want += int(vis.sum())
+    assert bench.sampled_pairs(rows, N, causal, sl, bm, 128, Nk=Nk) == want
