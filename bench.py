@@ -571,6 +571,180 @@ def io_sweep_summary(fetch_csv, write_csv, l2_csv, cfetch_csv, cwrite_csv, cl2_c
     return "\n".join(out) + "\n"
 
 
+# ------------------------------------------------------- HBM bytes vs N
+
+HBM_N = (1024, 2048, 4096, 8192, 16384, 32768, 65536)
+HBM_B, HBM_H, HBM_D = 1, 8, 64
+HBM_KINDS = ("causal", "blocksparse")
+HBM_SEED = 11
+HBM_REPS = 3
+# Requests that leave L2 for memory, in 32-byte units (gfx950 TCC counters):
+# reads and writes whose address is in the GPU's own HBM.
+DRAM_COUNTERS = ("TCC_EA0_RDREQ_DRAM_32B_sum", "TCC_EA0_WRREQ_WRITE_DRAM_32B_sum")
+
+
+def _template_args(name: str):
+    """Template arguments of a demangled kernel name, as strings."""
+    if "<" not in name:
+        return []
+    inner = name[name.index("<") + 1:name.index(">")]
+    return [a.strip() for a in inner.split(",")]
+
+
+def _has_block_mask(kernel: str, name: str) -> bool:
+    """Whether a dispatch ran the block-mask instantiation: the fifth template
+    argument of fwd_bf16_kernel<W, G, D, SEQLEN, BMASK, DROP>, the fourth of
+    bwd_kernel<D, CAUSAL, SEQLEN, BMASK, DROP>."""
+    args = _template_args(name)
+    pos = 4 if kernel == "fwd_bf16_kernel" else 3
+    return len(args) > pos and args[pos] == "true"
+
+
+def hbm_sweep_run(ns, kinds, reps: int) -> int:
+    """fa_fwd and fa_bwd on B=1, H=8, d=64 for every N and mask kind (causal;
+    block-sparse: 128 x 128 tiles, diagonal plus each off-diagonal tile with
+    p = 1/16, non-causal): one untimed and `reps` event-timed launches of
+    each, in a fixed order, one JSON line per configuration.  Under rocprofv3
+    --pmc a dispatch is told apart by kernel, block-mask instantiation and
+    workgroup count, all recorded in the line."""
+    import torch
+    import exact_io_aware_64_amd as fa
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+    rng = np.random.default_rng(HBM_SEED)
+    nmax = max(ns)
+    full = wl.draw_tensors(rng, HBM_B, HBM_H, nmax, HBM_D, "bf16", count=4)
+    for N in ns:
+        q, k, v, do = (torch.from_numpy(np.ascontiguousarray(x[:, :, :N])).to(torch.bfloat16)
+                       .to(dev) for x in full)
+        for kind in kinds:
+            causal = kind == "causal"
+            bm_np = None if causal else wl.draw_block_mask(
+                np.random.default_rng(HBM_SEED + N), N, 1 / 16)
+            bm = None if bm_np is None else torch.from_numpy(bm_np).to(dev)
+            o = torch.empty_like(q)
+            lse = torch.empty((HBM_B, HBM_H, N), dtype=torch.float32, device=dev)
+            dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+            kw = dict(scale=1 / 8, causal=causal, block_mask=bm)
+            fwd = fa.prepare_fwd(q, k, v, o, lse, **kw)
+            bwd = fa.prepare_bwd(q, k, v, o, do, lse, dq, dk, dv, **kw)
+            fwd()
+            bwd()
+            evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(reps)]
+            for e in evs:
+                e[0].record(stream)
+                fwd()
+                e[1].record(stream)
+                bwd()
+                e[2].record(stream)
+            torch.cuda.synchronize()
+            fms = float(np.median([e[0].elapsed_time(e[1]) for e in evs]))
+            bms = float(np.median([e[1].elapsed_time(e[2]) for e in evs]))
+            pairs = visible_pairs(N, HBM_H, causal, None, bm_np, 128, HBM_B)
+            kb = kernel_bytes(HBM_B, HBM_H, N, HBM_D, 2, None)
+            nqt = -(-N // 128)
+            groups = fa.fa_fwd_key_groups(fa.FA_BF16, HBM_B, HBM_H, N, N, HBM_D, 128)
+            print(json.dumps(dict(
+                mode="hbm-sweep", N=N, kind=kind, pairs=pairs, fwd_ms=fms, bwd_ms=bms,
+                fwd_tflops=4.0 * HBM_D * pairs / (fms * 1e-3) / 1e12,
+                bwd_tflops=10.0 * HBM_D * pairs / (bms * 1e-3) / 1e12,
+                fwd_workgroups=nqt * HBM_B * HBM_H, fwd_threads=256 * groups,
+                bwd_workgroups=2 * nqt * HBM_B * HBM_H,
+                compulsory_fwd=kb["fwd_bf16_kernel"], compulsory_bwd=kb["bwd_kernel"])),
+                flush=True)
+            del o, lse, dq, dk, dv, fwd, bwd
+        del q, k, v, do
+    return 0
+
+
+def hbm_sweep_summary(fetch_csv, write_csv, dram_csv, cfetch_csv, cwrite_csv, cdram_csv, log,
+                      command, copy_bytes, mall_csv=None, mall_log=None) -> str:
+    """profiles/hbm_vs_n.md: bytes per launch of fa_fwd and fa_bwd across N and
+    mask kind (means over each configuration's dispatches), four counters,
+    each scaled by what it reads for a plain device copy of known size."""
+    def copy_max(path, counter):
+        return max(v[counter] for v in _per_dispatch(path, (counter,)).values())
+    f_fetch = copy_bytes / (copy_max(cfetch_csv, "FETCH_SIZE") * 1024.0)
+    f_write = copy_bytes / (copy_max(cwrite_csv, "WRITE_SIZE") * 1024.0)
+    f_drd = copy_bytes / copy_max(cdram_csv, DRAM_COUNTERS[0])
+    f_dwr = copy_bytes / copy_max(cdram_csv, DRAM_COUNTERS[1])
+    cfg = {}
+    with open(log) as fh:
+        for line in fh:
+            if line.startswith("{") and '"hbm-sweep"' in line:
+                r = json.loads(line)
+                bmask = r["kind"] == "blocksparse"
+                cfg[("fwd_bf16_kernel", bmask, r["fwd_workgroups"])] = r
+                cfg[("bwd_kernel", bmask, r["bwd_workgroups"])] = r
+    meas = {}
+    for path, counters in ((fetch_csv, ("FETCH_SIZE",)), (write_csv, ("WRITE_SIZE",)),
+                           (dram_csv, DRAM_COUNTERS)):
+        for d in _per_dispatch(path, counters).values():
+            if d["kernel"] not in KERNELS:
+                continue
+            key = (d["kernel"], _has_block_mask(d["kernel"], d["name"]), d["grid"] // d["wg"])
+            if key not in cfg:
+                continue
+            r = cfg[key]
+            acc = meas.setdefault((r["N"], r["kind"], d["kernel"]), {})
+            for c in counters:
+                acc.setdefault(c, []).append(d.get(c, 0.0))
+    rows = []
+    for (N, kind, kern) in sorted(meas, key=lambda x: (x[1], x[2] != "fwd_bf16_kernel", x[0])):
+        m = {c: float(np.mean(v)) for c, v in meas[(N, kind, kern)].items()}
+        fwd = kern == "fwd_bf16_kernel"
+        r = next(v for v in cfg.values() if v["N"] == N and v["kind"] == kind)
+        comp = r["compulsory_fwd" if fwd else "compulsory_bwd"]
+        fetch = m.get("FETCH_SIZE", float("nan")) * 1024.0 * f_fetch
+        write = m.get("WRITE_SIZE", float("nan")) * 1024.0 * f_write
+        drd = m.get(DRAM_COUNTERS[0], float("nan")) * f_drd
+        dwr = m.get(DRAM_COUNTERS[1], float("nan")) * f_dwr
+        us = 1e3 * r["fwd_ms" if fwd else "bwd_ms"]
+        rows.append((kind, "fwd" if fwd else "bwd", N, us,
+                     r["fwd_tflops" if fwd else "bwd_tflops"], comp / 1e6, fetch / 1e6,
+                     write / 1e6, drd / 1e6, dwr / 1e6, (fetch + write) / comp,
+                     (drd + dwr) / comp, (drd + dwr) / N / 1e3))
+    out = ["# HBM bytes vs N: fa_fwd and fa_bwd, B=1 H=8 d=64, causal and block-sparse", "",
+           "Command (repository root, MI355X, `TMPDIR=/tmp`):", "", "```", command, "```", "",
+           "Per launch, mean over the configuration's dispatches (one untimed and three timed "
+           "launches each).  *compulsory* = every tensor the kernel must read or write once "
+           "(forward: Q, K, V, O and L; backward: Q, K, V, O, dO, L, dQ, dK, dV).  Measured: "
+           "*fetch* = FETCH_SIZE and *write* = WRITE_SIZE (bytes leaving L2 toward memory); "
+           "*DRAM rd* = TCC_EA0_RDREQ_DRAM_32B and *DRAM wr* = TCC_EA0_WRREQ_WRITE_DRAM_32B "
+           "(requests leaving L2 whose address lies in the GPU's own HBM, 32-byte units).  "
+           "Each is scaled by the same counter over a "
+           f"{copy_bytes >> 20} MiB device copy (factors: fetch x {f_fetch:.3f}, write x "
+           f"{f_write:.3f}, DRAM rd x {f_drd:.2f} B, DRAM wr x {f_dwr:.2f} B).  Block-sparse: "
+           "128 x 128 tile mask, diagonal plus each off-diagonal tile with p = 1/16, "
+           "non-causal.  Time: median of the timed launches (events) in the same run.", "",
+           "| mask | pass | N | us | TFLOP/s | compulsory MB | fetch MB | write MB | DRAM rd MB "
+           "| DRAM wr MB | (fetch+write) / compulsory | DRAM / compulsory | DRAM KB per row |",
+           "|---|---|---|---|---|---|---|---|---|---|---|---|---|"]
+    for r in rows:
+        out.append("| %s | %s | %d | %.1f | %.0f | %.1f | %.1f | %.1f | %.1f | %.1f | %.2f | "
+                   "%.2f | %.1f |" % r)
+    if mall_csv and mall_log:
+        sizes = []
+        with open(mall_log) as fh:
+            for line in fh:
+                if line.startswith("{") and '"copy"' in line:
+                    sizes.append(json.loads(line))
+        if sizes:
+            c = sizes[-1]
+            # the copies, not the fill that initialises the source
+            big = [d for d in _per_dispatch(mall_csv, DRAM_COUNTERS).values()
+                   if "fill" not in d["name"].lower()]
+            rd = float(np.median([d[DRAM_COUNTERS[0]] for d in big])) * f_drd
+            wr = float(np.median([d[DRAM_COUNTERS[1]] for d in big])) * f_dwr
+            out += ["", "Infinity Cache probe: a plain copy of "
+                    f"{c['bytes_read'] >> 20} MiB (larger than the 8 x 4 MB of L2, smaller than "
+                    f"the 256 MB Infinity Cache), repeated: {c['ms'] * 1e3:.1f} us per copy, "
+                    f"{c['GBps_read_plus_write']:.0f} GB/s read + write; DRAM rd "
+                    f"{rd / 1e6:.1f} MB and DRAM wr {wr / 1e6:.1f} MB per copy (median over "
+                    f"{len(big)} dispatches)."]
+    return "\n".join(out) + "\n"
+
+
 # ------------------------------------------------------------ HBM traffic
 
 KERNEL_SOURCES = {
@@ -770,14 +944,24 @@ def main(argv=None):
     ap.add_argument("--cold-reps", type=int, default=50,
                     help="launches of each kernel timed after a 1 GiB cache-evicting write "
                          "(0: none)")
-    ap.add_argument("--mode", default="attention", choices=["attention", "copy", "io-sweep"],
+    ap.add_argument("--mode", default="attention",
+                    choices=["attention", "copy", "io-sweep", "hbm-sweep"],
                     help="copy: time a plain 1 GiB device copy (counter calibration); "
-                         "io-sweep: dense forward over N x query-tile height (fa_fwd_tiled)")
+                         "io-sweep: dense forward over N x query-tile height (fa_fwd_tiled); "
+                         "hbm-sweep: fa_fwd + fa_bwd over N, causal and block-sparse")
     ap.add_argument("--sweep-n", default=",".join(str(n) for n in SWEEP_N))
     ap.add_argument("--io-summary", nargs=7, metavar=("FETCH_CSV", "WRITE_CSV", "L2_CSV",
                                                      "COPY_FETCH_CSV", "COPY_WRITE_CSV",
                                                      "COPY_L2_CSV", "SWEEP_LOG"),
                     help="write profiles/io_sweep.md from rocprofv3 runs of --mode io-sweep")
+    ap.add_argument("--hbm-n", default=",".join(str(n) for n in HBM_N))
+    ap.add_argument("--hbm-summary", nargs=7, metavar=("FETCH_CSV", "WRITE_CSV", "DRAM_CSV",
+                                                      "COPY_FETCH_CSV", "COPY_WRITE_CSV",
+                                                      "COPY_DRAM_CSV", "SWEEP_LOG"),
+                    help="write profiles/hbm_vs_n.md from rocprofv3 runs of --mode hbm-sweep")
+    ap.add_argument("--mall-probe", nargs=2, metavar=("DRAM_CSV", "COPY_LOG"),
+                    help="with --hbm-summary: DRAM counters and log of a copy that fits the "
+                         "Infinity Cache")
     ap.add_argument("--copy-mib", type=int, default=1024)
     ap.add_argument("--pmc-summary", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV",
                                                      "COPY_FETCH_CSV", "COPY_WRITE_CSV"),
@@ -797,6 +981,15 @@ def main(argv=None):
         md = io_sweep_summary(*args.io_summary, command=args.pmc_command,
                               copy_bytes=args.copy_mib << 20)
         with open(os.path.join(ROOT, "profiles", "io_sweep.md"), "w") as fh:
+            fh.write(md)
+        print(md)
+        return 0
+    if args.hbm_summary:
+        mall = args.mall_probe or (None, None)
+        md = hbm_sweep_summary(*args.hbm_summary, command=args.pmc_command,
+                               copy_bytes=args.copy_mib << 20, mall_csv=mall[0],
+                               mall_log=mall[1])
+        with open(os.path.join(ROOT, "profiles", "hbm_vs_n.md"), "w") as fh:
             fh.write(md)
         print(md)
         return 0
@@ -830,6 +1023,8 @@ def main(argv=None):
         return copy_calibration(args.copy_mib, args.steps, args.warmup)
     if args.mode == "io-sweep":
         return io_sweep_run([int(x) for x in args.sweep_n.split(",")], SWEEP_BQ, SWEEP_REPS)
+    if args.mode == "hbm-sweep":
+        return hbm_sweep_run([int(x) for x in args.hbm_n.split(",")], HBM_KINDS, HBM_REPS)
 
     w = wl.WORKLOADS[args.workload]
     inp = wl.make_inputs(w)
