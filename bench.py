@@ -96,9 +96,11 @@ def visible_pairs(N: int, H: int, causal: bool, seqlens, block_mask, mask_block:
 
 
 def kernel_bytes(B, H, N, d, esize, seqlens, Nk=None):
-    """Compulsory HBM bytes per launch of each kernel: every tensor the kernel
-    must read or write once (keys and values only up to each sequence's key
-    length), plus the fp32 row statistic L.  N queries, Nk keys (default N)."""
+    """Compulsory HBM bytes per call of each pass: every tensor the pass must
+    read or write once (keys and values only up to each sequence's key
+    length), plus the fp32 row statistics: L, and for the backward pass D
+    (written by its first kernel, read by its second).  N queries, Nk keys
+    (default N)."""
     Nk = N if Nk is None else Nk
     t = B * H * N * d * esize
     tk = B * H * Nk * d * esize
@@ -106,22 +108,27 @@ def kernel_bytes(B, H, N, d, esize, seqlens, Nk=None):
                                 else int(np.minimum(seqlens, Nk).sum()))
     rowstat = B * H * N * 4
     return {
-        "fwd_bf16_kernel": 2 * t + 2 * kv_valid + rowstat,    # Q, O; K, V; L
-        "bwd_kernel": 4 * t + 2 * tk + 2 * kv_valid + rowstat,  # Q, O, dO, dQ; dK, dV; K, V; L
+        "fa_fwd": 2 * t + 2 * kv_valid + rowstat,    # Q, O; K, V; L
+        # Q, O, dO, dQ; dK, dV; K, V; L; D written and read
+        "fa_bwd": 4 * t + 2 * tk + 2 * kv_valid + 3 * rowstat,
     }
 
 
 def kernel_flops(d, pairs):
-    """Algorithmic FLOPs per launch: the forward pass is two products over the
+    """Algorithmic FLOPs per call: the forward pass is two products over the
     visible pairs (S, O; 2*d each), the backward pass five (S recomputed, dV,
     dP, dQ, dK).  The backward kernel's second recomputation of S and dP (in
     its dQ workgroups) duplicates work and is not credited."""
-    return {"fwd_bf16_kernel": 4.0 * d * pairs, "bwd_kernel": 10.0 * d * pairs}
+    return {"fa_fwd": 4.0 * d * pairs, "fa_bwd": 10.0 * d * pairs}
 
 
 # ------------------------------------------------------------------- timing
 
-KERNELS = ("fwd_bf16_kernel", "bwd_kernel")
+# The two C calls of a step and the kernels each launches, in order: fa_bwd
+# writes D = rowsum(dO * O) with dsum_kernel, then runs bwd_kernel.
+PASSES = ("fa_fwd", "fa_bwd")
+PASS_KERNELS = {"fa_fwd": ("fwd_bf16_kernel",), "fa_bwd": ("dsum_kernel", "bwd_kernel")}
+KERNELS = ("fwd_bf16_kernel", "dsum_kernel", "bwd_kernel")
 DROPOUT_SEED = 2024  # Philox key of the --dropout runs (offset 0)
 
 
@@ -132,7 +139,8 @@ def measure_key(workload: str, dropout_p: float) -> str:
 
 
 def run_gpu(w: wl.Workload, inp: dict, steps: int, warmup: int, prewarm_s: float = 1.0,
-            dropout_p: float = 0.0, cold_reps: int = 0, event_reps: int = 50):
+            dropout_p: float = 0.0, cold_reps: int = 0, event_reps: int = 50,
+            restricted_rerun: bool = True):
     """Times `steps` steps after `warmup` untimed ones.  One step is fa_fwd
     then fa_bwd (fa_fwd alone for a forward-only workload), each a single
     kernel launch on the current stream; the wall clock around the timed
@@ -171,7 +179,7 @@ def run_gpu(w: wl.Workload, inp: dict, steps: int, warmup: int, prewarm_s: float
     # argument marshalling done once, so the host keeps ahead of the GPU
     fwd = fa.prepare_fwd(q, k, v, o, lse, **kw)
     bwd = fa.prepare_bwd(q, k, v, o, do, lse, dq, dk, dv, **kw) if w.backward else None
-    kernels = KERNELS if w.backward else KERNELS[:1]
+    kernels = PASSES if w.backward else PASSES[:1]
 
     # ev: [start, after launch 0, after launch 1, ...] of a sampled step
     def step(ev=None):
@@ -227,7 +235,7 @@ def run_gpu(w: wl.Workload, inp: dict, steps: int, warmup: int, prewarm_s: float
     # workloads the backward pass rerun with dO kept on the sampled rows only
     # (its dK, dV are the oracle's restricted gradients)
     restricted = None
-    if bwd is not None and inp.get("rows") is not None:
+    if restricted_rerun and bwd is not None and inp.get("rows") is not None:
         rows = torch.from_numpy(inp["rows"]).to(dev)
         do_r = torch.zeros_like(do)
         idx = rows[..., None].expand(-1, -1, -1, do.shape[-1])
@@ -650,7 +658,7 @@ def hbm_sweep_run(ns, kinds, reps: int) -> int:
                 bwd_tflops=10.0 * HBM_D * pairs / (bms * 1e-3) / 1e12,
                 fwd_workgroups=nqt * HBM_B * HBM_H, fwd_threads=256 * groups,
                 bwd_workgroups=2 * nqt * HBM_B * HBM_H,
-                compulsory_fwd=kb["fwd_bf16_kernel"], compulsory_bwd=kb["bwd_kernel"])),
+                compulsory_fwd=kb["fa_fwd"], compulsory_bwd=kb["fa_bwd"])),
                 flush=True)
             del o, lse, dq, dk, dv, fwd, bwd
         del q, k, v, do
@@ -679,16 +687,28 @@ def hbm_sweep_summary(fetch_csv, write_csv, dram_csv, cfetch_csv, cwrite_csv, cd
     meas = {}
     for path, counters in ((fetch_csv, ("FETCH_SIZE",)), (write_csv, ("WRITE_SIZE",)),
                            (dram_csv, DRAM_COUNTERS)):
-        for d in _per_dispatch(path, counters).values():
-            if d["kernel"] not in KERNELS:
+        disp = _per_dispatch(path, counters)
+        # a pass's counts: its kernels' dispatches summed; dsum_kernel is
+        # charged to the bwd_kernel dispatch that follows it
+        pending = {c: 0.0 for c in counters}
+        for i in sorted(disp):
+            d = disp[i]
+            if d["kernel"] == "dsum_kernel":
+                for c in counters:
+                    pending[c] += d.get(c, 0.0)
+                continue
+            if d["kernel"] not in ("fwd_bf16_kernel", "bwd_kernel"):
                 continue
             key = (d["kernel"], _has_block_mask(d["kernel"], d["name"]), d["grid"] // d["wg"])
+            extra = pending if d["kernel"] == "bwd_kernel" else {c: 0.0 for c in counters}
+            if d["kernel"] == "bwd_kernel":
+                pending = {c: 0.0 for c in counters}
             if key not in cfg:
                 continue
             r = cfg[key]
             acc = meas.setdefault((r["N"], r["kind"], d["kernel"]), {})
             for c in counters:
-                acc.setdefault(c, []).append(d.get(c, 0.0))
+                acc.setdefault(c, []).append(d.get(c, 0.0) + extra[c])
     rows = []
     for (N, kind, kern) in sorted(meas, key=lambda x: (x[1], x[2] != "fwd_bf16_kernel", x[0])):
         m = {c: float(np.mean(v)) for c, v in meas[(N, kind, kern)].items()}
@@ -706,9 +726,11 @@ def hbm_sweep_summary(fetch_csv, write_csv, dram_csv, cfetch_csv, cwrite_csv, cd
                      (drd + dwr) / comp, (drd + dwr) / N / 1e3))
     out = ["# HBM bytes vs N: fa_fwd and fa_bwd, B=1 H=8 d=64, causal and block-sparse", "",
            "Command (repository root, MI355X, `TMPDIR=/tmp`):", "", "```", command, "```", "",
-           "Per launch, mean over the configuration's dispatches (one untimed and three timed "
-           "launches each).  *compulsory* = every tensor the kernel must read or write once "
-           "(forward: Q, K, V, O and L; backward: Q, K, V, O, dO, L, dQ, dK, dV).  Measured: "
+           "Per call, mean over the configuration's calls (one untimed and three timed "
+           "calls each; the backward call's two kernels, dsum_kernel and bwd_kernel, "
+           "summed).  *compulsory* = every tensor the pass must read or write once "
+           "(forward: Q, K, V, O and L; backward: Q, K, V, O, dO, L, dQ, dK, dV, and D "
+           "written and read once).  Measured: "
            "*fetch* = FETCH_SIZE and *write* = WRITE_SIZE (bytes leaving L2 toward memory); "
            "*DRAM rd* = TCC_EA0_RDREQ_DRAM_32B and *DRAM wr* = TCC_EA0_WRREQ_WRITE_DRAM_32B "
            "(requests leaving L2 whose address lies in the GPU's own HBM, 32-byte units).  "
@@ -749,6 +771,7 @@ def hbm_sweep_summary(fetch_csv, write_csv, dram_csv, cfetch_csv, cwrite_csv, cd
 
 KERNEL_SOURCES = {
     "fwd_bf16_kernel": ("fa_fwd_bf16.hip",),
+    "dsum_kernel": ("fa_bwd_bf16.h", "fa_bwd_bf16.hip", "fa_bwd_bf16_d128.hip"),
     "bwd_kernel": ("fa_bwd_bf16.h", "fa_bwd_bf16.hip", "fa_bwd_bf16_d128.hip"),
 }
 COMMON_SOURCES = ("fa_device.h", "fa_internal.h")
@@ -879,18 +902,22 @@ def pipe_summary(counter_csv: str, workload: str, command: str) -> str:
     return "\n".join(out) + "\n"
 
 
-def traffic_for(kernel: str, workload: str):
-    """Measured HBM bytes per launch of `kernel` on `workload`, or None when
-    no record exists or the kernel changed since the counters were taken."""
+def traffic_for(pass_name: str, workload: str):
+    """Measured HBM bytes per call of a pass (the sum over its kernels) on
+    `workload`, or None when no record exists or one of its kernels changed
+    since the counters were taken."""
     path = os.path.join(ROOT, "profiles", f"hbm_traffic_{workload}.json")
     if not os.path.exists(path):
         return None
     with open(path) as fh:
         rec = json.load(fh)
-    ent = rec.get("kernels", {}).get(kernel)
-    if not ent or ent.get("source_sha256") != kernel_source_hash(kernel):
-        return None
-    return float(ent["bytes_per_launch"])
+    total = 0.0
+    for kernel in PASS_KERNELS[pass_name]:
+        ent = rec.get("kernels", {}).get(kernel)
+        if not ent or ent.get("source_sha256") != kernel_source_hash(kernel):
+            return None
+        total += float(ent["bytes_per_launch"])
+    return total
 
 
 def trace_summary(stats_csv: str, bench_log: str, workload: str, command: str) -> str:
@@ -912,9 +939,14 @@ def trace_summary(stats_csv: str, bench_log: str, workload: str, command: str) -
            "| kernel | calls | avg us | min us | max us | % time |", "|---|---|---|---|---|---|"]
     for k, n, av, mn, mx, pc in rows:
         out.append(f"| {k} | {n} | {av:.2f} | {mn:.2f} | {mx:.2f} | {pc:.2f} |")
+    avg = {k: av for k, n, av, mn, mx, pc in rows}
+    per_call = [f"{p} = {' + '.join(ks)}: {sum(avg[k] for k in ks):.2f} us"
+                for p, ks in PASS_KERNELS.items() if all(k in avg for k in ks)]
+    if per_call:
+        out += ["", "Per C call (sum of its kernels' averages): " + "; ".join(per_call) + "."]
     if line:
         km = {k: round(v * 1e3, 2) for k, v in line["kernel_ms"].items()}
-        out += ["", "Bench line of the same run (HIP events on the launch stream, us per launch):",
+        out += ["", "Bench line of the same run (HIP events on the launch stream, us per call):",
                 "", f"- kernels: {km}",
                 (f"- fwd {line['fwd_tflops']:.1f} TFLOP/s, bwd {line['bwd_tflops']:.1f} "
                  f"TFLOP/s, fwd+bwd {line['value']:.1f} TFLOP/s "
@@ -1036,19 +1068,20 @@ def main(argv=None):
 
     wall_ms, kernel_ms, median_ms, cold_ms, props, outs = run_gpu(
         w, inp, args.steps, args.warmup, args.prewarm_s, args.dropout, args.cold_reps,
-        args.event_reps)
+        args.event_reps, restricted_rerun=args.cpu_baseline == "on")
     import exact_io_aware_64_amd as fa
     key_groups = fa.fa_fwd_key_groups(fa.FA_BF16 if w.dtype == "bf16" else fa.FA_F32, w.B, w.H,
                                       w.N, w.n_keys, w.d, 128)
-    fwd_ms = kernel_ms["fwd_bf16_kernel"]
-    bwd_ms = kernel_ms.get("bwd_kernel")
+    fwd_ms = kernel_ms["fa_fwd"]
+    bwd_ms = kernel_ms.get("fa_bwd")
     peak = PEAK_TFLOPS[w.dtype]
     tf_fb = (flops_f + flops_b) / (wall_ms * 1e-3) / 1e12
     tf_f = flops_f / (fwd_ms * 1e-3) / 1e12
     tf_b = flops_b / (bwd_ms * 1e-3) / 1e12 if bwd_ms else None
 
-    # Roofline of the dominant kernel (largest device time per step): its
-    # algorithmic FLOPs and compulsory bytes per launch against its own
+    # Roofline of the dominant call (largest device time per step; fa_bwd is
+    # dsum_kernel then bwd_kernel, back to back on the stream): its
+    # algorithmic FLOPs and compulsory bytes per call against its own
     # event-timed duration.
     kflops = kernel_flops(w.d, pairs)
     kbytes = kernel_bytes(w.B, w.H, w.N, w.d, esize, inp["seqlens"], Nk=w.n_keys)
@@ -1064,7 +1097,8 @@ def main(argv=None):
         ach = kbytes[dom] / (ms * 1e-3) / 1e9
         roofline = dict(kernel=dom, bound="hbm", achieved=ach, peak=PEAK_HBM_GBS, unit="GB/s",
                         frac=ach / PEAK_HBM_GBS)
-    roofline.update(traffic=traffic_for(dom, key), flops_per_launch=kflops[dom],
+    roofline.update(kernel=" + ".join(PASS_KERNELS[dom]), call=dom,
+                    traffic=traffic_for(dom, key), flops_per_launch=kflops[dom],
                     compulsory_bytes_per_launch=kbytes[dom], launch_ms=ms)
 
     base = None

@@ -153,6 +153,23 @@ def _check(st: int):
         raise FaError(st, fa_last_error())
 
 
+def _workspace(q, workspace, Nq: int):
+    """The backward workspace: `workspace` itself when given, else a fresh
+    device buffer of fa_bwd_workspace_bytes for q's problem (None when no
+    workspace is needed)."""
+    if workspace is not None:
+        return workspace
+    B, H = q.shape[0], q.shape[1]
+    try:
+        code = _dtype_code(q)
+    except TypeError:
+        return None  # rejected later with the other arguments
+    nb = fa_bwd_workspace_bytes(code, B, H, Nq, q.shape[3])
+    if nb == 0 or q.device.type != "cuda":
+        return None
+    return _torch().empty(nb, dtype=_torch().uint8, device=q.device)
+
+
 def _check_aux(q, Nq: int, Nk: int, lse, seqlens_k, block_mask, mask_block: int, tensors):
     """Checks what the library reads through raw pointers without knowing
     their types or sizes, before any C call: lse fp32 contiguous [B, H, N_q];
@@ -230,10 +247,12 @@ def fa_fwd_qk(q, k, v, o, lse, *, scale: float, causal: bool = False, seqlens_k=
 def fa_bwd_qk(q, k, v, o, dout, lse, dq, dk, dv, workspace=None, *, scale: float,
               causal: bool = False, seqlens_k=None, block_mask=None, mask_block: int = 128,
               dropout_p: float = 0.0, seed: int = 0, offset: int = 0, stream=None) -> None:
-    """Calls fa_bwd_qk (the forward call's lengths, masks and dropout)."""
+    """Calls fa_bwd_qk (the forward call's lengths, masks and dropout).  A
+    workspace is allocated when none is given."""
     lib = load_library()
     B, H, Nq, Nk, d = _check_qk(q, k, (("o", o), ("dout", dout), ("dq", dq)),
                                 (("v", v), ("dk", dk), ("dv", dv)))
+    workspace = _workspace(q, workspace, Nq)
     _check_aux(q, Nq, Nk, lse, seqlens_k, block_mask, mask_block,
                (("k", k), ("v", v), ("o", o), ("dout", dout), ("dq", dq), ("dk", dk),
                 ("dv", dv), ("workspace", workspace)))
@@ -299,6 +318,7 @@ def _bwd_args(q, k, v, o, dout, lse, dq, dk, dv, workspace, scale, causal, seqle
               block_mask, mask_block):
     named = (("k", k), ("v", v), ("o", o), ("dout", dout), ("dq", dq), ("dk", dk), ("dv", dv))
     B, H, N, d = _check_like(q, named)
+    workspace = _workspace(q, workspace, N)
     _check_aux(q, N, N, lse, seqlens_k, block_mask, mask_block,
                named + (("workspace", workspace),))
     return (_dtype_code(q), _ptr(q), _strides(q), _ptr(k), _strides(k), _ptr(v), _strides(v),
@@ -311,7 +331,8 @@ def _bwd_args(q, k, v, o, dout, lse, dq, dk, dv, workspace, scale, causal, seqle
 def fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, workspace=None, *, scale: float,
            causal: bool = False, seqlens_k=None, block_mask=None, mask_block: int = 128,
            stream=None) -> None:
-    """Calls fa_bwd; dq, dk, dv are written in full."""
+    """Calls fa_bwd; dq, dk, dv are written in full.  A workspace of
+    fa_bwd_workspace_bytes is allocated when none is given."""
     lib = load_library()
     args = _bwd_args(q, k, v, o, dout, lse, dq, dk, dv, workspace, scale, causal, seqlens_k,
                      block_mask, mask_block)
@@ -336,6 +357,7 @@ def fa_bwd_dq(q, k, v, o, dout, lse, dq, workspace=None, *, scale: float,
     lib = load_library()
     named = (("k", k), ("v", v), ("o", o), ("dout", dout), ("dq", dq))
     B, H, N, d = _check_like(q, named)
+    workspace = _workspace(q, workspace, N)
     _check_aux(q, N, N, lse, seqlens_k, block_mask, mask_block,
                named + (("workspace", workspace),))
     nbytes = _nbytes(workspace)
@@ -354,6 +376,7 @@ def fa_bwd_dkdv(q, k, v, o, dout, lse, dk, dv, workspace=None, *, scale: float,
     lib = load_library()
     named = (("k", k), ("v", v), ("o", o), ("dout", dout), ("dk", dk), ("dv", dv))
     B, H, N, d = _check_like(q, named)
+    workspace = _workspace(q, workspace, N)
     _check_aux(q, N, N, lse, seqlens_k, block_mask, mask_block,
                named + (("workspace", workspace),))
     nbytes = _nbytes(workspace)
@@ -412,6 +435,7 @@ def prepare_bwd(q, k, v, o, dout, lse, dq, dk, dv, workspace=None, *, scale: flo
     """fa_bwd (or fa_bwd_dropout when dropout_p > 0, fa_bwd_qk when k has
     another length) with fixed arguments."""
     lib = load_library()
+    workspace = _workspace(q, workspace, q.shape[2])
     keep = (q, k, v, o, dout, lse, dq, dk, dv, workspace, seqlens_k, block_mask)
     if k.shape[2] != q.shape[2]:
         B, H, Nq, Nk, d = _check_qk(q, k, (("o", o), ("dout", dout), ("dq", dq)),
@@ -466,9 +490,7 @@ def backward(q, k, v, o, dout, lse, *, scale: float, causal: bool = False, seqle
     dq = torch.empty((B, H, N, d), dtype=q.dtype, device=q.device)
     dk = torch.empty((B, H, Nk, d), dtype=q.dtype, device=q.device)
     dv = torch.empty_like(dk)
-    if workspace is None:
-        nb = fa_bwd_workspace_bytes(_dtype_code(q), B, H, max(N, Nk), d)
-        workspace = torch.empty(nb, dtype=torch.uint8, device=q.device) if nb else None
+    workspace = _workspace(q, workspace, N)
     kw = dict(scale=scale, causal=causal, seqlens_k=seqlens_k, block_mask=block_mask,
               mask_block=mask_block)
     if Nk != N:

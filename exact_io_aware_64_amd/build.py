@@ -34,8 +34,11 @@ VGPR_FORM = ["-mllvm", "-amdgpu-mfma-vgpr-form"]
 # Per-source flags.  The d = 128 backward runs one wave per SIMD and keeps its
 # accumulators in the accumulation registers; its 64-slot tile loop is past
 # the default limit for fully unrolling a loop.
+UNROLL = ["-mllvm", "-pragma-unroll-threshold=200000"]
 SOURCE_FLAGS = {
-    "fa_bwd_bf16_d128.hip": ["-mllvm", "-pragma-unroll-threshold=200000"],
+    "fa_bwd_bf16_d128.hip": UNROLL,
+    # the d = 128 dropout forward's 32-slot tile loop needs the same limit
+    "fa_fwd_bf16.hip": VGPR_FORM + UNROLL,
 }
 
 

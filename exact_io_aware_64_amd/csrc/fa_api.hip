@@ -113,10 +113,11 @@ fa_status fwd_impl(fa_dtype dtype, const void* q, fa_strides q_strides, const vo
   if ((st = make_dropout(dropout_p, seed, offset, &drop)) != FA_OK) return st;
   if (block_q != 64 && block_q != 128 && block_q != 256)
     return fail(FA_ERR_INVALID_ARG, "block_q must be 64, 128 or 256 (got %d)", block_q);
-  if (d != 64 && (dtype != FA_BF16 || drop.t < 256 || block_q != 128))
+  if (d != 64 && (dtype != FA_BF16 || block_q != 128))
     return fail(FA_ERR_UNSUPPORTED,
-                "head dimension %d is built for the bf16 forward pass without dropout and "
-                "with block_q 128 only", d);
+                "head dimension %d is built for the bf16 forward pass with block_q 128 only", d);
+  if (drop.t < 256 && block_q != 128)
+    return fail(FA_ERR_UNSUPPORTED, "dropout is built with block_q 128 only");
   if (block_q != 128 && dtype != FA_BF16)
     return fail(FA_ERR_UNSUPPORTED, "block_q other than 128 is built for bf16 only");
   if (block_mask != nullptr && mask_block % block_q != 0)
@@ -197,13 +198,11 @@ fa_status fa_fwd_dropout(fa_dtype dtype, const void* q, fa_strides q_strides, co
 }
 
 size_t fa_bwd_workspace_bytes(fa_dtype dtype, int B, int H, int N, int d) {
-  // Every kernel of the backward pass keeps its row statistics on chip.
-  (void)dtype;
-  (void)B;
-  (void)H;
-  (void)N;
+  // The bf16 backward pass writes D_i = dot(dO_i, O_i) of every query row to
+  // the workspace before its main kernel; the fp32 kernels keep D on chip.
   (void)d;
-  return 0;
+  if (dtype != FA_BF16 || B <= 0 || H <= 0 || N <= 0) return 0;
+  return fa::bwd_workspace_bytes(B, H, N);
 }
 
 int fa_fwd_key_groups(fa_dtype dtype, int B, int H, int N, int N_k, int d, int block_q) {
@@ -256,8 +255,6 @@ fa_status bwd_impl(int phases, fa_dtype dtype, const void* q, fa_strides q_strid
     return fail(FA_ERR_INVALID_ARG, "seqlens_k is not 4-byte aligned");
   fa::Dropout drop{};
   if ((st = make_dropout(dropout_p, seed, offset, &drop)) != FA_OK) return st;
-  if (d != 64 && drop.t < 256)
-    return fail(FA_ERR_UNSUPPORTED, "head dimension %d is built without dropout only", d);
 
   fa::BwdArgs a{};
   a.q = q;
@@ -266,6 +263,7 @@ fa_status bwd_impl(int phases, fa_dtype dtype, const void* q, fa_strides q_strid
   a.o = o;
   a.dout = dout;
   a.lse = lse;
+  a.dsum = need > 0 ? static_cast<float*>(workspace) : nullptr;
   a.dq = dq;
   a.dk = dk;
   a.dv = dv;

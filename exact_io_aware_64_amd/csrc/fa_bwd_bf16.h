@@ -11,17 +11,21 @@
 // One kernel, launched once, whose workgroups take one of two roles; no
 // gradient needs atomics or a transpose of dS, and the roles share nothing:
 //  * dQ role: query-stationary, like the forward.  Each lane owns one query
-//    with its Q, dO fragments, L and D in registers (D computed from its own
-//    dO and O rows); K/V tiles stream through LDS.  S^T = K Q^T and
+//    with its Q, dO fragments, L and D in registers; K/V tiles stream through
+//    LDS.  S^T = K Q^T and
 //    dP^T = V dO^T come out of the MFMA with one query per lane, and
 //    dQ^T = K^T dS^T takes dS^T straight from the accumulator.
 //  * dK/dV role: key-stationary.  Each lane owns one key with its K, V
-//    fragments in registers; Q, dO and O tiles and L stream through LDS, and
-//    each wave computes D for the rows it copied.  S = Q K^T and dP = dO V^T
+//    fragments in registers; Q and dO tiles, L and D stream through LDS.  S = Q K^T and dP = dO V^T
 //    come out with one key per lane, which is exactly the B operand of
 //    dV^T = dO^T P and dK^T = Q^T dS.
 // One launch carries both roles, heaviest work first, so that the GPU stays
-// busy to the end without a second kernel's launch gap and tail.  Masked
+// busy to the end without a second kernel's launch gap and tail.  It is
+// preceded by a small pass that writes D_i = dot(dO_i, O_i) of every query
+// row to the workspace: the dK/dV role would otherwise copy an O tile into
+// LDS next to every Q and dO tile it stages, only to form D (a third more
+// tile traffic and LDS writes; the pass measured 4-6 % faster at 16K causal
+// and 64K block-sparse, and even at 1K).  Masked
 // tiles are skipped exactly as in the forward pass.
 //
 // Dropout (DROP), with keep indicator Z and keep scale s:
@@ -99,30 +103,24 @@ __device__ __forceinline__ void dq_role(const BwdArgs& a, int item, uint16_t* s_
       (const uint16_t*)a.k + b * a.sk.b + hh * a.sk.h, slice_bytes(a.Nk, a.sk.s, 2, D));
   const __amdgpu_buffer_rsrc_t rv = make_rsrc(
       (const uint16_t*)a.v + b * a.sv.b + hh * a.sv.h, slice_bytes(a.Nk, a.sv.s, 2, D));
-  const __amdgpu_buffer_rsrc_t ro = make_rsrc(
-      (const uint16_t*)a.o + b * a.so.b + hh * a.so.h, slice_bytes(a.N, a.so.s, 2, D));
   const __amdgpu_buffer_rsrc_t rdo = make_rsrc(
       (const uint16_t*)a.dout + b * a.sdo.b + hh * a.sdo.h, slice_bytes(a.N, a.sdo.s, 2, D));
   const int ssk = (int)a.sk.s * 2, ssv = (int)a.sv.s * 2;
 
   // Q and dO fragments (B operands, lane (r, hl) holds row qi, columns
-  // 16 ks + 8 hl .. +7) and D_i = dot(dO_i, O_i) over the two wave halves.
+  // 16 ks + 8 hl .. +7) and D_i from the pre-pass.
   bf16x8 qf[KS], dof[KS];
   float Dq = 0.f;
   {
     const int oq = qi * (int)a.sq.s * 2 + 16 * hl;
     const int odo = qi * (int)a.sdo.s * 2 + 16 * hl;
-    const int oo = qi * (int)a.so.s * 2 + 16 * hl;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       qf[ks] = as_bf16x8(ldb16(rq, oq + 32 * ks));
       dof[ks] = as_bf16x8(ldb16(rdo, odo + 32 * ks));
-      const bf16x8 of = as_bf16x8(ldb16(ro, oo + 32 * ks));
-#pragma unroll
-      for (int e = 0; e < 8; ++e) Dq += (float)dof[ks][e] * (float)of[e];
     }
+    if (qi < a.N) Dq = a.dsum[(int64_t)bh * a.N + qi];
   }
-  Dq = half_sum(Dq);
   float L2 = kInf;  // +inf makes every probability of a dead or padding row 0
   if (qi < a.N) {
     const float L = a.lse[(int64_t)bh * a.N + qi];
@@ -144,7 +142,6 @@ __device__ __forceinline__ void dq_role(const BwdArgs& a, int item, uint16_t* s_
   for (int hi = 0; hi < 2; ++hi)
 #pragma unroll
     for (int db = 0; db < 2; ++db) troff[hi][db] = tr_off(lane, hi, db);
-  static_assert(!DROP || D == 64, "dropout is built for D = 64");
 
   auto tile_at = [&](int it) FA_INLINE -> int {
     if constexpr (BMASK) return tlist[it];
@@ -245,15 +242,15 @@ __device__ __forceinline__ void dq_role(const BwdArgs& a, int item, uint16_t* s_
         spread_chunks<2 * KS, 2 * KS>(t, [&](int cc) FA_INLINE { probs(0, cc); });
         spread_chunks<4 * KS, 2 * DB>(t, [&](int cc) FA_INLINE { probs(1, cc); });
       }
-      if constexpr (DROP) {  // half t / 4, in the MFMA-only slots 0..7
-        if (t < 8) {
-          DropBlock& z = zb[t >> 2];
-          if ((t & 3) == 0)
-            drop_start(z, (uint32_t)((k0 >> 2) + 8 * (t >> 2) + 2 * (lane & 3) + hl),
+      if constexpr (DROP) {  // half t / KS, in the MFMA-only slots 0 .. 2 KS - 1
+        if (t < 2 * KS) {
+          const int half = t / KS, u = t % KS;
+          DropBlock& z = zb[half];
+          if (u == 0)
+            drop_start(z, (uint32_t)((k0 >> 2) + 8 * half + 2 * (lane & 3) + hl),
                        (uint32_t)(qi >> 2), (uint32_t)bh, a.drop.offset);
-          const int r0 = (10 * (t & 3)) >> 2, r1 = (10 * ((t & 3) + 1)) >> 2;
-          philox_rounds(z.v, a.drop.seed_lo, a.drop.seed_hi, r0, r1);
-          if ((t & 3) == 3) drop_finish<false>(z, lane);
+          philox_rounds(z.v, a.drop.seed_lo, a.drop.seed_hi, (10 * u) / KS, (10 * (u + 1)) / KS);
+          if (u == KS - 1) drop_finish<false>(z, lane);
         }
       }
       FA_FENCE();
@@ -308,14 +305,13 @@ __device__ __forceinline__ void dq_role(const BwdArgs& a, int item, uint16_t* s_
 // ---------------------------------------------------------------- dK, dV
 
 // dK, dV for the 128 keys of work item `item` (key tile, batch, head).
-// s_q0/s_do0/s_o0 and s_q1/s_do1/s_o1 are the two Q/dO/O tile buffers; s_nl
-// and s_nd hold -L / scale and -D of each buffer's 64 rows.  With D = 128 the
+// s_q0/s_do0 and s_q1/s_do1 are the two Q/dO tile buffers; s_nl and s_nd
+// hold -L / scale and -D of each buffer's 64 rows.  With D = 128 the
 // accumulators of dK^T and dV^T take 128 registers per lane; that variant
 // runs one wave per SIMD and keeps them in the accumulation registers.
 template <int D, bool CAUSAL, bool SEQLEN, bool BMASK, bool DROP>
 __device__ __forceinline__ void dkdv_role(const BwdArgs& a, int item, uint16_t* s_q0,
-                                          uint16_t* s_do0, uint16_t* s_o0, uint16_t* s_q1,
-                                          uint16_t* s_do1, uint16_t* s_o1,
+                                          uint16_t* s_do0, uint16_t* s_q1, uint16_t* s_do1,
                                           float (*s_nl)[kTile], float (*s_nd)[kTile],
                                           uint16_t* s_list, int* s_scan) {
   const int tid = threadIdx.x, lane = tid & 63;
@@ -324,7 +320,6 @@ __device__ __forceinline__ void dkdv_role(const BwdArgs& a, int item, uint16_t* 
   const int BH = a.B * a.H;
   constexpr int KS = D / 16;                  // contraction steps over d
   constexpr int DBo = D / 32;                 // 32-row blocks of dK^T, dV^T
-  static_assert(!DROP || D == 64, "dropout is built for D = 64");
   // Causal: key tile 0 sees every query, so ascending items are heaviest first.
   const int kt = item / BH;
   const int bh = item % BH;
@@ -364,10 +359,8 @@ __device__ __forceinline__ void dkdv_role(const BwdArgs& a, int item, uint16_t* 
         make_rsrc((const uint16_t*)a.v + b * a.sv.b + hh * a.sv.h, slice_bytes(a.Nk, a.sv.s, 2, D));
     const __amdgpu_buffer_rsrc_t rdo = make_rsrc(
         (const uint16_t*)a.dout + b * a.sdo.b + hh * a.sdo.h, slice_bytes(a.N, a.sdo.s, 2, D));
-    const __amdgpu_buffer_rsrc_t ro = make_rsrc(
-        (const uint16_t*)a.o + b * a.so.b + hh * a.so.h, slice_bytes(a.N, a.so.s, 2, D));
     const float* lse = a.lse + (int64_t)bh * a.N;
-    const int ssq = (int)a.sq.s * 2, ssdo = (int)a.sdo.s * 2, sso = (int)a.so.s * 2;
+    const int ssq = (int)a.sq.s * 2, ssdo = (int)a.sdo.s * 2;
 
     // K and V fragments (B operands): lane (r, hl) holds row kj, columns
     // 16 ks + 8 hl .. +7.
@@ -399,58 +392,40 @@ __device__ __forceinline__ void dkdv_role(const BwdArgs& a, int item, uint16_t* 
 #pragma unroll
       for (int db = 0; db < 2; ++db) troff[hi][db] = tr_off(lane, hi, db);
 
-    // Raw L of row qs + tid (threads 0..63), converted only when it is
-    // written to LDS so that no wait on the load sits at the start of a tile.
-    // Rows past N read as 0 through the buffer resources.
-    float lraw = 0.f;
+    // Raw L and D of row qs + tid (threads 0..63), converted only when they
+    // are written to LDS so that no wait on the loads sits at the start of a
+    // tile.  Rows past N read as 0 through the buffer resources.
+    float lraw = 0.f, draw = 0.f;
     int lrow = 0;
     const __amdgpu_buffer_rsrc_t rl = make_rsrc(lse, (uint32_t)a.N * 4);
+    const __amdgpu_buffer_rsrc_t rds = make_rsrc(a.dsum + (int64_t)bh * a.N, (uint32_t)a.N * 4);
     auto tile_at = [&](int it) FA_INLINE -> int {
       if constexpr (BMASK) return tlist[it];
       return qt_lo + it;
     };
-    // Q, dO and O tiles go straight to LDS; L through registers.
-    auto gload = [&](int t, uint16_t* qt_, uint16_t* dt_, uint16_t* ot_) FA_INLINE {
+    // Q and dO tiles go straight to LDS; L and D through registers.
+    auto gload = [&](int t, uint16_t* qt_, uint16_t* dt_) FA_INLINE {
       const int qs = t * kTile;
 #pragma unroll
       for (int j = 0; j < (D > 64 ? D / 64 : 1); ++j) {
         stage_tile(rq, qs, ssq, qt_ + j * kTileElems, w, lane, 128 * j);
         stage_tile(rdo, qs, ssdo, dt_ + j * kTileElems, w, lane, 128 * j);
-        stage_tile(ro, qs, sso, ot_ + j * kTileElems, w, lane, 128 * j);
       }
       if (tid < kTile) {
         lrow = qs + tid;
         lraw = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rl, 4 * lrow, 0, 0));
+        draw = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rds, 4 * lrow, 0, 0));
       }
     };
-    // After the wave's own copies are complete: -L / scale of the tile's
-    // rows (threads 0..63) and -D of the 16 rows this wave copied, D_i =
-    // dot(dO_i, O_i) over four lanes per row.  The barrier that follows
-    // publishes both to every wave.
-    auto swrite = [&](int buf, const uint16_t* dt_, const uint16_t* ot_) FA_INLINE {
+    // After the loads are complete: -L / scale and -D of the tile's rows
+    // (threads 0..63); the barrier that follows publishes them to every wave.
+    auto swrite = [&](int buf) FA_INLINE {
       if (tid < kTile) {
         // -inf makes every probability of a dead or missing row 0
         const bool live = lrow < a.N && lraw != -kInf;
         s_nl[buf][tid] = live ? -lraw * inv_scale : -kInf;
+        s_nd[buf][tid] = -draw;  // rows past N read as zeros: D = 0
       }
-      // lanes 0..31: rows 8 w .. 8 w + 7, lanes 32..63: rows 8 w + 32 .. + 39
-      const int rl = stage_row(w, lane >> 2 << 3 & 63, lane >> 5), qq = lane & 3;
-      float acc = 0.f;
-      if constexpr (D == 32) {  // 8 columns per lane
-        const int off = toff(rl, 8 * qq);
-        acc = dot8_bf16(tile_row8(dt_, off), tile_row8(ot_, off), acc);
-      } else {  // 16 columns per lane in each 64-column block
-#pragma unroll
-        for (int j = 0; j < D / 64; ++j)
-#pragma unroll
-          for (int cc = 0; cc < 2; ++cc) {
-            const int off = j * kTileElems + toff(rl, 16 * qq + 8 * cc);
-            acc = dot8_bf16(tile_row8(dt_, off), tile_row8(ot_, off), acc);
-          }
-      }
-      acc += quad_xor1(acc);
-      acc += quad_xor2(acc);
-      if (qq == 0) s_nd[buf][rl] = -acc;  // rows past N read as zeros: D = 0
     };
 
     // One 64-query tile as 32 issue slots, each holding one MFMA, a share
@@ -572,16 +547,17 @@ __device__ __forceinline__ void dkdv_role(const BwdArgs& a, int item, uint16_t* 
           spread_chunks<2 * KS, 2 * KS>(t, [&](int cc) FA_INLINE { probs(0, cc); });
           spread_chunks<4 * KS, 4 * DBo>(t, [&](int cc) FA_INLINE { probs(1, cc); });
         }
-        if constexpr (DROP) {  // half t / 4, in slots 0..7
-          if (t < 8) {
-            DropBlock& z = zb[t >> 2];
-            if ((t & 3) == 0)
+        if constexpr (DROP) {  // half t / KS, in slots 0 .. 2 KS - 1
+          if (t < 2 * KS) {
+            const int half = t / KS, u = t % KS;
+            DropBlock& z = zb[half];
+            if (u == 0)
               drop_start(z, (uint32_t)(kj >> 2),
-                         (uint32_t)((qs >> 2) + 8 * (t >> 2) + 2 * (lane & 3) + hl),
+                         (uint32_t)((qs >> 2) + 8 * half + 2 * (lane & 3) + hl),
                          (uint32_t)bh, a.drop.offset);
-            const int r0 = (10 * (t & 3)) >> 2, r1 = (10 * ((t & 3) + 1)) >> 2;
-            philox_rounds(z.v, a.drop.seed_lo, a.drop.seed_hi, r0, r1);
-            if ((t & 3) == 3) drop_finish<true>(z, lane);
+            philox_rounds(z.v, a.drop.seed_lo, a.drop.seed_hi, (10 * u) / KS,
+                          (10 * (u + 1)) / KS);
+            if (u == KS - 1) drop_finish<true>(z, lane);
           }
         }
         FA_FENCE();
@@ -601,9 +577,9 @@ __device__ __forceinline__ void dkdv_role(const BwdArgs& a, int item, uint16_t* 
     };
 
     if (nlist > 0) {
-      gload(tile_at(0), s_q0, s_do0, s_o0);
+      gload(tile_at(0), s_q0, s_do0);
       __builtin_amdgcn_s_waitcnt(0);
-      swrite(0, s_do0, s_o0);
+      swrite(0);
     }
     // Every load issued so far (K, V fragments, first tile) is complete here;
     // saying so also keeps the loop's wait counts from covering them.
@@ -612,16 +588,16 @@ __device__ __forceinline__ void dkdv_role(const BwdArgs& a, int item, uint16_t* 
 
     // Two tiles per trip so that each buffer is a fixed array.
     for (int it = 0; it < nlist; it += 2) {
-      if (it + 1 < nlist) gload(tile_at(it + 1), s_q1, s_do1, s_o1);
+      if (it + 1 < nlist) gload(tile_at(it + 1), s_q1, s_do1);
       compute(it, 0, s_q0, s_do0);
       __builtin_amdgcn_s_waitcnt(0);
-      if (it + 1 < nlist) swrite(1, s_do1, s_o1);
+      if (it + 1 < nlist) swrite(1);
       __syncthreads();
       if (it + 1 >= nlist) break;
-      if (it + 2 < nlist) gload(tile_at(it + 2), s_q0, s_do0, s_o0);
+      if (it + 2 < nlist) gload(tile_at(it + 2), s_q0, s_do0);
       compute(it + 1, 1, s_q1, s_do1);
       __builtin_amdgcn_s_waitcnt(0);
-      if (it + 2 < nlist) swrite(0, s_do0, s_o0);
+      if (it + 2 < nlist) swrite(0);
       __syncthreads();
     }
   }
@@ -658,15 +634,13 @@ template <int D, bool CAUSAL, bool SEQLEN, bool BMASK, bool DROP>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 64 ? 2 : 1, D == 64 ? 2 : 8))) void bwd_kernel(
     BwdArgs a, int phases) {
   constexpr int KB = D > 64 ? D / 64 : 1;   // 64-column blocks per LDS tile
-  // Six tile arrays: the dQ role uses two per buffer (K, V), the dK/dV role
-  // three (Q, dO, O).  Separate arrays, so that the copies into one buffer
-  // and the reads of the other never alias.
+  // Four tile arrays, two per buffer: K and V in the dQ role, Q and dO in
+  // the dK/dV role.  Separate arrays, so that the copies into one buffer and
+  // the reads of the other never alias.
   __shared__ __attribute__((aligned(16))) uint16_t s_a0[KB * kTileElems];
   __shared__ __attribute__((aligned(16))) uint16_t s_b0[KB * kTileElems];
-  __shared__ __attribute__((aligned(16))) uint16_t s_c0[KB * kTileElems];
   __shared__ __attribute__((aligned(16))) uint16_t s_a1[KB * kTileElems];
   __shared__ __attribute__((aligned(16))) uint16_t s_b1[KB * kTileElems];
-  __shared__ __attribute__((aligned(16))) uint16_t s_c1[KB * kTileElems];
   __shared__ __attribute__((aligned(16))) float s_nl[2][kTile];  // -L / scale
   __shared__ __attribute__((aligned(16))) float s_nd[2][kTile];  // -D
   __shared__ uint16_t s_list[BMASK ? kMaxListTiles : 1];
@@ -719,14 +693,49 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 64 ? 2
     item = id;
   }
   if (dkdv)
-    dkdv_role<D, CAUSAL, SEQLEN, BMASK, DROP>(a, item, s_a0, s_b0, s_c0, s_a1, s_b1, s_c1,
-                                              s_nl, s_nd, s_list, s_scan);
+    dkdv_role<D, CAUSAL, SEQLEN, BMASK, DROP>(a, item, s_a0, s_b0, s_a1, s_b1, s_nl, s_nd,
+                                              s_list, s_scan);
   else
     dq_role<D, CAUSAL, SEQLEN, BMASK, DROP>(a, item, s_a0, s_b0, s_a1, s_b1, s_list, s_scan);
 }
 
+// D_i = dot(dO_i, O_i) of every query row into a.dsum (fp32 [B*H*N]): 64
+// rows per workgroup, four threads per row, each taking a quarter of the
+// row's D elements in 16-byte loads (rows are 16-byte aligned).
+template <int D>
+__global__ __launch_bounds__(256) void dsum_kernel(BwdArgs a) {
+  const int tid = threadIdx.x;
+  const int nrt = (a.N + 63) / 64;
+  const int bh = blockIdx.x / nrt, rt = blockIdx.x % nrt;
+  const int b = bh / a.H, hh = bh % a.H;
+  const int row = rt * 64 + (tid >> 2), part = tid & 3;
+  float acc = 0.f;
+  if (row < a.N) {
+    const uint16_t* dop = (const uint16_t*)a.dout + b * a.sdo.b + hh * a.sdo.h +
+                          (int64_t)row * a.sdo.s + part * (D / 4);
+    const uint16_t* op =
+        (const uint16_t*)a.o + b * a.so.b + hh * a.so.h + (int64_t)row * a.so.s + part * (D / 4);
+#pragma unroll
+    for (int c = 0; c < D / 4; c += 8)
+      acc = dot8_bf16(*reinterpret_cast<const bf16x8*>(dop + c),
+                      *reinterpret_cast<const bf16x8*>(op + c), acc);
+  }
+  acc += quad_xor1(acc);
+  acc += quad_xor2(acc);
+  if (part == 0 && row < a.N) a.dsum[(int64_t)bh * a.N + row] = acc;
+}
+
 template <int HD, bool C, bool S, bool M, bool D>
 hipError_t launch(const BwdArgs& a, int phases, hipStream_t stream) {
+  {
+    BwdArgs c = a;
+    void* args[] = {&c};
+    const int nrt = (a.N + 63) / 64;
+    const hipError_t e =
+        hipLaunchKernel((const void*)&dsum_kernel<HD>, dim3((unsigned)(nrt * a.B * a.H)),
+                        dim3(256), args, 0, stream);
+    if (e != hipSuccess) return e;
+  }
   BwdArgs copy = a;
   int ph = phases;
   void* args[] = {&copy, &ph};

@@ -1,4 +1,4 @@
-// Attention backward, bf16, head dimension 128 (no dropout).  The kernel
+// Attention backward, bf16, head dimension 128, with and without dropout.  The kernel
 // templates are in fa_bwd_bf16.h.  This file is compiled without the flag that
 // keeps MFMA accumulators in the architectural VGPRs: at one wave per SIMD the
 // dK/dV role's accumulators (64 KB of dK^T and dV^T per wave) then live in the
@@ -10,7 +10,8 @@ namespace fa {
 
 hipError_t launch_bwd_bf16_d128(const BwdArgs& a, bool causal, int phases,
                                 hipStream_t stream) {
-  return dispatch<128, false>(a, causal, phases, stream);
+  return a.drop.t < 256 ? dispatch<128, true>(a, causal, phases, stream)
+                        : dispatch<128, false>(a, causal, phases, stream);
 }
 
 }  // namespace fa

@@ -82,7 +82,6 @@ constexpr float kSumLimit = 4096.f;    // largest partial sum the fast path acce
 template <int W, int G, int D, bool SEQLEN, bool BMASK, bool DROP>
 __global__ __launch_bounds__(64 * W * G) __attribute__((amdgpu_waves_per_eu((D == 64 && (W == 4 || (W == 2 && !BMASK))) ? 3 : 1, 8))) void fwd_bf16_kernel(FwdArgs a) {
   static_assert(D == 32 || D == 64 || D == 128, "head dimension 32, 64 or 128");
-  static_assert(!DROP || D == 64, "dropout is built for D = 64");
   constexpr int kBR = 32 * W;
   constexpr int KB = D > 64 ? D / 64 : 1;  // 64-column blocks per tile
   constexpr int KS = D / 16;               // contraction steps of S^T; slots per phase
@@ -300,14 +299,17 @@ __global__ __launch_bounds__(64 * W * G) __attribute__((amdgpu_waves_per_eu((D =
                        o[db]);
       }
       if (t + LEAD < 4 * KS) load_a(t + LEAD);
-      if constexpr (DROP) {  // half i / 2: rounds 0..4 in even slots, 5..9 in odd
+      if constexpr (DROP) {  // half i / (KS / 2), its ten rounds over KS / 2 slots
         if (ph == 0) {
-          DropBlock& z = zb[i >> 1];
-          if ((i & 1) == 0)
-            drop_start(z, (uint32_t)((k0 >> 2) + 8 * (i >> 1) + 2 * (lane & 3) + hl),
+          constexpr int NSUB = KS / 2;
+          const int half = i / NSUB, u = i % NSUB;
+          DropBlock& z = zb[half];
+          if (u == 0)
+            drop_start(z, (uint32_t)((k0 >> 2) + 8 * half + 2 * (lane & 3) + hl),
                        (uint32_t)(qi >> 2), (uint32_t)bh, a.drop.offset);
-          philox_rounds(z.v, a.drop.seed_lo, a.drop.seed_hi, 5 * (i & 1), 5 * (i & 1) + 5);
-          if (i & 1) drop_finish<false>(z, lane);
+          philox_rounds(z.v, a.drop.seed_lo, a.drop.seed_hi, (10 * u) / NSUB,
+                        (10 * (u + 1)) / NSUB);
+          if (u == NSUB - 1) drop_finish<false>(z, lane);
         }
       }
       if (ph == 1 || ph == 2) {  // P of half ph - 1, four elements per call
@@ -481,11 +483,15 @@ int fwd_key_groups(int B, int H, int N, int Nk, int d, int block_q) {
 
 hipError_t launch_fwd_bf16(const FwdArgs& a, bool causal, int block_q, int d,
                            hipStream_t stream) {
-  // the host allows d != 64 only without dropout and with block_q = 128
-  if (d == 32) return dispatch<4, 32, false, groups_for_d(32)>(a, causal, stream);
-  if (d == 128) return dispatch<4, 128, false, groups_for_d(128)>(a, causal, stream);
-  if (a.drop.t < 256)  // block_q == 128
-    return dispatch<4, 64, true, groups_for_d(64)>(a, causal, stream);
+  // the host allows dropout and d != 64 only with block_q = 128
+  const bool drop = a.drop.t < 256;
+  if (d == 32)
+    return drop ? dispatch<4, 32, true, groups_for_d(32)>(a, causal, stream)
+                : dispatch<4, 32, false, groups_for_d(32)>(a, causal, stream);
+  if (d == 128)
+    return drop ? dispatch<4, 128, true, groups_for_d(128)>(a, causal, stream)
+                : dispatch<4, 128, false, groups_for_d(128)>(a, causal, stream);
+  if (drop) return dispatch<4, 64, true, groups_for_d(64)>(a, causal, stream);
   if (block_q == 64) return dispatch<2, 64, false>(a, causal, stream);
   if (block_q == 256) return dispatch<8, 64, false>(a, causal, stream);
   return dispatch<4, 64, false, groups_for_d(64)>(a, causal, stream);

@@ -54,6 +54,7 @@ struct BwdArgs {
   const void* o;
   const void* dout;
   const float* lse;
+  float* dsum;  // D_i = dot(dO_i, O_i), fp32 [B*H*N] (the caller's workspace)
   void* dq;
   void* dk;
   void* dv;
@@ -84,7 +85,12 @@ hipError_t launch_fwd_bf16(const FwdArgs& a, bool causal, int block_q, int d,
 // on the current device: 3 (2 for d = 128) when block_q is 128, the keys span
 // at least 1024 rows and the grid holds at most one query tile per CU, else 1.
 int fwd_key_groups(int B, int H, int N, int Nk, int d, int block_q);
-// d: head dimension, 32, 64 or 128 (64 with dropout).
+// Bytes of the bf16 backward's workspace: D for every query row.
+inline size_t bwd_workspace_bytes(int B, int H, int N) {
+  return (((size_t)B * H * N * 4) + 255) & ~(size_t)255;
+}
+// d: head dimension, 32, 64 or 128 (64 with dropout).  a.dsum must hold
+// bwd_workspace_bytes(B, H, N) bytes.
 hipError_t launch_bwd_bf16(const BwdArgs& a, bool causal, int phases, int d,
                            hipStream_t stream);
 // The d = 128 instantiation of the above, from its own translation unit.

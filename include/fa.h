@@ -57,8 +57,7 @@ typedef enum fa_status {
   FA_ERR_INVALID_ARG = 1, /* null pointer, bad size, stride or alignment, scale <= 0,
                              workspace too small, bad mask_block, bad dropout_p */
   FA_ERR_UNSUPPORTED = 2, /* valid request the library does not implement (d other than
-                             32/64/128, d != 64 with fp32 or dropout, too many mask
-                             tiles) */
+                             32/64/128, d != 64 with fp32, too many mask tiles) */
   FA_ERR_HIP = 3          /* a HIP launch reported an error */
 } fa_status;
 
@@ -77,8 +76,8 @@ typedef struct fa_strides {
  *   o            device pointer, same element type, written in full.
  *   lse          device fp32 [B*H*N], contiguous, written in full (L above).
  *   B, H, N      >= 1.
- *   d            head dimension: 64; 32 and 128 for FA_BF16 without dropout
- *                (FA_ERR_UNSUPPORTED otherwise).
+ *   d            head dimension: 32, 64 or 128 for FA_BF16, with or without
+ *                dropout; 64 for FA_F32 (FA_ERR_UNSUPPORTED otherwise).
  *   scale        score scale (> 0, finite), typically 1/sqrt(d).
  *   causal       nonzero: key j is visible to query i only if j <= i.
  *   seqlens_k    NULL, or device int32[B]: keys j >= seqlens_k[b] are masked
@@ -105,10 +104,17 @@ fa_status fa_fwd(fa_dtype dtype,
                  hipStream_t stream);
 
 /*
- * fa_bwd_workspace_bytes -- device workspace that fa_bwd, fa_bwd_dq and
- * fa_bwd_dkdv need.  Every kernel of the library keeps its per-row statistics
- * (L, D = dot(dO_i, O_i)) on chip, so the result is 0 for every problem; the
- * workspace arguments are kept so that a future kernel may use them.
+ * fa_bwd_workspace_bytes -- device workspace that fa_bwd, fa_bwd_dq,
+ * fa_bwd_dkdv, fa_bwd_dropout and fa_bwd_qk need.  The bf16 backward pass
+ * first writes D_i = dot(dO_i, O_i) of every query row there (fp32, one
+ * value per row; the quantity its gradient formula subtracts from dP, which
+ * the pages leave to be derived -- researchpapers.dev explainer, "tiling and
+ * recomputation": the backward pass recomputes from saved statistics), and
+ * its main kernel reads it back.  Result: 4 * B * H * N bytes rounded up to
+ * a multiple of 256 for FA_BF16 (N = the number of query rows, N_q for
+ * fa_bwd_qk), 0 for FA_F32 (whose kernels keep D on chip) and for
+ * non-positive sizes.  Linear in N: nothing of size N x N.  The contents on
+ * return are D (callers may ignore them); they need no initialisation.
  */
 size_t fa_bwd_workspace_bytes(fa_dtype dtype, int B, int H, int N, int d);
 
@@ -136,15 +142,17 @@ int fa_fwd_key_groups(fa_dtype dtype, int B, int H, int N, int N_k, int d, int b
  * fa_bwd -- backward pass: writes dQ, dK and dV in full (zeros for keys that
  * no query sees, e.g. keys past seqlens_k).  The scores and probabilities are
  * recomputed tile by tile from q, k and the forward's lse; nothing of size
- * N x N is read or written.  One kernel launch.
+ * N x N is read or written.  Two kernel launches: the D pass, then one
+ * kernel for all of dQ, dK and dV.
  *
  *   q, k, v, o, lse  the forward pass's inputs and outputs (o and lse as
  *                    written by fa_fwd with the same mask arguments).
  *   dout             upstream gradient dO, [B][H][N][d] through its strides.
  *   dq, dk, dv       outputs, element type dtype, through their strides.
  *   workspace        device buffer of at least fa_bwd_workspace_bytes(...) bytes
- *                    (16-byte aligned); may be NULL when that size is 0, as it is
- *                    for every problem.
+ *                    (16-byte aligned), overwritten; may be NULL only when that
+ *                    size is 0 (FA_ERR_INVALID_ARG otherwise).  Two backward
+ *                    calls that run at the same time need separate workspaces.
  *   remaining arguments as for fa_fwd and must match the forward call.
  */
 fa_status fa_bwd(fa_dtype dtype,

@@ -43,8 +43,12 @@ def test_status_strings():
 
 
 def test_workspace_bytes():
-    # every backward kernel keeps its row statistics on chip
-    assert fa.fa_bwd_workspace_bytes(0, 8, 12, 1024, 64) == 0
+    # bf16: one fp32 D per query row, rounded up to 256 bytes; fp32 kernels
+    # keep D on chip
+    assert fa.fa_bwd_workspace_bytes(0, 8, 12, 1024, 64) == 8 * 12 * 1024 * 4
+    assert fa.fa_bwd_workspace_bytes(0, 1, 8, 65536, 64) == 8 * 65536 * 4
+    assert fa.fa_bwd_workspace_bytes(0, 1, 1, 3, 128) == 256
+    assert fa.fa_bwd_workspace_bytes(0, 2, 3, 100, 32) == 2560
     assert fa.fa_bwd_workspace_bytes(1, 1, 1, 3, 64) == 0
     assert fa.fa_bwd_workspace_bytes(0, 0, 1, 3, 64) == 0
 
@@ -112,6 +116,10 @@ def test_fwd_rejects_bad_arguments(kw, status, msg):
     (dict(dtype=1, sdv=bnd.fa_strides(64, 64, 66)), 1, "multiples of 4"),
     (dict(d=96), 2, "head dimension"),
     (dict(d=32, dtype=1), 2, "head dimension"),
+    (dict(ws=None, wsb=0), 1, "workspace is NULL"),
+    (dict(wsb=4095), 1, "workspace too small"),
+    (dict(ws=A + 8), 1, "workspace is not 16-byte aligned"),
+    (dict(B=2, wsb=4096), 1, "workspace too small"),
 ])
 def test_bwd_rejects_bad_arguments(kw, status, msg):
     assert _bwd(**kw) == status
@@ -142,6 +150,7 @@ def _bwd_dkdv(**kw):
     (dict(o=A + 4), 1, "o is not 16-byte aligned"),
     (dict(lse=None), 1, "lse is NULL"),
     (dict(N=0), 1, "must be positive"),
+    (dict(ws=None, wsb=0), 1, "workspace is NULL"),
 ])
 def test_bwd_dq_rejects_bad_arguments(kw, status, msg):
     assert _bwd_dq(**kw) == status
@@ -155,6 +164,7 @@ def test_bwd_dq_rejects_bad_arguments(kw, status, msg):
     (dict(do=None), 1, "dout is NULL"),
     (dict(d=96), 2, "head dimension"),
     (dict(d=128, dtype=1), 2, "head dimension"),
+    (dict(wsb=1024), 1, "workspace too small"),
 ])
 def test_bwd_dkdv_rejects_bad_arguments(kw, status, msg):
     assert _bwd_dkdv(**kw) == status
@@ -187,7 +197,7 @@ def _fwd_drop(**kw):
 def _bwd_drop(**kw):
     lib = fa.load_library()
     args = dict(dtype=0, q=A, sq=S, k=A, sk=S, v=A, sv=S, o=A, so=S, do=A, sdo=S, lse=A,
-                dq=A, sdq=S, dk=A, sdk=S, dv=A, sdv=S, ws=None, wsb=0, B=1, H=1, N=1024,
+                dq=A, sdq=S, dk=A, sdk=S, dv=A, sdv=S, ws=A, wsb=4096, B=1, H=1, N=1024,
                 d=64, scale=0.125, causal=0, seqlens=None, bmask=None, mb=128, p=0.1, seed=1,
                 offset=0, stream=None)
     args.update(kw)
@@ -200,7 +210,9 @@ BAD_DROPOUT = [
     (dict(p=float("nan")), 1, "dropout_p must lie in [0, 1)"),
     (dict(p=0.999), 1, "rounds to dropping every pair"),
     (dict(p=0.1, q=None), 1, "q is NULL"),
-    (dict(p=0.1, d=32), 2, "head dimension"),
+    (dict(p=0.1, d=96), 2, "head dimension"),
+    (dict(p=0.1, d=32, dtype=1), 2, "head dimension"),
+    (dict(p=0.1, d=128, dtype=1), 2, "head dimension"),
 ]
 
 

@@ -40,16 +40,16 @@ def test_kernel_bytes():
     kb = bench.kernel_bytes(8, 12, 1024, 64, 2, None)
     t = 8 * 12 * 1024 * 64 * 2
     row = 8 * 12 * 1024 * 4
-    assert kb["fwd_bf16_kernel"] == 4 * t + row
-    assert kb["bwd_kernel"] == 8 * t + row
+    assert kb["fa_fwd"] == 4 * t + row
+    assert kb["fa_bwd"] == 8 * t + 3 * row  # L read, D written and read
     kb2 = bench.kernel_bytes(2, 1, 100, 64, 2, np.array([50, 100]))
-    assert kb2["fwd_bf16_kernel"] == 2 * (2 * 100 * 64 * 2) + 2 * (150 * 64 * 2) + 2 * 100 * 4
+    assert kb2["fa_fwd"] == 2 * (2 * 100 * 64 * 2) + 2 * (150 * 64 * 2) + 2 * 100 * 4
 
 
 def test_kernel_flops_are_the_method():
     kf = bench.kernel_flops(64, 1000)
-    assert kf["fwd_bf16_kernel"] == 4 * 64 * 1000
-    assert kf["bwd_kernel"] == 10 * 64 * 1000
+    assert kf["fa_fwd"] == 4 * 64 * 1000
+    assert kf["fa_bwd"] == 10 * 64 * 1000
 
 
 def test_more_than_one_gpu_is_refused(capsys):
@@ -102,8 +102,8 @@ def test_rectangular_pairs_match_brute_force(N, Nk, causal, seqlens, p):
 def test_rectangular_kernel_bytes():
     kb = bench.kernel_bytes(1, 2, 100, 64, 2, None, Nk=300)
     tq, tk = 2 * 100 * 64 * 2, 2 * 300 * 64 * 2
-    assert kb["fwd_bf16_kernel"] == 2 * tq + 2 * tk + 2 * 100 * 4
-    assert kb["bwd_kernel"] == 4 * tq + 4 * tk + 2 * 100 * 4
+    assert kb["fa_fwd"] == 2 * tq + 2 * tk + 2 * 100 * 4
+    assert kb["fa_bwd"] == 4 * tq + 4 * tk + 3 * 2 * 100 * 4
 
 
 def test_pipe_metrics_formulas():

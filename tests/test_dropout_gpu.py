@@ -67,13 +67,17 @@ def _visible(B, N, causal, seqlens):
     return vis
 
 
-def _zeros(B, H, N, dtype):
-    return np.zeros((B, H, N, 64), np.float32)
+def _zeros(B, H, N, d=64):
+    return np.zeros((B, H, N, d), np.float32)
 
 
-@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+# (dtype, head dimension): fp32 is built for d = 64 only
+DTYPE_D = [("bf16", 64), ("f32", 64), ("bf16", 32), ("bf16", 128)]
+
+
+@pytest.mark.parametrize("dtype,d", DTYPE_D)
 @pytest.mark.parametrize("causal,padded", [(False, False), (True, False), (True, True)])
-def test_keep_mask_bit_exact_forward_and_dv(dtype, causal, padded):
+def test_keep_mask_bit_exact_forward_and_dv(dtype, d, causal, padded):
     fa = _fa()
     import torch
     B, H, N, p = 2, 3, 300, 0.5
@@ -81,15 +85,16 @@ def test_keep_mask_bit_exact_forward_and_dv(dtype, causal, padded):
     sl = opt_dev(seqlens)
     vis = _visible(B, N, causal, seqlens)
     z = _oracle_keep(B, H, N, p)
-    _say(f"[dropout mask fwd/dv] {dtype} causal={causal} padded={padded}")
-    zero = _zeros(B, H, N, dtype)
+    _say(f"[dropout mask fwd/dv] {dtype} d={d} causal={causal} padded={padded}")
+    zero = _zeros(B, H, N, d)
     q0 = to_dev(zero, dtype)
     kw = dict(scale=0.125, causal=causal, seqlens_k=sl, dropout_p=p, seed=SEED, offset=OFFSET)
     got_f = np.zeros((B, H, N, N), dtype=bool)
     got_b = np.zeros((B, H, N, N), dtype=bool)
-    for w0 in range(0, N, 64):
-        wn = min(64, N - w0)
-        onehot = np.zeros((B, H, N, 64), np.float32)
+    win = min(64, d)  # keys (queries) read back per call: one per output column
+    for w0 in range(0, N, win):
+        wn = min(win, N - w0)
+        onehot = np.zeros((B, H, N, d), np.float32)
         onehot[:, :, w0:w0 + wn, :][:, :, np.arange(wn), np.arange(wn)] = 1.0
         oh = to_dev(onehot, dtype)
         # forward: V one-hot over keys w0 .. w0 + wn
@@ -106,24 +111,25 @@ def test_keep_mask_bit_exact_forward_and_dv(dtype, causal, padded):
     _say(f"[dropout mask fwd/dv] ok, kept {want.sum()} of {vis.sum() * H} visible pairs")
 
 
-@pytest.mark.parametrize("dtype", ["bf16", "f32"])
-def test_keep_mask_bit_exact_dq_and_dk_signs(dtype):
+@pytest.mark.parametrize("dtype,d", DTYPE_D)
+def test_keep_mask_bit_exact_dq_and_dk_signs(dtype, d):
     fa = _fa()
     import torch
     B, H, N, p = 2, 2, 300, 0.5
     z = _oracle_keep(B, H, N, p)
-    _say(f"[dropout mask dq/dk] {dtype}")
-    zero = _zeros(B, H, N, dtype)
+    _say(f"[dropout mask dq/dk] {dtype} d={d}")
+    zero = _zeros(B, H, N, d)
     z0 = to_dev(zero, dtype)
-    e0 = np.zeros((B, H, N, 64), np.float32)
+    e0 = np.zeros((B, H, N, d), np.float32)
     e0[..., 0] = 1.0
     ones0 = to_dev(e0, dtype)  # v_j = dO_i = e_0, so dO_i . v_j = 1
     kw = dict(scale=0.125, causal=False, dropout_p=p, seed=SEED, offset=OFFSET)
     sign_q = np.zeros((B, H, N, N), dtype=np.int8)
     sign_k = np.zeros((B, H, N, N), dtype=np.int8)
-    for w0 in range(0, N, 64):
-        wn = min(64, N - w0)
-        onehot = np.zeros((B, H, N, 64), np.float32)
+    win = min(64, d)
+    for w0 in range(0, N, win):
+        wn = min(win, N - w0)
+        onehot = np.zeros((B, H, N, d), np.float32)
         onehot[:, :, w0:w0 + wn, :][:, :, np.arange(wn), np.arange(wn)] = 1.0
         oh = to_dev(onehot, dtype)
         # dQ role: Q = 0, K one-hot over keys w0 ..
@@ -176,6 +182,24 @@ def _check_random(case, p, seed, offset, tag):
 def test_dropout_parity_dense(dtype, N, causal):
     case = wl.random_case(2, 2, N, 64, dtype=dtype, seed=N + causal, causal=causal)
     _check_random(case, 0.1, SEED + N, 3, f"{dtype} N={N} causal={causal}")
+
+
+@pytest.mark.parametrize("d", [32, 128])
+@pytest.mark.parametrize("N", [17, 300, 1000])
+@pytest.mark.parametrize("causal", [False, True])
+def test_dropout_parity_head_dims(d, N, causal):
+    case = wl.random_case(2, 2, N, d, seed=N + d + causal, causal=causal)
+    _check_random(case, 0.1, SEED + N + d, 3, f"bf16 d={d} N={N} causal={causal}")
+
+
+@pytest.mark.parametrize("d", [32, 128])
+@pytest.mark.parametrize("masks", ["seqlens", "block", "both"])
+def test_dropout_parity_head_dims_masks(d, masks):
+    seqlens = "random" if masks in ("seqlens", "both") else None
+    keep = 0.5 if masks in ("block", "both") else None
+    case = wl.random_case(3, 2, 640, d, seed=31 + d, causal=True, seqlens=seqlens,
+                          block_keep_p=keep)
+    _check_random(case, 0.3, 777, 2, f"d={d} masks={masks}")
 
 
 @pytest.mark.parametrize("masks", ["seqlens", "block", "both"])
@@ -253,6 +277,42 @@ def test_sampled_full_size_gpt2_with_dropout():
     errs["dK"] = relfro(to_np(dk_r), gk)
     errs["dV"] = relfro(to_np(dv_r), gv)
     _say(f"[dropout sampled] {errs}")
+    tol = TOL["bf16"]
+    assert excess_over(to_np(o)[idx], O, tol["O"] * _keep_scale(p)) <= 0, errs
+    assert errs["L"] <= tol["L"], errs
+    for name in ("dQ", "dK", "dV"):
+        assert errs[name] <= tol["G"], (name, errs)
+
+
+def test_sampled_full_size_d128_training_with_dropout():
+    """Causal training shape with head dimension 128 (B=2, H=16, N=4096, bf16)
+    with p = 0.1: O, L and dQ on 128 sampled rows per head; dK, dV of the
+    problem whose dO is zero outside the sample."""
+    fa = _fa()
+    w = wl.WORKLOADS["train_causal_b2h16n4096d128"]
+    case = wl.make_inputs(w)
+    rows = case["rows"][:, :, :128]
+    p, seed, offset = 0.1, 2024, 0
+    _say("[dropout sampled] train_causal_b2h16n4096d128 p=0.1")
+    q, k, v, do, _, _ = device_inputs(dict(case, dtype="bf16"))
+    kw = dict(scale=w.scale, causal=True, dropout_p=p, seed=seed, offset=offset)
+    o, lse = fa.forward(q, k, v, **kw)
+    dq, _, _ = fa.backward(q, k, v, o, do, lse, **kw)
+    O, L = dref.forward(case["q"], case["k"], case["v"], w.scale, p, seed, offset, causal=True,
+                        rows=rows)
+    do_r = np.zeros_like(case["do"])
+    for b in range(w.B):
+        for h in range(w.H):
+            do_r[b, h, rows[b, h]] = case["do"][b, h, rows[b, h]]
+    gq, gk, gv = dref.backward(case["q"], case["k"], case["v"], do_r, w.scale, p, seed, offset,
+                               causal=True, rows=rows)
+    idx = (np.arange(w.B)[:, None, None], np.arange(w.H)[None, :, None], rows)
+    errs = dict(O=maxabs(to_np(o)[idx], O), L=maxabs(to_np(lse)[idx], L),
+                dQ=relfro(to_np(dq)[idx], gq))
+    _, dk_r, dv_r = fa.backward(q, k, v, o, to_dev(do_r, "bf16"), lse, **kw)
+    errs["dK"] = relfro(to_np(dk_r), gk)
+    errs["dV"] = relfro(to_np(dv_r), gv)
+    _say(f"[dropout sampled d128] {errs}")
     tol = TOL["bf16"]
     assert excess_over(to_np(o)[idx], O, tol["O"] * _keep_scale(p)) <= 0, errs
     assert errs["L"] <= tol["L"], errs

@@ -133,12 +133,17 @@ def test_headdim_backward_separate_lengths(d, Nq, Nk):
         assert relfro(to_np(a), b) <= TOL["bf16"]["G"], name
 
 
-def test_other_head_dims_reject_dropout():
+@pytest.mark.parametrize("d", [32, 128])
+def test_fp32_other_head_dims_are_rejected(d):
+    # the fp32 kernels are built for d = 64 (bf16 takes 32, 64 and 128, with
+    # or without dropout)
     import exact_io_aware_64_amd as fa
-    case = wl.random_case(1, 1, 64, 128, seed=1)
+    case = wl.random_case(1, 1, 64, d, dtype="f32", seed=1)
     q, k, v, do, _, _ = device_inputs(case)
-    with pytest.raises(fa.FaError, match="without dropout"):
+    with pytest.raises(fa.FaError, match="head dimension"):
         fa.forward(q, k, v, scale=0.1, dropout_p=0.1, seed=1)
+    with pytest.raises(fa.FaError, match="head dimension"):
+        fa.forward(q, k, v, scale=0.1)
 
 
 def test_d128_workload_sampled():
