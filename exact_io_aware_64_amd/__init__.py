@@ -13,6 +13,7 @@ from ._binding import (  # noqa: F401
     bwd,
     fa_bwd,
     fa_bwd_dkdv,
+    fa_bwd_noalloc,
     fa_bwd_dq,
     fa_bwd_qk,
     fa_bwd_dropout,

@@ -22,7 +22,7 @@ FA_ERR_UNSUPPORTED = 2
 FA_ERR_HIP = 3
 
 # Public entry points declared in include/fa.h.
-EXPORTED = ("fa_fwd", "fa_bwd", "fa_bwd_dq", "fa_bwd_dkdv", "fa_fwd_dropout",
+EXPORTED = ("fa_fwd", "fa_bwd", "fa_bwd_noalloc", "fa_bwd_dq", "fa_bwd_dkdv", "fa_fwd_dropout",
             "fa_bwd_dropout", "fa_fwd_tiled", "fa_fwd_qk", "fa_bwd_qk",
             "fa_bwd_workspace_bytes", "fa_fwd_key_groups", "fa_status_string",
             "fa_last_error")
@@ -60,6 +60,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.fa_bwd.restype = I
     lib.fa_bwd.argtypes = [I, P, S, P, S, P, S, P, S, P, S, P, P, S, P, S, P, S, P,
                            ctypes.c_size_t, I, I, I, I, F, I, P, P, I, P]
+    lib.fa_bwd_noalloc.restype = I
+    lib.fa_bwd_noalloc.argtypes = [I, P, S, P, S, P, S, P, S, P, S, P, P, S, P, S, P, S,
+                                   I, I, I, I, F, I, P, P, I, P]
     lib.fa_bwd_dq.restype = I
     lib.fa_bwd_dq.argtypes = [I, P, S, P, S, P, S, P, S, P, S, P, P, S, P, ctypes.c_size_t,
                               I, I, I, I, F, I, P, P, I, P]
@@ -337,6 +340,24 @@ def fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, workspace=None, *, scale: float,
     args = _bwd_args(q, k, v, o, dout, lse, dq, dk, dv, workspace, scale, causal, seqlens_k,
                      block_mask, mask_block)
     _check(lib.fa_bwd(*args, _stream(q, stream)))
+
+
+def fa_bwd_noalloc(q, k, v, o, dout, lse, dq, dk, dv, *, scale: float, causal: bool = False,
+                   seqlens_k=None, block_mask=None, mask_block: int = 128,
+                   stream=None) -> None:
+    """Calls fa_bwd_noalloc: fa_bwd with D in the library's own scratch array
+    (no workspace; calls that overlap on one GPU race)."""
+    lib = load_library()
+    named = (("k", k), ("v", v), ("o", o), ("dout", dout), ("dq", dq), ("dk", dk), ("dv", dv))
+    B, H, N, d = _check_like(q, named)
+    _check_aux(q, N, N, lse, seqlens_k, block_mask, mask_block, named)
+    st = lib.fa_bwd_noalloc(_dtype_code(q), _ptr(q), _strides(q), _ptr(k), _strides(k),
+                            _ptr(v), _strides(v), _ptr(o), _strides(o), _ptr(dout),
+                            _strides(dout), _ptr(lse), _ptr(dq), _strides(dq), _ptr(dk),
+                            _strides(dk), _ptr(dv), _strides(dv), B, H, N, d, float(scale),
+                            int(bool(causal)), _ptr(seqlens_k), _ptr(block_mask),
+                            int(mask_block), _stream(q, stream))
+    _check(st)
 
 
 def fa_bwd_dropout(q, k, v, o, dout, lse, dq, dk, dv, workspace=None, *, scale: float,

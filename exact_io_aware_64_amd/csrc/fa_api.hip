@@ -5,6 +5,8 @@
 
 #include <math.h>
 #include <stdarg.h>
+
+#include <mutex>
 #include <stdio.h>
 #include <string.h>
 
@@ -214,6 +216,43 @@ int fa_fwd_key_groups(fa_dtype dtype, int B, int H, int N, int N_k, int d, int b
 
 namespace {
 
+// Device memory of the allocation-free backward entry point (fa_bwd_noalloc):
+// D of up to kScratchRows query rows.  Each GPU the library runs on holds its
+// own copy of this array until the process ends.  Host code never uses the
+// array's name as a device address (on the host it is only a stand-in): the
+// address is read once per device with hipGetSymbolAddress and kept in
+// g_scratch_ptr.
+constexpr size_t kScratchRows = (size_t)1 << 22;
+__device__ __align__(256) float scratch[kScratchRows];
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+// The scratch array's address on the current device, read on the first call
+// made with that device current.
+fa_status scratch_address(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(FA_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(FA_ERR_UNSUPPORTED, "device %d: fa_bwd_noalloc supports devices 0..%d", dev,
+                kMaxDevices - 1);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || p == nullptr)
+      return fail(FA_ERR_HIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev,
+                  hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return FA_OK;
+}
+
+// static_scratch: use the library's scratch array instead of the caller's
+// workspace (whose arguments are then ignored); sizes beyond it are rejected
+// before any HIP call.
 fa_status bwd_impl(int phases, fa_dtype dtype, const void* q, fa_strides q_strides,
                    const void* k, fa_strides k_strides, const void* v, fa_strides v_strides,
                    const void* o, fa_strides o_strides, const void* dout,
@@ -222,12 +261,21 @@ fa_status bwd_impl(int phases, fa_dtype dtype, const void* q, fa_strides q_strid
                    void* workspace, size_t workspace_bytes, int B, int H, int N, int Nk, int d,
                    float scale, int causal, const int32_t* seqlens_k,
                    const uint8_t* block_mask, int mask_block, float dropout_p, uint64_t seed,
-                   uint32_t offset, hipStream_t stream) {
+                   uint32_t offset, hipStream_t stream, bool static_scratch = false) {
   int al = 0;
   fa_status st = check_common(dtype, B, H, N, Nk, d, scale, block_mask, mask_block, &al);
   if (st != FA_OK) return st;
   if (d != 64 && dtype != FA_BF16)
     return fail(FA_ERR_UNSUPPORTED, "head dimension %d is built for bf16 only", d);
+  const size_t need = fa_bwd_workspace_bytes(dtype, B, H, N, d);
+  if (static_scratch) {
+    if (need > sizeof(scratch))
+      return fail(FA_ERR_UNSUPPORTED,
+                  "fa_bwd_noalloc: B * H * N = %lld query rows exceed its %zu-row scratch array",
+                  (long long)B * H * N, kScratchRows);
+    workspace = nullptr;
+    workspace_bytes = need;
+  }
   if ((st = check_tensor("q", q, q_strides, al, N)) != FA_OK) return st;
   if ((st = check_tensor("k", k, k_strides, al, Nk)) != FA_OK) return st;
   if ((st = check_tensor("v", v, v_strides, al, Nk)) != FA_OK) return st;
@@ -242,8 +290,7 @@ fa_status bwd_impl(int phases, fa_dtype dtype, const void* q, fa_strides q_strid
   }
   if (lse == nullptr) return fail(FA_ERR_INVALID_ARG, "lse is NULL");
   if (!aligned16(lse)) return fail(FA_ERR_INVALID_ARG, "lse is not 16-byte aligned");
-  const size_t need = fa_bwd_workspace_bytes(dtype, B, H, N, d);
-  if (need > 0) {
+  if (need > 0 && !static_scratch) {
     if (workspace == nullptr) return fail(FA_ERR_INVALID_ARG, "workspace is NULL");
     if (!aligned16(workspace))
       return fail(FA_ERR_INVALID_ARG, "workspace is not 16-byte aligned");
@@ -255,6 +302,9 @@ fa_status bwd_impl(int phases, fa_dtype dtype, const void* q, fa_strides q_strid
     return fail(FA_ERR_INVALID_ARG, "seqlens_k is not 4-byte aligned");
   fa::Dropout drop{};
   if ((st = make_dropout(dropout_p, seed, offset, &drop)) != FA_OK) return st;
+  if (static_scratch && need > 0) {  // every argument checked: the first HIP calls
+    if ((st = scratch_address(&workspace)) != FA_OK) return st;
+  }
 
   fa::BwdArgs a{};
   a.q = q;
@@ -340,6 +390,20 @@ fa_status fa_bwd_dropout(fa_dtype dtype, const void* q, fa_strides q_strides, co
                   v_strides, o, o_strides, dout, dout_strides, lse, dq, dq_strides, dk,
                   dk_strides, dv, dv_strides, workspace, workspace_bytes, B, H, N, N, d, scale,
                   causal, seqlens_k, block_mask, mask_block, dropout_p, seed, offset, stream);
+}
+
+fa_status fa_bwd_noalloc(fa_dtype dtype, const void* q, fa_strides q_strides, const void* k,
+                         fa_strides k_strides, const void* v, fa_strides v_strides,
+                         const void* o, fa_strides o_strides, const void* dout,
+                         fa_strides dout_strides, const float* lse, void* dq,
+                         fa_strides dq_strides, void* dk, fa_strides dk_strides, void* dv,
+                         fa_strides dv_strides, int B, int H, int N, int d, float scale,
+                         int causal, const int32_t* seqlens_k, const uint8_t* block_mask,
+                         int mask_block, hipStream_t stream) {
+  return bwd_impl(fa::kPhaseDQ | fa::kPhaseDKDV, dtype, q, q_strides, k, k_strides, v,
+                  v_strides, o, o_strides, dout, dout_strides, lse, dq, dq_strides, dk,
+                  dk_strides, dv, dv_strides, nullptr, 0, B, H, N, N, d, scale, causal,
+                  seqlens_k, block_mask, mask_block, 0.f, 0, 0, stream, true);
 }
 
 fa_status fa_bwd_dq(fa_dtype dtype, const void* q, fa_strides q_strides, const void* k,

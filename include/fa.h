@@ -173,6 +173,45 @@ fa_status fa_bwd(fa_dtype dtype,
                  hipStream_t stream);
 
 /*
+ * fa_bwd_noalloc -- fa_bwd for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation): the same two kernels and results as fa_bwd, but D lives in a
+ * scratch array inside the library instead of a caller workspace, so there
+ * are no workspace arguments.  The call itself allocates nothing (no
+ * hipMalloc, hipFree or allocating library routine).
+ *
+ *   arguments    as for fa_bwd, without workspace and workspace_bytes.
+ *   limit        B * H * N <= 4194304 query rows for FA_BF16 (the array holds
+ *                16 MiB of fp32 D); larger problems return FA_ERR_UNSUPPORTED
+ *                before any HIP call.  FA_F32 needs no scratch.
+ *   memory       each GPU the library runs on holds its own copy of the array
+ *                (16 MiB) until the process ends; its device address is read
+ *                once per device, on the first call made with that device
+ *                current.
+ *   concurrency  every call on one GPU shares that GPU's array, whose contents
+ *                are the last call's D: two calls that overlap in time on one
+ *                GPU (different streams, or different host threads without
+ *                ordering) race and give wrong gradients.  Calls ordered on
+ *                one stream are safe.  Nothing in the array has to start at
+ *                zero (every row a call reads is written by that call first).
+ */
+fa_status fa_bwd_noalloc(fa_dtype dtype,
+                         const void* q, fa_strides q_strides,
+                         const void* k, fa_strides k_strides,
+                         const void* v, fa_strides v_strides,
+                         const void* o, fa_strides o_strides,
+                         const void* dout, fa_strides dout_strides,
+                         const float* lse,
+                         void* dq, fa_strides dq_strides,
+                         void* dk, fa_strides dk_strides,
+                         void* dv, fa_strides dv_strides,
+                         int B, int H, int N, int d,
+                         float scale, int causal,
+                         const int32_t* seqlens_k,
+                         const uint8_t* block_mask, int mask_block,
+                         hipStream_t stream);
+
+/*
  * fa_bwd_dq, fa_bwd_dkdv -- the two halves of fa_bwd, each one kernel launch
  * of its own: fa_bwd_dq writes dQ, fa_bwd_dkdv writes dK and dV.  They are
  * independent of each other (either may run alone, in any order or on

@@ -276,3 +276,26 @@ def test_fwd_qk_rejects_bad_arguments(kw, status, msg):
 def test_short_python_names():
     # fa.fwd / fa.bwd are the allocating calls under their short names
     assert fa.fwd is fa.forward and fa.bwd is fa.backward
+
+
+def _bwd_noalloc(**kw):
+    lib = fa.load_library()
+    args = dict(dtype=0, q=A, sq=S, k=A, sk=S, v=A, sv=S, o=A, so=S, do=A, sdo=S, lse=A,
+                dq=A, sdq=S, dk=A, sdk=S, dv=A, sdv=S, B=1, H=1, N=1024, d=64, scale=0.125,
+                causal=0, seqlens=None, bmask=None, mb=128, stream=None)
+    args.update(kw)
+    return lib.fa_bwd_noalloc(*args.values())
+
+
+@pytest.mark.parametrize("kw,status,msg", [
+    # 64 x 65537 query rows: one more than its scratch array holds
+    (dict(H=64, N=65537, sq=bnd.fa_strides(0, 65537 * 64, 64)), 2, "exceed"),
+    (dict(B=2, H=32, N=65537, sq=bnd.fa_strides(0, 65537 * 64, 64)), 2, "exceed"),
+    (dict(dq=None), 1, "dq is NULL"),
+    (dict(lse=None), 1, "lse is NULL"),
+    (dict(d=96), 2, "head dimension"),
+    (dict(scale=-1.0), 1, "scale"),
+])
+def test_bwd_noalloc_rejects_bad_arguments(kw, status, msg):
+    assert _bwd_noalloc(**kw) == status
+    assert msg in fa.fa_last_error()
