@@ -242,7 +242,7 @@ __global__ __launch_bounds__(64 * W * G) __attribute__((amdgpu_waves_per_eu((D =
           if (32 * kb + 8 * (e >> 2) + (e & 3) > lim) sv = -kInf;
         }
         p[x] = fast_exp2(__builtin_fmaf(sv, c, -m));
-        ps[kb] += p[x];
+        ps[kb] = (e == 0) ? p[x] : ps[kb] + p[x];  // the first term starts the sum
         if constexpr (DROP) p[x] = drop_keep(zb[kb], e, a.drop.t) ? p[x] : 0.f;
       }
       const int st = 2 * kb + (e0 >> 3), wd = (e0 & 7) >> 1;
