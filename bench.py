@@ -879,7 +879,9 @@ def pipe_summary(counter_csv: str, workload: str, command: str) -> str:
            "busy; VALU busy: share of SIMD cycles executing a vector instruction (MfmaUtil "
            "and VALUBusy); CU busy: share of CU cycles with waves resident; LDS conflict: "
            "bank-conflict cycles per LDS-active cycle; trans/MFMA: fp32 transcendental "
-           "(exp2) instructions per MFMA instruction.", "",
+           "(exp2) instructions per MFMA instruction. A clock above the chip's 2.4 GHz "
+           "(dispatches of a few µs, whose GRBM_GUI_ACTIVE window overlaps their "
+           "neighbours) and trans/MFMA of a kernel without MFMAs are shown as —.", "",
            "| kernel | dispatches | µs | cycles | clock GHz | MFMA busy | VALU busy | CU busy | "
            "LDS conflict | trans/MFMA |", "|---|---|---|---|---|---|---|---|---|---|"]
     for k, disp in sorted(per.items()):
@@ -889,10 +891,13 @@ def pipe_summary(counter_csv: str, workload: str, command: str) -> str:
         mean = {n: float(np.mean([d[n] for d in full])) for n in PIPE_COUNTERS}
         ns = float(np.mean([d["_ns"] for d in full]))
         m = pipe_metrics(mean)
+        clock = m["gui_cycles"] / ns
+        clock_s = f"{clock:.2f}" if clock <= 2.45 else "—"
+        tpm = f"{m['trans_per_mfma']:.2f}" if mean["SQ_INSTS_MFMA"] > 0 else "—"
         out.append(f"| {k} | {len(full)} | {ns / 1e3:.1f} | {m['gui_cycles']:.0f} | "
-                   f"{m['gui_cycles'] / ns:.2f} | {100 * m['mfma_busy']:.1f} % | "
+                   f"{clock_s} | {100 * m['mfma_busy']:.1f} % | "
                    f"{100 * m['valu_busy']:.1f} % | {100 * m['cu_busy']:.1f} % | "
-                   f"{100 * m['lds_conflict']:.2f} % | {m['trans_per_mfma']:.2f} |")
+                   f"{100 * m['lds_conflict']:.2f} % | {tpm} |")
     out += ["", "Raw means per dispatch:", ""]
     for k, disp in sorted(per.items()):
         full = [d for d in disp.values() if all(n in d for n in PIPE_COUNTERS)]
