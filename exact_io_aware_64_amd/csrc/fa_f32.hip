@@ -1,17 +1,17 @@
-// fp32 attention (forward and backward) on the vector ALUs.
+// fp32 attention backward on the vector ALUs (the fp32 forward runs on the
+// matrix cores, fa_fwd_f32.hip).
 //
 // Same tiled algorithm as the bf16 kernels -- K/V (or Q/dO) tiles of 64 rows
-// staged in LDS, online softmax with a running maximum and sum in the
-// forward pass, probabilities recomputed from L in the backward pass
-// (researchpapers.dev explainer, "tiling and recomputation") -- but every
-// product is an fp32 FMA, so results stay within ~1e-6 of exact.  One thread
-// owns one query (forward, dQ) or one key (dK/dV); every thread of a
-// workgroup reads the same LDS row at the same time (a broadcast).  This path
-// serves full-precision callers and small problems; the bf16 MFMA kernels are
-// the throughput path.  With dropout, each thread makes one Philox call per
-// four consecutive pairs of its loop: the block of query i and keys j..j+3
-// gives key j % 4's byte of word i % 4 (forward, dQ); the block of queries
-// i..i+3 and key j gives byte j % 4 of each word (dK/dV).
+// staged in LDS, probabilities recomputed from L (researchpapers.dev
+// explainer, "tiling and recomputation") -- but every product is an fp32
+// FMA, so results stay within ~1e-6 of exact.  One thread owns one query
+// (dQ) or one key (dK/dV); every thread of a workgroup reads the same LDS
+// row at the same time (a broadcast).  This path serves full-precision
+// callers and small problems; the bf16 MFMA kernels are the throughput path.
+// With dropout, each thread makes one Philox call per four consecutive pairs
+// of its loop: the block of query i and keys j..j+3 gives key j % 4's byte
+// of word i % 4 (dQ); the block of queries i..i+3 and key j gives byte j % 4
+// of each word (dK/dV).
 #include "fa_device.h"
 
 namespace fa {
@@ -76,83 +76,6 @@ __device__ __forceinline__ bool keep_byte(uint32_t word, int byte, uint32_t t) {
 __device__ __forceinline__ uint32_t pick4(const uint32_t (&w)[4], int i) {
   const uint32_t lo = (i & 1) ? w[1] : w[0], hi = (i & 1) ? w[3] : w[2];
   return (i & 2) ? hi : lo;
-}
-
-template <bool DROP>
-__global__ __launch_bounds__(64) void fwd_f32_kernel(FwdArgs a, int causal) {
-  __shared__ __attribute__((aligned(16))) float s_k[kTile * kD];
-  __shared__ __attribute__((aligned(16))) float s_v[kTile * kD];
-  const int tid = threadIdx.x;
-  const int BH = a.B * a.H;
-  const int qt = blockIdx.x / BH, bh = blockIdx.x % BH;
-  const int b = bh / a.H, hh = bh % a.H;
-  const int q0 = qt * kTile, qi = q0 + tid;
-  int kv_len = a.Nk;
-  if (a.seqlens) kv_len = min(max(a.seqlens[b], 0), a.Nk);
-  const int kend = causal ? min(kv_len, q0 + kTile + a.coff) : kv_len;
-  const float* Q = (const float*)a.q + b * a.sq.b + hh * a.sq.h;
-  const float* K = (const float*)a.k + b * a.sk.b + hh * a.sk.h;
-  const float* V = (const float*)a.v + b * a.sv.b + hh * a.sv.h;
-
-  float q[kD], o[kD];
-  if (qi < a.N) load_row(q, Q + (int64_t)qi * a.sq.s);
-  else
-    for (int e = 0; e < kD; ++e) q[e] = 0.f;
-  for (int e = 0; e < kD; ++e) o[e] = 0.f;
-  float m = -kInf, l = 0.f;
-  const float c = a.scale_log2;
-
-  for (int k0 = 0; k0 < kend; k0 += kTile) {
-    if (!tile_kept(a.bmask, a.n_mask_k, a.mask_block, q0, k0)) continue;
-    const int kk = k0 + tid;
-    stage_row(s_k + tid * kD, K + (int64_t)kk * a.sk.s, kk < a.Nk);
-    stage_row(s_v + tid * kD, V + (int64_t)kk * a.sv.s, kk < a.Nk);
-    __syncthreads();
-    // keep bit j of this query and key k0 + j (all ones without dropout)
-    uint64_t keep = ~0ull;
-    if constexpr (DROP) {
-      keep = 0;
-#pragma unroll 1
-      for (int g = 0; g < kTile / 4; ++g) {
-        uint32_t w[4];
-        drop_call(w, a.drop, qi >> 2, (k0 >> 2) + g, bh);
-        const uint32_t word = pick4(w, qi & 3);
-#pragma unroll
-        for (int y = 0; y < 4; ++y)
-          if (keep_byte(word, y, a.drop.t)) keep |= 1ull << (4 * g + y);
-      }
-    }
-    float s[kTile];
-    float mx = -kInf;
-#pragma unroll
-    for (int j = 0; j < kTile; ++j) {
-      const int key = k0 + j;
-      const bool vis = key < kv_len && (!causal || key <= qi + a.coff);
-      s[j] = vis ? dot_lds(q, s_k + j * kD) : -kInf;
-      mx = fmaxf(mx, s[j]);
-    }
-    const float m_new = fmaxf(m, mx * c);
-    const float m_use = (m_new == -kInf) ? 0.f : m_new;
-    const float alpha = fast_exp2(m - m_use);
-    l *= alpha;
-#pragma unroll
-    for (int e = 0; e < kD; ++e) o[e] *= alpha;
-#pragma unroll
-    for (int j = 0; j < kTile; ++j) {
-      float p = fast_exp2(__builtin_fmaf(s[j], c, -m_use));
-      l += p;
-      if constexpr (DROP) p = ((keep >> j) & 1) ? p : 0.f;
-#pragma unroll
-      for (int e = 0; e < kD; ++e) o[e] = __builtin_fmaf(p, s_v[j * kD + e], o[e]);
-    }
-    m = m_new;
-    __syncthreads();
-  }
-  if (qi < a.N) {
-    store_row((float*)a.o + b * a.so.b + hh * a.so.h + (int64_t)qi * a.so.s, o,
-              l > 0.f ? (DROP ? a.drop.scale : 1.f) / l : 0.f);
-    a.lse[(int64_t)bh * a.N + qi] = l > 0.f ? (m + __builtin_amdgcn_logf(l)) * kLn2 : -kInf;
-  }
 }
 
 // dQ for one query per thread.
@@ -291,16 +214,6 @@ __global__ __launch_bounds__(64) void dkdv_f32_kernel(BwdArgs a, int causal) {
 }
 
 }  // namespace
-
-hipError_t launch_fwd_f32(const FwdArgs& a, bool causal, hipStream_t stream) {
-  FwdArgs copy = a;
-  int cz = causal ? 1 : 0;
-  void* args[] = {&copy, &cz};
-  dim3 grid((unsigned)(((a.N + kTile - 1) / kTile) * a.B * a.H)), block(64);
-  const void* fn = a.drop.t < 256 ? (const void*)&fwd_f32_kernel<true>
-                                  : (const void*)&fwd_f32_kernel<false>;
-  return hipLaunchKernel(fn, grid, block, args, 0, stream);
-}
 
 hipError_t launch_bwd_f32(const BwdArgs& a, bool causal, int phases, hipStream_t stream) {
   BwdArgs copy = a;

@@ -163,6 +163,15 @@ def test_f32_masks(causal):
     check_full(case, tag=f"f32 masks causal={causal}")
 
 
+@pytest.mark.parametrize("N", [1, 17, 64, 65, 127, 128, 129, 300])
+@pytest.mark.parametrize("causal", [False, True])
+def test_f32_edge_lengths(N, causal):
+    """fp32 forward (128-row workgroups on the fp32 matrix cores) and backward
+    at lengths around its tile sizes."""
+    case = wl.random_case(2, 2, N, 64, dtype="f32", seed=N * 5 + causal, causal=causal)
+    check_full(case, tag=f"f32 N={N} causal={causal}")
+
+
 def test_key_lengths_zero_and_full():
     """len 0 (every row fully masked: O = 0, L = -inf, zero gradients), len 1
     and len N in one batch."""
