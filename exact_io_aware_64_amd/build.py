@@ -21,7 +21,7 @@ LIB = os.path.join(PKG, "libfa.so")
 ARCH = "gfx950"
 
 SOURCES = ["fa_api.hip", "fa_fwd_bf16.hip", "fa_bwd_bf16.hip", "fa_bwd_bf16_d128.hip",
-           "fa_f32.hip", "fa_fwd_f32.hip"]
+           "fa_fwd_f32.hip", "fa_bwd_f32.hip"]
 
 # Packed fp32 instructions are disabled for all device code: the compiler
 # would otherwise pair independent fp32 operations into them.
