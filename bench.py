@@ -128,7 +128,13 @@ def kernel_flops(d, pairs):
 # writes D = rowsum(dO * O) with dsum_kernel, then runs bwd_kernel.
 PASSES = ("fa_fwd", "fa_bwd")
 PASS_KERNELS = {"fa_fwd": ("fwd_bf16_kernel",), "fa_bwd": ("dsum_kernel", "bwd_kernel")}
-KERNELS = ("fwd_bf16_kernel", "dsum_kernel", "bwd_kernel")
+# the fp32 path's kernels per C call
+PASS_KERNELS_F32 = {"fa_fwd": ("fwd_f32_kernel",), "fa_bwd": ("dq_f32_kernel", "dkdv_f32_kernel")}
+
+
+def pass_kernels(dtype: str) -> dict:
+    return PASS_KERNELS if dtype == "bf16" else PASS_KERNELS_F32
+
 DROPOUT_SEED = 2024  # Philox key of the --dropout runs (offset 0)
 
 
@@ -773,19 +779,24 @@ KERNEL_SOURCES = {
     "fwd_bf16_kernel": ("fa_fwd_bf16.hip",),
     "dsum_kernel": ("fa_bwd_bf16.h", "fa_bwd_bf16.hip", "fa_bwd_bf16_d128.hip"),
     "bwd_kernel": ("fa_bwd_bf16.h", "fa_bwd_bf16.hip", "fa_bwd_bf16_d128.hip"),
+    "fwd_f32_kernel": ("fa_f32_tile.h", "fa_fwd_f32.hip"),
+    "dq_f32_kernel": ("fa_f32_tile.h", "fa_bwd_f32.hip"),
+    "dkdv_f32_kernel": ("fa_f32_tile.h", "fa_bwd_f32.hip"),
 }
 COMMON_SOURCES = ("fa_device.h", "fa_internal.h")
 
 
 def kernel_source_hash(kernel: str) -> str:
-    """sha256 over the sources a kernel is compiled from and the build flags."""
+    """sha256 over the sources a kernel is compiled from and the compiler
+    flags of its translation units."""
+    from exact_io_aware_64_amd import build as B
     pkg = os.path.join(ROOT, "exact_io_aware_64_amd")
     h = hashlib.sha256()
     for f in KERNEL_SOURCES[kernel] + COMMON_SOURCES:
         with open(os.path.join(pkg, "csrc", f), "rb") as fh:
             h.update(fh.read())
-    with open(os.path.join(pkg, "build.py"), "rb") as fh:
-        h.update(fh.read())
+        if f.endswith(".hip"):
+            h.update(" ".join(B.source_flags(f)).encode())
     return h.hexdigest()
 
 
@@ -907,7 +918,7 @@ def pipe_summary(counter_csv: str, workload: str, command: str) -> str:
     return "\n".join(out) + "\n"
 
 
-def traffic_for(pass_name: str, workload: str):
+def traffic_for(pass_name: str, workload: str, dtype: str = "bf16"):
     """Measured HBM bytes per call of a pass (the sum over its kernels) on
     `workload`, or None when no record exists or one of its kernels changed
     since the counters were taken."""
@@ -917,7 +928,7 @@ def traffic_for(pass_name: str, workload: str):
     with open(path) as fh:
         rec = json.load(fh)
     total = 0.0
-    for kernel in PASS_KERNELS[pass_name]:
+    for kernel in pass_kernels(dtype)[pass_name]:
         ent = rec.get("kernels", {}).get(kernel)
         if not ent or ent.get("source_sha256") != kernel_source_hash(kernel):
             return None
@@ -946,7 +957,8 @@ def trace_summary(stats_csv: str, bench_log: str, workload: str, command: str) -
         out.append(f"| {k} | {n} | {av:.2f} | {mn:.2f} | {mx:.2f} | {pc:.2f} |")
     avg = {k: av for k, n, av, mn, mx, pc in rows}
     per_call = [f"{p} = {' + '.join(ks)}: {sum(avg[k] for k in ks):.2f} us"
-                for p, ks in PASS_KERNELS.items() if all(k in avg for k in ks)]
+                for table in (PASS_KERNELS, PASS_KERNELS_F32)
+                for p, ks in table.items() if all(k in avg for k in ks)]
     if per_call:
         out += ["", "Per C call (sum of its kernels' averages): " + "; ".join(per_call) + "."]
     if line:
@@ -1102,8 +1114,8 @@ def main(argv=None):
         ach = kbytes[dom] / (ms * 1e-3) / 1e9
         roofline = dict(kernel=dom, bound="hbm", achieved=ach, peak=PEAK_HBM_GBS, unit="GB/s",
                         frac=ach / PEAK_HBM_GBS)
-    roofline.update(kernel=" + ".join(PASS_KERNELS[dom]), call=dom,
-                    traffic=traffic_for(dom, key), flops_per_launch=kflops[dom],
+    roofline.update(kernel=" + ".join(pass_kernels(w.dtype)[dom]), call=dom,
+                    traffic=traffic_for(dom, key, w.dtype), flops_per_launch=kflops[dom],
                     compulsory_bytes_per_launch=kbytes[dom], launch_ms=ms)
 
     base = None
