@@ -135,6 +135,7 @@ PASS_KERNELS_F32 = {"fa_fwd": ("fwd_f32_kernel",), "fa_bwd": ("dq_f32_kernel", "
 def pass_kernels(dtype: str) -> dict:
     return PASS_KERNELS if dtype == "bf16" else PASS_KERNELS_F32
 
+
 DROPOUT_SEED = 2024  # Philox key of the --dropout runs (offset 0)
 
 
