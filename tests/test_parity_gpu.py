@@ -211,8 +211,9 @@ def _product_magnitudes(q, k, v, do, scale):
             np.abs(p).T @ np.abs(do))
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("kind", ["plus", "minus", "mixed"])
-def test_huge_scores_stay_finite(kind):
+def test_huge_scores_stay_finite(kind, dtype):
     """Scores of +-20000 for every pair (the overflow / underflow examples of
     the safe-softmax discussion): results stay finite and match the oracle.
     L is checked to a few fp32 ulps at its magnitude.  With all keys equal the
@@ -227,7 +228,7 @@ def test_huge_scores_stay_finite(kind):
     rng = np.random.default_rng(0)
     v = wl.round_to_bf16(rng.standard_normal((1, 1, N, d)).astype(np.float32))
     do = wl.round_to_bf16(rng.standard_normal((1, 1, N, d)).astype(np.float32))
-    case = dict(q=q, k=k, v=v, do=do, scale=0.125, causal=False, dtype="bf16",
+    case = dict(q=q, k=k, v=v, do=do, scale=0.125, causal=False, dtype=dtype,
                 seqlens=None, block_mask=None)
     qd, kd, vd, dod, _, _ = device_inputs(case)
     o, lse = gpu_forward(case, qd, kd, vd, None, None)
