@@ -172,6 +172,19 @@ def test_f32_edge_lengths(N, causal):
     check_full(case, tag=f"f32 N={N} causal={causal}")
 
 
+@pytest.mark.parametrize("mask_block", [256, 384])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("causal", [False, True])
+def test_larger_mask_blocks(mask_block, dtype, causal):
+    """Tile masks over 256 and 384 rows (each mask entry covers several of
+    the kernels' 64- and 128-row tiles), with key lengths, forward and
+    backward."""
+    case = wl.random_case(2, 2, 1000, 64, dtype=dtype, seed=mask_block + 7 * causal,
+                          causal=causal, seqlens="random", block_keep_p=0.6,
+                          mask_block=mask_block)
+    check_full(case, tag=f"{dtype} mask_block={mask_block} causal={causal}")
+
+
 def test_key_lengths_zero_and_full():
     """len 0 (every row fully masked: O = 0, L = -inf, zero gradients), len 1
     and len N in one batch."""
