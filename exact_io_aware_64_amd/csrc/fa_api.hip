@@ -115,9 +115,8 @@ fa_status fwd_impl(fa_dtype dtype, const void* q, fa_strides q_strides, const vo
   if ((st = make_dropout(dropout_p, seed, offset, &drop)) != FA_OK) return st;
   if (block_q != 64 && block_q != 128 && block_q != 256)
     return fail(FA_ERR_INVALID_ARG, "block_q must be 64, 128 or 256 (got %d)", block_q);
-  if (d != 64 && (dtype != FA_BF16 || block_q != 128))
-    return fail(FA_ERR_UNSUPPORTED,
-                "head dimension %d is built for the bf16 forward pass with block_q 128 only", d);
+  if (d != 64 && block_q != 128)
+    return fail(FA_ERR_UNSUPPORTED, "head dimension %d is built with block_q 128 only", d);
   if (drop.t < 256 && block_q != 128)
     return fail(FA_ERR_UNSUPPORTED, "dropout is built with block_q 128 only");
   if (block_q != 128 && dtype != FA_BF16)
@@ -150,7 +149,7 @@ fa_status fwd_impl(fa_dtype dtype, const void* q, fa_strides q_strides, const vo
   a.n_mask_k = (Nk + a.mask_block - 1) / a.mask_block;
   a.drop = drop;
   const hipError_t e = dtype == FA_BF16 ? fa::launch_fwd_bf16(a, causal != 0, block_q, d, stream)
-                                        : fa::launch_fwd_f32(a, causal != 0, stream);
+                                        : fa::launch_fwd_f32(a, causal != 0, d, stream);
   return hip_status(e);
 }
 
@@ -265,8 +264,6 @@ fa_status bwd_impl(int phases, fa_dtype dtype, const void* q, fa_strides q_strid
   int al = 0;
   fa_status st = check_common(dtype, B, H, N, Nk, d, scale, block_mask, mask_block, &al);
   if (st != FA_OK) return st;
-  if (d != 64 && dtype != FA_BF16)
-    return fail(FA_ERR_UNSUPPORTED, "head dimension %d is built for bf16 only", d);
   const size_t need = fa_bwd_workspace_bytes(dtype, B, H, N, d);
   if (static_scratch) {
     if (need > sizeof(scratch))
@@ -339,7 +336,7 @@ fa_status bwd_impl(int phases, fa_dtype dtype, const void* q, fa_strides q_strid
   a.n_mask_k = (Nk + a.mask_block - 1) / a.mask_block;
   a.drop = drop;
   const hipError_t e = dtype == FA_BF16 ? fa::launch_bwd_bf16(a, causal != 0, phases, d, stream)
-                                        : fa::launch_bwd_f32(a, causal != 0, phases, stream);
+                                        : fa::launch_bwd_f32(a, causal != 0, phases, d, stream);
   return hip_status(e);
 }
 

@@ -19,7 +19,8 @@
 //    and dK^T += Q^T dS the queries (column reads of the dO and Q tiles).
 //    L and D of a tile's rows go to LDS next to the tile: D from the dO
 //    rows in LDS and O rows fetched one tile ahead.
-// The operand pairing and the LDS layout are those of fa_f32_tile.h; every
+// Head dimension D = 32, 64 or 128.  The operand pairing and the LDS layout
+// are those of fa_f32_tile.h; every
 // product is fp32 accumulated in fp32, so results stay within ~1e-6 of
 // exact.  Each 64-row tile is taken as two 32-row blocks so that only one
 // block's S and dP accumulators are live at a time.
@@ -33,8 +34,6 @@
 namespace fa {
 namespace {
 
-using f32t::kD;
-using f32t::kTileF;
 constexpr int kW = 4;         // waves per workgroup
 constexpr int kBR = 32 * kW;  // query (dQ) or key (dK/dV) rows per workgroup
 
@@ -47,9 +46,13 @@ __device__ __forceinline__ uint32_t keep_word(const Dropout& d, int kq, int qq, 
 
 // ------------------------------------------------------------------- dQ
 
-template <bool DROP>
-__global__ __launch_bounds__(64 * kW) __attribute__((amdgpu_waves_per_eu(2, 2))) void
+// Two waves per SIMD at D <= 64; at D = 128 the Q and dO rows alone take
+// 128 registers and the four tiles 128 KiB of LDS: one wave per SIMD.
+template <int D, bool DROP>
+__global__ __launch_bounds__(64 * kW) __attribute__((amdgpu_waves_per_eu(D == 128 ? 1 : 2, D == 128 ? 1 : 2))) void
 dq_f32_kernel(BwdArgs a, int causal) {
+  constexpr int kTileF = f32t::Geo<D>::kTileF;
+  constexpr int NDB = D / 32;
   __shared__ __attribute__((aligned(16))) float s_k0[kTileF];
   __shared__ __attribute__((aligned(16))) float s_v0[kTileF];
   __shared__ __attribute__((aligned(16))) float s_k1[kTileF];
@@ -70,28 +73,28 @@ dq_f32_kernel(BwdArgs a, int causal) {
   const int ntk = (kend + 63) / 64;
 
   const __amdgpu_buffer_rsrc_t rq = make_rsrc(
-      (const float*)a.q + b * a.sq.b + hh * a.sq.h, slice_bytes(a.N, a.sq.s, 4, kD));
+      (const float*)a.q + b * a.sq.b + hh * a.sq.h, slice_bytes(a.N, a.sq.s, 4, D));
   const __amdgpu_buffer_rsrc_t rdo = make_rsrc(
-      (const float*)a.dout + b * a.sdo.b + hh * a.sdo.h, slice_bytes(a.N, a.sdo.s, 4, kD));
+      (const float*)a.dout + b * a.sdo.b + hh * a.sdo.h, slice_bytes(a.N, a.sdo.s, 4, D));
   const __amdgpu_buffer_rsrc_t ro = make_rsrc(
-      (const float*)a.o + b * a.so.b + hh * a.so.h, slice_bytes(a.N, a.so.s, 4, kD));
+      (const float*)a.o + b * a.so.b + hh * a.so.h, slice_bytes(a.N, a.so.s, 4, D));
   const __amdgpu_buffer_rsrc_t rk = make_rsrc(
-      (const float*)a.k + b * a.sk.b + hh * a.sk.h, slice_bytes(a.Nk, a.sk.s, 4, kD));
+      (const float*)a.k + b * a.sk.b + hh * a.sk.h, slice_bytes(a.Nk, a.sk.s, 4, D));
   const __amdgpu_buffer_rsrc_t rv = make_rsrc(
-      (const float*)a.v + b * a.sv.b + hh * a.sv.h, slice_bytes(a.Nk, a.sv.s, 4, kD));
+      (const float*)a.v + b * a.sv.b + hh * a.sv.h, slice_bytes(a.Nk, a.sv.s, 4, D));
   const int ssk = (int)a.sk.s * 4, ssv = (int)a.sv.s * 4;
 
   // Q and dO fragments of this lane's query (rows past N read as zeros), D
   // from the dO and O rows (the two wave halves hold the two halves of them).
-  float qf[32], dof[32];
-  f32t::load_frag(rq, qi, (int)a.sq.s * 4, hl, qf);
-  f32t::load_frag(rdo, qi, (int)a.sdo.s * 4, hl, dof);
+  float qf[D / 2], dof[D / 2];
+  f32t::load_frag<D>(rq, qi, (int)a.sq.s * 4, hl, qf);
+  f32t::load_frag<D>(rdo, qi, (int)a.sdo.s * 4, hl, dof);
   float Dq = 0.f;
   {
-    float of_[32];
-    f32t::load_frag(ro, qi, (int)a.so.s * 4, hl, of_);
+    float of_[D / 2];
+    f32t::load_frag<D>(ro, qi, (int)a.so.s * 4, hl, of_);
 #pragma unroll
-    for (int x = 0; x < 32; ++x) Dq = __builtin_fmaf(dof[x], of_[x], Dq);
+    for (int x = 0; x < D / 2; ++x) Dq = __builtin_fmaf(dof[x], of_[x], Dq);
     Dq += __shfl_xor(Dq, 32, 64);
   }
   float L2 = kInf;  // +inf makes every probability of a dead or padding row 0
@@ -101,19 +104,19 @@ dq_f32_kernel(BwdArgs a, int causal) {
   }
   const float c = a.scale_log2;
 
-  f32x16 acc[2];
-  acc[0] = zero16();
-  acc[1] = zero16();
+  f32x16 acc[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) acc[db] = zero16();
 
   auto kept = [&](int t) FA_INLINE -> bool {
     if (a.bmask == nullptr) return true;
     return a.bmask[(int64_t)(q0 / a.mask_block) * a.n_mask_k + (t * 64) / a.mask_block] != 0;
   };
   auto stage = [&](int t, float* kt, float* vt) FA_INLINE {
-    f32t::stage(rk, t * 64, ssk, kt, w, lane);
-    f32t::stage(rv, t * 64, ssv, vt, w, lane);
+    f32t::stage<D, kW>(rk, t * 64, ssk, kt, w, lane);
+    f32t::stage<D, kW>(rv, t * 64, ssv, vt, w, lane);
   };
-  f32t::Offsets of;
+  f32t::Offsets<D> of;
   of.init(r, hl);
 
   auto compute = [&](int t, const float* kt, const float* vt) FA_INLINE {
@@ -124,8 +127,8 @@ dq_f32_kernel(BwdArgs a, int causal) {
     const int lim = min(kv_len - 1, causal ? qi + a.coff : a.Nk) - k0 - 4 * hl;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-      f32x16 st = f32t::row_product(kt, of, kb, qf);   // S^T
-      f32x16 dpt = f32t::row_product(vt, of, kb, dof);  // dP^T
+      f32x16 st = f32t::row_product<D>(kt, of, kb, qf);   // S^T
+      f32x16 dpt = f32t::row_product<D>(vt, of, kb, dof);  // dP^T
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         [[maybe_unused]] uint32_t word = 0;
@@ -142,7 +145,7 @@ dq_f32_kernel(BwdArgs a, int causal) {
           st[e] = p * (dp - Dq);  // dS^T
         }
       }
-      f32t::col_product(kt, of, kb, st, acc);  // dQ^T += K^T dS^T
+      f32t::col_product<D>(kt, of, kb, st, acc);  // dQ^T += K^T dS^T
     }
   };
 
@@ -172,28 +175,23 @@ dq_f32_kernel(BwdArgs a, int causal) {
 
   if (qi < a.N) {
     float* out = (float*)a.dq + b * a.sdq.b + hh * a.sdq.h + (int64_t)qi * a.sdq.s;
-    // element e of block db holds dQ[qi][32 db + 8 (e / 4) + 4 hl + e % 4]
-#pragma unroll
-    for (int db = 0; db < 2; ++db)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        f32x4 v4;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) v4[i] = acc[db][4 * j + i] * a.scale;
-        *reinterpret_cast<f32x4*>(out + 32 * db + 8 * j + 4 * hl) = v4;
-      }
+    f32t::store_rows<D>(out, hl, acc, a.scale);
   }
 }
 
 // ---------------------------------------------------------------- dK, dV
 
-// One wave per SIMD: K and V rows, both accumulator pairs, one block's S and
-// dP and the O rows fetched for the next tile's D need more than the 256
-// registers of two waves.  Its work is almost all matrix instructions, whose
-// dependent chains one wave keeps issuing back to back.
-template <bool DROP>
-__global__ __launch_bounds__(64 * kW) __attribute__((amdgpu_waves_per_eu(1, 1))) void
+// One wave per SIMD at D >= 64: K and V rows, both accumulator sets, one
+// block's S and dP and the O rows fetched for the next tile's D need more
+// than the 256 registers of two waves.  Its work is almost all matrix
+// instructions, whose dependent chains one wave keeps issuing back to back.
+// At D = 32 everything fits in half of that: two waves per SIMD.
+template <int D, bool DROP>
+__global__ __launch_bounds__(64 * kW) __attribute__((amdgpu_waves_per_eu(D == 32 ? 2 : 1, D == 32 ? 2 : 1))) void
 dkdv_f32_kernel(BwdArgs a, int causal) {
+  constexpr int kTileF = f32t::Geo<D>::kTileF;
+  constexpr int NDB = D / 32;
+  constexpr int NQ = D / 16;  // 16-byte pieces of a quarter row
   __shared__ __attribute__((aligned(16))) float s_q0[kTileF];
   __shared__ __attribute__((aligned(16))) float s_g0[kTileF];
   __shared__ __attribute__((aligned(16))) float s_q1[kTileF];
@@ -213,26 +211,27 @@ dkdv_f32_kernel(BwdArgs a, int causal) {
   if (a.seqlens) kv_len = min(max(a.seqlens[b], 0), a.Nk);
 
   const __amdgpu_buffer_rsrc_t rq = make_rsrc(
-      (const float*)a.q + b * a.sq.b + hh * a.sq.h, slice_bytes(a.N, a.sq.s, 4, kD));
+      (const float*)a.q + b * a.sq.b + hh * a.sq.h, slice_bytes(a.N, a.sq.s, 4, D));
   const __amdgpu_buffer_rsrc_t rdo = make_rsrc(
-      (const float*)a.dout + b * a.sdo.b + hh * a.sdo.h, slice_bytes(a.N, a.sdo.s, 4, kD));
+      (const float*)a.dout + b * a.sdo.b + hh * a.sdo.h, slice_bytes(a.N, a.sdo.s, 4, D));
   const __amdgpu_buffer_rsrc_t ro = make_rsrc(
-      (const float*)a.o + b * a.so.b + hh * a.so.h, slice_bytes(a.N, a.so.s, 4, kD));
+      (const float*)a.o + b * a.so.b + hh * a.so.h, slice_bytes(a.N, a.so.s, 4, D));
   const __amdgpu_buffer_rsrc_t rk = make_rsrc(
-      (const float*)a.k + b * a.sk.b + hh * a.sk.h, slice_bytes(a.Nk, a.sk.s, 4, kD));
+      (const float*)a.k + b * a.sk.b + hh * a.sk.h, slice_bytes(a.Nk, a.sk.s, 4, D));
   const __amdgpu_buffer_rsrc_t rv = make_rsrc(
-      (const float*)a.v + b * a.sv.b + hh * a.sv.h, slice_bytes(a.Nk, a.sv.s, 4, kD));
+      (const float*)a.v + b * a.sv.b + hh * a.sv.h, slice_bytes(a.Nk, a.sv.s, 4, D));
   const __amdgpu_buffer_rsrc_t rl =
       make_rsrc(a.lse + (int64_t)bh * a.N, (uint32_t)a.N * 4);
   const int ssq = (int)a.sq.s * 4, ssdo = (int)a.sdo.s * 4, sso = (int)a.so.s * 4;
 
-  f32x16 dkt[2], dvt[2];
-  dkt[0] = dkt[1] = dvt[0] = dvt[1] = zero16();
+  f32x16 dkt[NDB], dvt[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) dkt[db] = dvt[db] = zero16();
 
   if (k0 < kv_len) {
-    float kf[32], vf[32];
-    f32t::load_frag(rk, kj, (int)a.sk.s * 4, hl, kf);
-    f32t::load_frag(rv, kj, (int)a.sv.s * 4, hl, vf);
+    float kf[D / 2], vf[D / 2];
+    f32t::load_frag<D>(rk, kj, (int)a.sk.s * 4, hl, kf);
+    f32t::load_frag<D>(rv, kj, (int)a.sv.s * 4, hl, vf);
     const float c = a.scale_log2;
     const int nq = (a.N + 63) / 64;
     // causal: the first query that sees key k0 is k0 - coff
@@ -247,27 +246,28 @@ dkdv_f32_kernel(BwdArgs a, int causal) {
     // fetched when the tile's copy is issued and its dO quarter read from
     // the tile once the copy has landed.
     const int srow = tid >> 2, spart = tid & 3;
-    f32x4 oq[4];
+    f32x4 oq[NQ];
     float lraw = 0.f;
     auto fetch_o = [&](int t) FA_INLINE {
       const int row = t * 64 + srow;
 #pragma unroll
-      for (int x = 0; x < 4; ++x)
+      for (int x = 0; x < NQ; ++x)
         oq[x] = __builtin_bit_cast(
-            f32x4, __builtin_amdgcn_raw_buffer_load_b128(ro, row * sso + 64 * spart + 16 * x, 0, 0));
+            f32x4, __builtin_amdgcn_raw_buffer_load_b128(ro, row * sso + D * spart + 16 * x, 0, 0));
       lraw = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rl, 4 * row, 0, 0));
     };
     auto stage = [&](int t, float* qt_, float* gt_) FA_INLINE {
-      f32t::stage(rq, t * 64, ssq, qt_, w, lane);
-      f32t::stage(rdo, t * 64, ssdo, gt_, w, lane);
+      f32t::stage<D, kW>(rq, t * 64, ssq, qt_, w, lane);
+      f32t::stage<D, kW>(rdo, t * 64, ssdo, gt_, w, lane);
       fetch_o(t);
     };
     // After the tile's copy is visible to every wave: L and D of its rows.
     auto stats = [&](int t, const float* gt_, int buf) FA_INLINE {
       float dd = 0.f;
 #pragma unroll
-      for (int x = 0; x < 4; ++x) {
-        const f32x4 g4 = *reinterpret_cast<const f32x4*>(gt_ + f32t::foff(srow, 16 * spart + 4 * x));
+      for (int x = 0; x < NQ; ++x) {
+        const f32x4 g4 =
+            *reinterpret_cast<const f32x4*>(gt_ + f32t::foff<D>(srow, (D / 4) * spart + 4 * x));
 #pragma unroll
         for (int i = 0; i < 4; ++i) dd = __builtin_fmaf(g4[i], oq[x][i], dd);
       }
@@ -284,13 +284,13 @@ dkdv_f32_kernel(BwdArgs a, int causal) {
       // causal: no query of the tile sees any key of this wave
       if (causal && qs + 63 < kw - a.coff) return;
       // the offsets are recomputed per tile: registers are short here
-      f32t::Offsets of;
+      f32t::Offsets<D> of;
       of.init_here(lane);
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb) {
         // S, then P as it enters dV (dropped pairs 0); dP, then dS.
-        f32x16 sc = f32t::row_product(qt_, of, qb, kf);
-        f32x16 dp = f32t::row_product(gt_, of, qb, vf);
+        f32x16 sc = f32t::row_product<D>(qt_, of, qb, kf);
+        f32x16 dp = f32t::row_product<D>(gt_, of, qb, vf);
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
           // element e = 4 g + i holds query qs + 32 qb + 8 g + 4 hl + i
@@ -321,8 +321,8 @@ dkdv_f32_kernel(BwdArgs a, int causal) {
             dp[e] = p * (dpe - d4[i]);
           }
         }
-        f32t::col_product(gt_, of, qb, sc, dvt);  // dV^T += dO^T P
-        f32t::col_product(qt_, of, qb, dp, dkt);  // dK^T += Q^T dS
+        f32t::col_product<D>(gt_, of, qb, sc, dvt);  // dV^T += dO^T P
+        f32t::col_product<D>(qt_, of, qb, dp, dkt);  // dK^T += Q^T dS
       }
     };
 
@@ -360,45 +360,40 @@ dkdv_f32_kernel(BwdArgs a, int causal) {
   if (kj < a.Nk) {
     float* kout = (float*)a.dk + b * a.sdk.b + hh * a.sdk.h + (int64_t)kj * a.sdk.s;
     float* vout = (float*)a.dv + b * a.sdv.b + hh * a.sdv.h + (int64_t)kj * a.sdv.s;
-    const float vs = DROP ? a.drop.scale : 1.f;
-    // element e of block db holds row 32 db + 8 (e / 4) + 4 hl + e % 4 of dK^T, dV^T
-#pragma unroll
-    for (int db = 0; db < 2; ++db)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        f32x4 k4, v4;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          k4[i] = dkt[db][4 * j + i] * a.scale;
-          v4[i] = dvt[db][4 * j + i] * vs;
-        }
-        *reinterpret_cast<f32x4*>(kout + 32 * db + 8 * j + 4 * hl) = k4;
-        *reinterpret_cast<f32x4*>(vout + 32 * db + 8 * j + 4 * hl) = v4;
-      }
+    f32t::store_rows<D>(kout, hl, dkt, a.scale);
+    f32t::store_rows<D>(vout, hl, dvt, DROP ? a.drop.scale : 1.f);
   }
 }
 
-}  // namespace
-
-hipError_t launch_bwd_f32(const BwdArgs& a, bool causal, int phases, hipStream_t stream) {
-  BwdArgs copy = a;
-  int cz = causal ? 1 : 0;
-  void* args[] = {&copy, &cz};
+template <int D>
+hipError_t launch_bwd_f32_d(void** args, const BwdArgs& a, int phases, hipStream_t stream) {
   const dim3 block(64 * kW);
   const bool drop = a.drop.t < 256;
   if (phases & kPhaseDQ) {
     const dim3 grid((unsigned)(((a.N + kBR - 1) / kBR) * a.B * a.H));
-    const void* fn = drop ? (const void*)&dq_f32_kernel<true> : (const void*)&dq_f32_kernel<false>;
+    const void* fn =
+        drop ? (const void*)&dq_f32_kernel<D, true> : (const void*)&dq_f32_kernel<D, false>;
     const hipError_t e = hipLaunchKernel(fn, grid, block, args, 0, stream);
     if (e != hipSuccess) return e;
   }
   if (phases & kPhaseDKDV) {
     const dim3 grid((unsigned)(((a.Nk + kBR - 1) / kBR) * a.B * a.H));
     const void* fn =
-        drop ? (const void*)&dkdv_f32_kernel<true> : (const void*)&dkdv_f32_kernel<false>;
+        drop ? (const void*)&dkdv_f32_kernel<D, true> : (const void*)&dkdv_f32_kernel<D, false>;
     return hipLaunchKernel(fn, grid, block, args, 0, stream);
   }
   return hipSuccess;
+}
+
+}  // namespace
+
+hipError_t launch_bwd_f32(const BwdArgs& a, bool causal, int phases, int d, hipStream_t stream) {
+  BwdArgs copy = a;
+  int cz = causal ? 1 : 0;
+  void* args[] = {&copy, &cz};
+  return d == 32   ? launch_bwd_f32_d<32>(args, a, phases, stream)
+         : d == 64 ? launch_bwd_f32_d<64>(args, a, phases, stream)
+                   : launch_bwd_f32_d<128>(args, a, phases, stream);
 }
 
 }  // namespace fa

@@ -9,7 +9,9 @@
 // exact: this path serves full-precision callers.
 //
 // One workgroup (4 waves) owns 128 query rows of one (batch, head); each wave
-// owns 32 of them, with its Q rows in registers.  S^T = K Q^T contracts the
+// owns 32 of them, with its Q rows in registers.  Head dimension D = 32, 64
+// or 128; at D = 128 the four double-buffered tiles fill 128 KiB of LDS, so
+// one workgroup (one wave per SIMD) runs per CU.  S^T = K Q^T contracts the
 // head dimension (row reads of the K tile), O^T += V^T P^T the keys (column
 // reads of the V tile, the probabilities straight from the S^T accumulator);
 // the operand pairing and the LDS layout are those of fa_f32_tile.h.  The
@@ -28,15 +30,16 @@
 namespace fa {
 namespace {
 
-using f32t::kD;
-using f32t::kTileF;
 constexpr int kW = 4;         // waves per workgroup
 constexpr int kBR = 32 * kW;  // query rows per workgroup
 
-// Two waves per SIMD (the LDS holds two workgroups' double-buffered tiles).
-template <bool DROP>
-__global__ __launch_bounds__(64 * kW) __attribute__((amdgpu_waves_per_eu(2, 2))) void
+// Two waves per SIMD at D <= 64 (the LDS holds two workgroups'
+// double-buffered tiles), one at D = 128.
+template <int D, bool DROP>
+__global__ __launch_bounds__(64 * kW) __attribute__((amdgpu_waves_per_eu(D == 128 ? 1 : 2, D == 128 ? 1 : 2))) void
 fwd_f32_kernel(FwdArgs a, int causal) {
+  constexpr int kTileF = f32t::Geo<D>::kTileF;
+  constexpr int NDB = D / 32;
   __shared__ __attribute__((aligned(16))) float s_k0[kTileF];
   __shared__ __attribute__((aligned(16))) float s_v0[kTileF];
   __shared__ __attribute__((aligned(16))) float s_k1[kTileF];
@@ -57,20 +60,20 @@ fwd_f32_kernel(FwdArgs a, int causal) {
   const int ntk = (kend + 63) / 64;
 
   const __amdgpu_buffer_rsrc_t rq = make_rsrc(
-      (const float*)a.q + b * a.sq.b + hh * a.sq.h, slice_bytes(a.N, a.sq.s, 4, kD));
+      (const float*)a.q + b * a.sq.b + hh * a.sq.h, slice_bytes(a.N, a.sq.s, 4, D));
   const __amdgpu_buffer_rsrc_t rk = make_rsrc(
-      (const float*)a.k + b * a.sk.b + hh * a.sk.h, slice_bytes(a.Nk, a.sk.s, 4, kD));
+      (const float*)a.k + b * a.sk.b + hh * a.sk.h, slice_bytes(a.Nk, a.sk.s, 4, D));
   const __amdgpu_buffer_rsrc_t rv = make_rsrc(
-      (const float*)a.v + b * a.sv.b + hh * a.sv.h, slice_bytes(a.Nk, a.sv.s, 4, kD));
+      (const float*)a.v + b * a.sv.b + hh * a.sv.h, slice_bytes(a.Nk, a.sv.s, 4, D));
   const int ssk = (int)a.sk.s * 4, ssv = (int)a.sv.s * 4;
 
-  // Q[qi][8 g + 4 hl .. +3] for g = 0..7 (rows past N read as zeros).
-  float qf[32];
-  f32t::load_frag(rq, qi, (int)a.sq.s * 4, hl, qf);
+  // Q[qi][8 g + 4 hl .. +3] for g < D / 8 (rows past N read as zeros).
+  float qf[D / 2];
+  f32t::load_frag<D>(rq, qi, (int)a.sq.s * 4, hl, qf);
 
-  f32x16 o[2];
-  o[0] = zero16();
-  o[1] = zero16();
+  f32x16 o[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) o[db] = zero16();
   float m = -kInf, l = 0.f;
   const float c = a.scale_log2;
 
@@ -79,10 +82,10 @@ fwd_f32_kernel(FwdArgs a, int causal) {
     return a.bmask[(int64_t)(q0 / a.mask_block) * a.n_mask_k + (t * 64) / a.mask_block] != 0;
   };
   auto stage = [&](int t, float* kt, float* vt) FA_INLINE {
-    f32t::stage(rk, t * 64, ssk, kt, w, lane);
-    f32t::stage(rv, t * 64, ssv, vt, w, lane);
+    f32t::stage<D, kW>(rk, t * 64, ssk, kt, w, lane);
+    f32t::stage<D, kW>(rv, t * 64, ssv, vt, w, lane);
   };
-  f32t::Offsets of;
+  f32t::Offsets<D> of;
   of.init(r, hl);
 
   auto compute = [&](int t, const float* kt, const float* vt) FA_INLINE {
@@ -91,8 +94,8 @@ fwd_f32_kernel(FwdArgs a, int causal) {
     of.refresh();
     // S^T of keys k0 + 32 kb + (0..31) x this wave's 32 queries.
     f32x16 s[2];
-    s[0] = f32t::row_product(kt, of, 0, qf);
-    s[1] = f32t::row_product(kt, of, 1, qf);
+    s[0] = f32t::row_product<D>(kt, of, 0, qf);
+    s[1] = f32t::row_product<D>(kt, of, 1, qf);
     // Element e of block kb holds key k0 + 32 kb + 8 (e / 4) + 4 hl + e % 4.
     const int lim = min(kv_len - 1, causal ? qi + a.coff : a.Nk) - k0 - 4 * hl;
     float mx = -kInf;
@@ -109,7 +112,7 @@ fwd_f32_kernel(FwdArgs a, int causal) {
     const float alpha = fast_exp2(m - m_use);
     l *= alpha;
 #pragma unroll
-    for (int db = 0; db < 2; ++db)
+    for (int db = 0; db < NDB; ++db)
 #pragma unroll
       for (int e = 0; e < 16; ++e) o[db][e] *= alpha;
     m = m_new;
@@ -139,8 +142,8 @@ fwd_f32_kernel(FwdArgs a, int causal) {
       }
     }
     // O^T += V^T P^T over the 64 keys.
-    f32t::col_product(vt, of, 0, s[0], o);
-    f32t::col_product(vt, of, 1, s[1], o);
+    f32t::col_product<D>(vt, of, 0, s[0], o);
+    f32t::col_product<D>(vt, of, 1, s[1], o);
   };
 
   int it = 0;
@@ -172,30 +175,26 @@ fwd_f32_kernel(FwdArgs a, int causal) {
     float inv = lt > 0.f ? 1.f / lt : 0.f;
     if constexpr (DROP) inv *= a.drop.scale;
     float* op = (float*)a.o + b * a.so.b + hh * a.so.h + (int64_t)qi * a.so.s;
-    // element e of block db holds O[qi][32 db + 8 (e / 4) + 4 hl + e % 4]
-#pragma unroll
-    for (int db = 0; db < 2; ++db)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        f32x4 v4;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) v4[i] = o[db][4 * j + i] * inv;
-        *reinterpret_cast<f32x4*>(op + 32 * db + 8 * j + 4 * hl) = v4;
-      }
+    f32t::store_rows<D>(op, hl, o, inv);
     if (hl == 0)
       a.lse[(int64_t)bh * a.N + qi] = lt > 0.f ? (m + __builtin_amdgcn_logf(lt)) * kLn2 : -kInf;
   }
 }
 
+template <int D>
+const void* fwd_f32_fn(bool drop) {
+  return drop ? (const void*)&fwd_f32_kernel<D, true> : (const void*)&fwd_f32_kernel<D, false>;
+}
+
 }  // namespace
 
-hipError_t launch_fwd_f32(const FwdArgs& a, bool causal, hipStream_t stream) {
+hipError_t launch_fwd_f32(const FwdArgs& a, bool causal, int d, hipStream_t stream) {
   FwdArgs copy = a;
   int cz = causal ? 1 : 0;
   void* args[] = {&copy, &cz};
   dim3 grid((unsigned)(((a.N + kBR - 1) / kBR) * a.B * a.H)), block(64 * kW);
-  const void* fn = a.drop.t < 256 ? (const void*)&fwd_f32_kernel<true>
-                                  : (const void*)&fwd_f32_kernel<false>;
+  const bool drop = a.drop.t < 256;
+  const void* fn = d == 32 ? fwd_f32_fn<32>(drop) : d == 64 ? fwd_f32_fn<64>(drop) : fwd_f32_fn<128>(drop);
   return hipLaunchKernel(fn, grid, block, args, 0, stream);
 }
 

@@ -96,7 +96,7 @@ hipError_t launch_bwd_bf16(const BwdArgs& a, bool causal, int phases, int d,
 // The d = 128 instantiation of the above, from its own translation unit.
 hipError_t launch_bwd_bf16_d128(const BwdArgs& a, bool causal, int phases,
                                 hipStream_t stream);
-hipError_t launch_fwd_f32(const FwdArgs& a, bool causal, hipStream_t stream);
-hipError_t launch_bwd_f32(const BwdArgs& a, bool causal, int phases, hipStream_t stream);
+hipError_t launch_fwd_f32(const FwdArgs& a, bool causal, int d, hipStream_t stream);
+hipError_t launch_bwd_f32(const BwdArgs& a, bool causal, int phases, int d, hipStream_t stream);
 
 }  // namespace fa

@@ -57,7 +57,7 @@ typedef enum fa_status {
   FA_ERR_INVALID_ARG = 1, /* null pointer, bad size, stride or alignment, scale <= 0,
                              workspace too small, bad mask_block, bad dropout_p */
   FA_ERR_UNSUPPORTED = 2, /* valid request the library does not implement (d other than
-                             32/64/128, d != 64 with fp32, too many mask tiles) */
+                             32/64/128, too many mask tiles) */
   FA_ERR_HIP = 3          /* a HIP launch reported an error */
 } fa_status;
 
@@ -76,8 +76,8 @@ typedef struct fa_strides {
  *   o            device pointer, same element type, written in full.
  *   lse          device fp32 [B*H*N], contiguous, written in full (L above).
  *   B, H, N      >= 1.
- *   d            head dimension: 32, 64 or 128 for FA_BF16, with or without
- *                dropout; 64 for FA_F32 (FA_ERR_UNSUPPORTED otherwise).
+ *   d            head dimension: 32, 64 or 128, either dtype, with or without
+ *                dropout (FA_ERR_UNSUPPORTED otherwise).
  *   scale        score scale (> 0, finite), typically 1/sqrt(d).
  *   causal       nonzero: key j is visible to query i only if j <= i.
  *   seqlens_k    NULL, or device int32[B]: keys j >= seqlens_k[b] are masked

@@ -91,8 +91,8 @@ def _bwd(**kw):
     (dict(B=0), 1, "must be positive"),
     (dict(N=-5), 1, "must be positive"),
     (dict(d=96), 2, "head dimension"),
-    (dict(d=128, dtype=1), 2, "head dimension"),
-    (dict(d=32, dtype=1), 2, "head dimension"),
+    (dict(d=96, dtype=1), 2, "head dimension"),
+    (dict(d=256, dtype=1), 2, "head dimension"),
     (dict(scale=0.0), 1, "scale"),
     (dict(scale=float("nan")), 1, "scale"),
     (dict(dtype=7), 1, "dtype"),
@@ -115,7 +115,7 @@ def test_fwd_rejects_bad_arguments(kw, status, msg):
     (dict(do=A + 4), 1, "dout is not 16-byte aligned"),
     (dict(dtype=1, sdv=bnd.fa_strides(64, 64, 66)), 1, "multiples of 4"),
     (dict(d=96), 2, "head dimension"),
-    (dict(d=32, dtype=1), 2, "head dimension"),
+    (dict(d=96, dtype=1), 2, "head dimension"),
     (dict(ws=None, wsb=0), 1, "workspace is NULL"),
     (dict(wsb=4095), 1, "workspace too small"),
     (dict(ws=A + 8), 1, "workspace is not 16-byte aligned"),
@@ -163,7 +163,7 @@ def test_bwd_dq_rejects_bad_arguments(kw, status, msg):
     (dict(o=None), 1, "o is NULL"),
     (dict(do=None), 1, "dout is NULL"),
     (dict(d=96), 2, "head dimension"),
-    (dict(d=128, dtype=1), 2, "head dimension"),
+    (dict(d=256, dtype=1), 2, "head dimension"),
     (dict(wsb=1024), 1, "workspace too small"),
 ])
 def test_bwd_dkdv_rejects_bad_arguments(kw, status, msg):
@@ -211,8 +211,8 @@ BAD_DROPOUT = [
     (dict(p=0.999), 1, "rounds to dropping every pair"),
     (dict(p=0.1, q=None), 1, "q is NULL"),
     (dict(p=0.1, d=96), 2, "head dimension"),
-    (dict(p=0.1, d=32, dtype=1), 2, "head dimension"),
-    (dict(p=0.1, d=128, dtype=1), 2, "head dimension"),
+    (dict(p=0.1, d=96, dtype=1), 2, "head dimension"),
+    (dict(p=0.1, d=256, dtype=1), 2, "head dimension"),
 ]
 
 

@@ -1,8 +1,8 @@
-"""GPU parity of the bf16 forward pass with head dimensions 32 and 128 (the
-kernel family is templated on d; d = 64 has its own tests) against the fp64
-oracle: edge lengths, causal, key lengths, tile masks, both layouts and
-separate query / key lengths, for the forward and the backward pass; dropout
-is built for d = 64 only."""
+"""GPU parity of attention with head dimensions 32 and 128, bf16 and fp32
+(both kernel families are templated on d; d = 64 has its own tests), against
+the fp64 oracle: edge lengths, causal, key lengths, tile masks, both layouts
+and separate query / key lengths, for the forward and the backward pass
+(dropout at these head dimensions is covered with the other dropout tests)."""
 import sys
 
 import numpy as np
@@ -27,62 +27,71 @@ def _check(case, tag, layout="bhsd"):
     o, lse = gpu_forward(case, q, k, v, sl, bm)
     O, L = ref.forward(case["q"], case["k"], case["v"], **oracle_args(case))
     eo, el = maxabs(to_np(o), O), maxabs(to_np(lse), L)
+    tol = TOL[case["dtype"]]
     assert np.array_equal(np.isinf(to_np(lse)), np.isinf(L)), "dead rows differ"
-    assert eo <= TOL["bf16"]["O"] and el <= TOL["bf16"]["L"], (eo, el)
+    assert eo <= tol["O"] and el <= tol["L"], (eo, el)
     _say(f"[headdim] {tag} ok O={eo:.2e} L={el:.2e}")
 
 
+DTYPES = ["bf16", "f32"]
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
 @pytest.mark.parametrize("d", [32, 128])
 @pytest.mark.parametrize("N", [1, 17, 63, 64, 65, 300, 1000])
 @pytest.mark.parametrize("causal", [False, True])
-def test_headdim_dense(d, N, causal):
-    case = wl.random_case(2, 3, N, d, seed=N + d + causal, causal=causal)
-    _check(case, f"d={d} N={N} causal={causal}")
+def test_headdim_dense(dtype, d, N, causal):
+    case = wl.random_case(2, 3, N, d, dtype=dtype, seed=N + d + causal, causal=causal)
+    _check(case, f"{dtype} d={d} N={N} causal={causal}")
 
 
+@pytest.mark.parametrize("dtype", DTYPES)
 @pytest.mark.parametrize("d", [32, 128])
 @pytest.mark.parametrize("masks", ["seqlens", "block", "both"])
-def test_headdim_masks(d, masks):
+def test_headdim_masks(dtype, d, masks):
     seqlens = "random" if masks in ("seqlens", "both") else None
     keep = 0.5 if masks in ("block", "both") else None
-    case = wl.random_case(3, 2, 700, d, seed=d, causal=True, seqlens=seqlens,
+    case = wl.random_case(3, 2, 700, d, dtype=dtype, seed=d, causal=True, seqlens=seqlens,
                           block_keep_p=keep)
-    _check(case, f"d={d} masks={masks}")
+    _check(case, f"{dtype} d={d} masks={masks}")
 
 
+@pytest.mark.parametrize("dtype", DTYPES)
 @pytest.mark.parametrize("d", [32, 128])
-def test_headdim_strided_layout(d):
-    case = wl.random_case(2, 4, 257, d, seed=3 * d, causal=True)
-    _check(case, f"d={d} bshd", layout="bshd")
+def test_headdim_strided_layout(dtype, d):
+    case = wl.random_case(2, 4, 257, d, dtype=dtype, seed=3 * d, causal=True)
+    _check(case, f"{dtype} d={d} bshd", layout="bshd")
 
 
+@pytest.mark.parametrize("dtype", DTYPES)
 @pytest.mark.parametrize("d", [32, 128])
 @pytest.mark.parametrize("Nq,Nk", [(1, 900), (200, 900), (900, 200)])
-def test_headdim_separate_lengths(d, Nq, Nk):
+def test_headdim_separate_lengths(dtype, d, Nq, Nk):
     import exact_io_aware_64_amd as fa
     rng = np.random.default_rng(Nq + Nk + d)
-    (q,) = wl.draw_tensors(rng, 2, 2, Nq, d, "bf16", count=1)
-    k, v = wl.draw_tensors(rng, 2, 2, Nk, d, "bf16", count=2)
-    _say(f"[headdim] d={d} Nq={Nq} Nk={Nk}")
-    o, lse = fa.forward(to_dev(q, "bf16"), to_dev(k, "bf16"), to_dev(v, "bf16"),
+    (q,) = wl.draw_tensors(rng, 2, 2, Nq, d, dtype, count=1)
+    k, v = wl.draw_tensors(rng, 2, 2, Nk, d, dtype, count=2)
+    _say(f"[headdim] {dtype} d={d} Nq={Nq} Nk={Nk}")
+    o, lse = fa.forward(to_dev(q, dtype), to_dev(k, dtype), to_dev(v, dtype),
                         scale=d ** -0.5, causal=True)
     O, L = ref.forward(q, k, v, d ** -0.5, causal=True)
     eo, el = maxabs(to_np(o), O), maxabs(to_np(lse), L)
-    assert eo <= TOL["bf16"]["O"] and el <= TOL["bf16"]["L"], (eo, el)
+    assert eo <= TOL[dtype]["O"] and el <= TOL[dtype]["L"], (eo, el)
 
 
+@pytest.mark.parametrize("dtype", DTYPES)
 @pytest.mark.parametrize("d", [32, 128])
-def test_headdim_full_size(d):
+def test_headdim_full_size(dtype, d):
     """B=4, H=16, N=2048 causal (a 7B-model-like attention shape for d=128)."""
-    case = wl.random_case(4, 16, 2048, d, seed=99 + d, causal=True)
+    case = wl.random_case(4, 16, 2048, d, dtype=dtype, seed=99 + d, causal=True)
     rows = wl.sample_rows(np.random.default_rng(d), 4, 16, 2048, 256)
-    _say(f"[headdim] full size d={d}")
+    _say(f"[headdim] full size {dtype} d={d}")
     q, k, v, _, sl, bm = device_inputs(case)
     o, lse = gpu_forward(case, q, k, v, sl, bm)
     O, L = ref.forward(case["q"], case["k"], case["v"], rows=rows, **oracle_args(case))
     idx = (np.arange(4)[:, None, None], np.arange(16)[None, :, None], rows)
     eo, el = maxabs(to_np(o)[idx], O), maxabs(to_np(lse)[idx], L)
-    assert eo <= TOL["bf16"]["O"] and el <= TOL["bf16"]["L"], (eo, el)
+    assert eo <= TOL[dtype]["O"] and el <= TOL[dtype]["L"], (eo, el)
 
 
 def _check_bwd(case, tag):
@@ -94,56 +103,61 @@ def _check_bwd(case, tag):
     g = ref.backward(case["q"], case["k"], case["v"], case["do"], **oracle_args(case))
     errs = {n: relfro(to_np(a), b) for n, a, b in zip(("dQ", "dK", "dV"), (dq, dk, dv), g)}
     for n, e in errs.items():
-        assert e <= TOL["bf16"]["G"], (n, errs)
+        assert e <= TOL[case["dtype"]]["G"], (n, errs)
         assert np.all(np.isfinite(to_np(dict(dQ=dq, dK=dk, dV=dv)[n])))
     _say(f"[headdim bwd] {tag} ok {errs}")
 
 
+@pytest.mark.parametrize("dtype", DTYPES)
 @pytest.mark.parametrize("d", [32, 128])
 @pytest.mark.parametrize("N", [1, 17, 64, 65, 300, 1000])
 @pytest.mark.parametrize("causal", [False, True])
-def test_headdim_backward_dense(d, N, causal):
-    _check_bwd(wl.random_case(2, 2, N, d, seed=N + d + 5 * causal, causal=causal),
-               f"d={d} N={N} causal={causal}")
+def test_headdim_backward_dense(dtype, d, N, causal):
+    _check_bwd(wl.random_case(2, 2, N, d, dtype=dtype, seed=N + d + 5 * causal, causal=causal),
+               f"{dtype} d={d} N={N} causal={causal}")
 
 
+@pytest.mark.parametrize("dtype", DTYPES)
 @pytest.mark.parametrize("d", [32, 128])
 @pytest.mark.parametrize("masks", ["seqlens", "block", "both"])
-def test_headdim_backward_masks(d, masks):
+def test_headdim_backward_masks(dtype, d, masks):
     seqlens = "random" if masks in ("seqlens", "both") else None
     keep = 0.5 if masks in ("block", "both") else None
-    _check_bwd(wl.random_case(3, 2, 700, d, seed=d + 1, causal=True, seqlens=seqlens,
-                              block_keep_p=keep), f"d={d} masks={masks}")
+    _check_bwd(wl.random_case(3, 2, 700, d, dtype=dtype, seed=d + 1, causal=True,
+                              seqlens=seqlens, block_keep_p=keep),
+               f"{dtype} d={d} masks={masks}")
 
 
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("d", [32, 128])
+def test_headdim_backward_strided_layout(dtype, d):
+    from tests.gpu_util import gpu_backward, relfro
+    case = wl.random_case(2, 3, 257, d, dtype=dtype, seed=7 * d, causal=True)
+    _say(f"[headdim bwd] {dtype} d={d} bshd")
+    q, k, v, do, sl, bm = device_inputs(case, layout="bshd")
+    o, lse = gpu_forward(case, q, k, v, sl, bm)
+    grads = gpu_backward(case, q, k, v, o, do, lse, sl, bm)
+    g = ref.backward(case["q"], case["k"], case["v"], case["do"], **oracle_args(case))
+    for name, a, b in zip(("dQ", "dK", "dV"), grads, g):
+        assert relfro(to_np(a), b) <= TOL[dtype]["G"], name
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
 @pytest.mark.parametrize("d", [32, 128])
 @pytest.mark.parametrize("Nq,Nk", [(200, 900), (900, 200)])
-def test_headdim_backward_separate_lengths(d, Nq, Nk):
+def test_headdim_backward_separate_lengths(dtype, d, Nq, Nk):
     from tests.gpu_util import relfro
     import exact_io_aware_64_amd as fa
     rng = np.random.default_rng(Nq * 3 + Nk + d)
-    q, do = wl.draw_tensors(rng, 2, 2, Nq, d, "bf16", count=2)
-    k, v = wl.draw_tensors(rng, 2, 2, Nk, d, "bf16", count=2)
-    _say(f"[headdim bwd] d={d} Nq={Nq} Nk={Nk}")
-    tq, tk, tv, tdo = (to_dev(x, "bf16") for x in (q, k, v, do))
+    q, do = wl.draw_tensors(rng, 2, 2, Nq, d, dtype, count=2)
+    k, v = wl.draw_tensors(rng, 2, 2, Nk, d, dtype, count=2)
+    _say(f"[headdim bwd] {dtype} d={d} Nq={Nq} Nk={Nk}")
+    tq, tk, tv, tdo = (to_dev(x, dtype) for x in (q, k, v, do))
     o, lse = fa.forward(tq, tk, tv, scale=d ** -0.5, causal=True)
     grads = fa.backward(tq, tk, tv, o, tdo, lse, scale=d ** -0.5, causal=True)
     g = ref.backward(q, k, v, do, d ** -0.5, causal=True)
     for name, a, b in zip(("dQ", "dK", "dV"), grads, g):
-        assert relfro(to_np(a), b) <= TOL["bf16"]["G"], name
-
-
-@pytest.mark.parametrize("d", [32, 128])
-def test_fp32_other_head_dims_are_rejected(d):
-    # the fp32 kernels are built for d = 64 (bf16 takes 32, 64 and 128, with
-    # or without dropout)
-    import exact_io_aware_64_amd as fa
-    case = wl.random_case(1, 1, 64, d, dtype="f32", seed=1)
-    q, k, v, do, _, _ = device_inputs(case)
-    with pytest.raises(fa.FaError, match="head dimension"):
-        fa.forward(q, k, v, scale=0.1, dropout_p=0.1, seed=1)
-    with pytest.raises(fa.FaError, match="head dimension"):
-        fa.forward(q, k, v, scale=0.1)
+        assert relfro(to_np(a), b) <= TOL[dtype]["G"], name
 
 
 def test_d128_workload_sampled():
