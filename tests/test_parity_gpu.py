@@ -81,7 +81,8 @@ def _sampled_inputs(name):
 
 @pytest.mark.parametrize("name", ["long_causal_b1h16n16384", "blocksparse_b1h8n65536",
                                   "prefill_causal_b1h16q2048k16384",
-                                  "train_causal_b2h16n4096d128"])
+                                  "train_causal_b2h16n4096d128",
+                                  "train_causal_f32_b2h16n4096d128"])
 def test_sampled_workload(name):
     """Full-size run checked on sampled query rows (O, L, dQ exact per row),
     a second backward with dO zeroed outside the sample (dK, dV exact for that
@@ -89,7 +90,7 @@ def test_sampled_workload(name):
     import torch
     _say(f"[parity] {name} sampled")
     case = _sampled_inputs(name)
-    tol = TOL["bf16"]
+    tol = TOL[case["dtype"]]
     rows = case["rows"]
     B, H, N, d = case["q"].shape
     q, k, v, do, sl, bm = device_inputs(case)
@@ -121,7 +122,7 @@ def test_sampled_workload(name):
     for b in range(B):
         for h in range(H):
             do_r[b, h, rows[b, h]] = case["do"][b, h, rows[b, h]]
-    dor = to_dev(do_r, "bf16")
+    dor = to_dev(do_r, case["dtype"])
     _, dk_r, dv_r = gpu_backward(case, q, k, v, o, dor, lse, sl, bm)
     ek = relfro(to_np(dk_r), gk)
     ev = relfro(to_np(dv_r), gv)

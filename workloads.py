@@ -74,6 +74,10 @@ WORKLOADS = {
         Workload("train_causal_b2h16n4096d128", 2, 16, 4096, 128, "bf16", True, 128 ** -0.5, 9,
                  sample_rows=256,
                  summary="causal attention with head dimension 128, forward and backward, bf16"),
+        Workload("train_causal_f32_b2h16n4096d128", 2, 16, 4096, 128, "f32", True,
+                 128 ** -0.5, 10, sample_rows=256,
+                 summary="causal attention with head dimension 128, forward and backward, "
+                         "fp32"),
         Workload("prefill_causal_b1h16q2048k16384", 1, 16, 2048, 64, "bf16", True, 1 / 8, 7,
                  std=0.5, sample_rows=512, Nk=16384,
                  summary="chunked prefill: 2048 new queries over 16384 keys (14336 cached), "
