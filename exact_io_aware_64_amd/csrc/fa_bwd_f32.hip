@@ -391,9 +391,12 @@ hipError_t launch_bwd_f32(const BwdArgs& a, bool causal, int phases, int d, hipS
   BwdArgs copy = a;
   int cz = causal ? 1 : 0;
   void* args[] = {&copy, &cz};
-  return d == 32   ? launch_bwd_f32_d<32>(args, a, phases, stream)
-         : d == 64 ? launch_bwd_f32_d<64>(args, a, phases, stream)
-                   : launch_bwd_f32_d<128>(args, a, phases, stream);
+  switch (d) {
+    case 32: return launch_bwd_f32_d<32>(args, a, phases, stream);
+    case 64: return launch_bwd_f32_d<64>(args, a, phases, stream);
+    case 128: return launch_bwd_f32_d<128>(args, a, phases, stream);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 }  // namespace fa

@@ -194,7 +194,11 @@ hipError_t launch_fwd_f32(const FwdArgs& a, bool causal, int d, hipStream_t stre
   void* args[] = {&copy, &cz};
   dim3 grid((unsigned)(((a.N + kBR - 1) / kBR) * a.B * a.H)), block(64 * kW);
   const bool drop = a.drop.t < 256;
-  const void* fn = d == 32 ? fwd_f32_fn<32>(drop) : d == 64 ? fwd_f32_fn<64>(drop) : fwd_f32_fn<128>(drop);
+  const void* fn = d == 32    ? fwd_f32_fn<32>(drop)
+                   : d == 64  ? fwd_f32_fn<64>(drop)
+                   : d == 128 ? fwd_f32_fn<128>(drop)
+                              : nullptr;
+  if (fn == nullptr) return hipErrorInvalidValue;
   return hipLaunchKernel(fn, grid, block, args, 0, stream);
 }
 

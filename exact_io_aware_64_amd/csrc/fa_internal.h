@@ -78,7 +78,7 @@ constexpr int kPhaseDQ = 1;
 constexpr int kPhaseDKDV = 2;
 
 // block_q: query rows per workgroup, 64, 128 or 256 (128 with dropout);
-// d: head dimension, 32, 64 or 128 (64 with dropout or block_q != 128).
+// d: head dimension, 32, 64 or 128 (64 when block_q != 128).
 hipError_t launch_fwd_bf16(const FwdArgs& a, bool causal, int block_q, int d,
                            hipStream_t stream);
 // Wave groups per query tile that launch_fwd_bf16 splits the key range over
@@ -89,13 +89,15 @@ int fwd_key_groups(int B, int H, int N, int Nk, int d, int block_q);
 inline size_t bwd_workspace_bytes(int B, int H, int N) {
   return (((size_t)B * H * N * 4) + 255) & ~(size_t)255;
 }
-// d: head dimension, 32, 64 or 128 (64 with dropout).  a.dsum must hold
+// d: head dimension, 32, 64 or 128.  a.dsum must hold
 // bwd_workspace_bytes(B, H, N) bytes.
 hipError_t launch_bwd_bf16(const BwdArgs& a, bool causal, int phases, int d,
                            hipStream_t stream);
 // The d = 128 instantiation of the above, from its own translation unit.
 hipError_t launch_bwd_bf16_d128(const BwdArgs& a, bool causal, int phases,
                                 hipStream_t stream);
+// The fp32 kernels: 128 query (key) rows per workgroup, d = 32, 64 or 128
+// (hipErrorInvalidValue otherwise); no workspace, each kernel forms D itself.
 hipError_t launch_fwd_f32(const FwdArgs& a, bool causal, int d, hipStream_t stream);
 hipError_t launch_bwd_f32(const BwdArgs& a, bool causal, int phases, int d, hipStream_t stream);
 
