@@ -19,10 +19,10 @@ def _say(msg):
     sys.stdout.flush()
 
 
-def _case(B, H, Nq, Nk, dtype="bf16", seed=0, seqlens=None, block_p=None, mask_block=128):
+def _case(B, H, Nq, Nk, dtype="bf16", seed=0, seqlens=None, block_p=None, mask_block=128, d=64):
     rng = np.random.default_rng(seed)
-    q, do = wl.draw_tensors(rng, B, H, Nq, 64, dtype, count=2)
-    k, v = wl.draw_tensors(rng, B, H, Nk, 64, dtype, count=2)
+    q, do = wl.draw_tensors(rng, B, H, Nq, d, dtype, count=2)
+    k, v = wl.draw_tensors(rng, B, H, Nk, d, dtype, count=2)
     sl = None
     if seqlens == "random":
         sl = rng.integers(0, Nk + 1, size=B).astype(np.int32)
@@ -99,6 +99,15 @@ def test_qk_f32(Nq, Nk, causal):
 def test_qk_dropout(Nq, Nk):
     _check(_case(2, 2, Nq, Nk, seed=11), True, f"dropout Nq={Nq} Nk={Nk}", p=0.2, seed=77,
            offset=2)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("d", [32, 64, 128])
+@pytest.mark.parametrize("Nq,Nk", [(100, 900), (900, 100)])
+def test_qk_dropout_key_lengths_head_dims(dtype, d, Nq, Nk):
+    c = _case(2, 2, Nq, Nk, dtype=dtype, seed=13 + d, seqlens="random", d=d)
+    _check(c, True, f"dropout {dtype} d={d} Nq={Nq} Nk={Nk} key lengths", p=0.2, seed=78,
+           offset=3)
 
 
 def test_qk_decode_long_cache():
