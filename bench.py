@@ -147,11 +147,14 @@ def measure_key(workload: str, dropout_p: float) -> str:
 
 def run_gpu(w: wl.Workload, inp: dict, steps: int, warmup: int, prewarm_s: float = 1.0,
             dropout_p: float = 0.0, cold_reps: int = 0, event_reps: int = 50,
-            restricted_rerun: bool = True):
+            restricted_rerun: bool = True, graph: bool = False):
     """Times `steps` steps after `warmup` untimed ones.  One step is fa_fwd
     then fa_bwd (fa_fwd alone for a forward-only workload), each a single
     kernel launch on the current stream; the wall clock around the timed
-    steps (synchronised on both sides) gives the step time.
+    steps (synchronised on both sides) gives the step time.  With `graph`
+    the step's calls are recorded once into a HIP graph (captured on a side
+    stream) and every prewarm, warmup and timed step is one replay of it:
+    the host then submits one graph instead of each call's launches.
 
     Before the warmup steps the step runs untimed for `prewarm_s` seconds of
     wall time: an idle MI355X takes a few milliseconds of sustained load to
@@ -200,18 +203,37 @@ def run_gpu(w: wl.Workload, inp: dict, steps: int, warmup: int, prewarm_s: float
             if ev is not None:
                 ev[2].record(stream)
 
+    timed_step = step
+    if graph:
+        side = torch.cuda.Stream(device=dev)
+        fwd_s = fa.prepare_fwd(q, k, v, o, lse, stream=side.cuda_stream, **kw)
+        bwd_s = (fa.prepare_bwd(q, k, v, o, do, lse, dq, dk, dv, stream=side.cuda_stream, **kw)
+                 if w.backward else None)
+        torch.cuda.synchronize()
+        with torch.cuda.stream(side):  # first calls outside the capture
+            fwd_s()
+            if bwd_s is not None:
+                bwd_s()
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=side):
+            fwd_s()
+            if bwd_s is not None:
+                bwd_s()
+        timed_step = g.replay
+
     torch.cuda.synchronize()
     t_end = time.perf_counter() + prewarm_s
     while time.perf_counter() < t_end:
         for _ in range(8):
-            step()
+            timed_step()
         torch.cuda.synchronize()
     for _ in range(warmup):
-        step()
+        timed_step()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(steps):
-        step()
+        timed_step()
     torch.cuda.synchronize()
     wall_ms = (time.perf_counter() - t0) * 1e3 / steps
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(kernels) + 1)]
@@ -988,6 +1010,8 @@ def main(argv=None):
                     help="drop probability on P (fa_fwd_dropout / fa_bwd_dropout); the FLOP "
                          "count is the same as without dropout")
     ap.add_argument("--cpu-baseline", default="on", choices=["on", "off"])
+    ap.add_argument("--graph", action="store_true",
+                    help="time the steps as replays of one HIP graph holding the step's calls")
     ap.add_argument("--event-reps", type=int, default=50,
                     help="steps after the timed ones whose launches are bracketed by HIP "
                          "events (per-kernel device time)")
@@ -1086,7 +1110,7 @@ def main(argv=None):
 
     wall_ms, kernel_ms, median_ms, cold_ms, props, outs = run_gpu(
         w, inp, args.steps, args.warmup, args.prewarm_s, args.dropout, args.cold_reps,
-        args.event_reps, restricted_rerun=args.cpu_baseline == "on")
+        args.event_reps, restricted_rerun=args.cpu_baseline == "on", graph=args.graph)
     import exact_io_aware_64_amd as fa
     key_groups = fa.fa_fwd_key_groups(fa.FA_BF16 if w.dtype == "bf16" else fa.FA_F32, w.B, w.H,
                                       w.N, w.n_keys, w.d, 128)
@@ -1143,7 +1167,8 @@ def main(argv=None):
                    "causal": w.causal, "key_padding": inp["seqlens"] is not None,
                    "block_sparse": inp["block_mask"] is not None, "pairs": pairs,
                    "dropout_p": args.dropout, "step": "fwd+bwd" if w.backward else "fwd",
-                   "fwd_key_groups": key_groups},
+                   "fwd_key_groups": key_groups,
+                   "step_launch": "hip graph" if args.graph else "eager"},
         "fwd_tflops": tf_f,
         "bwd_tflops": tf_b,
         "fwd_ms": fwd_ms,
