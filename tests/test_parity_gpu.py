@@ -178,51 +178,60 @@ def test_f32_edge_lengths(N, causal):
     check_full(case, tag=f"f32 N={N} causal={causal}")
 
 
+@pytest.mark.parametrize("d", [32, 64, 128])
 @pytest.mark.parametrize("mask_block", [256, 384])
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("causal", [False, True])
-def test_larger_mask_blocks(mask_block, dtype, causal):
+def test_larger_mask_blocks(mask_block, dtype, causal, d):
     """Tile masks over 256 and 384 rows (each mask entry covers several of
     the kernels' 64- and 128-row tiles), with key lengths, forward and
     backward."""
-    case = wl.random_case(2, 2, 1000, 64, dtype=dtype, seed=mask_block + 7 * causal,
+    case = wl.random_case(2, 2, 1000, d, dtype=dtype, seed=mask_block + 7 * causal + d,
                           causal=causal, seqlens="random", block_keep_p=0.6,
                           mask_block=mask_block)
-    check_full(case, tag=f"{dtype} mask_block={mask_block} causal={causal}")
+    check_full(case, tag=f"{dtype} d={d} mask_block={mask_block} causal={causal}")
 
 
+@pytest.mark.parametrize("d", [32, 64, 128])
 @pytest.mark.parametrize("scale", [0.03, 0.4])
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
-def test_other_scales(scale, dtype):
+def test_other_scales(scale, dtype, d):
     """Softmax scales other than 1/sqrt(d): nearly flat (0.03) and sharp (0.4)
     distributions, causal with key lengths, forward and backward.  A sharp
     softmax puts rows on one or a few keys, |O| up to the largest |v| (> 4),
     where half an ulp of the stored bf16 value exceeds a flat 1e-2: O is
     held to 1e-2 + 2^-8 |O*| there, as for dropout and N_q != N_k."""
-    case = wl.random_case(2, 2, 500, 64, dtype=dtype, seed=int(scale * 100), causal=True,
+    case = wl.random_case(2, 2, 500, d, dtype=dtype, seed=int(scale * 100) + d, causal=True,
                           seqlens="random", scale=scale)
-    check_full(case, tag=f"{dtype} scale={scale}", o_rel=2.0 ** -8 if dtype == "bf16" else 0.0)
+    check_full(case, tag=f"{dtype} d={d} scale={scale}",
+               o_rel=2.0 ** -8 if dtype == "bf16" else 0.0)
 
 
-def test_key_lengths_zero_and_full():
+@pytest.mark.parametrize("d", [32, 64, 128])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_key_lengths_zero_and_full(dtype, d):
     """len 0 (every row fully masked: O = 0, L = -inf, zero gradients), len 1
     and len N in one batch."""
-    case = wl.random_case(3, 2, 200, 64, seed=9, seqlens=[0, 1, 200])
-    check_full(case, tag="seqlens 0/1/N")
+    case = wl.random_case(3, 2, 200, d, dtype=dtype, seed=9, seqlens=[0, 1, 200])
+    check_full(case, tag=f"{dtype} d={d} seqlens 0/1/N")
 
 
-def test_empty_block_mask_rows():
+@pytest.mark.parametrize("d", [32, 64, 128])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_empty_block_mask_rows(dtype, d):
     rng = np.random.default_rng(4)
-    case = wl.random_case(1, 2, 512, 64, seed=4)
+    case = wl.random_case(1, 2, 512, d, dtype=dtype, seed=4)
     bm = (rng.random((4, 4)) < 0.5).astype(np.uint8)
     bm[1, :] = 0      # query tile 1 sees nothing
     bm[:, 3] = 0      # key tile 3 is seen by nobody (zero dK, dV)
     case["block_mask"] = bm
-    check_full(case, tag="empty mask row/column")
+    check_full(case, tag=f"{dtype} d={d} empty mask row/column")
 
 
-def test_block_mask_all_ones_equals_dense():
-    case = wl.random_case(1, 2, 384, 64, seed=8, causal=True)
+@pytest.mark.parametrize("d", [32, 64, 128])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_block_mask_all_ones_equals_dense(dtype, d):
+    case = wl.random_case(1, 2, 384, d, dtype=dtype, seed=8, causal=True)
     q, k, v, do, _, _ = device_inputs(case)
     o1, l1 = gpu_forward(case, q, k, v, None, None)
     ones = opt_dev(np.ones((3, 3), np.uint8))
