@@ -288,17 +288,19 @@ def test_sampled_full_size_gpt2_with_dropout():
         assert errs[name] <= tol["G"], (name, errs)
 
 
-def test_sampled_full_size_d128_training_with_dropout():
-    """Causal training shape with head dimension 128 (B=2, H=16, N=4096, bf16)
-    with p = 0.1: O, L and dQ on 128 sampled rows per head; dK, dV of the
-    problem whose dO is zero outside the sample."""
+@pytest.mark.parametrize("name", ["train_causal_b2h16n4096d128",
+                                  "train_causal_f32_b2h16n4096d128"])
+def test_sampled_full_size_d128_training_with_dropout(name):
+    """Causal training shape with head dimension 128 (B=2, H=16, N=4096, bf16
+    and fp32) with p = 0.1: O, L and dQ on 128 sampled rows per head; dK, dV
+    of the problem whose dO is zero outside the sample."""
     fa = _fa()
-    w = wl.WORKLOADS["train_causal_b2h16n4096d128"]
+    w = wl.WORKLOADS[name]
     case = wl.make_inputs(w)
     rows = case["rows"][:, :, :128]
     p, seed, offset = 0.1, 2024, 0
-    _say("[dropout sampled] train_causal_b2h16n4096d128 p=0.1")
-    q, k, v, do, _, _ = device_inputs(dict(case, dtype="bf16"))
+    _say(f"[dropout sampled] {name} p=0.1")
+    q, k, v, do, _, _ = device_inputs(case)
     kw = dict(scale=w.scale, causal=True, dropout_p=p, seed=seed, offset=offset)
     o, lse = fa.forward(q, k, v, **kw)
     dq, _, _ = fa.backward(q, k, v, o, do, lse, **kw)
@@ -313,12 +315,13 @@ def test_sampled_full_size_d128_training_with_dropout():
     idx = (np.arange(w.B)[:, None, None], np.arange(w.H)[None, :, None], rows)
     errs = dict(O=maxabs(to_np(o)[idx], O), L=maxabs(to_np(lse)[idx], L),
                 dQ=relfro(to_np(dq)[idx], gq))
-    _, dk_r, dv_r = fa.backward(q, k, v, o, to_dev(do_r, "bf16"), lse, **kw)
+    _, dk_r, dv_r = fa.backward(q, k, v, o, to_dev(do_r, w.dtype), lse, **kw)
     errs["dK"] = relfro(to_np(dk_r), gk)
     errs["dV"] = relfro(to_np(dv_r), gv)
     _say(f"[dropout sampled d128] {errs}")
-    tol = TOL["bf16"]
-    assert excess_over(to_np(o)[idx], O, tol["O"] * _keep_scale(p)) <= 0, errs
+    tol = TOL[w.dtype]
+    rel = 2.0 ** -8 if w.dtype == "bf16" else 2.0 ** -24
+    assert excess_over(to_np(o)[idx], O, tol["O"] * _keep_scale(p), rel) <= 0, errs
     assert errs["L"] <= tol["L"], errs
     for name in ("dQ", "dK", "dV"):
         assert errs[name] <= tol["G"], (name, errs)
